@@ -1,0 +1,344 @@
+"""fp64 CPU oracle for retained-mass block-sparse self-attention (LoSA).
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library never
+calls it and shares no code, tables or constants with it; the two meet only
+in the seeded input generator (``synthetic``), which holds no arithmetic of
+the method.
+
+Every function restates a definition from page 1, "LoSA: Near-Lossless
+Sparse Attention for Training-Free Video Diffusion Acceleration":
+
+* Motivation Summary -- dense attention A = softmax(Q K^T / sqrt(d)) per head;
+  block attention mass M(i, j) = sum over the query block's rows and the key
+  block's columns of A; Recall and Coverage of a block pattern.
+* Methodology Summary, one-time pattern construction -- per head and query
+  block, sort key blocks by decreasing mass and keep the shortest prefix whose
+  cumulative mass reaches theta times the block's total mass.
+* Methodology Summary, sparse attention with a frozen pattern -- softmax over
+  the retained keys only (discarded keys leave the denominator), no forced
+  local or diagonal blocks.
+
+Readings taken where the page is silent (each is also listed with the design
+notes of the repository):
+
+* Tokens at or beyond N (padding up to a whole number of blocks) are not
+  tokens: they are masked out of every softmax and mass, rows beyond N are not
+  queries (their output is 0) and are excluded from the block average.
+* M is stored as the row mean (the page's M divided by the number of valid
+  rows of the query block), so each row of blocks sums to 1.  The selection is
+  unchanged because the target scales with the total.
+* Selection target: p times the *computed* row total.  Ties in mass: lower
+  block index first.  p = 1 keeps every block.  Non-finite or negative masses
+  count as 0.
+* Cumulative-sum arithmetic ("contract rule"): the page's cumulative sum is
+  evaluated exactly in integers so any summation order gives one answer:
+  e = exponent of the row maximum (max = f * 2^e, f in [1/2, 1)),
+  q_j = ceil(m_j * 2^(51 - e)) (an exact power-of-two scaling, so every
+  positive mass is at least one unit), P = floor(p * 2^32 + 1/2),
+  T = ceil(P * sum_j q_j / 2^32), s = the least prefix length whose integer
+  sum is >= T.  A plain fp64 argsort + cumsum is kept beside it as a cross-check.
+* Output lists are CSR with ascending block indices per row; the work order
+  lists rows by kept-block count, descending, ties by row index ascending.
+
+Row numbering: row r = (b * H + h) * n_q + i for batch b, head h, query block i.
+Inputs are fp64 arrays [B, H, N_alloc, d] holding the exact values the GPU sees.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "softmax_scale",
+    "attention_probs",
+    "dense_attention",
+    "block_mass",
+    "block_mass_rows",
+    "sanitize_masses",
+    "select_contract",
+    "select_contract_row",
+    "select_float_row",
+    "select_float",
+    "p_fixed",
+    "sparse_attention",
+    "sparse_attention_rows",
+    "budget_order",
+    "recall",
+    "coverage",
+    "row_id",
+    "row_split",
+]
+
+
+def softmax_scale(head_dim: int, scale: Optional[float] = None) -> float:
+    """1/sqrt(d) (Motivation Summary: A = softmax(Q K^T / sqrt(d)))."""
+    return 1.0 / math.sqrt(head_dim) if scale is None or scale <= 0 else float(scale)
+
+
+def row_id(b: int, h: int, i: int, heads: int, n_q: int) -> int:
+    return (b * heads + h) * n_q + i
+
+
+def row_split(r: int, heads: int, n_q: int) -> Tuple[int, int, int]:
+    bh, i = divmod(r, n_q)
+    b, h = divmod(bh, heads)
+    return b, h, i
+
+
+def attention_probs(q_rows: np.ndarray, k_keys: np.ndarray, scale: float) -> np.ndarray:
+    """Row softmax of q_rows k_keys^T * scale over the given keys (fp64)."""
+    s = (q_rows @ k_keys.T) * scale
+    s -= s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_valid: int,
+                    scale: Optional[float] = None, chunk: int = 1024) -> np.ndarray:
+    """Dense self-attention O = softmax(Q K^T * scale) V over the N valid keys.
+
+    Motivation Summary (definition of A).  Rows >= N are written as 0.
+    """
+    B, H, Na, d = q.shape
+    sc = softmax_scale(d, scale)
+    out = np.zeros((B, H, Na, v.shape[-1]), np.float64)
+    for b in range(B):
+        for h in range(H):
+            kk, vv = k[b, h, :n_valid], v[b, h, :n_valid]
+            for r0 in range(0, n_valid, chunk):
+                r1 = min(n_valid, r0 + chunk)
+                a = attention_probs(q[b, h, r0:r1], kk, sc)
+                out[b, h, r0:r1] = a @ vv
+    return out
+
+
+def _block_sums(a: np.ndarray, n_valid: int, C: int, n_k: int) -> np.ndarray:
+    """Sum columns of a [rows, n_valid] into key blocks of C tokens -> [rows, n_k]."""
+    rows = a.shape[0]
+    pad = np.zeros((rows, n_k * C), np.float64)
+    pad[:, :n_valid] = a
+    return pad.reshape(rows, n_k, C).sum(axis=2)
+
+
+def block_mass_rows(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
+                    rows: Iterable[Tuple[int, int, int]], scale: Optional[float] = None) -> np.ndarray:
+    """Block masses for the listed (b, h, i) query blocks only -> [len(rows), n_k].
+
+    M(i, j) = mean over valid query rows q of block i of the sum over valid
+    keys k of block j of A(q, k)  (Motivation Summary, block attention mass;
+    row-mean form).
+    """
+    d = q.shape[-1]
+    sc = softmax_scale(d, scale)
+    n_k = -(-n_valid // C)
+    rows = list(rows)
+    out = np.zeros((len(rows), n_k), np.float64)
+    for t, (b, h, i) in enumerate(rows):
+        r0, r1 = i * R, min((i + 1) * R, n_valid)
+        if r1 <= r0:
+            continue
+        a = attention_probs(q[b, h, r0:r1], k[b, h, :n_valid], sc)
+        out[t] = _block_sums(a, n_valid, C, n_k).mean(axis=0)
+    return out
+
+
+def block_mass(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
+               scale: Optional[float] = None) -> np.ndarray:
+    """All block masses M [B, H, n_q, n_k] (fp64, row-mean form)."""
+    B, H = q.shape[:2]
+    n_q = -(-n_valid // R)
+    n_k = -(-n_valid // C)
+    M = np.zeros((B, H, n_q, n_k), np.float64)
+    for b in range(B):
+        for h in range(H):
+            M[b, h] = block_mass_rows(q, k, n_valid, R, C, [(b, h, i) for i in range(n_q)], scale)
+    return M
+
+
+def sanitize_masses(m: np.ndarray) -> np.ndarray:
+    """Non-finite, negative and negative-zero masses count as 0 (fp32 in, fp32 out)."""
+    m = np.asarray(m, dtype=np.float32)
+    good = np.isfinite(m) & (m > 0)
+    return np.where(good, m, np.float32(0.0)).astype(np.float32)
+
+
+def p_fixed(p: float) -> int:
+    """p as a 32-bit fixed-point fraction: floor(p * 2^32 + 1/2), p in (0, 1]."""
+    if not (0.0 < p <= 1.0):
+        raise ValueError("p must lie in (0, 1]")
+    return int(math.floor(p * 4294967296.0 + 0.5))
+
+
+def _fixed_point_units(m32: np.ndarray) -> np.ndarray:
+    """q_j = ceil(m_j * 2^(51 - e)), e = frexp exponent of the row maximum.
+
+    m_j is fp32, so m_j * 2^(51-e) is exact in fp64 (a power-of-two scaling of
+    a 24-bit significand) and below 2^51; ceil and the cast to uint64 are exact.
+    """
+    mx = float(m32.max()) if m32.size else 0.0
+    if mx <= 0.0:
+        return np.zeros(m32.shape, np.uint64)
+    e = math.frexp(mx)[1]
+    scaled = np.ldexp(m32.astype(np.float64), 51 - e)
+    return np.ceil(scaled).astype(np.uint64)
+
+
+def select_contract_row(m32: np.ndarray, p: float) -> Tuple[np.ndarray, int]:
+    """One row of the one-time pattern construction under the contract rule.
+
+    Methodology Summary (one-time pattern construction): pi sorts key blocks
+    by decreasing mass (ties: lower index first), s = min m such that the
+    prefix mass reaches the target, omega = pi(1..s).  Returns the kept block
+    indices in ascending order and s.
+    """
+    m32 = sanitize_masses(m32)
+    n_k = m32.shape[0]
+    pi = np.argsort(-m32, kind="stable")  # mass descending, stable -> index ascending on ties
+    P = p_fixed(p)
+    if P == 1 << 32:
+        s = n_k
+    else:
+        units = _fixed_point_units(m32)
+        prefix = np.cumsum(units[pi], dtype=np.uint64)
+        total = int(prefix[-1])
+        T = -((-P * total) >> 32)  # ceil(P * total / 2^32), exact Python integers
+        s = int(np.argmax(prefix >= np.uint64(T))) + 1
+    return np.sort(pi[:s]), s
+
+
+def select_float_row(m: np.ndarray, p: float) -> Tuple[np.ndarray, int, float]:
+    """Plain fp64 cross-check: argsort + cumsum, target p * row total.
+
+    Returns (kept ascending, s, margin) where margin = cum(s) - target is how
+    far the deciding prefix lies from the target.
+    """
+    m64 = sanitize_masses(m).astype(np.float64)
+    n_k = m64.shape[0]
+    pi = np.argsort(-m64, kind="stable")
+    if p >= 1.0:
+        return np.sort(pi), n_k, math.inf
+    cum = np.cumsum(m64[pi])
+    target = p * cum[-1]
+    s = int(np.argmax(cum >= target)) + 1
+    margin = min(abs(cum[s - 1] - target), abs(cum[s - 2] - target) if s >= 2 else math.inf)
+    return np.sort(pi[:s]), s, margin
+
+
+def select_contract(M32: np.ndarray, p) -> Tuple[np.ndarray, np.ndarray]:
+    """CSR lists for every row of M32 [B, H, n_q, n_k] (fp32).
+
+    ``p`` is a scalar or one value per head.  Returns (row_ptr int64 [rows+1],
+    col_idx int32 [nnz]).
+    """
+    B, H, n_q, n_k = M32.shape
+    p_h = np.broadcast_to(np.asarray(p, dtype=np.float64), (H,))
+    counts = np.zeros(B * H * n_q, np.int64)
+    cols: List[np.ndarray] = []
+    for b in range(B):
+        for h in range(H):
+            for i in range(n_q):
+                kept, s = select_contract_row(M32[b, h, i], float(p_h[h]))
+                counts[row_id(b, h, i, H, n_q)] = s
+                cols.append(kept.astype(np.int32))
+    row_ptr = np.zeros(B * H * n_q + 1, np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    col_idx = np.concatenate(cols) if cols else np.zeros(0, np.int32)
+    return row_ptr, col_idx
+
+
+def select_float(M: np.ndarray, p) -> Tuple[np.ndarray, np.ndarray, List[Tuple[int, float]]]:
+    """fp64 argsort+cumsum selection of every row; also returns per-row margins."""
+    B, H, n_q, n_k = M.shape
+    p_h = np.broadcast_to(np.asarray(p, dtype=np.float64), (H,))
+    counts = np.zeros(B * H * n_q, np.int64)
+    cols, margins = [], []
+    for b in range(B):
+        for h in range(H):
+            for i in range(n_q):
+                kept, s, mg = select_float_row(M[b, h, i], float(p_h[h]))
+                r = row_id(b, h, i, H, n_q)
+                counts[r] = s
+                cols.append(kept.astype(np.int32))
+                margins.append((r, mg))
+    row_ptr = np.zeros(B * H * n_q + 1, np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    return row_ptr, np.concatenate(cols), margins
+
+
+def _kept_tokens(blocks: Sequence[int], C: int, n_valid: int) -> np.ndarray:
+    parts = [np.arange(j * C, min((j + 1) * C, n_valid)) for j in blocks]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+def sparse_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_valid: int,
+                          R: int, C: int, row_ptr: np.ndarray, col_idx: np.ndarray,
+                          rows: Iterable[Tuple[int, int, int]],
+                          scale: Optional[float] = None) -> List[np.ndarray]:
+    """Frozen-pattern sparse attention for the listed (b, h, i) query blocks.
+
+    Methodology Summary (sparse attention with a frozen pattern):
+    O(q) = sum over retained keys k of exp(q.k * scale) / (sum over retained
+    keys k' of exp(q.k' * scale)) * v_k, the retained keys being the valid
+    tokens of the kept blocks of q's query block.  Returns one [rows_i, d]
+    array per listed block (valid rows only); an empty list gives zeros.
+    """
+    B, H, Na, d = q.shape
+    sc = softmax_scale(d, scale)
+    n_q = -(-n_valid // R)
+    out = []
+    for (b, h, i) in rows:
+        r = row_id(b, h, i, H, n_q)
+        blocks = col_idx[int(row_ptr[r]):int(row_ptr[r + 1])]
+        r0, r1 = i * R, min((i + 1) * R, n_valid)
+        keys = _kept_tokens(blocks, C, n_valid)
+        if keys.size == 0 or r1 <= r0:
+            out.append(np.zeros((max(r1 - r0, 0), v.shape[-1]), np.float64))
+            continue
+        a = attention_probs(q[b, h, r0:r1], k[b, h, keys], sc)
+        out.append(a @ v[b, h, keys])
+    return out
+
+
+def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_valid: int,
+                     R: int, C: int, row_ptr: np.ndarray, col_idx: np.ndarray,
+                     scale: Optional[float] = None) -> np.ndarray:
+    """Frozen-pattern sparse attention for every row -> O [B, H, N_alloc, d] (0 beyond N)."""
+    B, H, Na, d = q.shape
+    n_q = -(-n_valid // R)
+    O = np.zeros((B, H, Na, v.shape[-1]), np.float64)
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(n_q)]
+    res = sparse_attention_rows(q, k, v, n_valid, R, C, row_ptr, col_idx, rows, scale)
+    for (b, h, i), o in zip(rows, res):
+        O[b, h, i * R:i * R + o.shape[0]] = o
+    return O
+
+
+def budget_order(row_ptr: np.ndarray) -> np.ndarray:
+    """Work order: rows by kept-block count descending, ties by row index ascending."""
+    counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
+    return np.argsort(-counts, kind="stable").astype(np.int64)
+
+
+def recall(M: np.ndarray, row_ptr: np.ndarray, col_idx: np.ndarray, n_valid: int, R: int) -> float:
+    """Recall(omega) = kept block mass / total block mass (Motivation Summary).
+
+    Uses the page's un-normalised mass, i.e. the row-mean M times the number
+    of valid query rows of each block.
+    """
+    B, H, n_q, n_k = M.shape
+    w = np.array([min(R, n_valid - i * R) for i in range(n_q)], np.float64)
+    Mw = M * w[None, None, :, None]
+    flat = Mw.reshape(B * H * n_q, n_k)
+    kept = 0.0
+    for r in range(flat.shape[0]):
+        kept += flat[r, col_idx[int(row_ptr[r]):int(row_ptr[r + 1])]].sum()
+    return float(kept / flat.sum())
+
+
+def coverage(row_ptr: np.ndarray, batch: int, heads: int, n_q: int, n_k: int) -> float:
+    """Coverage(omega) = (1/H) sum_h sum_i |omega_i^h| / (n_q n_k), averaged over batch."""
+    nnz = int(np.asarray(row_ptr)[-1])
+    return nnz / float(batch * heads * n_q * n_k)

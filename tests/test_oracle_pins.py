@@ -1,0 +1,321 @@
+"""Pins for the fp64 oracle: checks against what the LoSA page and the
+mathematics fix, independent of the oracle's own code paths.
+
+Page cited throughout: "LoSA: Near-Lossless Sparse Attention for
+Training-Free Video Diffusion Acceleration".
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_qkv(rng, B, H, Na, d, n_valid, scale_q=1.0):
+    q = rng.standard_normal((B, H, Na, d)) * scale_q
+    k = rng.standard_normal((B, H, Na, d))
+    v = rng.standard_normal((B, H, Na, d))
+    for t in (q, k, v):
+        t[:, :, n_valid:] = 0.0
+    return q, k, v
+
+
+# ---------------------------------------------------------------- dense attention
+
+@pytest.mark.parametrize("n_valid,Na", [(200, 256), (256, 256), (97, 128)])
+def test_dense_matches_library_sdpa(n_valid, Na):
+    """Motivation Summary: A = softmax(Q K^T / sqrt(d)); pinned to torch's SDPA (fp64, CPU)."""
+    rng = np.random.default_rng(1)
+    q, k, v = _rand_qkv(rng, 1, 2, Na, 32, n_valid, scale_q=2.0)
+    ours = O.dense_attention(q, k, v, n_valid)
+    mask = torch.zeros(Na, dtype=torch.bool)
+    mask[:n_valid] = True
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=mask[None, None, None, :].expand(1, 2, Na, Na))
+    ref = ref.numpy()
+    assert np.abs(ours[:, :, :n_valid] - ref[:, :, :n_valid]).max() < 1e-12
+    assert np.all(ours[:, :, n_valid:] == 0.0)
+
+
+def test_attention_two_key_closed_form():
+    """Scores 0 and ln 3 give weights 1/4 and 3/4."""
+    q = np.array([[1.0]])
+    k = np.array([[0.0], [math.log(3.0)]])
+    a = O.attention_probs(q, k, 1.0)
+    assert np.allclose(a, [[0.25, 0.75]], atol=1e-15, rtol=0)
+
+
+# ---------------------------------------------------------------- block masses
+
+@pytest.mark.parametrize("n_valid,R,C", [(300, 64, 64), (256, 32, 64), (333, 128, 32), (64, 64, 64)])
+def test_mass_rows_sum_to_one_and_nonnegative(n_valid, R, C):
+    """Methodology Summary: each query row of A sums to one, so a query block of size R holds mass R
+    (row-mean form: each row of blocks sums to 1)."""
+    rng = np.random.default_rng(2)
+    Na = max(-(-n_valid // R) * R, -(-n_valid // C) * C)
+    q, k, _ = _rand_qkv(rng, 2, 2, Na, 16, n_valid, scale_q=3.0)
+    M = O.block_mass(q, k, n_valid, R, C)
+    assert M.min() >= 0.0
+    assert np.abs(M.sum(axis=-1) - 1.0).max() < 1e-12
+
+
+def test_mass_zero_query_closed_form():
+    """Q = 0 => A uniform over the N valid keys => M(i, j) = |valid keys of block j| / N."""
+    n_valid, R, C = 150, 32, 64
+    rng = np.random.default_rng(3)
+    Na = 192
+    _, k, _ = _rand_qkv(rng, 1, 1, Na, 8, n_valid)
+    q = np.zeros_like(k)
+    M = O.block_mass(q, k, n_valid, R, C)
+    expect = np.array([64, 64, 22], np.float64) / n_valid
+    assert np.abs(M[0, 0] - expect[None, :]).max() < 1e-15
+
+
+def test_mass_single_key_block():
+    """n_k = 1 => every mass is 1."""
+    rng = np.random.default_rng(4)
+    q, k, _ = _rand_qkv(rng, 1, 1, 64, 8, 50, 4.0)
+    M = O.block_mass(q, k, 50, 16, 64)
+    assert M.shape[-1] == 1 and np.abs(M - 1.0).max() < 1e-14
+
+
+def test_mass_brute_force_double_sum():
+    """Row-mean mass equals the page's double sum over (q, k) divided by the valid rows, by direct loops."""
+    rng = np.random.default_rng(5)
+    n_valid, R, C, d = 45, 16, 8, 4
+    Na = 48
+    q, k, _ = _rand_qkv(rng, 1, 1, Na, d, n_valid, 2.0)
+    M = O.block_mass(q, k, n_valid, R, C)
+    sc = 1.0 / math.sqrt(d)
+    for i in range(3):
+        for j in range(6):
+            tot, rows = 0.0, 0
+            for qq in range(i * R, min((i + 1) * R, n_valid)):
+                rows += 1
+                logits = [sum(q[0, 0, qq, t] * k[0, 0, kk, t] for t in range(d)) * sc for kk in range(n_valid)]
+                mx = max(logits)
+                z = sum(math.exp(x - mx) for x in logits)
+                tot += sum(math.exp(logits[kk] - mx) / z for kk in range(j * C, min((j + 1) * C, n_valid)))
+            assert abs(M[0, 0, i, j] - tot / rows) < 1e-13
+
+
+# ---------------------------------------------------------------- selection
+
+def test_golden_selection_cases():
+    with open(os.path.join(GOLDEN, "selection_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        m = np.array(c["masses"], np.float32)
+        kept, s = O.select_contract_row(m, c["p"])
+        assert kept.tolist() == c["kept"], c
+        assert s == len(c["kept"])
+        kept_f, s_f, _ = O.select_float_row(m, c["p"])
+        assert kept_f.tolist() == c["kept"], c
+
+
+def _exact_units(m32):
+    """Independent exact restatement of q_j = ceil(m_j * 2^(51-e)) with Fractions."""
+    vals = [Fraction(float(x)) for x in m32]
+    mx = max(vals)
+    if mx == 0:
+        return [0] * len(vals)
+    _, e = math.frexp(float(mx))
+    scale = Fraction(2) ** (51 - e)
+    return [math.ceil(v * scale) for v in vals]
+
+
+def test_fixed_point_units_exact():
+    rng = np.random.default_rng(6)
+    rows = [rng.random(40).astype(np.float32),
+            (rng.random(40) ** 8).astype(np.float32),
+            np.array([1e-40, 3e-41, 2e-39, 0.0], np.float32),  # denormals
+            np.array([1.0, 0.5, 0.25, 2.0 ** -60], np.float32)]
+    for m in rows:
+        got = O.losa_oracle._fixed_point_units(O.sanitize_masses(m)).tolist()
+        assert got == _exact_units(O.sanitize_masses(m)), m
+        assert max(got) <= 2 ** 51
+        assert all(g >= 1 for g, x in zip(got, m) if x > 0)
+
+
+def _brute_force_min_card(m32, p):
+    """Minimum cardinality of a block subset whose exact mass reaches p_eff * total (all 2^n subsets)."""
+    vals = [Fraction(float(x)) for x in m32]
+    target = Fraction(O.p_fixed(p), 2 ** 32) * sum(vals)
+    n = len(vals)
+    best, best_sets = None, []
+    for r in range(1, n + 1):
+        for comb in itertools.combinations(range(n), r):
+            if sum(vals[j] for j in comb) >= target:
+                best_sets.append(comb)
+        if best_sets:
+            best = r
+            break
+    return best, best_sets, target, vals
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_selection_brute_force_16_blocks(seed):
+    """Greedy by mass is optimal for minimum cardinality: s equals the brute-force minimum, and with
+    distinct masses the kept set is the unique heaviest minimum-size set."""
+    rng = np.random.default_rng(100 + seed)
+    n = 12 if seed < 3 else 16
+    m = (rng.random(n) ** 3 + 1e-3).astype(np.float32)
+    p = [0.5, 0.9, 0.99, 0.75, 0.95, 0.6][seed]
+    kept, s = O.select_contract_row(m, p)
+    if n == 16:
+        # full 2^16 enumeration of subset masses (exact in fp64: exponent span < 29 bits)
+        masks = np.arange(1 << n, dtype=np.int64)
+        bits = ((masks[:, None] >> np.arange(n)) & 1).astype(np.float64)
+        sums = bits @ m.astype(np.float64)
+        card = bits.sum(axis=1)
+        target = float(Fraction(O.p_fixed(p), 2 ** 32) * sum(Fraction(float(x)) for x in m))
+        feas = sums >= target
+        min_card = int(card[feas].min())
+        heaviest = masks[feas & (card == min_card)][np.argmax(sums[feas & (card == min_card)])]
+        heavy_set = [j for j in range(n) if (heaviest >> j) & 1]
+        assert s == min_card
+        assert kept.tolist() == heavy_set
+    else:
+        best, sets, target, vals = _brute_force_min_card(m, p)
+        assert s == best
+        heaviest = max(sets, key=lambda c: sum(vals[j] for j in c))
+        assert kept.tolist() == list(heaviest)
+
+
+@pytest.mark.parametrize("p", [0.5, 0.9, 0.95, 0.99, 0.995])
+def test_selection_minimal_prefix_invariant(p):
+    """cum(s) >= target > cum(s-1): dropping the smallest kept block falls below p; retained mass >= p."""
+    rng = np.random.default_rng(7)
+    for _ in range(50):
+        m = rng.dirichlet(np.full(64, 0.3)).astype(np.float32)
+        kept, s = O.select_contract_row(m, p)
+        tot = sum(Fraction(float(x)) for x in m)
+        target = Fraction(O.p_fixed(p), 2 ** 32) * tot
+        kept_mass = sum(Fraction(float(m[j])) for j in kept)
+        assert kept_mass >= target
+        smallest = min(kept, key=lambda j: (m[j], -j))
+        assert kept_mass - Fraction(float(m[smallest])) < target
+        # every dropped block is no heavier than every kept block
+        dropped = np.setdiff1d(np.arange(64), kept)
+        if dropped.size:
+            assert m[dropped].max() <= m[kept].min()
+
+
+def test_selection_p_one_keeps_all_and_nonfinite_policy():
+    m = np.array([0.5, np.nan, -0.1, np.inf, 0.25, 0.0], np.float32)
+    kept, s = O.select_contract_row(m, 1.0)
+    assert kept.tolist() == list(range(6))
+    kept, s = O.select_contract_row(m, 0.9)
+    assert kept.tolist() == [0, 4]  # non-finite and negative masses count as 0
+
+
+def test_contract_matches_float_cumsum_on_workload0():
+    L = S.make_layer("0")
+    M = O.block_mass(L.f64("q"), L.f64("k"), 1024, 64, 64).astype(np.float32)
+    for p in (0.5, 0.9, 0.95, 0.99):
+        a = O.select_contract(M, p)
+        b = O.select_float(M, p)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- sparse attention
+
+def test_sparse_p_one_equals_dense():
+    """Methodology Summary (sparse attention): with every block kept the frozen-pattern output is dense attention."""
+    rng = np.random.default_rng(8)
+    n_valid, R, C = 200, 64, 32
+    q, k, v = _rand_qkv(rng, 1, 2, 256, 16, n_valid, 2.0)
+    M = O.block_mass(q, k, n_valid, R, C).astype(np.float32)
+    rp, ci = O.select_contract(M, 1.0)
+    assert int(rp[-1]) == 2 * 4 * 7
+    Os = O.sparse_attention(q, k, v, n_valid, R, C, rp, ci)
+    Od = O.dense_attention(q, k, v, n_valid)
+    assert np.abs(Os - Od).max() < 1e-12
+
+
+def test_sparse_single_block_is_library_softmax_attention():
+    """A one-block list is plain softmax attention over that block's keys (torch SDPA on the slice)."""
+    rng = np.random.default_rng(9)
+    n_valid, R, C = 150, 32, 64
+    q, k, v = _rand_qkv(rng, 1, 1, 192, 16, n_valid, 2.0)
+    n_q = 5
+    row_ptr = np.arange(n_q + 1)
+    col_idx = np.array([1, 0, 2, 1, 2], np.int32)
+    Os = O.sparse_attention(q, k, v, n_valid, R, C, row_ptr, col_idx)
+    for i in range(n_q):
+        j = col_idx[i]
+        keys = slice(j * C, min((j + 1) * C, n_valid))
+        r0, r1 = i * R, min((i + 1) * R, n_valid)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[0, 0, r0:r1][None]), torch.from_numpy(k[0, 0, keys][None]),
+            torch.from_numpy(v[0, 0, keys][None]))[0].numpy()
+        assert np.abs(Os[0, 0, r0:r1] - ref).max() < 1e-12
+    assert np.all(Os[0, 0, n_valid:] == 0)
+
+
+def test_sparse_zero_query_mean_of_kept_values():
+    """Q = 0 => uniform weights over the retained keys => O = mean of V over the kept tokens."""
+    rng = np.random.default_rng(10)
+    n_valid, R, C = 100, 32, 32
+    _, k, v = _rand_qkv(rng, 1, 1, 128, 8, n_valid)
+    q = np.zeros_like(k)
+    row_ptr = np.array([0, 2, 3, 3 + 4, 8])
+    col_idx = np.array([0, 3, 1, 0, 1, 2, 3, 2], np.int32)
+    Os = O.sparse_attention(q, k, v, n_valid, R, C, row_ptr, col_idx)
+    toks = [np.r_[0:32, 96:100], np.r_[32:64], np.r_[0:100], np.r_[64:96]]
+    for i, t in enumerate(toks):
+        r1 = min((i + 1) * R, n_valid)
+        assert np.abs(Os[0, 0, i * R:r1] - v[0, 0, t].mean(axis=0)).max() < 1e-14
+
+
+def test_recall_at_construction_and_coverage():
+    """Construction retains at least p of each block row's mass; recall and coverage follow the definitions."""
+    L = S.make_layer("0")
+    q, k = L.f64("q"), L.f64("k")
+    M = O.block_mass(q, k, 1024, 64, 64)
+    for p in (0.5, 0.9):
+        rp, ci = O.select_contract(M.astype(np.float32), p)
+        flat = M.reshape(-1, 16)
+        for r in range(flat.shape[0]):
+            assert flat[r, ci[rp[r]:rp[r + 1]]].sum() >= p * flat[r].sum() - 1e-6
+        rec = O.recall(M, rp, ci, 1024, 64)
+        assert rec >= p - 1e-6
+        assert O.coverage(rp, 1, 2, 16, 16) == rp[-1] / 512.0
+
+
+def test_budget_order():
+    rp = np.array([0, 3, 5, 8, 9, 11])
+    order = O.budget_order(rp)
+    assert order.tolist() == [0, 2, 1, 4, 3]
+
+
+# ---------------------------------------------------------------- generator
+
+def test_generator_deterministic_and_head_subset():
+    a = S.make_layer("0")
+    b = S.make_layer("0")
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.v, b.v)
+    c = S.make_layer("0", heads=[1])
+    assert np.array_equal(c.k[:, 0], a.k[:, 1])
+    assert np.all(a.q[:, :, 1024:] == 0)
+    t = S.make_layer("1", tokens=300, n_heads=3)
+    assert t.q.shape == (1, 3, 320, 128) and t.q.dtype == np.uint16
+    assert np.all(t.q[:, :, 300:] == 0)
+
+
+def test_bf16_rounding_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.5], np.float32)
+    got = S.f64_from_bf16_bits(S.bf16_bits_from_f32(x))
+    assert got.tolist() == [1.0, 1.0, 1.0 + 4 * 2 ** -8, 1.0, -2.5]
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
