@@ -1,0 +1,76 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, the bf16
+// matrix-core tile product, loads, wave reductions and the XCD-aware
+// workgroup mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace losa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16x16x32 bf16 matrix-core product: D = A (16 x 32) * B (32 x 16) + C.
+// Lane l feeds row (l & 15) of A and column (l & 15) of B with eight
+// k-elements each; the k-elements must be laid out identically in A and B
+// (any such layout gives the same contraction).  D: lane l holds column
+// (l & 15), rows 4 * (l >> 4) + [0, 4).
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;  // round to nearest even (v_cvt_pk_bf16_f32)
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, kWave);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+// Workgroup ids are handed to the 8 XCDs round-robin; map them so that each
+// XCD works through one contiguous range of tasks (neighbouring tasks share
+// K/V rows, so they then share that XCD's L2).  A bijection on [0, n).
+__device__ __forceinline__ int xcd_task(int bid, int n) {
+  constexpr int kXcd = 8;
+  const int xcd = bid % kXcd;
+  const int local = bid / kXcd;
+  const int base = n / kXcd;
+  const int rem = n % kXcd;
+  const int start = xcd * base + (xcd < rem ? xcd : rem);
+  return start + local;
+}
+
+}  // namespace losa

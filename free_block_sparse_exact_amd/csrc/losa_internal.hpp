@@ -1,0 +1,60 @@
+// Internal interface between the C ABI (losa_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace losa {
+
+// Validated geometry of one call, derived from losa_shape on the host.
+struct Geom {
+  int B, H, N, Na, D, R, C, nq, nk;
+  int bf16;          // 1: Q/K/V are bf16, 0: f32
+  float scale;       // softmax scale (1/sqrt(d) by default)
+  float scale_log2;  // scale * log2(e): scores in log2 units
+  int64_t qs[3], ks[3], vs[3], os[3];
+  int rows() const { return B * H * nq; }
+};
+
+// Per-head fixed-point selection thresholds P = floor(p * 2^32 + 1/2),
+// passed by value as a kernel argument.
+constexpr int kMaxHeadsP = 128;
+struct PTable {
+  uint64_t P[kMaxHeadsP];
+  int per_head;  // 0: P[0] for every head
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// True when the bf16 matrix-core kernels cover this geometry.
+inline bool mfma_path(const Geom& g) {
+  return g.bf16 && (g.D == 64 || g.D == 128) && (g.R == 64 || g.R == 128);
+}
+
+// Block masses: lse2 is workspace of B*H*Na floats.
+hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, float* lse2,
+                             hipStream_t stream);
+
+// Selection.
+struct SelectWs {
+  int32_t* counts;      // [rows]
+  uint64_t* kappa;      // [rows] boundary sort key of the last kept block
+  int32_t* chunk_hist;  // [(nk + 1) * nchunk] histogram of counts per row chunk, then offsets
+  int nchunk;
+};
+constexpr int kOrderChunk = 256;  // rows per placement chunk for the budget order
+size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base);
+hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr,
+                         int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t stream);
+
+hipError_t launch_retained_mass(const Geom& g, const float* M, const int32_t* row_ptr,
+                                const int32_t* col_idx, float* kept, hipStream_t stream);
+
+// Sparse attention; vt is workspace of B*H*D*Na bf16 on the matrix-core path.
+size_t attn_ws_bytes(const Geom& g);
+hipError_t launch_sparse_attn(const Geom& g, const void* Q, const void* K, const void* V,
+                              const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
+                              void* O, int o_bf16, void* ws, hipStream_t stream);
+
+}  // namespace losa

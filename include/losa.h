@@ -1,0 +1,188 @@
+/*
+ * losa.h -- C ABI of the retained-mass block-sparse self-attention library
+ * (gfx950 / MI355X).
+ *
+ * The three calls follow page 1, "LoSA: Near-Lossless Sparse Attention for
+ * Training-Free Video Diffusion Acceleration":
+ *
+ *   losa_block_mass   exact block attention masses      (Motivation Summary;
+ *                     Methodology Summary, one-time pattern construction)
+ *   losa_select       retained-mass (top-p) key-block lists, CSR
+ *                     (Methodology Summary, one-time pattern construction)
+ *   losa_sparse_attn  softmax attention over the frozen lists only
+ *                     (Methodology Summary, sparse attention with a frozen
+ *                     pattern)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.  Every pointer named Q, K, V, O, M, row_ptr, col_idx, order, ws,
+ *   kept is DEVICE memory owned by the caller; the library allocates nothing
+ *   and keeps no pointer after a call returns.  The only host pointers are the
+ *   losa_shape, the p array of losa_select and the size_t out-parameters.
+ * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
+ *   returns without waiting.  Outputs are valid once the stream reaches them.
+ * Errors.  Argument checks run on the host before any HIP call; a failed
+ *   check returns its status and enqueues nothing.  LOSA_ERR_HIP reports a
+ *   failed launch (hipGetLastError after the launches).  After any error the
+ *   contents of the output buffers are unspecified.  No call throws.
+ * Threads.  The library has no mutable global state; calls are thread-safe.
+ *   Calls on one stream run in order; two calls writing the same buffers on
+ *   different streams race.
+ *
+ * Tensor layout.  Q, K, V (and O) are [batch, heads, tokens_alloc, head_dim]
+ *   with the element strides given in losa_shape (batch, head, token), the
+ *   head_dim axis contiguous.  Rows tokens..tokens_alloc-1 are padding: they
+ *   are never keys, never counted as queries, and O is written as 0 there.
+ *   Base pointers must be 16-byte aligned and strides multiples of 8 (bf16)
+ *   or 4 (f32) elements.
+ * Blocks.  n_q = ceil(tokens / q_block) query blocks and n_k = ceil(tokens /
+ *   k_block) key blocks per (batch, head); the last block of each may be
+ *   partial.  A row r = (b * heads + h) * n_q + i names query block i of
+ *   head h of batch b.
+ */
+#ifndef LOSA_H
+#define LOSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOSA_ABI_VERSION 1
+/* Largest n_k accepted (key blocks per head), and largest head count that may
+ * carry its own p in losa_select. */
+#define LOSA_MAX_KEY_BLOCKS 4096
+#define LOSA_MAX_HEADS_P 128
+
+typedef enum losa_status {
+  LOSA_OK = 0,
+  LOSA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  LOSA_ERR_INVALID_ARG = 2, /* a size, stride, alignment or parameter is wrong  */
+  LOSA_ERR_UNSUPPORTED = 3, /* well-formed but outside what is implemented      */
+  LOSA_ERR_WORKSPACE = 4,   /* workspace smaller than the matching query says   */
+  LOSA_ERR_CAPACITY = 5,    /* col_idx capacity below batch*heads*n_q*n_k       */
+  LOSA_ERR_HIP = 6          /* a HIP launch failed                              */
+} losa_status;
+
+typedef enum losa_dtype { LOSA_F32 = 0, LOSA_BF16 = 1 } losa_dtype;
+
+typedef struct losa_shape {
+  int32_t batch;         /* >= 1                                                 */
+  int32_t heads;         /* >= 1                                                 */
+  int32_t tokens;        /* N, valid tokens per (batch, head), >= 1               */
+  int32_t tokens_alloc;  /* rows allocated per (batch, head), >= n_q*R and n_k*C  */
+  int32_t head_dim;      /* d: 64 or 128                                          */
+  int32_t q_block;       /* R: 32, 64 or 128                                      */
+  int32_t k_block;       /* C: 32, 64 or 128                                      */
+  losa_dtype dtype;      /* element type of Q, K and V                            */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) (the page's scaling)    */
+  int32_t reserved;      /* must be 0                                             */
+  int64_t q_stride[3];   /* element strides: batch, head, token                   */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];   /* read by losa_sparse_attn only                         */
+} losa_shape;
+
+/* ABI version of the loaded library (LOSA_ABI_VERSION it was built with). */
+int32_t losa_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* losa_status_string(losa_status status);
+
+/* ------------------------------------------------------------------------
+ * Exact block attention masses.
+ * Motivation Summary (block attention mass M(i, j) = sum over the query
+ * rows of block i and the key columns of block j of softmax(Q K^T scale)),
+ * in row-mean form: M[b, h, i, j] = that sum divided by the number of valid
+ * rows of query block i, so each row of blocks sums to 1.
+ *
+ * Computed in two passes over K: a flash-style pass for each row's
+ * log-sum-exp, then a second pass that accumulates exp(s - LSE) per key
+ * block.  Arithmetic: products and sums in fp32 (bf16 inputs are exact in
+ * fp32), exponentials in fp32.
+ *
+ * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
+ * ws: at least *bytes from losa_block_mass_workspace (row log-sum-exp).
+ * ------------------------------------------------------------------------ */
+losa_status losa_block_mass_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_block_mass(const losa_shape* shape, const void* Q, const void* K, float* M,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Retained-mass block selection.
+ * Methodology Summary (one-time pattern construction): per row, sort key
+ * blocks by decreasing mass and keep the shortest prefix whose cumulative
+ * mass reaches p times the row total.  Exact rules (the page leaves these
+ * open):
+ *   - ties in mass: the lower block index comes first;
+ *   - non-finite, negative and -0 masses count as 0;
+ *   - the cumulative sum is evaluated exactly in integers, so the result does
+ *     not depend on summation order: with e the binary exponent of the row
+ *     maximum (max = f * 2^e, 1/2 <= f < 1), each mass becomes
+ *     q_j = ceil(m_j * 2^(51 - e)); P = floor(p * 2^32 + 1/2);
+ *     T = ceil(P * sum_j q_j / 2^32); the kept count s is the least prefix
+ *     length whose integer sum is >= T (s >= 1; an all-zero row keeps block 0);
+ *   - p = 1 (P = 2^32) keeps every block.
+ *
+ * M: fp32 [batch, heads, n_q, n_k] contiguous (e.g. from losa_block_mass).
+ * p: HOST array of n_p doubles in (0, 1]; n_p = 1 (one p for all heads) or
+ *    n_p = heads (head h uses p[h]; heads <= LOSA_MAX_HEADS_P).
+ * row_ptr: int32 [batch*heads*n_q + 1]; row r's kept blocks are
+ *    col_idx[row_ptr[r] .. row_ptr[r+1]-1], in ascending block order.
+ * col_idx: int32, col_capacity >= batch*heads*n_q*n_k entries (the worst
+ *    case; the used length is row_ptr[last], read back by the caller).
+ * order: int32 [batch*heads*n_q] or NULL.  When given, receives the rows
+ *    sorted by kept-block count, descending, ties by row index ascending
+ *    (the work order losa_sparse_attn takes).
+ * ws: at least *bytes from losa_select_workspace.
+ * ------------------------------------------------------------------------ */
+losa_status losa_select_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_select(const losa_shape* shape, const float* M, const double* p, int32_t n_p,
+                        int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Frozen-pattern block-sparse attention.
+ * Methodology Summary (sparse attention with a frozen pattern): for each
+ * query q of query block i, O(q) = sum over retained keys k of
+ * exp(s_qk) / sum over retained keys k' of exp(s_qk') * v_k with
+ * s = q.k * scale; the retained keys are the valid tokens of the blocks
+ * listed for q's row; discarded keys are absent from the denominator; no
+ * block is added.  A row with an empty list gets O = 0.
+ *
+ * row_ptr/col_idx: CSR as produced by losa_select (any order of indices is
+ *    accepted; each index must lie in [0, n_k)).
+ * order: NULL (rows in index order) or a permutation of the rows giving the
+ *    order in which work is dispatched (losa_select's budget order).  The
+ *    result does not depend on it.
+ * O: [batch, heads, tokens_alloc, head_dim] with shape->o_stride, element
+ *    type o_dtype (LOSA_BF16 or LOSA_F32).
+ * ws: at least *bytes from losa_sparse_attn_workspace (a head_dim-major copy
+ *    of V for the bf16 matrix-core path; 0 bytes otherwise).
+ * Arithmetic: bf16 inputs use bf16 matrix products with fp32 accumulation,
+ * the probabilities rounded to bf16 for the P.V product; softmax statistics
+ * in fp32.  f32 inputs use fp32 throughout.
+ * ------------------------------------------------------------------------ */
+losa_status losa_sparse_attn_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_sparse_attn(const losa_shape* shape, const void* Q, const void* K, const void* V,
+                             const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
+                             void* O, losa_dtype o_dtype, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Retained mass of a pattern (for Recall, Motivation Summary).
+ * kept: fp32 [2 * batch*heads*n_q]: kept[2r] = sum of M[r, j] over the
+ * listed blocks of row r, kept[2r+1] = sum of M[r, j] over all j.  Recall
+ * follows by weighting row r with its number of valid query rows.
+ * ------------------------------------------------------------------------ */
+losa_status losa_retained_mass(const losa_shape* shape, const float* M, const int32_t* row_ptr,
+                               const int32_t* col_idx, float* kept, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOSA_H */
