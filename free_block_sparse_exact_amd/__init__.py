@@ -41,7 +41,8 @@ __all__ = [
     "STATUS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblosa.so")
+# LOSA_LIBRARY may name another build of the same library (e.g. for A/B timing).
+LIB_PATH = os.environ.get("LOSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblosa.so")
 
 LOSA_F32 = 0
 LOSA_BF16 = 1

@@ -4,25 +4,27 @@
 // only; discarded keys leave the denominator).
 //
 // bf16 matrix-core path (d in {64, 128}, R in {64, 128}):
-//   * one workgroup (4 waves) per 64-query tile of a row (two per row when
-//     R = 128); tiles are dispatched in the caller's budget order;
-//   * the row's kept blocks are cut into 32-key chunks and the waves split
-//     the chunks (wave w takes chunks w, w+4, ...).  Each wave keeps the
-//     whole tile's Q as a B operand and its own online-softmax state
-//     (running max m, sum l, O^T accumulators) for all 64 queries, and reads
-//     its K chunk and V chunk straight from global memory into registers --
-//     no LDS in the main loop;
+//   * a pre-pass packs K and V into lane-major operand copies per 32-token
+//     chunk (the exact register images of the MFMA A operands), so every
+//     operand load is 64 lanes x 16 contiguous bytes -- with K and V read in
+//     their natural layouts each 1 KB load split into ~48 cache accesses and
+//     the texture data path, not the matrix cores, set the pace;
+//   * one workgroup per 64-query tile of a row (two per row when R = 128),
+//     dispatched in the caller's budget order.  Its waves split the row's
+//     32-key chunks (wave kw of each query group takes chunks kw, kw+4, ...),
+//     each keeping its own online-softmax state for its queries; the four key
+//     groups are merged through LDS at the end.  The Q tile sits in LDS in
+//     the same lane-major form and is read per chunk;
 //   * S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA.  K rows are fed
-//     in the permuted order kappa(kt, rho) = 8*(rho>>2) + 4*kt + (rho&3) so
-//     that lane l ends up holding the eight consecutive keys 8*(l>>4)+[0,8)
-//     of every query (l & 15): exactly the k-layout of the P^T operand, so P
-//     goes from the S accumulators to the next MFMA without any exchange;
-//   * V is consumed as V^T (keys contiguous per lane): a transpose kernel
-//     writes a head_dim-major copy of V into the workspace first;
-//   * the max is raised lazily: O and l are rescaled only when a new score
-//     exceeds the running max by more than 8 (log2 units), so probabilities
-//     stay below 2^8 and the rescale is rare after the first chunk;
-//   * the four waves' partial states are merged through LDS at the end.
+//     in the permuted order kappa(kt, rho) = 8*(rho>>2) + 4*kt + (rho&3), so
+//     lane l ends up holding the eight consecutive keys 8*(l>>4)+[0,8) of
+//     query (l & 15): exactly the k-layout of the P^T operand, so P goes from
+//     the S accumulators to the next MFMA without any exchange;
+//   * no per-score maximum and no rescaling of O inside the loop (see the
+//     main loop); row sums use the bf16-rounded probabilities, matching the
+//     numerator;
+//   * the next chunk's K is requested as soon as the score MFMAs have read
+//     the current one, and V likewise after the P.V MFMAs.
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
 
@@ -30,227 +32,361 @@ namespace losa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kLazyMax = 8.0f;
 
-// V [B,H,Na,D] (strided) -> Vt [B*H][D][Lt] bf16, zero for tokens >= N.
-// 64x64 tiles through LDS.  Grid: (Lt/64, D/64, B*H), 256 threads.
-__global__ __launch_bounds__(256) void transpose_v_kernel(const Geom g, const __bf16* __restrict__ V,
-                                                          __bf16* __restrict__ Vt, int64_t Lt) {
-  __shared__ uint16_t tile[64][66];
-  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64, bh = blockIdx.z;
+// K and V -> lane-major operand copies, one 32-token chunk at a time, so that
+// every operand load in the attention kernel is 64 lanes x 16 contiguous
+// bytes (lane order), the pattern the vector memory path coalesces fully.
+//   Kp[bh][c][kt][dc][lane][8]: row 32c + 8*((lane&15)>>2) + 4*kt + (lane&3)
+//       of K, elements dc*32 + (lane>>4)*8 + [0,8) (the A operand of S^T = K Q^T
+//       for key tile kt and k-step dc);
+//   Vp[bh][c][dt][lane][8]: V[32c + (lane>>4)*8 + e][dt*16 + (lane&15)]
+//       for e in [0,8) (the A operand of O^T += V^T P^T for dim tile dt).
+// Tokens >= N are written as zeros.  Grid: (nch / 2, B*H) with nch even;
+// each workgroup packs 64 tokens (two chunks), V through an LDS tile.
+template <int D>
+__global__ __launch_bounds__(256) void pack_kv_kernel(const Geom g, const __bf16* __restrict__ K,
+                                                      const __bf16* __restrict__ V, __bf16* __restrict__ Kp,
+                                                      __bf16* __restrict__ Vp, int nch) {
+  constexpr int DC = D / 32, DT = D / 16;
+  __shared__ uint16_t vt[64][D + 2];
+  const int t0 = blockIdx.x * 64, bh = blockIdx.y;
   const int b = bh / g.H, h = bh - b * g.H;
-  const __bf16* Vbh = V + b * g.vs[0] + h * g.vs[1];
-  const uint16_t* Vu = reinterpret_cast<const uint16_t*>(Vbh);
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int tt = idx >> 6, dd = idx & 63;
+  const __bf16* Kbh = K + b * g.ks[0] + h * g.ks[1];
+  const uint16_t* Vbh = reinterpret_cast<const uint16_t*>(V + b * g.vs[0] + h * g.vs[1]);
+  for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
+    const int tt = idx / D, dd = idx - tt * D;
     const int tok = t0 + tt;
-    tile[tt][dd] = tok < g.N ? Vu[(int64_t)tok * g.vs[2] + d0 + dd] : (uint16_t)0;
+    vt[tt][dd] = tok < g.N ? Vbh[(int64_t)tok * g.vs[2] + dd] : (uint16_t)0;
+  }
+  const int64_t cbase = (int64_t)bh * nch + (t0 >> 5);
+  // K: 2 chunks x 2 key tiles x DC k-steps x 64 lanes pieces of 16 bytes.
+  for (int idx = threadIdx.x; idx < 2 * 2 * DC * 64; idx += 256) {
+    const int lane = idx & 63, rest = idx >> 6;
+    const int dc = rest % DC, kt = (rest / DC) & 1, cc = rest / (2 * DC);
+    const int lr = lane & 15;
+    const int tok = t0 + cc * 32 + ((lr >> 2) << 3) + kt * 4 + (lr & 3);
+    bf16x8 v = bf16x8{};
+    if (tok < g.N) v = load_bf16x8(Kbh + (int64_t)tok * g.ks[2] + dc * 32 + (lane >> 4) * 8);
+    *reinterpret_cast<bf16x8*>(Kp + ((cbase + cc) * 2 * DC * 64 + idx - cc * 2 * DC * 64) * 8) = v;
   }
   __syncthreads();
-  uint16_t* out = reinterpret_cast<uint16_t*>(Vt) + ((int64_t)bh * g.D + d0) * Lt;
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-    const int dd = idx >> 6, tt = idx & 63;
-    out[(int64_t)dd * Lt + t0 + tt] = tile[tt][dd];
+  // V: 2 chunks x DT dim tiles x 64 lanes pieces of 16 bytes.
+  for (int idx = threadIdx.x; idx < 2 * DT * 64; idx += 256) {
+    const int lane = idx & 63, dt = (idx >> 6) % DT, cc = idx / (DT * 64);
+    const int dv = dt * 16 + (lane & 15), k0 = cc * 32 + (lane >> 4) * 8;
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = vt[k0 + j][dv];
+    u32x4 pk;
+    pk[0] = e[0] | ((uint32_t)e[1] << 16);
+    pk[1] = e[2] | ((uint32_t)e[3] << 16);
+    pk[2] = e[4] | ((uint32_t)e[5] << 16);
+    pk[3] = e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<u32x4*>(Vp + ((cbase + cc) * DT * 64 + idx - cc * DT * 64) * 8) = pk;
   }
 }
 
-template <int D>
-struct AttnState {
-  static constexpr int DT = D / 16;
-  f32x4 o[DT][4];  // O^T: lane holds query (l & 15) of tile qt, dims dt*16 + 4*(l>>4) + r
-  float m[4], l[4];
-};
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                        float a7) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  return __builtin_convertvector((f32x8{a0, a1, a2, a3, a4, a5, a6, a7}), bf16x8);
+}
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
-                                                        const __bf16* __restrict__ K,
-                                                        const __bf16* __restrict__ Vt, int64_t Lt,
-                                                        const int32_t* __restrict__ row_ptr,
-                                                        const int32_t* __restrict__ col_idx,
-                                                        const int32_t* __restrict__ order, void* O,
-                                                        int o_bf16) {
+// Sum of the eight bf16 probabilities exactly as they enter the P.V product,
+// so the normaliser matches the numerator (v_dot2 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float s = __builtin_amdgcn_fdot2_f32_bf16(p.s01, ones, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.s23, ones, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.s45, ones, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(p.s67, ones, s, false);
+}
+
+// A chunk whose per-lane probability sum (relative to the running max)
+// exceeds this bound goes through the rescale path.
+constexpr float kPBound = 65536.0f;
+
+// Workgroup: 8 waves = 2 query halves (32 queries each) x 4 key groups.
+// Wave (qh, kw) keeps the running state of its 32 queries over the chunks
+// kw, kw+4, kw+8, ... of the row; at the end the four key groups of each
+// query half are merged through LDS.  32 queries per wave keep the state
+// within 256 registers, so two waves share each SIMD (one wave alone issues
+// vector instructions at about half the SIMD's rate).  The two query halves
+// of a key group read the same K and V chunks at about the same time.
+template <int kQT>
+constexpr int attn_waves() { return 4 * (4 / kQT); }
+
+template <int D, int kQT>
+__global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
+    const Geom g, const __bf16* __restrict__ Q, const __bf16* __restrict__ Kp, const __bf16* __restrict__ Vp,
+    int nch, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    const int32_t* __restrict__ order, void* O, int o_bf16) {
   constexpr int DC = D / 32, DT = D / 16;
-  extern __shared__ float lds[];  // merge slot: [64][D + 4] floats + m[64] + l[64]
+  constexpr int kAttnWaves = attn_waves<kQT>();
+  constexpr int LD = D + 4;   // merge slot row stride (floats)
+  extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]; then Q tile, lane-major, bf16
   const int qhalves = g.R / 64;
   const int tix = blockIdx.x;
-  const int ridx = tix / qhalves, qh = tix - ridx * qhalves;
+  const int ridx = tix / qhalves, qsub = tix - ridx * qhalves;
   const int row = order ? order[ridx] : ridx;
   const int bh = row / g.nq, i = row - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int kw = w & 3, qh = w >> 2;
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
-  const __bf16* Kbh = K + b * g.ks[0] + h * g.ks[1];
-  const __bf16* Vbh = Vt + (int64_t)bh * D * Lt;
-  const int row0 = i * g.R + qh * 64;
+  const __bf16* Kbh = Kp + (int64_t)bh * nch * (32 * D);
+  const __bf16* Vbh = Vp + (int64_t)bh * nch * (32 * D);
+  const int row0 = i * g.R + qsub * 64;
 
-  // Q as the B operand of S^T = K Q^T (padding rows -> 0).
-  bf16x8 qop[4][DC];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int qrow = row0 + qt * 16 + lr;
-#pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      bf16x8 v = load_bf16x8(Qbh + (int64_t)qrow * g.qs[2] + dc * 32 + lg * 8);
-      if (qrow >= g.N) v = bf16x8{};
-      qop[qt][dc] = v;
-    }
+  // Q tile (64 rows) in LDS, lane-major like the packed K: piece (qt, dc,
+  // lane) holds row qt*16 + (lane&15), elements dc*32 + (lane>>4)*8 + [0,8),
+  // so each wave's B-operand reads are 64 lanes x 16 contiguous bytes.
+  // Padding rows -> 0.
+  __bf16* qs = reinterpret_cast<__bf16*>(lds + 64 * LD + 128);
+  for (int idx = threadIdx.x; idx < 4 * DC * 64; idx += 64 * kAttnWaves) {
+    const int ln = idx & 63, dc = (idx >> 6) % DC, qt4 = idx / (DC * 64);
+    const int qrow = row0 + qt4 * 16 + (ln & 15);
+    bf16x8 v = load_bf16x8(Qbh + (int64_t)qrow * g.qs[2] + dc * 32 + (ln >> 4) * 8);
+    if (qrow >= g.N) v = bf16x8{};
+    *reinterpret_cast<bf16x8*>(qs + idx * 8) = v;
   }
+  __syncthreads();
+  const __bf16* qlane = qs + ((qh * kQT) * DC * 64 + lane) * 8;
 
-  AttnState<D> st;
+  f32x4 o[DT][kQT];
+  float m[kQT], l[kQT];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    st.m[qt] = kNegInf;
-    st.l[qt] = 0.f;
+  for (int qt = 0; qt < kQT; ++qt) {
+    m[qt] = kNegInf;
+    l[qt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const float c = g.scale_log2;
   const int beg = row_ptr[row], end = row_ptr[row + 1];
   const int sub = g.C / 32;
   const int nchunk = (end - beg) * sub;
-  // K row fed to A-operand row rho of key tile kt.
-  const int krow0 = ((lr >> 2) << 3) + (lr & 3);
 
-  for (int u = w; u < nchunk; u += 4) {
-    const int p = u / sub, sc = u - p * sub;
-    const int j = col_idx[beg + p];
-    const int kb = j * g.C + sc * 32;
-    if (kb >= g.N) continue;  // chunk lies wholly in the padding of the last block
-
-    bf16x8 kop[2][DC];
+  auto chunk_key = [&](int u) -> int {
+    const int p = u / sub;
+    return col_idx[beg + p] * g.C + (u - p * sub) * 32;
+  };
+  // Operand loads from the packed copies: 64 lanes x 16 contiguous bytes each.
+  auto load_k = [&](int kb, bf16x8 (&kop)[2][DC]) {
+    const __bf16* kc = Kbh + (int64_t)(kb >> 5) * (32 * D) + lane * 8;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        kop[kt][dc] = load_bf16x8(Kbh + (int64_t)(kb + krow0 + kt * 4) * g.ks[2] + dc * 32 + lg * 8);
-    bf16x8 vop[DT];
+      for (int dc = 0; dc < DC; ++dc) kop[kt][dc] = load_bf16x8(kc + (kt * DC + dc) * 512);
+  };
+  auto load_v = [&](int kb, bf16x8 (&vop)[DT]) {
+    const __bf16* vc = Vbh + (int64_t)(kb >> 5) * (32 * D) + lane * 8;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vop[dt] = load_bf16x8(Vbh + (int64_t)(dt * 16 + lr) * Lt + kb + lg * 8);
-
-    f32x4 acc[2][4];
+    for (int dt = 0; dt < DT; ++dt) vop[dt] = load_bf16x8(vc + dt * 512);
+  };
+  // S^T for one chunk: acc[kt][qt][r] = score of key kb + 8*lg + 4*kt + r for
+  // query qh*32 + qt*16 + lr.
+  auto scores = [&](const bf16x8 (&kop)[2][DC], f32x4 (&acc)[2][kQT]) {
+    asm volatile("" ::: "memory");  // keep the Q reads from LDS here (not hoisted into registers)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
+      for (int qt = 0; qt < kQT; ++qt) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) a = mfma_bf16(kop[kt][dc], qop[qt][dc], a);
+        for (int dc = 0; dc < DC; ++dc)
+          a = mfma_bf16(kop[kt][dc], *reinterpret_cast<const bf16x8*>(qlane + (qt * DC + dc) * 512), a);
         acc[kt][qt] = a;
       }
-
-    // acc[kt][qt][r] is the score of key kb + 8*lg + 4*kt + r.
-    const bool partial = kb + 32 > g.N;
-    float x[4][8];
-    float mx[4];
-    bool need = false;
+  };
+  // Padding keys of the last block's tail leave the softmax.
+  auto mask_tail = [&](int kb, f32x4 (&acc)[2][kQT]) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int r = 0; r < 4; ++r) {
+        const bool dead = kb + lg * 8 + kt * 4 + r >= g.N;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = acc[kt][qt][r] * c;
-          if (partial && kb + lg * 8 + kt * 4 + r >= g.N) v = kNegInf;
-          x[qt][kt * 4 + r] = v;
-        }
-      float t = fmaxf(fmaxf(fmaxf(x[qt][0], x[qt][1]), fmaxf(x[qt][2], x[qt][3])),
-                      fmaxf(fmaxf(x[qt][4], x[qt][5]), fmaxf(x[qt][6], x[qt][7])));
-      t = fmaxf(t, __shfl_xor(t, 16, kWave));
-      t = fmaxf(t, __shfl_xor(t, 32, kWave));
+        for (int qt = 0; qt < kQT; ++qt)
+          if (dead) acc[kt][qt][r] = kNegInf;
+      }
+  };
+  // Probabilities p = 2^(s*c - m) against the wave's fixed reference m, packed
+  // to bf16; the row sums take the packed values.  Returns whether some lane's
+  // sum left (0, kPBound] -- an overflow, or m not yet finite.
+  auto probs = [&](const f32x4 (&acc)[2][kQT], bf16x8 (&pop)[kQT]) -> bool {
+    bool over = false;
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      const float nm = -m[qt];
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
+      pop[qt] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      const float rs = sum_bf16x8(pop[qt]);
+      over |= !(rs <= kPBound);
+      l[qt] += rs;
+    }
+    return over;
+  };
+  auto chunk_max = [&](const f32x4 (&acc)[2][kQT], float (&mx)[kQT]) {
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      float t = mx[qt];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t = fmaxf(t, acc[e >> 2][qt][e & 3]);
       mx[qt] = t;
-      need |= t > st.m[qt] + kLazyMax;
     }
-    if (__any(need)) {
+  };
+  auto lanes_max = [&](float (&mx)[kQT]) {
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        if (mx[qt] > st.m[qt] + kLazyMax) {
-          const float alpha = fast_exp2(st.m[qt] - mx[qt]);  // 0 on the first chunk
-          st.l[qt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) st.o[dt][qt] *= alpha;
-          st.m[qt] = mx[qt];
-        }
-      }
+    for (int qt = 0; qt < kQT; ++qt) {
+      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 16, kWave));
+      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32, kWave));
     }
-    bf16x8 pop[4];
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      float pe[8];
-      float rs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pe[e] = fast_exp2(x[qt][e] - st.m[qt]);
-        rs += pe[e];
-      }
-      st.l[qt] += rs;
-      u32x4 pk;
-      pk[0] = pack_bf16x2(pe[0], pe[1]);
-      pk[1] = pack_bf16x2(pe[2], pe[3]);
-      pk[2] = pack_bf16x2(pe[4], pe[5]);
-      pk[3] = pack_bf16x2(pe[6], pe[7]);
-      pop[qt] = __builtin_bit_cast(bf16x8, pk);
-    }
+  };
+  auto pv = [&](const bf16x8 (&vop)[DT], const bf16x8 (&pop)[kQT]) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) st.o[dt][qt] = mfma_bf16(vop[dt], pop[qt], st.o[dt][qt]);
+      for (int qt = 0; qt < kQT; ++qt) o[dt][qt] = mfma_bf16(vop[dt], pop[qt], o[dt][qt]);
+  };
+
+  // No maximum is tracked per score and O is never rescaled inside the loop:
+  // the reference m is fixed at the wave's first chunk's maximum plus
+  // kHeadroom (log2 units), so later chunks may exceed it by up to
+  // kHeadroom + 16 before a sum leaves (0, kPBound]; terms more than ~60 below
+  // the maximum are negligible either way.  If that ever happens the wave
+  // drops its partial sums and recomputes its chunks in two passes (exact
+  // maximum first), so all probabilities are <= 1.
+  // K of the next chunk is requested as soon as the score MFMAs have read the
+  // current K, V of the next chunk once the P.V MFMAs have read the current V.
+  // Chunks wholly inside the padding of the last block are loaded (in bounds:
+  // below n_k*C) and fully masked rather than skipped.
+  constexpr float kHeadroom = 64.0f;
+  const int nmine = nchunk > kw ? (nchunk - kw + 3) / 4 : 0;
+  auto key_of = [&](int t) { return chunk_key(kw + 4 * (t < nmine ? t : nmine - 1)); };
+  bool fallback = false;
+  bf16x8 kop[2][DC], vop[DT];
+  if (nmine > 0) {
+    int kb = key_of(0);
+    load_k(kb, kop);
+    load_v(kb, vop);
+    for (int t = 0; t < nmine; ++t) {
+      const int kbn = key_of(t + 1);
+      f32x4 acc[2][kQT];
+      scores(kop, acc);
+      load_k(kbn, kop);
+      if (__builtin_expect(kb + 32 > g.N, 0)) mask_tail(kb, acc);
+      if (t == 0) {
+        float mx[kQT];
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) mx[qt] = kNegInf;
+        chunk_max(acc, mx);
+        lanes_max(mx);
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) m[qt] = mx[qt] * c + kHeadroom;  // -inf: forces the fallback
+      }
+      bf16x8 pop[kQT];
+      if (__builtin_expect(__any(probs(acc, pop)), 0)) { fallback = true; break; }
+      pv(vop, pop);
+      load_v(kbn, vop);
+      kb = kbn;
+    }
+  }
+  if (fallback) {
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      l[qt] = 0.f;
+      m[qt] = kNegInf;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int t = 0; t < nmine; ++t) {
+      const int kb2 = key_of(t);
+      load_k(kb2, kop);
+      f32x4 acc[2][kQT];
+      scores(kop, acc);
+      if (kb2 + 32 > g.N) mask_tail(kb2, acc);
+      chunk_max(acc, m);
+    }
+    lanes_max(m);
+    bool any_key = false;
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      any_key |= m[qt] != kNegInf;
+      m[qt] *= c;
+    }
+    if (__any(any_key)) {  // a key row is common to all queries, so the maxima are all finite
+      for (int t = 0; t < nmine; ++t) {
+        const int kb2 = key_of(t);
+        load_k(kb2, kop);
+        load_v(kb2, vop);
+        f32x4 acc[2][kQT];
+        scores(kop, acc);
+        if (kb2 + 32 > g.N) mask_tail(kb2, acc);
+        bf16x8 pop[kQT];
+        probs(acc, pop);
+        pv(vop, pop);
+      }
+    }
   }
 
   // Row sums: combine the four lane groups that share each query.
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    st.l[qt] += __shfl_xor(st.l[qt], 16, kWave);
-    st.l[qt] += __shfl_xor(st.l[qt], 32, kWave);
+  for (int qt = 0; qt < kQT; ++qt) {
+    l[qt] += __shfl_xor(l[qt], 16, kWave);
+    l[qt] += __shfl_xor(l[qt], 32, kWave);
   }
 
-  // Merge the waves' partial states: 3 -> 2 -> 1 -> 0 through one LDS slot.
-  constexpr int LD = D + 4;
-  float* so = lds;
-  float* sm = lds + 64 * LD;
-  float* sl = sm + 64;
+  // Merge the key groups of each query group: 3 -> 2 -> 1 -> 0 through one LDS slot per group.
+  float* so = lds + qh * kQT * 16 * LD;
+  float* sm = lds + 64 * LD + qh * kQT * 16;
+  float* sl = lds + 64 * LD + 64 + qh * kQT * 16;
   for (int src = 3; src >= 1; --src) {
     __syncthreads();
-    if (w == src) {
+    if (kw == src) {
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
+      for (int qt = 0; qt < kQT; ++qt) {
         const int qi = qt * 16 + lr;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(so + qi * LD + dt * 16 + lg * 4) = st.o[dt][qt];
-        if (lg == 0) { sm[qi] = st.m[qt]; sl[qi] = st.l[qt]; }
+          *reinterpret_cast<f32x4*>(so + qi * LD + dt * 16 + lg * 4) = o[dt][qt];
+        if (lg == 0) { sm[qi] = m[qt]; sl[qi] = l[qt]; }
       }
     }
     __syncthreads();
-    if (w == src - 1) {
+    if (kw == src - 1) {
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
+      for (int qt = 0; qt < kQT; ++qt) {
         const int qi = qt * 16 + lr;
         const float mo = sm[qi], lo = sl[qi];
-        const float mn = fmaxf(st.m[qt], mo);
-        const float a = st.m[qt] == kNegInf ? 0.f : fast_exp2(st.m[qt] - mn);
+        const float mn = fmaxf(m[qt], mo);
+        const float a = m[qt] == kNegInf ? 0.f : fast_exp2(m[qt] - mn);
         const float ao = mo == kNegInf ? 0.f : fast_exp2(mo - mn);
-        st.m[qt] = mn;
-        st.l[qt] = st.l[qt] * a + lo * ao;
+        m[qt] = mn;
+        l[qt] = l[qt] * a + lo * ao;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const f32x4 oo = *reinterpret_cast<const f32x4*>(so + qi * LD + dt * 16 + lg * 4);
-          st.o[dt][qt] = st.o[dt][qt] * a + oo * ao;
+          o[dt][qt] = o[dt][qt] * a + oo * ao;
         }
       }
     }
   }
 
-  if (w == 0) {
+  if (kw == 0) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      const int qrow = row0 + qt * 16 + lr;
-      const float inv = (qrow < g.N && st.l[qt] > 0.f) ? 1.0f / st.l[qt] : 0.f;
+    for (int qt = 0; qt < kQT; ++qt) {
+      const int qrow = row0 + (qh * kQT + qt) * 16 + lr;
+      const float inv = (qrow < g.N && l[qt] > 0.f) ? 1.0f / l[qt] : 0.f;
       const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = st.o[dt][qt] * inv;
+        const f32x4 v = o[dt][qt] * inv;
         const int d0 = dt * 16 + lg * 4;
         if (o_bf16) {
           u32x2 pk;
@@ -335,19 +471,28 @@ __global__ __launch_bounds__(128) void attn_simt_kernel(const Geom g, const T* _
   }
 }
 
-int64_t vt_len(const Geom& g) { return (int64_t)align_up((size_t)g.nk * g.C, 64); }
+#ifndef LOSA_ATTN_QUERY_TILES
+#define LOSA_ATTN_QUERY_TILES 4
+#endif
+// 16-query tiles per wave: 4 (4 waves per workgroup) or 2 (8 waves).
+constexpr int kAttnQueryTiles = LOSA_ATTN_QUERY_TILES;
+
+// 32-token chunks in the packed K/V copies (even, so the transpose's 64-token tiles cover it).
+int vt_chunks(const Geom& g) { return (int)(align_up((size_t)g.nk * g.C, 64) / 32); }
 
 template <int D>
 hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* V, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* order, void* O, int o_bf16, void* ws,
                        hipStream_t st) {
-  const int64_t Lt = vt_len(g);
-  __bf16* Vt = reinterpret_cast<__bf16*>(ws);
-  hipLaunchKernelGGL(transpose_v_kernel, dim3((unsigned)(Lt / 64), D / 64, g.B * g.H), dim3(256), 0, st, g,
-                     (const __bf16*)V, Vt, Lt);
-  const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float);
-  hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st, g,
-                     (const __bf16*)Q, (const __bf16*)K, (const __bf16*)Vt, Lt, row_ptr, col_idx, order, O,
+  constexpr int QT = kAttnQueryTiles;
+  const int nch = vt_chunks(g);
+  __bf16* Kp = reinterpret_cast<__bf16*>(ws);
+  __bf16* Vp = Kp + (size_t)g.B * g.H * nch * 32 * D;
+  hipLaunchKernelGGL((pack_kv_kernel<D>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
+                     (const __bf16*)K, (const __bf16*)V, Kp, Vp, nch);
+  const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float) + (size_t)64 * D * sizeof(uint16_t);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, QT>), dim3(g.rows() * (g.R / 64)), dim3(64 * attn_waves<QT>()), lds, st,
+                     g, (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, row_ptr, col_idx, order, O,
                      o_bf16);
   return hipGetLastError();
 }
@@ -364,7 +509,7 @@ hipError_t launch_simt(const Geom& g, const void* Q, const void* K, const void* 
 
 size_t attn_ws_bytes(const Geom& g) {
   if (!mfma_path(g)) return 0;
-  return (size_t)g.B * g.H * g.D * (size_t)vt_len(g) * sizeof(uint16_t);
+  return 2 * (size_t)g.B * g.H * g.D * (size_t)vt_chunks(g) * 32 * sizeof(uint16_t);  // packed K and V
 }
 
 hipError_t launch_sparse_attn(const Geom& g, const void* Q, const void* K, const void* V,
