@@ -65,7 +65,7 @@ losa_status check_input(const Geom& g, const void* p, const int64_t st[3]) {
 
 losa_status hip_status(hipError_t e) { return e == hipSuccess ? LOSA_OK : LOSA_ERR_HIP; }
 
-size_t mass_ws(const Geom& g) { return (size_t)g.B * g.H * g.Na * sizeof(float); }
+size_t mass_ws(const Geom& g) { return losa::mass_ws_bytes(g); }
 
 }  // namespace
 
@@ -105,7 +105,7 @@ losa_status losa_block_mass(const losa_shape* shape, const void* Q, const void* 
   if (!M || !ws) return LOSA_ERR_NULL;
   if (!aligned16(M)) return LOSA_ERR_INVALID_ARG;
   if (ws_bytes < mass_ws(g) || !aligned16(ws)) return LOSA_ERR_WORKSPACE;
-  return hip_status(losa::launch_block_mass(g, Q, K, M, reinterpret_cast<float*>(ws), stream));
+  return hip_status(losa::launch_block_mass(g, Q, K, M, ws, stream));
 }
 
 losa_status losa_select_workspace(const losa_shape* shape, size_t* bytes) {

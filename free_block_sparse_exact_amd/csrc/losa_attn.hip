@@ -27,64 +27,12 @@
 //     the current one, and V likewise after the P.V MFMAs.
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
+#include "losa_pack.hpp"
 
 namespace losa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-
-// K and V -> lane-major operand copies, one 32-token chunk at a time, so that
-// every operand load in the attention kernel is 64 lanes x 16 contiguous
-// bytes (lane order), the pattern the vector memory path coalesces fully.
-//   Kp[bh][c][kt][dc][lane][8]: row 32c + 8*((lane&15)>>2) + 4*kt + (lane&3)
-//       of K, elements dc*32 + (lane>>4)*8 + [0,8) (the A operand of S^T = K Q^T
-//       for key tile kt and k-step dc);
-//   Vp[bh][c][dt][lane][8]: V[32c + (lane>>4)*8 + e][dt*16 + (lane&15)]
-//       for e in [0,8) (the A operand of O^T += V^T P^T for dim tile dt).
-// Tokens >= N are written as zeros.  Grid: (nch / 2, B*H) with nch even;
-// each workgroup packs 64 tokens (two chunks), V through an LDS tile.
-template <int D>
-__global__ __launch_bounds__(256) void pack_kv_kernel(const Geom g, const __bf16* __restrict__ K,
-                                                      const __bf16* __restrict__ V, __bf16* __restrict__ Kp,
-                                                      __bf16* __restrict__ Vp, int nch) {
-  constexpr int DC = D / 32, DT = D / 16;
-  __shared__ uint16_t vt[64][D + 2];
-  const int t0 = blockIdx.x * 64, bh = blockIdx.y;
-  const int b = bh / g.H, h = bh - b * g.H;
-  const __bf16* Kbh = K + b * g.ks[0] + h * g.ks[1];
-  const uint16_t* Vbh = reinterpret_cast<const uint16_t*>(V + b * g.vs[0] + h * g.vs[1]);
-  for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
-    const int tt = idx / D, dd = idx - tt * D;
-    const int tok = t0 + tt;
-    vt[tt][dd] = tok < g.N ? Vbh[(int64_t)tok * g.vs[2] + dd] : (uint16_t)0;
-  }
-  const int64_t cbase = (int64_t)bh * nch + (t0 >> 5);
-  // K: 2 chunks x 2 key tiles x DC k-steps x 64 lanes pieces of 16 bytes.
-  for (int idx = threadIdx.x; idx < 2 * 2 * DC * 64; idx += 256) {
-    const int lane = idx & 63, rest = idx >> 6;
-    const int dc = rest % DC, kt = (rest / DC) & 1, cc = rest / (2 * DC);
-    const int lr = lane & 15;
-    const int tok = t0 + cc * 32 + ((lr >> 2) << 3) + kt * 4 + (lr & 3);
-    bf16x8 v = bf16x8{};
-    if (tok < g.N) v = load_bf16x8(Kbh + (int64_t)tok * g.ks[2] + dc * 32 + (lane >> 4) * 8);
-    *reinterpret_cast<bf16x8*>(Kp + ((cbase + cc) * 2 * DC * 64 + idx - cc * 2 * DC * 64) * 8) = v;
-  }
-  __syncthreads();
-  // V: 2 chunks x DT dim tiles x 64 lanes pieces of 16 bytes.
-  for (int idx = threadIdx.x; idx < 2 * DT * 64; idx += 256) {
-    const int lane = idx & 63, dt = (idx >> 6) % DT, cc = idx / (DT * 64);
-    const int dv = dt * 16 + (lane & 15), k0 = cc * 32 + (lane >> 4) * 8;
-    uint16_t e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = vt[k0 + j][dv];
-    u32x4 pk;
-    pk[0] = e[0] | ((uint32_t)e[1] << 16);
-    pk[1] = e[2] | ((uint32_t)e[3] << 16);
-    pk[2] = e[4] | ((uint32_t)e[5] << 16);
-    pk[3] = e[6] | ((uint32_t)e[7] << 16);
-    *reinterpret_cast<u32x4*>(Vp + ((cbase + cc) * DT * 64 + idx - cc * DT * 64) * 8) = pk;
-  }
-}
 
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
                                         float a7) {
@@ -477,8 +425,7 @@ __global__ __launch_bounds__(128) void attn_simt_kernel(const Geom g, const T* _
 // 16-query tiles per wave: 4 (4 waves per workgroup) or 2 (8 waves).
 constexpr int kAttnQueryTiles = LOSA_ATTN_QUERY_TILES;
 
-// 32-token chunks in the packed K/V copies (even, so the transpose's 64-token tiles cover it).
-int vt_chunks(const Geom& g) { return (int)(align_up((size_t)g.nk * g.C, 64) / 32); }
+int vt_chunks(const Geom& g) { return packed_chunks(g); }
 
 template <int D>
 hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* V, const int32_t* row_ptr,
@@ -488,7 +435,7 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* 
   const int nch = vt_chunks(g);
   __bf16* Kp = reinterpret_cast<__bf16*>(ws);
   __bf16* Vp = Kp + (size_t)g.B * g.H * nch * 32 * D;
-  hipLaunchKernelGGL((pack_kv_kernel<D>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
+  hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)V, Kp, Vp, nch);
   const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float) + (size_t)64 * D * sizeof(uint16_t);
   hipLaunchKernelGGL((attn_bf16_kernel<D, QT>), dim3(g.rows() * (g.R / 64)), dim3(64 * attn_waves<QT>()), lds, st,

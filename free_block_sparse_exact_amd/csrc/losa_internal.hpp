@@ -32,8 +32,10 @@ inline bool mfma_path(const Geom& g) {
   return g.bf16 && (g.D == 64 || g.D == 128) && (g.R == 64 || g.R == 128);
 }
 
-// Block masses: lse2 is workspace of B*H*Na floats.
-hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, float* lse2,
+// Block masses.  Workspace: row log-sum-exp (B*H*Na floats) and, on the
+// matrix-core path, a packed copy of K.
+size_t mass_ws_bytes(const Geom& g);
+hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, void* ws,
                              hipStream_t stream);
 
 // Selection.

@@ -20,6 +20,7 @@
 // and 4 keys per 16-key tile, so the per-query statistics live in lanes.
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
+#include "losa_pack.hpp"
 
 namespace losa {
 namespace {
@@ -50,17 +51,22 @@ struct QTile {
   }
 };
 
-// S^T for one 32-key chunk (keys kb + kt*16 + 4*lg + r in acc[kt][qt][r]).
+// K operand of one 32-key chunk from the packed copy (64 lanes x 16
+// contiguous bytes per load).  acc[kt][qt][r] then holds the score of key
+// kb + 8*lg + 4*kt + r (the packed row order) for query qt*16 + lr.
 template <int D>
-__device__ __forceinline__ void chunk_scores(const QTile<D>& q, const __bf16* Kbh, int64_t ts, int kb,
-                                             int lr, int lg, f32x4 (&acc)[2][4]) {
+__device__ __forceinline__ void load_kchunk(const __bf16* Kpbh, int kb, int lane, bf16x8 (&kop)[2][D / 32]) {
   constexpr int DC = D / 32;
-  bf16x8 kop[2][DC];
+  const __bf16* kc = Kpbh + (int64_t)(kb >> 5) * (32 * D) + lane * 8;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc)
-      kop[kt][dc] = load_bf16x8(Kbh + (int64_t)(kb + kt * 16 + lr) * ts + dc * 32 + lg * 8);
+    for (int dc = 0; dc < DC; ++dc) kop[kt][dc] = load_bf16x8(kc + (kt * DC + dc) * 512);
+}
+
+template <int D>
+__device__ __forceinline__ void chunk_scores(const QTile<D>& q, const bf16x8 (&kop)[2][D / 32], f32x4 (&acc)[2][4]) {
+  constexpr int DC = D / 32;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -72,11 +78,32 @@ __device__ __forceinline__ void chunk_scores(const QTile<D>& q, const __bf16* Kb
     }
 }
 
-// Pass 1.  Grid: B*H*ceil(N/64) workgroups of 256 threads.
+__device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&acc)[2][4]) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool dead = kb + lg * 8 + kt * 4 + r >= n_valid;
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+        if (dead) acc[kt][qt][r] = kNegInf;
+    }
+}
+
+// Pass 1.  Grid: B*H*ceil(N/64) workgroups of 256 threads (two per CU).
+// Each lane keeps, per query, a sum of 2^(s*c - m) over its own keys against
+// a reference m fixed at its first chunk's maximum plus kHeadroom (log2
+// units): no per-score maximum.  A term can only overflow if a later score
+// exceeds that maximum by more than ~190; terms more than ~85 below it flush
+// to 0, negligible against the maximum term.  If a lane's sum ever leaves
+// (0, 2^100] the wave recomputes its chunks in two passes (exact per-lane
+// maximum first).  Lanes, then waves, are merged at the end.
 template <int D>
-__global__ __launch_bounds__(256) void lse_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
-                                                       const __bf16* __restrict__ K,
-                                                       float* __restrict__ lse2) {
+__global__ __launch_bounds__(256, 2) void lse_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
+                                                          const __bf16* __restrict__ Kp, int nch,
+                                                          float* __restrict__ lse2) {
+  constexpr float kHeadroom = 64.0f;
+  constexpr float kSumBound = 1.2676506e30f;  // 2^100
   const int tiles = (g.N + 63) / 64;
   const int task = xcd_task(blockIdx.x, g.B * g.H * tiles);
   const int bh = task / tiles, t = task - bh * tiles;
@@ -84,7 +111,7 @@ __global__ __launch_bounds__(256) void lse_bf16_kernel(const Geom g, const __bf1
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
-  const __bf16* Kbh = K + b * g.ks[0] + h * g.ks[1];
+  const __bf16* Kpbh = Kp + (int64_t)bh * nch * (32 * D);
 
   QTile<D> q;
   q.load(Qbh, g.qs[2], t * 64, g.N, lr, lg);
@@ -94,29 +121,68 @@ __global__ __launch_bounds__(256) void lse_bf16_kernel(const Geom g, const __bf1
 
   const float c = g.scale_log2;
   const int nchunks = (g.N + 31) / 32;
-  for (int ch = w; ch < nchunks; ch += 4) {
-    const int kb = ch * 32;
-    f32x4 acc[2][4];
-    chunk_scores<D>(q, Kbh, g.ks[2], kb, lr, lg, acc);
-    const bool partial = kb + 32 > g.N;
+  const int nmine = nchunks > w ? (nchunks - w + 3) / 4 : 0;
+  bool fallback = false;
+  if (nmine > 0) {
+    bf16x8 kop[2][D / 32];
+    load_kchunk<D>(Kpbh, w * 32, lane, kop);
+    for (int it = 0; it < nmine; ++it) {
+      const int kb = (w + 4 * it) * 32;
+      f32x4 acc[2][4];
+      chunk_scores<D>(q, kop, acc);
+      if (it + 1 < nmine) load_kchunk<D>(Kpbh, kb + 128, lane, kop);
+      if (__builtin_expect(kb + 32 > g.N, 0)) mask_tail(kb, g.N, lg, acc);
+      if (it == 0) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      float x[8];
+        for (int qt = 0; qt < 4; ++qt) {
+          float mx = acc[0][qt][0];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = acc[kt][qt][r] * c;
-          if (partial && kb + kt * 16 + lg * 4 + r >= g.N) v = kNegInf;
-          x[kt * 4 + r] = v;
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, acc[e >> 2][qt][e & 3]);
+          m[qt] = mx * c + kHeadroom;  // -inf (all masked) forces the fallback
         }
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      const float mn = fmaxf(m[qt], mx);  // finite: every chunk holds a valid key
-      float sum = 0.f;
+      }
+      bool over = false;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum += fast_exp2(x[e] - mn);
-      s[qt] = s[qt] * fast_exp2(m[qt] - mn) + sum;
-      m[qt] = mn;
+      for (int qt = 0; qt < 4; ++qt) {
+        const float nm = -m[qt];
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
+        s[qt] += sum;
+        over |= !(s[qt] <= kSumBound);
+      }
+      if (__builtin_expect(__any(over), 0)) { fallback = true; break; }
+    }
+  }
+  if (fallback) {
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) { m[qt] = kNegInf; s[qt] = 0.f; }
+    bf16x8 kop[2][D / 32];
+    for (int it = 0; it < nmine; ++it) {
+      const int kb = (w + 4 * it) * 32;
+      load_kchunk<D>(Kpbh, kb, lane, kop);
+      f32x4 acc[2][4];
+      chunk_scores<D>(q, kop, acc);
+      if (kb + 32 > g.N) mask_tail(kb, g.N, lg, acc);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[qt] = fmaxf(m[qt], acc[e >> 2][qt][e & 3]);
+    }
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) m[qt] *= c;
+    for (int it = 0; it < nmine; ++it) {
+      const int kb = (w + 4 * it) * 32;
+      load_kchunk<D>(Kpbh, kb, lane, kop);
+      f32x4 acc[2][4];
+      chunk_scores<D>(q, kop, acc);
+      if (kb + 32 > g.N) mask_tail(kb, g.N, lg, acc);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const float nm = m[qt] == kNegInf ? 0.f : -m[qt];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[qt] += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
+      }
     }
   }
 
@@ -155,12 +221,14 @@ __global__ __launch_bounds__(256) void lse_bf16_kernel(const Geom g, const __bf1
   }
 }
 
-// Pass 2.  Grid: B*H*nq workgroups of 256*QG threads (QG = R/64 query groups).
+// Pass 2.  Grid: B*H*nq workgroups of 256*QG threads (QG = R/64 query groups),
+// two waves per SIMD.  Key block j goes to key group j % 4; its 32-key chunks
+// are summed as exp2(s*c - lse2_q) and reduced over the wave.
 template <int D, int QG>
-__global__ __launch_bounds__(256 * QG) void block_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
-                                                              const __bf16* __restrict__ K,
-                                                              const float* __restrict__ lse2,
-                                                              float* __restrict__ M) {
+__global__ __launch_bounds__(256 * QG, 2 / QG) void block_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
+                                                                      const __bf16* __restrict__ Kp, int nch,
+                                                                      const float* __restrict__ lse2,
+                                                                      float* __restrict__ M) {
   extern __shared__ float part[];  // [QG][nk]
   const int rows = g.B * g.H * g.nq;
   const int task = xcd_task(blockIdx.x, rows);
@@ -170,7 +238,7 @@ __global__ __launch_bounds__(256 * QG) void block_bf16_kernel(const Geom g, cons
   const int grp = w >> 2, kw = w & 3;
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
-  const __bf16* Kbh = K + b * g.ks[0] + h * g.ks[1];
+  const __bf16* Kpbh = Kp + (int64_t)bh * nch * (32 * D);
   const int row0 = i * g.R + grp * 64;
 
   QTile<D> q;
@@ -189,20 +257,17 @@ __global__ __launch_bounds__(256 * QG) void block_bf16_kernel(const Geom g, cons
     for (int sc = 0; sc < sub; ++sc) {
       const int kb = j * g.C + sc * 32;
       if (kb >= g.N) break;
+      bf16x8 kop[2][D / 32];
+      load_kchunk<D>(Kpbh, kb, lane, kop);
       f32x4 acc[2][4];
-      chunk_scores<D>(q, Kbh, g.ks[2], kb, lr, lg, acc);
-      const bool partial = kb + 32 > g.N;
+      chunk_scores<D>(q, kop, acc);
+      if (__builtin_expect(kb + 32 > g.N, 0)) mask_tail(kb, g.N, lg, acc);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int qt = 0; qt < 4; ++qt) {
+        const float nl = -l2[qt];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool dead = partial && kb + kt * 16 + lg * 4 + r >= g.N;
-#pragma unroll
-          for (int qt = 0; qt < 4; ++qt) {
-            const float e = fast_exp2(acc[kt][qt][r] * c - l2[qt]);
-            tot += dead ? 0.f : e;
-          }
-        }
+        for (int e = 0; e < 8; ++e) tot += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nl));
+      }
     }
     tot = wave_sum(tot);
     if (lane == 0) part[grp * g.nk + j] = tot;
@@ -323,26 +388,39 @@ hipError_t launch_simt(const Geom& g, const void* Q, const void* K, float* M, fl
 }
 
 template <int D>
-hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* lse2, hipStream_t st) {
+hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* lse2, __bf16* Kp,
+                       hipStream_t st) {
+  const int nch = packed_chunks(g);
+  hipLaunchKernelGGL((pack_kv_kernel<D, false>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
+                     (const __bf16*)K, (const __bf16*)nullptr, Kp, (__bf16*)nullptr, nch);
   const int tiles = (g.N + 63) / 64;
-  hipLaunchKernelGGL((lse_bf16_kernel<D>), dim3(g.B * g.H * tiles), dim3(256), 0, st, g,
-                     (const __bf16*)Q, (const __bf16*)K, lse2);
+  hipLaunchKernelGGL((lse_bf16_kernel<D>), dim3(g.B * g.H * tiles), dim3(256), 0, st, g, (const __bf16*)Q,
+                     (const __bf16*)Kp, nch, lse2);
   const size_t lds = (size_t)(g.R / 64) * g.nk * sizeof(float);
   if (g.R == 64)
-    hipLaunchKernelGGL((block_bf16_kernel<D, 1>), dim3(g.rows()), dim3(256), lds, st, g,
-                       (const __bf16*)Q, (const __bf16*)K, (const float*)lse2, M);
+    hipLaunchKernelGGL((block_bf16_kernel<D, 1>), dim3(g.rows()), dim3(256), lds, st, g, (const __bf16*)Q,
+                       (const __bf16*)Kp, nch, (const float*)lse2, M);
   else
-    hipLaunchKernelGGL((block_bf16_kernel<D, 2>), dim3(g.rows()), dim3(512), lds, st, g,
-                       (const __bf16*)Q, (const __bf16*)K, (const float*)lse2, M);
+    hipLaunchKernelGGL((block_bf16_kernel<D, 2>), dim3(g.rows()), dim3(512), lds, st, g, (const __bf16*)Q,
+                       (const __bf16*)Kp, nch, (const float*)lse2, M);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, float* lse2,
+size_t mass_ws_bytes(const Geom& g) {
+  size_t n = align_up((size_t)g.B * g.H * g.Na * sizeof(float), 256);  // row log-sum-exp (log2 units)
+  if (mfma_path(g)) n += (size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t);  // packed K
+  return n;
+}
+
+hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, void* ws,
                              hipStream_t stream) {
-  if (mfma_path(g)) return g.D == 128 ? launch_mfma<128>(g, Q, K, M, lse2, stream)
-                                      : launch_mfma<64>(g, Q, K, M, lse2, stream);
+  float* lse2 = reinterpret_cast<float*>(ws);
+  __bf16* Kp = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(ws) +
+                                         align_up((size_t)g.B * g.H * g.Na * sizeof(float), 256));
+  if (mfma_path(g)) return g.D == 128 ? launch_mfma<128>(g, Q, K, M, lse2, Kp, stream)
+                                      : launch_mfma<64>(g, Q, K, M, lse2, Kp, stream);
   if (g.bf16)
     return g.D == 128 ? launch_simt<__bf16, 128>(g, Q, K, M, lse2, stream)
                       : launch_simt<__bf16, 64>(g, Q, K, M, lse2, stream);
