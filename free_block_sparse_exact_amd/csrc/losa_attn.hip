@@ -13,8 +13,8 @@
 //     dispatched in the caller's budget order.  Its waves split the row's
 //     32-key chunks (wave kw of each query group takes chunks kw, kw+4, ...),
 //     each keeping its own online-softmax state for its queries; the four key
-//     groups are merged through LDS at the end.  The Q tile sits in LDS in
-//     the same lane-major form and is read per chunk;
+//     groups are merged through LDS at the end.  Each wave holds its Q tile
+//     as MFMA B operands in registers;
 //   * S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA.  K rows are fed
 //     in the permuted order kappa(kt, rho) = 8*(rho>>2) + 4*kt + (rho&3), so
 //     lane l ends up holding the eight consecutive keys 8*(l>>4)+[0,8) of
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   constexpr int DC = D / 32, DT = D / 16;
   constexpr int kAttnWaves = attn_waves<kQT>();
   constexpr int LD = D + 4;   // merge slot row stride (floats)
-  extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]; then Q tile, lane-major, bf16
+  extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]
   const int qhalves = g.R / 64;
   const int tix = blockIdx.x;
   const int ridx = tix / qhalves, qsub = tix - ridx * qhalves;
@@ -88,20 +88,19 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   const __bf16* Vbh = Vp + (int64_t)bh * nch * (32 * D);
   const int row0 = i * g.R + qsub * 64;
 
-  // Q tile (64 rows) in LDS, lane-major like the packed K: piece (qt, dc,
-  // lane) holds row qt*16 + (lane&15), elements dc*32 + (lane>>4)*8 + [0,8),
-  // so each wave's B-operand reads are 64 lanes x 16 contiguous bytes.
-  // Padding rows -> 0.
-  __bf16* qs = reinterpret_cast<__bf16*>(lds + 64 * LD + 128);
-  for (int idx = threadIdx.x; idx < 4 * DC * 64; idx += 64 * kAttnWaves) {
-    const int ln = idx & 63, dc = (idx >> 6) % DC, qt4 = idx / (DC * 64);
-    const int qrow = row0 + qt4 * 16 + (ln & 15);
-    bf16x8 v = load_bf16x8(Qbh + (int64_t)qrow * g.qs[2] + dc * 32 + (ln >> 4) * 8);
-    if (qrow >= g.N) v = bf16x8{};
-    *reinterpret_cast<bf16x8*>(qs + idx * 8) = v;
+  // Q as the B operand of S^T = K Q^T, held in registers for the whole row
+  // (padding rows -> 0).
+  bf16x8 qop[kQT][DC];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int qrow = row0 + (qh * kQT + qt) * 16 + lr;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      bf16x8 v = load_bf16x8(Qbh + (int64_t)qrow * g.qs[2] + dc * 32 + lg * 8);
+      if (qrow >= g.N) v = bf16x8{};
+      qop[qt][dc] = v;
+    }
   }
-  __syncthreads();
-  const __bf16* qlane = qs + ((qh * kQT) * DC * 64 + lane) * 8;
 
   f32x4 o[DT][kQT];
   float m[kQT], l[kQT];
@@ -138,7 +137,6 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   // S^T for one chunk: acc[kt][qt][r] = score of key kb + 8*lg + 4*kt + r for
   // query qh*32 + qt*16 + lr.
   auto scores = [&](const bf16x8 (&kop)[2][DC], f32x4 (&acc)[2][kQT]) {
-    asm volatile("" ::: "memory");  // keep the Q reads from LDS here (not hoisted into registers)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -146,7 +144,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc)
-          a = mfma_bf16(kop[kt][dc], *reinterpret_cast<const bf16x8*>(qlane + (qt * DC + dc) * 512), a);
+          a = mfma_bf16(kop[kt][dc], qop[qt][dc], a);
         acc[kt][qt] = a;
       }
   };
@@ -419,11 +417,10 @@ __global__ __launch_bounds__(128) void attn_simt_kernel(const Geom g, const T* _
   }
 }
 
-#ifndef LOSA_ATTN_QUERY_TILES
-#define LOSA_ATTN_QUERY_TILES 4
-#endif
-// 16-query tiles per wave: 4 (4 waves per workgroup) or 2 (8 waves).
-constexpr int kAttnQueryTiles = LOSA_ATTN_QUERY_TILES;
+// 16-query tiles per wave: 4 (4 waves per workgroup, one wave per SIMD).  With
+// 2 (8 waves, two per SIMD) the two query halves read every K/V chunk twice,
+// which saturates the texture path; 4 measured faster.
+constexpr int kAttnQueryTiles = 4;
 
 int vt_chunks(const Geom& g) { return packed_chunks(g); }
 
@@ -437,7 +434,7 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* 
   __bf16* Vp = Kp + (size_t)g.B * g.H * nch * 32 * D;
   hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)V, Kp, Vp, nch);
-  const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float) + (size_t)64 * D * sizeof(uint16_t);
+  const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float);
   hipLaunchKernelGGL((attn_bf16_kernel<D, QT>), dim3(g.rows() * (g.R / 64)), dim3(64 * attn_waves<QT>()), lds, st,
                      g, (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, row_ptr, col_idx, order, O,
                      o_bf16);
