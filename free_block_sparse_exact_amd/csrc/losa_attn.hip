@@ -75,7 +75,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   constexpr int LD = D + 4;   // merge slot row stride (floats)
   extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]
   const int qhalves = g.R / 64;
-  const int tix = blockIdx.x;
+  const int tix = xcd_block_task(blockIdx.x, gridDim.x);
   const int ridx = tix / qhalves, qsub = tix - ridx * qhalves;
   const int row = order ? order[ridx] : ridx;
   const int bh = row / g.nq, i = row - bh * g.nq;

@@ -73,4 +73,19 @@ __device__ __forceinline__ int xcd_task(int bid, int n) {
   return start + local;
 }
 
+// Workgroup id -> task for work lists whose neighbouring tasks read the same
+// data (rows of one head, in the budget order): consecutive blocks of 32
+// tasks are dealt to the 8 XCDs round-robin, so at any time each XCD's CUs
+// run 32 neighbouring tasks (sharing that XCD's L2) while every XCD still
+// draws from the whole list (keeping uneven budgets balanced across XCDs).
+// A bijection on [0, n); the tail beyond the last whole group of 8*32 tasks
+// keeps the identity.
+__device__ __forceinline__ int xcd_block_task(int bid, int n) {
+  constexpr int kXcd = 8, kBlock = 32, kGroup = kXcd * kBlock;
+  const int full = n / kGroup * kGroup;
+  if (bid >= full) return bid;
+  const int xcd = bid % kXcd, local = bid / kXcd;
+  return (local / kBlock) * kGroup + xcd * kBlock + (local % kBlock);
+}
+
 }  // namespace losa
