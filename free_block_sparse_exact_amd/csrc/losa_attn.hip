@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   const int row = order ? order[ridx] : ridx;
   const int bh = row / g.nq, i = row - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kw = w & 3, qh = w >> 2;
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
@@ -205,43 +205,103 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   // the reference m is fixed at the wave's first chunk's maximum plus
   // kHeadroom (log2 units), so later chunks may exceed it by up to
   // kHeadroom + 16 before a sum leaves (0, kPBound]; terms more than ~60 below
-  // the maximum are negligible either way.  If that ever happens the wave
-  // drops its partial sums and recomputes its chunks in two passes (exact
-  // maximum first), so all probabilities are <= 1.
-  // K of the next chunk is requested as soon as the score MFMAs have read the
-  // current K, V of the next chunk once the P.V MFMAs have read the current V.
-  // Chunks wholly inside the padding of the last block are loaded (in bounds:
-  // below n_k*C) and fully masked rather than skipped.
+  // the maximum are negligible either way.  If that ever happens the wave,
+  // once through its chunks, drops its partial sums and recomputes them in
+  // two passes (exact maximum first), so all probabilities are <= 1.  The
+  // loop has a single exit: an early exit makes the register allocator shuffle
+  // the O accumulators on every trip.
+  //
+  // Software pipeline: iteration t issues the score MFMAs of chunk t+1 next to
+  // the softmax of chunk t, then P.V of chunk t; the scheduler is asked to
+  // alternate one MFMA with two vector instructions.  K of chunk t+2 is
+  // requested once the score MFMAs have read K, V of chunk t+1 once P.V has
+  // read V.
+  //
+  // Padding keys of the last block score exactly 0 against the zero rows of
+  // the packed K, which can lie far above every real score of a row, so they
+  // must leave the softmax; the loop itself does no masking.  With C <= 128 a
+  // wave owns at most one 32-key chunk of the last block: a partly padded one
+  // is moved to the front of the wave's sequence (the first chunk is masked
+  // explicitly), a wholly padded one is dropped.  Indices within a row are
+  // distinct, so the last block occurs at most once.
   constexpr float kHeadroom = 64.0f;
-  const int nmine = nchunk > kw ? (nchunk - kw + 3) / 4 : 0;
-  auto key_of = [&](int t) { return chunk_key(kw + 4 * (t < nmine ? t : nmine - 1)); };
+  int nmine = nchunk > kw ? (nchunk - kw + 3) / 4 : 0;
+  int swap_a = 0, swap_b = 0;  // positions exchanged in the wave's chunk sequence
+  if (g.N != g.nk * g.C && nmine > 0) {
+    const int n = end - beg;
+    int pos = -1;  // position of the last block in the row's list
+    for (int base = 0; base < n; base += 4 * kWave) {
+      uint64_t hit[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = base + j * kWave + lane;
+        hit[j] = __ballot(x < n && col_idx[beg + x] == g.nk - 1);
+      }
+#pragma unroll
+      for (int j = 3; j >= 0; --j)
+        if (hit[j]) pos = base + j * kWave + __builtin_ctzll(hit[j]);
+      if (pos >= 0) break;
+    }
+    if (pos >= 0) {
+      for (int s = 0; s < sub; ++s) {
+        const int u = pos * sub + s;
+        if ((u & 3) != kw) continue;
+        const int key0 = (g.nk - 1) * g.C + 32 * s, t = u >> 2;
+        if (key0 >= g.N) {             // wholly padding: move it last and drop it
+          swap_a = t;
+          swap_b = nmine - 1;
+          --nmine;
+        } else if (key0 + 32 > g.N) {  // partly padding: move it first
+          swap_b = t;
+        }
+      }
+    }
+  }
+  auto key_of = [&](int t) {
+    t = t < nmine ? t : nmine - 1;
+    t = t == swap_a ? swap_b : (t == swap_b ? swap_a : t);
+    return chunk_key(kw + 4 * t);
+  };
   bool fallback = false;
   bf16x8 kop[2][DC], vop[DT];
   if (nmine > 0) {
     int kb = key_of(0);
     load_k(kb, kop);
     load_v(kb, vop);
-    for (int t = 0; t < nmine; ++t) {
-      const int kbn = key_of(t + 1);
-      f32x4 acc[2][kQT];
-      scores(kop, acc);
-      load_k(kbn, kop);
-      if (__builtin_expect(kb + 32 > g.N, 0)) mask_tail(kb, acc);
-      if (t == 0) {
-        float mx[kQT];
+    f32x4 acc[2][kQT];
+    scores(kop, acc);
+    load_k(key_of(1), kop);
+    if (kb + 32 > g.N) mask_tail(kb, acc);
+    {
+      float mx[kQT];
 #pragma unroll
-        for (int qt = 0; qt < kQT; ++qt) mx[qt] = kNegInf;
-        chunk_max(acc, mx);
-        lanes_max(mx);
+      for (int qt = 0; qt < kQT; ++qt) mx[qt] = kNegInf;
+      chunk_max(acc, mx);
+      lanes_max(mx);
 #pragma unroll
-        for (int qt = 0; qt < kQT; ++qt) m[qt] = mx[qt] * c + kHeadroom;  // -inf: forces the fallback
-      }
-      bf16x8 pop[kQT];
-      if (__builtin_expect(__any(probs(acc, pop)), 0)) { fallback = true; break; }
-      pv(vop, pop);
-      load_v(kbn, vop);
-      kb = kbn;
+      for (int qt = 0; qt < kQT; ++qt) m[qt] = mx[qt] * c + kHeadroom;  // -inf: forces the fallback
     }
+    bool over_any = false;
+    for (int t = 0; t < nmine; ++t) {
+      f32x4 accn[2][kQT];
+      scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
+      load_k(key_of(t + 2), kop);
+      bf16x8 pop[kQT];
+      const bool over = probs(acc, pop);  // chunk t
+      pv(vop, pop);
+      load_v(key_of(t + 1), vop);
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // then two vector ALU ops
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = accn[kt][qt];
+      over_any |= over;
+    }
+    fallback = __any(over_any);
   }
   if (fallback) {
 #pragma unroll

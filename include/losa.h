@@ -154,14 +154,17 @@ losa_status losa_select(const losa_shape* shape, const float* M, const double* p
  * block is added.  A row with an empty list gets O = 0.
  *
  * row_ptr/col_idx: CSR as produced by losa_select (any order of indices is
- *    accepted; each index must lie in [0, n_k)).
+ *    accepted; each index must lie in [0, n_k) and occur at most once in a
+ *    row -- a repeated index gives an unspecified O, never an access outside
+ *    the buffers).
  * order: NULL (rows in index order) or a permutation of the rows giving the
  *    order in which work is dispatched (losa_select's budget order).  The
  *    result does not depend on it.
  * O: [batch, heads, tokens_alloc, head_dim] with shape->o_stride, element
  *    type o_dtype (LOSA_BF16 or LOSA_F32).
- * ws: at least *bytes from losa_sparse_attn_workspace (a head_dim-major copy
- *    of V for the bf16 matrix-core path; 0 bytes otherwise).
+ * ws: at least *bytes from losa_sparse_attn_workspace (bf16 matrix-core
+ *    path: K and V repacked in 32-token chunks as matrix-core operands, zero
+ *    beyond the last valid token; 0 bytes otherwise).
  * Arithmetic: bf16 inputs use bf16 matrix products with fp32 accumulation,
  * the probabilities rounded to bf16 for the P.V product; softmax statistics
  * in fp32.  f32 inputs use fp32 throughout.

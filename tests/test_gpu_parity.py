@@ -251,3 +251,48 @@ def test_retained_mass_matches_recall():
     rec_gpu = (kept[:, 0] * wr).sum() / (kept[:, 1] * wr).sum()
     rec_ref = O.recall(c["M32"].astype(np.float64), c["rp"], c["ci"], c["N"], c["R"])
     assert abs(rec_gpu - rec_ref) < 1e-5
+
+
+@pytest.mark.parametrize("shift", [225.0, 2500.0])
+@pytest.mark.parametrize("N", [1000, 970])
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_negative_logits_with_padded_tail(shift, N, shuffle):
+    """All logits of a row far below zero, keys padded in the last block.
+
+    Keys share one large direction u and queries point against it, so every
+    raw score is about -shift (scaled logits about -20, or about -220 where
+    2^-m of a zero score overflows fp32).  Padding keys (>= N) would score
+    exactly 0, far above every real key: they must leave the softmax.  N = 970
+    leaves the last 32-key chunk wholly padding; shuffled lists put the
+    padded block anywhere in a row's list.
+    """
+    rng = np.random.default_rng(int(shift) + N + 7 * shuffle)
+    H, d, R = 2, 128, 64
+    Na = -(-N // R) * R
+    nq = Na // R
+    a = float(np.sqrt(shift))
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = -a * u + rng.standard_normal((1, H, Na, d)) * 0.7
+    k = a * u + rng.standard_normal((1, H, Na, d)) * 0.7
+    v = rng.standard_normal((1, H, Na, d))
+    bits = [S.bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
+    q64, k64, v64 = (S.f64_from_bf16_bits(b) for b in bits)
+    rows = H * nq
+    lists = [np.arange(nq, dtype=np.int32) for _ in range(rows)]
+    if shuffle:
+        for l in lists:
+            rng.shuffle(l)
+    rp = np.arange(rows + 1, dtype=np.int64) * nq
+    ci = np.concatenate(lists)
+    ref = O.sparse_attention(q64, k64, v64, N, R, R, rp, ci)
+    s_max = max(float((q64[0, h, :N] @ k64[0, h, :N].T).max()) for h in range(H)) * O.softmax_scale(d)
+    say(f"shift {shift}: largest scaled logit {s_max:.1f}")
+    assert s_max < -10
+    qd, kd, vd = (to_device(b, "bf16") for b in bits)
+    rp_d, ci_d = csr_to_device(rp, ci)
+    Og = F.losa_sparse_attn(qd, kd, vd, rp_d, ci_d, None, N, R, R, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = float(np.abs(Og.cpu().numpy()[:, :, :N] - ref[:, :, :N]).max())
+    say(f"negative logits shift {shift} N {N} shuffle {shuffle}: max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
