@@ -27,9 +27,17 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  Sparse attention: matrix instructions take the form
+# whose result and accumulator live in vector registers.  Its scores feed
+# vector arithmetic straight away, and with one wave per SIMD the O
+# accumulators fit beside them; the default form parks results in AGPRs and
+# spends ~100 register moves per 32-key chunk copying them back and forth.
+EXTRA_FLAGS = {"losa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -98,6 +98,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
     for (int dc = 0; dc < DC; ++dc) {
       bf16x8 v = load_bf16x8(Qbh + (int64_t)qrow * g.qs[2] + dc * 32 + lg * 8);
       if (qrow >= g.N) v = bf16x8{};
+      asm("" : "+a"(v));  // only matrix instructions read Q: keep it in AGPRs (waits once, per row)
       qop[qt][dc] = v;
     }
   }
@@ -138,15 +139,14 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   // query qh*32 + qt*16 + lr.
   auto scores = [&](const bf16x8 (&kop)[2][DC], f32x4 (&acc)[2][kQT]) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          a = mfma_bf16(kop[kt][dc], qop[qt][dc], a);
-        acc[kt][qt] = a;
-      }
+      for (int dc = 0; dc < DC; ++dc)  // each K operand's four uses back to back
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = mfma_bf16(kop[kt][dc], qop[qt][dc], acc[kt][qt]);
+    }
   };
   // Padding keys of the last block's tail leave the softmax.
   auto mask_tail = [&](int kb, f32x4 (&acc)[2][kQT]) {
@@ -262,6 +262,18 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
     t = t == swap_a ? swap_b : (t == swap_b ? swap_a : t);
     return chunk_key(kw + 4 * t);
   };
+  // The loop reads its chunk keys from registers: lane j of a window holds
+  // key_of(base + j), so a key costs one lane read instead of a dependent
+  // scalar load of col_idx.  Two windows cover 128 chunks; the next one is
+  // loaded 64 iterations before it is needed.
+  const int sub_shift = __builtin_ctz(sub);
+  auto key_window = [&](int base) -> int {
+    int t = base + lane;
+    t = t < nmine ? t : nmine - 1;
+    t = t == swap_a ? swap_b : (t == swap_b ? swap_a : t);
+    const int u = kw + 4 * t, p = u >> sub_shift;
+    return col_idx[beg + p] * g.C + (u - (p << sub_shift)) * 32;
+  };
   bool fallback = false;
   bf16x8 kop[2][DC], vop[DT];
   if (nmine > 0) {
@@ -282,14 +294,26 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
       for (int qt = 0; qt < kQT; ++qt) m[qt] = mx[qt] * c + kHeadroom;  // -inf: forces the fallback
     }
     bool over_any = false;
+    int win_base = 0;
+    int win0 = key_window(0), win1 = key_window(64);
     for (int t = 0; t < nmine; ++t) {
+      if (t == win_base + 64) {  // keys t+1, t+2 now lie in [win_base + 64, win_base + 128)
+        win_base += 64;
+        win0 = win1;
+        win1 = key_window(win_base + 64);
+      }
+      auto key_at = [&](int i) {  // both lanes read, then a select: no branch inside the body
+        const int r = i - win_base;
+        const int k0 = __builtin_amdgcn_readlane(win0, r & 63), k1 = __builtin_amdgcn_readlane(win1, r & 63);
+        return r < 64 ? k0 : k1;
+      };
       f32x4 accn[2][kQT];
       scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
-      load_k(key_of(t + 2), kop);
+      load_k(key_at(t + 2), kop);
       bf16x8 pop[kQT];
       const bool over = probs(acc, pop);  // chunk t
       pv(vop, pop);
-      load_v(key_of(t + 1), vop);
+      load_v(key_at(t + 1), vop);
 #pragma unroll
       for (int i = 0; i < 64; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
