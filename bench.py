@@ -24,7 +24,11 @@ Other modes (used to produce the committed profile summaries):
                         write the traffic summary from the counter CSVs of a
                         FETCH_SIZE run F and a WRITE_SIZE run W of this
                         benchmark, and of the copy calibration under the same
-                        two counters (CF, CW).
+                        two counters (CF, CW);
+  --summarize-trace DIR NAME "CMD"
+                        write profiles/NAME.md from the kernel statistics of a
+                        rocprofv3 --kernel-trace --stats run (DIR) of the
+                        command CMD.
 """
 from __future__ import annotations
 
@@ -44,9 +48,21 @@ sys.path.insert(0, ROOT)
 METRIC = "block-sparse attn ms & effective TFLOP/s at p=0.99 (1 GPU); mass+select ms"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_traffic_wan13b_480p.json")
-ATTN_SOURCES = ["free_block_sparse_exact_amd/csrc/losa_attn.hip", "free_block_sparse_exact_amd/csrc/losa_pack.hpp",
-                "free_block_sparse_exact_amd/csrc/losa_device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_wan13b_480p.json")
+_CSRC = "free_block_sparse_exact_amd/csrc/"
+# sources each call's kernels are built from (a traffic figure is reported only while they are unchanged)
+CALL_SOURCES = {
+    "losa_sparse_attn": [_CSRC + "losa_attn.hip", _CSRC + "losa_pack.hpp", _CSRC + "losa_device.hpp",
+                         "free_block_sparse_exact_amd/_build.py"],
+    "losa_block_mass": [_CSRC + "losa_mass.hip", _CSRC + "losa_pack.hpp", _CSRC + "losa_device.hpp",
+                        "free_block_sparse_exact_amd/_build.py"],
+}
+# kernel name fragment -> (part, call) for the traffic summary
+PMC_KERNELS = [("attn_bf16_kernel", "attn", "losa_sparse_attn"),
+               ("pack_kv_kernelILi128ELb1", "pack_kv", "losa_sparse_attn"),
+               ("lse_bf16_kernel", "lse", "losa_block_mass"),
+               ("block_bf16_kernel", "block", "losa_block_mass"),
+               ("pack_kv_kernelILi128ELb0", "pack_k", "losa_block_mass")]
 
 
 def log(*a):
@@ -116,15 +132,19 @@ def cpu_baseline(layer, wl, rows_wanted, p, budget_s=20.0):
     }
 
 
-def load_traffic(nnz_launch: int):
-    """Traffic of the sparse-attention call from the committed PMC summary, if still current."""
+def load_traffic(call: str):
+    """HBM bytes per launch of one library call from the committed PMC summary,
+    if the call's kernel sources are unchanged since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None, "no PMC summary"
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("sources_sha256_16") != sources_hash(ATTN_SOURCES):
+    c = t.get("calls", {}).get(call)
+    if c is None:
+        return None, "call not in the PMC summary"
+    if c.get("sources_sha256_16") != sources_hash(CALL_SOURCES[call]):
         return None, "kernel sources changed since the counters were taken"
-    return t.get("bytes_per_call"), t.get("command")
+    return c.get("bytes"), t.get("command")
 
 
 class Buffers:
@@ -154,9 +174,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "NAME", "COMMAND"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -239,15 +263,18 @@ def main():
                    "GBps": sel_bytes / (sel_ms * 1e-3) / 1e9,
                    "frac_hbm_peak": sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
-    traffic, traffic_src = load_traffic(nnz) if wl.wid == "1" else (None, "measured for the Wan2.1-1.3B shape only")
-    if attn_ms >= mass_ms:
-        roofline = {"kernel": "losa_sparse_attn", "bound": "mfma", "achieved": attn_tflops,
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                    "traffic": traffic, "traffic_source": traffic_src}
-    else:
-        roofline = {"kernel": "losa_block_mass", "bound": "mfma", "achieved": mass_tflops,
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": mass_tflops / PEAK_BF16_TFLOPS,
-                    "traffic": None, "traffic_source": "not measured for this call"}
+    def traffic_of(call):
+        return load_traffic(call) if wl.wid == "1" else (None, "measured for the Wan2.1-1.3B shape only")
+
+    # The dominant kernel is attn_bf16_kernel (the mass call splits its time over two kernels).
+    traffic, traffic_src = traffic_of("losa_sparse_attn")
+    roofline = {"kernel": "losa_sparse_attn (pack_kv_kernel + attn_bf16_kernel)", "bound": "mfma",
+                "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "traffic_source": traffic_src}
+    traffic, traffic_src = traffic_of("losa_block_mass")
+    roofline_mass = {"kernel": "losa_block_mass (pack_kv_kernel + lse_bf16_kernel + block_bf16_kernel)",
+                     "bound": "mfma", "achieved": mass_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": mass_tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "traffic_source": traffic_src}
     cpu = None
     if args.cpu_rows > 0:
         log("timing the CPU oracle baseline ...")
@@ -276,6 +303,7 @@ def main():
         "coverage": nnz / float(rows * nk),
         "kernels": kernels,
         "roofline": roofline,
+        "roofline_mass": roofline_mass,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
@@ -390,8 +418,9 @@ def copy_calibration():
 
 
 def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
-    """Per-launch HBM traffic of the sparse-attention call from rocprofv3 CSVs,
-    scaled by a plain copy of 1 GiB (FETCH_SIZE/WRITE_SIZE are in KiB)."""
+    """Per-launch HBM traffic of the mass and sparse-attention calls from
+    rocprofv3 CSVs, scaled by a plain copy of 1 GiB (FETCH_SIZE/WRITE_SIZE
+    are in KiB)."""
     import csv
 
     def read(d, counter):
@@ -410,30 +439,76 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
     ff, wf = copy_factor(copy_fetch_dir, "FETCH_SIZE"), copy_factor(copy_write_dir, "WRITE_SIZE")
 
-    def per_call(tab, key):
+    def per_launch(tab, key):
         vals = [v for k, vs in tab.items() if key in k for v in vs]
         return float(np.mean(vals)) if vals else 0.0
 
-    parts = {}
-    for key, label in (("attn_bf16_kernel", "attn"), ("pack_kv_kernelILi128ELb1", "pack_kv")):
-        f_raw, w_raw = per_call(fetch, key), per_call(write, key)
-        parts[label] = {"fetch_bytes_raw": f_raw, "write_bytes_raw": w_raw,
-                        "bytes": f_raw * (ff or 1.0) + w_raw * (wf or 1.0)}
-    raw = sum(p["bytes"] for p in parts.values())
+    calls = {}
+    for key, part, call in PMC_KERNELS:
+        f_raw, w_raw = per_launch(fetch, key), per_launch(write, key)
+        c = calls.setdefault(call, {"sources_sha256_16": sources_hash(CALL_SOURCES[call]), "kernels": {}, "bytes": 0.0})
+        b = f_raw * (ff or 1.0) + w_raw * (wf or 1.0)
+        c["kernels"][part] = {"fetch_kib_raw": f_raw / 1024.0, "write_kib_raw": w_raw / 1024.0, "bytes": b}
+        c["bytes"] += b
     out = {
-        "call": "losa_sparse_attn (pack_kv + attn), Wan2.1-1.3B 480p shape, p = 0.99",
-        "sources_sha256_16": sources_hash(ATTN_SOURCES),
+        "workload": "Wan2.1-1.3B 480p layer shape (12 heads x 128, 32760 tokens, 64-token blocks), p = 0.99",
         "copy_scale": {"FETCH_SIZE": ff, "WRITE_SIZE": wf},
-        "kernels": parts,
-        "bytes_per_call": raw,
-        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python bench.py --steps 1 "
-                   "--warmup 1 --cpu-rows 0; copy scale from python bench.py --copy-calibration under the same "
-                   "counters",
+        "calls": calls,
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -o run -- python -u "
+                   "bench.py --steps 1 --warmup 1 --cpu-rows 0; copy scale from rocprofv3 --pmc <same counter> -- "
+                   "python -u bench.py --copy-calibration; summary by python bench.py --summarize-pmc",
     }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+# kernel name fragment -> (short name, call it belongs to)
+TRACE_KERNELS = [
+    ("attn_bf16_kernel", "attn_bf16_kernel", "losa_sparse_attn"),
+    ("pack_kv_kernelILi128ELb1", "pack_kv_kernel (K and V)", "losa_sparse_attn"),
+    ("pack_kv_kernelILi128ELb0", "pack_kv_kernel (K only)", "losa_block_mass"),
+    ("lse_bf16_kernel", "lse_bf16_kernel", "losa_block_mass"),
+    ("block_bf16_kernel", "block_bf16_kernel", "losa_block_mass"),
+    ("cut_kernel", "cut_kernel", "losa_select"),
+    ("scan_kernel", "scan_kernel", "losa_select"),
+    ("compact_kernel", "compact_kernel", "losa_select"),
+    ("place_kernel", "place_kernel", "losa_select"),
+    ("fill_i32_kernel", "fill_i32_kernel", "losa_select"),
+    ("retained_kernel", "retained_kernel", "losa_retained_mass"),
+]
+
+
+def summarize_trace(trace_dir, name, command):
+    """Short text summary of a rocprofv3 --kernel-trace --stats run: average
+    duration per kernel and per library call (the sums that the HIP events in
+    this benchmark bracket)."""
+    import csv
+    path = os.path.join(trace_dir, "run_kernel_stats.csv")
+    rows = list(csv.DictReader(open(path)))
+    lines = [f"# rocprofv3 kernel statistics: {name}", "",
+             "Command (run from the repository root, after building the library):", "",
+             "    " + command, "",
+             "| kernel | call | launches | average us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|---|"]
+    per_call = {}
+    for r in rows:
+        label = next(((short, call) for frag, short, call in TRACE_KERNELS if frag in r["Name"]), None)
+        if label is None:
+            continue
+        short, call = label
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| {short} | {call} | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+        per_call[call] = per_call.get(call, 0.0) + avg
+    lines += ["", "Average per library call (sum of its kernels' average durations):", ""]
+    lines += [f"* {call}: {us / 1e3:.3f} ms" for call, us in per_call.items()]
+    lines.append("")
+    out = os.path.join(ROOT, "profiles", name + ".md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":
