@@ -60,8 +60,7 @@ CALL_SOURCES = {
 # kernel name fragment -> (part, call) for the traffic summary
 PMC_KERNELS = [("attn_bf16_kernel", "attn", "losa_sparse_attn"),
                ("pack_kv_kernelILi128ELb1", "pack_kv", "losa_sparse_attn"),
-               ("lse_bf16_kernel", "lse", "losa_block_mass"),
-               ("block_bf16_kernel", "block", "losa_block_mass"),
+               ("mass_bf16_kernel", "mass", "losa_block_mass"),
                ("pack_kv_kernelILi128ELb0", "pack_k", "losa_block_mass")]
 
 
@@ -250,7 +249,7 @@ def main():
 
     kept_flop = 4.0 * d * R * C * nnz
     dense_flop = 4.0 * d * float(Na) * float(Na) * H
-    mass_flop = 4.0 * d * float(N) * float(N) * H  # two Q K^T passes over all valid scores
+    mass_flop = 2.0 * d * float(N) * float(N) * H  # one Q K^T product over all valid scores
     attn_tflops = kept_flop / (attn_ms * 1e-3) / 1e12
     mass_tflops = mass_flop / (mass_ms * 1e-3) / 1e12
     sel_bytes = 4.0 * rows * nk + 4.0 * nnz + 8.0 * rows
@@ -258,7 +257,7 @@ def main():
         "sparse_attn": {"ms": attn_ms, "tflops": attn_tflops, "frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
                         "launches": "pack_kv + attn"},
         "block_mass": {"ms": mass_ms, "tflops": mass_tflops, "frac_bf16_peak": mass_tflops / PEAK_BF16_TFLOPS,
-                       "launches": "pack_k + lse + block"},
+                       "launches": "pack_k + mass"},
         "select": {"ms": sel_ms, "algorithmic_bytes": sel_bytes,
                    "GBps": sel_bytes / (sel_ms * 1e-3) / 1e9,
                    "frac_hbm_peak": sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
@@ -272,7 +271,7 @@ def main():
                 "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "traffic_source": traffic_src}
     traffic, traffic_src = traffic_of("losa_block_mass")
-    roofline_mass = {"kernel": "losa_block_mass (pack_kv_kernel + lse_bf16_kernel + block_bf16_kernel)",
+    roofline_mass = {"kernel": "losa_block_mass (pack_kv_kernel + mass_bf16_kernel)",
                      "bound": "mfma", "achieved": mass_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": mass_tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "traffic_source": traffic_src}
     cpu = None
@@ -469,8 +468,7 @@ TRACE_KERNELS = [
     ("attn_bf16_kernel", "attn_bf16_kernel", "losa_sparse_attn"),
     ("pack_kv_kernelILi128ELb1", "pack_kv_kernel (K and V)", "losa_sparse_attn"),
     ("pack_kv_kernelILi128ELb0", "pack_kv_kernel (K only)", "losa_block_mass"),
-    ("lse_bf16_kernel", "lse_bf16_kernel", "losa_block_mass"),
-    ("block_bf16_kernel", "block_bf16_kernel", "losa_block_mass"),
+    ("mass_bf16_kernel", "mass_bf16_kernel", "losa_block_mass"),
     ("cut_kernel", "cut_kernel", "losa_select"),
     ("scan_kernel", "scan_kernel", "losa_select"),
     ("compact_kernel", "compact_kernel", "losa_select"),

@@ -2,22 +2,26 @@
 // attention mass; Methodology Summary: masses at the construction step are
 // exact, not estimated).
 //
-// Two passes over K per query tile:
-//   pass 1  row log-sum-exp: a flash-style sweep over all valid keys keeping
-//           a running maximum and sum (log2 units: scores are pre-multiplied
-//           by scale*log2(e));
-//   pass 2  M[b,h,i,j] = (1/valid rows of block i) * sum over rows q of block
-//           i and valid keys k of block j of exp2(s_qk - lse2_q).
-// Both passes compute the same scores with the same instruction sequence, so
-// pass 2 sees exactly the scores pass 1 normalised.
+//   M[b,h,i,j] = (1/valid rows of block i) * sum over rows q of block i and
+//                valid keys k of block j of exp(s_qk - lse_q),
+// with s = q.k * scale and lse_q the log-sum-exp of row q over all valid keys.
 //
-// bf16 matrix-core path (d in {64, 128}, R in {64, 128}): a workgroup of four
-// waves owns a 64-row query tile; the waves split the KEYS (wave w takes
-// 32-key chunks w, w+4, ...), each holding the whole tile's Q as the B
-// operand, so K is read straight from global memory into registers with no
-// LDS staging and no wave reads another's keys.  S^T = K Q^T is formed with
-// 16x16x32 bf16 MFMA: lane l then owns query (l & 15) of each 16-query tile
-// and 4 keys per 16-key tile, so the per-query statistics live in lanes.
+// bf16 matrix-core path (d in {64, 128}, R in {64, 128}): ONE pass over K.
+// A workgroup owns one query block (R/64 groups of 64 rows, four waves per
+// group); the waves of a group split the KEY BLOCKS (wave w takes blocks
+// j = w, w+4, ...).  For every query a wave fixes a reference m at its first
+// chunk's maximum plus kHeadroom (log2 units; scores are pre-multiplied by
+// scale*log2(e)), sums 2^(s*c - m) per key block, writes that per-(query,
+// block) sum to a workspace S and keeps the row total.  Once the four waves
+// are merged, lse_q is known, and the workgroup reads S back:
+//   M[i,j] = (1/rows) * sum_q S[q,j] * 2^(m_q,w(j) - lse_q).
+// The scores and exponentials are computed once (a two-pass form computes
+// both twice); S costs 4 bytes per (query row, key block) of HBM traffic each
+// way.  S^T = K Q^T is formed with 16x16x32 bf16 MFMA: lane l owns query
+// (l & 15) of each 16-query tile and 4 keys per 16-key tile.
+//
+// fp32 inputs (and bf16 shapes outside the matrix-core path) take a SIMT
+// two-pass path: row log-sum-exp first, then the block sums.
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
 #include "losa_pack.hpp"
@@ -90,76 +94,105 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
     }
 }
 
-// Pass 1.  Grid: B*H*ceil(N/64) workgroups of 256 threads (two per CU).
-// Each lane keeps, per query, a sum of 2^(s*c - m) over its own keys against
-// a reference m fixed at its first chunk's maximum plus kHeadroom (log2
-// units): no per-score maximum.  A term can only overflow if a later score
-// exceeds that maximum by more than ~190; terms more than ~85 below it flush
-// to 0, negligible against the maximum term.  If a lane's sum ever leaves
-// (0, 2^100] the wave recomputes its chunks in two passes (exact per-lane
-// maximum first).  Lanes, then waves, are merged at the end.
-template <int D>
-__global__ __launch_bounds__(256, 2) void lse_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
-                                                          const __bf16* __restrict__ Kp, int nch,
-                                                          float* __restrict__ lse2) {
+// Grid: B*H*nq workgroups of 256*QG threads (QG = R/64 query groups), two
+// waves per SIMD.  A term 2^(s*c - m) can only overflow if a score exceeds the
+// wave's first-chunk maximum by more than ~190 (log2 units); terms more than
+// ~60 below the row maximum flush to 0, negligible against it.  If a block sum
+// or the row total leaves [0, 2^100] (or m is not finite), the wave recomputes
+// its blocks against its exact maximum instead, overwriting its S entries.
+template <int D, int QG>
+__global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
+                                                                     const __bf16* __restrict__ Kp, int nch,
+                                                                     float* __restrict__ S, float* __restrict__ M) {
   constexpr float kHeadroom = 64.0f;
   constexpr float kSumBound = 1.2676506e30f;  // 2^100
-  const int tiles = (g.N + 63) / 64;
-  const int task = xcd_task(blockIdx.x, g.B * g.H * tiles);
-  const int bh = task / tiles, t = task - bh * tiles;
+  __shared__ float s_ref[QG][4][64], s_tot[QG][4][64];
+  extern __shared__ float part[];  // [QG][nk] per-group partial masses (QG > 1)
+  const int rows = g.B * g.H * g.nq;
+  const int task = xcd_task(blockIdx.x, rows);
+  const int bh = task / g.nq, i = task - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w >> 2, kw = w & 3;
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
   const __bf16* Kpbh = Kp + (int64_t)bh * nch * (32 * D);
+  const int row0 = i * g.R + grp * 64;
+  float* Sg = S + ((int64_t)task * QG + grp) * g.nk * 64;  // [nk][64] of this query group
 
   QTile<D> q;
-  q.load(Qbh, g.qs[2], t * 64, g.N, lr, lg);
-  float m[4], s[4];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) { m[qt] = kNegInf; s[qt] = 0.f; }
+  q.load(Qbh, g.qs[2], row0, g.N, lr, lg);
 
   const float c = g.scale_log2;
-  const int nchunks = (g.N + 31) / 32;
-  const int nmine = nchunks > w ? (nchunks - w + 3) / 4 : 0;
-  bool fallback = false;
-  if (nmine > 0) {
+  const int sub = g.C / 32, sub_shift = __builtin_ctz(sub);
+  const int nb = g.nk > kw ? (g.nk - kw + 3) / 4 : 0;  // my key blocks kw, kw+4, ...
+  const int nu = nb * sub;                              // their 32-key chunks
+  auto chunk_kb = [&](int u) { return (kw + 4 * (u >> sub_shift)) * g.C + 32 * (u & (sub - 1)); };
+
+  // One sweep over my chunks against the reference m (exact = false: m is set
+  // from the first chunk).  Returns whether a sum left [0, 2^100].
+  float m[4], tot[4];
+  auto sweep = [&](bool fixed_from_first) -> bool {
+    bool over = false;
+    float blk[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) { tot[qt] = 0.f; blk[qt] = 0.f; }
     bf16x8 kop[2][D / 32];
-    load_kchunk<D>(Kpbh, w * 32, lane, kop);
-    for (int it = 0; it < nmine; ++it) {
-      const int kb = (w + 4 * it) * 32;
+    load_kchunk<D>(Kpbh, chunk_kb(0), lane, kop);
+    for (int u = 0; u < nu; ++u) {
+      const int kb = chunk_kb(u);
       f32x4 acc[2][4];
       chunk_scores<D>(q, kop, acc);
-      if (it + 1 < nmine) load_kchunk<D>(Kpbh, kb + 128, lane, kop);
+      if (u + 1 < nu) load_kchunk<D>(Kpbh, chunk_kb(u + 1), lane, kop);
       if (__builtin_expect(kb + 32 > g.N, 0)) mask_tail(kb, g.N, lg, acc);
-      if (it == 0) {
+      if (fixed_from_first && u == 0) {
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) {
           float mx = acc[0][qt][0];
 #pragma unroll
           for (int e = 1; e < 8; ++e) mx = fmaxf(mx, acc[e >> 2][qt][e & 3]);
-          m[qt] = mx * c + kHeadroom;  // -inf (all masked) forces the fallback
+          mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+          m[qt] = mx * c + kHeadroom;  // finite: the first chunk holds a valid key
         }
       }
-      bool over = false;
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
         const float nm = -m[qt];
         float sum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
-        s[qt] += sum;
-        over |= !(s[qt] <= kSumBound);
+        blk[qt] += sum;
       }
-      if (__builtin_expect(__any(over), 0)) { fallback = true; break; }
-    }
-  }
-  if (fallback) {
+      if ((u & (sub - 1)) == sub - 1) {  // block complete: sum the four lane groups, store, add to the totals
+        const int j = kw + 4 * (u >> sub_shift);
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) { m[qt] = kNegInf; s[qt] = 0.f; }
+        for (int qt = 0; qt < 4; ++qt) {
+          blk[qt] += __shfl_xor(blk[qt], 16, kWave);
+          blk[qt] += __shfl_xor(blk[qt], 32, kWave);
+          tot[qt] += blk[qt];
+          over |= !(blk[qt] <= kSumBound);
+        }
+        const float v = lg == 0 ? blk[0] : lg == 1 ? blk[1] : lg == 2 ? blk[2] : blk[3];
+        Sg[(int64_t)j * 64 + lane] = v;  // lane = query qt*16 + lr with qt = lg
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) blk[qt] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) over |= !(tot[qt] <= kSumBound);
+    return __any(over);
+  };
+
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) { m[qt] = kNegInf; tot[qt] = 0.f; }
+  if (nu > 0 && sweep(true)) {
+    // Exact maximum over my keys, then the sums again against it (all terms <= 1).
     bf16x8 kop[2][D / 32];
-    for (int it = 0; it < nmine; ++it) {
-      const int kb = (w + 4 * it) * 32;
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) m[qt] = kNegInf;
+    for (int u = 0; u < nu; ++u) {
+      const int kb = chunk_kb(u);
       load_kchunk<D>(Kpbh, kb, lane, kop);
       f32x4 acc[2][4];
       chunk_scores<D>(q, kop, acc);
@@ -170,116 +203,51 @@ __global__ __launch_bounds__(256, 2) void lse_bf16_kernel(const Geom g, const __
         for (int e = 0; e < 8; ++e) m[qt] = fmaxf(m[qt], acc[e >> 2][qt][e & 3]);
     }
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) m[qt] *= c;
-    for (int it = 0; it < nmine; ++it) {
-      const int kb = (w + 4 * it) * 32;
-      load_kchunk<D>(Kpbh, kb, lane, kop);
-      f32x4 acc[2][4];
-      chunk_scores<D>(q, kop, acc);
-      if (kb + 32 > g.N) mask_tail(kb, g.N, lg, acc);
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const float nm = m[qt] == kNegInf ? 0.f : -m[qt];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[qt] += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
-      }
+    for (int qt = 0; qt < 4; ++qt) {
+      m[qt] = fmaxf(m[qt], __shfl_xor(m[qt], 16, kWave));
+      m[qt] = fmaxf(m[qt], __shfl_xor(m[qt], 32, kWave));
+      m[qt] *= c;
     }
+    sweep(false);
   }
 
-  // Merge the four lanes that share each query, then the four waves.
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float mo = __shfl_xor(m[qt], o, kWave);
-      const float so = __shfl_xor(s[qt], o, kWave);
-      const float mn = fmaxf(m[qt], mo);
-      float acc = 0.f;
-      if (m[qt] != kNegInf) acc += s[qt] * fast_exp2(m[qt] - mn);
-      if (mo != kNegInf) acc += so * fast_exp2(mo - mn);
-      m[qt] = mn;
-      s[qt] = acc;
-    }
-  }
-  __shared__ float sm[4][64], ss[4][64];
+  // Merge the four key groups of each query: lse_q, then this wave's factor
+  // 2^(m - lse) for the query its lane stored (padding rows get 0).
   if (lg == 0) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) { sm[w][qt * 16 + lr] = m[qt]; ss[w][qt * 16 + lr] = s[qt]; }
+    for (int qt = 0; qt < 4; ++qt) { s_ref[grp][kw][qt * 16 + lr] = m[qt]; s_tot[grp][kw][qt * 16 + lr] = tot[qt]; }
   }
   __syncthreads();
-  if (threadIdx.x < 64) {
-    const int qi = threadIdx.x;
+  float f = 0.f;
+  {
     float mm = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, sm[ww][qi]);
-    float tot = 0.f;
+    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, s_ref[grp][ww][lane]);
+    float l = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww)
-      if (sm[ww][qi] != kNegInf) tot += ss[ww][qi] * fast_exp2(sm[ww][qi] - mm);
-    const int row = t * 64 + qi;
-    lse2[(int64_t)bh * g.Na + row] = mm + __log2f(tot);
+      if (s_ref[grp][ww][lane] != kNegInf) l += s_tot[grp][ww][lane] * fast_exp2(s_ref[grp][ww][lane] - mm);
+    const float mine = s_ref[grp][kw][lane];
+    if (row0 + lane < g.N && mine != kNegInf) f = fast_exp2(mine - mm) / l;
   }
-}
-
-// Pass 2.  Grid: B*H*nq workgroups of 256*QG threads (QG = R/64 query groups),
-// two waves per SIMD.  Key block j goes to key group j % 4; its 32-key chunks
-// are summed as exp2(s*c - lse2_q) and reduced over the wave.
-template <int D, int QG>
-__global__ __launch_bounds__(256 * QG, 2 / QG) void block_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
-                                                                      const __bf16* __restrict__ Kp, int nch,
-                                                                      const float* __restrict__ lse2,
-                                                                      float* __restrict__ M) {
-  extern __shared__ float part[];  // [QG][nk]
-  const int rows = g.B * g.H * g.nq;
-  const int task = xcd_task(blockIdx.x, rows);
-  const int bh = task / g.nq, i = task - bh * g.nq;
-  const int b = bh / g.H, h = bh - b * g.H;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int grp = w >> 2, kw = w & 3;
-  const int lr = lane & 15, lg = lane >> 4;
-  const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
-  const __bf16* Kpbh = Kp + (int64_t)bh * nch * (32 * D);
-  const int row0 = i * g.R + grp * 64;
-
-  QTile<D> q;
-  q.load(Qbh, g.qs[2], row0, g.N, lr, lg);
-  float l2[4];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int row = row0 + qt * 16 + lr;
-    l2[qt] = row < g.N ? lse2[(int64_t)bh * g.Na + row] : kPosInf;  // padding rows add 0
-  }
-
-  const float c = g.scale_log2;
-  const int sub = g.C / 32;
-  for (int j = kw; j < g.nk; j += 4) {
-    float tot = 0.f;
-    for (int sc = 0; sc < sub; ++sc) {
-      const int kb = j * g.C + sc * 32;
-      if (kb >= g.N) break;
-      bf16x8 kop[2][D / 32];
-      load_kchunk<D>(Kpbh, kb, lane, kop);
-      f32x4 acc[2][4];
-      chunk_scores<D>(q, kop, acc);
-      if (__builtin_expect(kb + 32 > g.N, 0)) mask_tail(kb, g.N, lg, acc);
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const float nl = -l2[qt];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tot += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nl));
-      }
-    }
-    tot = wave_sum(tot);
-    if (lane == 0) part[grp * g.nk + j] = tot;
-  }
-  __syncthreads();
   const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
   float* Mrow = M + (int64_t)task * g.nk;
-  for (int j = threadIdx.x; j < g.nk; j += blockDim.x) {
-    float v = part[j];
+  for (int bb = 0; bb < nb; ++bb) {
+    const int j = kw + 4 * bb;
+    const float v = wave_sum(Sg[(int64_t)j * 64 + lane] * f);
+    if (lane == 0) {
+      if (QG == 1) Mrow[j] = v * inv_rows;
+      else part[grp * g.nk + j] = v;
+    }
+  }
+  if (QG > 1) {
+    __syncthreads();
+    for (int j = threadIdx.x; j < g.nk; j += blockDim.x) {
+      float v = part[j];
 #pragma unroll
-    for (int gg = 1; gg < QG; ++gg) v += part[gg * g.nk + j];
-    Mrow[j] = v * inv_rows;
+      for (int gg = 1; gg < QG; ++gg) v += part[gg * g.nk + j];
+      Mrow[j] = v * inv_rows;
+    }
   }
 }
 
@@ -388,39 +356,42 @@ hipError_t launch_simt(const Geom& g, const void* Q, const void* K, float* M, fl
 }
 
 template <int D>
-hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* lse2, __bf16* Kp,
+hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* S, __bf16* Kp,
                        hipStream_t st) {
   const int nch = packed_chunks(g);
   hipLaunchKernelGGL((pack_kv_kernel<D, false>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)nullptr, Kp, (__bf16*)nullptr, nch);
-  const int tiles = (g.N + 63) / 64;
-  hipLaunchKernelGGL((lse_bf16_kernel<D>), dim3(g.B * g.H * tiles), dim3(256), 0, st, g, (const __bf16*)Q,
-                     (const __bf16*)Kp, nch, lse2);
-  const size_t lds = (size_t)(g.R / 64) * g.nk * sizeof(float);
   if (g.R == 64)
-    hipLaunchKernelGGL((block_bf16_kernel<D, 1>), dim3(g.rows()), dim3(256), lds, st, g, (const __bf16*)Q,
-                       (const __bf16*)Kp, nch, (const float*)lse2, M);
+    hipLaunchKernelGGL((mass_bf16_kernel<D, 1>), dim3(g.rows()), dim3(256), 0, st, g, (const __bf16*)Q,
+                       (const __bf16*)Kp, nch, S, M);
   else
-    hipLaunchKernelGGL((block_bf16_kernel<D, 2>), dim3(g.rows()), dim3(512), lds, st, g, (const __bf16*)Q,
-                       (const __bf16*)Kp, nch, (const float*)lse2, M);
+    hipLaunchKernelGGL((mass_bf16_kernel<D, 2>), dim3(g.rows()), dim3(512), (size_t)2 * g.nk * sizeof(float), st,
+                       g, (const __bf16*)Q, (const __bf16*)Kp, nch, S, M);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Workspace.  Matrix-core path: per-(query row, key block) sums S, fp32
+// [B*H*nq][R/64][nk][64], then the packed K.  SIMT path: the row log-sum-exp
+// in log2 units, fp32 [B*H][N_alloc].
+static size_t mass_s_bytes(const Geom& g) {
+  return align_up((size_t)g.B * g.H * g.nq * (g.R / 64) * g.nk * 64 * sizeof(float), 256);
+}
+
 size_t mass_ws_bytes(const Geom& g) {
-  size_t n = align_up((size_t)g.B * g.H * g.Na * sizeof(float), 256);  // row log-sum-exp (log2 units)
-  if (mfma_path(g)) n += (size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t);  // packed K
-  return n;
+  if (mfma_path(g)) return mass_s_bytes(g) + (size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t);
+  return (size_t)g.B * g.H * g.Na * sizeof(float);
 }
 
 hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, void* ws,
                              hipStream_t stream) {
+  if (mfma_path(g)) {
+    float* S = reinterpret_cast<float*>(ws);
+    __bf16* Kp = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(ws) + mass_s_bytes(g));
+    return g.D == 128 ? launch_mfma<128>(g, Q, K, M, S, Kp, stream) : launch_mfma<64>(g, Q, K, M, S, Kp, stream);
+  }
   float* lse2 = reinterpret_cast<float*>(ws);
-  __bf16* Kp = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(ws) +
-                                         align_up((size_t)g.B * g.H * g.Na * sizeof(float), 256));
-  if (mfma_path(g)) return g.D == 128 ? launch_mfma<128>(g, Q, K, M, lse2, Kp, stream)
-                                      : launch_mfma<64>(g, Q, K, M, lse2, Kp, stream);
   if (g.bf16)
     return g.D == 128 ? launch_simt<__bf16, 128>(g, Q, K, M, lse2, stream)
                       : launch_simt<__bf16, 64>(g, Q, K, M, lse2, stream);

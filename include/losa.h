@@ -105,7 +105,11 @@ const char* losa_status_string(losa_status status);
  * fp32), exponentials in fp32.
  *
  * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
- * ws: at least *bytes from losa_block_mass_workspace (row log-sum-exp).
+ * ws: at least *bytes from losa_block_mass_workspace.  bf16 matrix-core path:
+ *    per-(query row, key block) partial sums, 4 * batch*heads*n_q*q_block*n_k
+ *    bytes (805 MB for 12 heads x 32760 tokens, 64-token blocks), then K
+ *    repacked in 32-token chunks; other paths: the row log-sum-exp,
+ *    4 * batch*heads*tokens_alloc bytes.
  * ------------------------------------------------------------------------ */
 losa_status losa_block_mass_workspace(const losa_shape* shape, size_t* bytes);
 losa_status losa_block_mass(const losa_shape* shape, const void* Q, const void* K, float* M,

@@ -296,3 +296,49 @@ def test_negative_logits_with_padded_tail(shift, N, shuffle):
     err = float(np.abs(Og.cpu().numpy()[:, :, :N] - ref[:, :, :N]).max())
     say(f"negative logits shift {shift} N {N} shuffle {shuffle}: max abs err {err:.3e}")
     assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("R", [64, 128])
+def test_overflow_fallback_paths(R):
+    """Keys [0, 256) score at least ~170 (log2 units) below all later keys.
+
+    Both the mass kernel and the attention kernel fix a reference at each
+    wave's first chunk of keys, which here lies in the low class, so later
+    chunks overflow that reference and every wave takes its exact two-pass
+    fallback.  Masses of the low-class blocks (about 2^-170 of the row or less) are
+    below fp32's normal range: for reference masses under 2^-126 the check is
+    |M_gpu - M_ref| <= 2^-126; above, relative error <= MASS_RTOL.
+    """
+    rng = np.random.default_rng(2024 + R)
+    H, d, N = 2, 128, 1000
+    Na = -(-N // R) * R
+    a = 27.0
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = a * u + rng.standard_normal((1, H, Na, d)) * 0.3
+    k = a * u + rng.standard_normal((1, H, Na, d)) * 0.3
+    k[:, :, :256] = -a * u + rng.standard_normal((1, H, 256, d)) * 0.3
+    v = rng.standard_normal((1, H, Na, d))
+    bits = [S.bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
+    q64, k64, v64 = (S.f64_from_bf16_bits(b) for b in bits)
+    qd, kd, vd = (to_device(b, "bf16") for b in bits)
+    M_ref = O.block_mass(q64, k64, N, R, R)
+    M_gpu = F.losa_block_mass(qd, kd, N, R, R).cpu().numpy().astype(np.float64)
+    tiny = 2.0 ** -126
+    small = M_ref < tiny
+    assert small.any() and (~small).any()
+    assert np.abs(M_gpu[small] - M_ref[small]).max() <= tiny
+    rel = float((np.abs(M_gpu[~small] - M_ref[~small]) / M_ref[~small]).max())
+    say(f"fallback R={R}: mass rel err {rel:.2e} on {(~small).sum()} normal masses")
+    assert rel <= MASS_RTOL
+    nq = Na // R
+    rows = H * nq
+    rp = np.arange(rows + 1, dtype=np.int64) * nq
+    ci = np.tile(np.arange(nq, dtype=np.int32), rows)
+    ref = O.sparse_attention(q64, k64, v64, N, R, R, rp, ci)
+    rp_d, ci_d = csr_to_device(rp, ci)
+    Og = F.losa_sparse_attn(qd, kd, vd, rp_d, ci_d, None, N, R, R, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = float(np.abs(Og.cpu().numpy()[:, :, :N] - ref[:, :, :N]).max())
+    say(f"fallback R={R}: O max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
