@@ -81,7 +81,7 @@ def cpu_baseline(layer, wl, rows_wanted, p, budget_s=20.0):
     of the same layer and scale to the full step and to kept-block TFLOP/s."""
     import oracle as O
     import synthetic as S
-    R = C = wl.block
+    R, C = wl.block, wl.key_block
     N, H, d = wl.tokens, wl.heads, wl.head_dim
     nq = wl.n_blocks
     rng = np.random.default_rng(7)
@@ -195,7 +195,7 @@ def main():
     wl = S.get_workload(args.workload)
     if wl.steps > 1:
         return run_reuse(args, wl)
-    R = C = wl.block
+    R, C = wl.block, wl.key_block
     N, Na, H, d = wl.tokens, wl.tokens_alloc, wl.heads, wl.head_dim
     log(f"workload {wl.wid} {wl.name}: H={H} d={d} N={N} block={R} p={wl.p}")
     t0 = time.time()
@@ -292,7 +292,7 @@ def main():
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded random-Fourier-feature Q/K + N(0,1) noise and sinks, N(0,1) V; no trained weights)",
         "config": {"workload": wl.name, "batch": 1, "heads": H, "head_dim": d, "tokens": N, "tokens_alloc": Na,
-                   "block": R, "p": wl.p, "parallelism": "single GPU"},
+                   "block": R, "k_block": C, "p": wl.p, "parallelism": "single GPU"},
         "sparse_attn_ms": attn_ms,
         "mass_select_ms": mass_ms + sel_ms,
         "mass_ms": mass_ms,
@@ -314,7 +314,7 @@ def run_reuse(args, wl):
     import torch
     import free_block_sparse_exact_amd as F
     import synthetic as S
-    R = C = wl.block
+    R, C = wl.block, wl.key_block
     N, Na, H, d = wl.tokens, wl.tokens_alloc, wl.heads, wl.head_dim
     dev = torch.device("cuda:0")
     log(f"workload {wl.wid} {wl.name}: {wl.steps} steps, construction at step {wl.construct_step}")
@@ -389,7 +389,7 @@ def run_reuse(args, wl):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; Q/K drift q_s = q_0 + 0.02 s N(0,1) per step; no trained weights)",
-        "config": {"workload": wl.name, "heads": H, "head_dim": d, "tokens": N, "block": R,
+        "config": {"workload": wl.name, "heads": H, "head_dim": d, "tokens": N, "block": R, "k_block": C,
                    "p_per_head": p_heads, "construct_step": wl.construct_step, "parallelism": "single GPU"},
         "construct_mass_select_ms": construct_ms,
         "sparse_attn_ms_mean": mean_sparse,

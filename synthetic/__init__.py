@@ -80,6 +80,11 @@ class Workload:
     steps: int = 1
     construct_step: int = 0
     per_head_p: Tuple[float, ...] = ()
+    k_block: int = 0  # key-block size C when it differs from the query-block size R (= block)
+
+    @property
+    def key_block(self) -> int:
+        return self.k_block or self.block
 
     @property
     def tokens(self) -> int:
@@ -91,8 +96,12 @@ class Workload:
         return -(-self.tokens // self.block)
 
     @property
+    def n_key_blocks(self) -> int:
+        return -(-self.tokens // self.key_block)
+
+    @property
     def tokens_alloc(self) -> int:
-        return self.n_blocks * self.block
+        return max(self.n_blocks * self.block, self.n_key_blocks * self.key_block)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -105,6 +114,10 @@ WORKLOADS: Dict[str, Workload] = {
                   steps=50, construct_step=2, per_head_p=(0.90, 0.95, 0.99, 0.995)),
     "1s": Workload("1s", "wan13b_sparse", 12, 128, (21, 30, 52), 64, "bf16", 0.99,
                    amplitude=11.0, seed=11),
+    # workload 3's layer (same seed) with the page's own block shape: 128-token
+    # query blocks, 32-token key blocks
+    "3n": Workload("3n", "hunyuan_720p_r128_c32", 24, 128, (33, 45, 80), 128, "bf16", 0.99, seed=3,
+                   k_block=32),
 }
 
 

@@ -31,12 +31,12 @@ def _head_f64(arr, dtype, b, h):
     return S.to_f64(arr[b:b + 1, h:h + 1], dtype)
 
 
-@pytest.mark.parametrize("wid", ["1", "2", "3"])
+@pytest.mark.parametrize("wid", ["1", "2", "3", "3n"])
 def test_fullsize_pipeline_sampled_rows(wid):
     wl = S.get_workload(wid)
-    R = C = wl.block
+    R, C = wl.block, wl.key_block
     N, Na, H = wl.tokens, wl.tokens_alloc, wl.heads
-    say(f"workload {wid} ({wl.name}): H={H} N={N} block={R}")
+    say(f"workload {wid} ({wl.name}): H={H} N={N} R={R} C={C}")
     with Timer("generate"):
         layer = S.make_layer(wl)
     q, k, v = layer_to_device(layer)
@@ -46,7 +46,8 @@ def test_fullsize_pipeline_sampled_rows(wid):
         Og = F.losa_sparse_attn(q, k, v, rp, ci, order, N, R, C)
         torch.cuda.synchronize()
     nq = wl.n_blocks
-    rows = sample_rows(H, nq, seed=100 + int(wid), n_uniform=24)
+    nk = wl.n_key_blocks
+    rows = sample_rows(H, nq, seed=100 + wl.seed, n_uniform=24)
     ridx = [O.row_id(b, h, i, H, nq) for (b, h, i) in rows]
     M_rows = M.view(-1, M.shape[-1])[torch.tensor(ridx, device="cuda")].cpu().numpy()
     rp_h = rp.cpu().numpy().astype(np.int64)
@@ -56,7 +57,7 @@ def test_fullsize_pipeline_sampled_rows(wid):
     cnt = np.diff(rp_h)
     assert np.array_equal(np.sort(order_h), np.arange(len(cnt)))
     assert np.array_equal(order_h, np.argsort(-cnt, kind="stable"))
-    say(f"  nnz={int(rp_h[-1])} coverage={rp_h[-1] / (len(cnt) * nq):.4f} budgets {cnt.min()}..{cnt.max()}")
+    say(f"  nnz={int(rp_h[-1])} coverage={rp_h[-1] / (len(cnt) * nk):.4f} budgets {cnt.min()}..{cnt.max()}")
 
     by_head = {}
     for t, (b, h, i) in enumerate(rows):
@@ -123,13 +124,13 @@ def _synthetic_masses(rng, shape):
     return M.reshape(shape)
 
 
-@pytest.mark.parametrize("wid", ["1", "2", "3", "4"])
+@pytest.mark.parametrize("wid", ["1", "2", "3", "4", "3n"])
 def test_select_bit_exact_full_shape(wid):
     wl = S.get_workload(wid)
-    R = C = wl.block
-    nq = wl.n_blocks
-    shape = (1, wl.heads, nq, nq)
-    rng = np.random.default_rng(200 + int(wid))
+    R, C = wl.block, wl.key_block
+    nq, nk = wl.n_blocks, wl.n_key_blocks
+    shape = (1, wl.heads, nq, nk)
+    rng = np.random.default_rng(200 + wl.seed + (50 if wl.k_block else 0))
     M = _synthetic_masses(rng, shape)
     p = wl.p
     if wl.per_head_p:
