@@ -129,14 +129,30 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
   const int nu = nb * sub;                              // their 32-key chunks
   auto chunk_kb = [&](int u) { return (kw + 4 * (u >> sub_shift)) * g.C + 32 * (u & (sub - 1)); };
 
-  // One sweep over my chunks against the reference m (exact = false: m is set
-  // from the first chunk).  Returns whether a sum left [0, 2^100].
-  float m[4], tot[4];
+  // Block sums: lane (lg, lr) holds partial sums over its keys for queries
+  // qt*16 + lr, qt = 0..3; the totals over the four lane groups are formed so
+  // that lane (lg, lr) ends with the one for query lg*16 + lr (the one it
+  // stores): two values swapped with the lane 32 away, then one with the lane
+  // 16 away.
+  auto reduce_mine = [&](const float (&v)[4]) -> float {
+    const bool lo2 = lg < 2, even = (lg & 1) == 0;
+    const float a = __shfl_xor(lo2 ? v[2] : v[0], 32, kWave);
+    const float b2 = __shfl_xor(lo2 ? v[3] : v[1], 32, kWave);
+    const float x0 = (lo2 ? v[0] : v[2]) + a, x1 = (lo2 ? v[1] : v[3]) + b2;
+    const float r = __shfl_xor(even ? x1 : x0, 16, kWave);
+    return (even ? x0 : x1) + r;
+  };
+
+  // One sweep over my chunks against the reference m (fixed_from_first: m is
+  // set from the first chunk).  tot = this lane's query's total.  Returns
+  // whether a sum left [0, 2^100].
+  float m[4], tot;
   auto sweep = [&](bool fixed_from_first) -> bool {
     bool over = false;
     float blk[4];
+    tot = 0.f;
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) { tot[qt] = 0.f; blk[qt] = 0.f; }
+    for (int qt = 0; qt < 4; ++qt) blk[qt] = 0.f;
     bf16x8 kop[2][D / 32];
     load_kchunk<D>(Kpbh, chunk_kb(0), lane, kop);
     for (int u = 0; u < nu; ++u) {
@@ -164,28 +180,23 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
         for (int e = 0; e < 8; ++e) sum += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
         blk[qt] += sum;
       }
-      if ((u & (sub - 1)) == sub - 1) {  // block complete: sum the four lane groups, store, add to the totals
+      if ((u & (sub - 1)) == sub - 1) {  // block complete: store this lane's query's sum, add it to the total
         const int j = kw + 4 * (u >> sub_shift);
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          blk[qt] += __shfl_xor(blk[qt], 16, kWave);
-          blk[qt] += __shfl_xor(blk[qt], 32, kWave);
-          tot[qt] += blk[qt];
-          over |= !(blk[qt] <= kSumBound);
-        }
-        const float v = lg == 0 ? blk[0] : lg == 1 ? blk[1] : lg == 2 ? blk[2] : blk[3];
-        Sg[(int64_t)j * 64 + lane] = v;  // lane = query qt*16 + lr with qt = lg
+        const float v = reduce_mine(blk);
+        tot += v;
+        over |= !(v <= kSumBound);
+        Sg[(int64_t)j * 64 + lane] = v;  // lane = query lg*16 + lr
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) blk[qt] = 0.f;
       }
     }
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) over |= !(tot[qt] <= kSumBound);
+    over |= !(tot <= kSumBound);
     return __any(over);
   };
 
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) { m[qt] = kNegInf; tot[qt] = 0.f; }
+  for (int qt = 0; qt < 4; ++qt) m[qt] = kNegInf;
+  tot = 0.f;
   if (nu > 0 && sweep(true)) {
     // Exact maximum over my keys, then the sums again against it (all terms <= 1).
     bf16x8 kop[2][D / 32];
@@ -213,10 +224,8 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
 
   // Merge the four key groups of each query: lse_q, then this wave's factor
   // 2^(m - lse) for the query its lane stored (padding rows get 0).
-  if (lg == 0) {
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) { s_ref[grp][kw][qt * 16 + lr] = m[qt]; s_tot[grp][kw][qt * 16 + lr] = tot[qt]; }
-  }
+  s_ref[grp][kw][lane] = lg == 0 ? m[0] : lg == 1 ? m[1] : lg == 2 ? m[2] : m[3];  // lane = query lg*16 + lr
+  s_tot[grp][kw][lane] = tot;
   __syncthreads();
   float f = 0.f;
   {
