@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblosa.so")
-SOURCES = ["losa_api.cpp", "losa_mass.hip", "losa_select.hip", "losa_attn.hip"]
+SOURCES = ["losa_api.cpp", "losa_mass.hip", "losa_select.hip", "losa_attn.hip", "losa_dense.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -32,7 +32,7 @@ FLAGS = [
 # vector arithmetic straight away, and with one wave per SIMD the O
 # accumulators fit beside them; the default form parks results in AGPRs and
 # spends ~100 register moves per 32-key chunk copying them back and forth.
-EXTRA_FLAGS = {"losa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"losa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "losa_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

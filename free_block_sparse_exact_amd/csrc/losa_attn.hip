@@ -34,23 +34,6 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
-                                        float a7) {
-  typedef float f32x8 __attribute__((ext_vector_type(8)));
-  return __builtin_convertvector((f32x8{a0, a1, a2, a3, a4, a5, a6, a7}), bf16x8);
-}
-
-// Sum of the eight bf16 probabilities exactly as they enter the P.V product,
-// so the normaliser matches the numerator (v_dot2 against (1, 1)).
-__device__ __forceinline__ float sum_bf16x8(bf16x8 p) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float s = __builtin_amdgcn_fdot2_f32_bf16(p.s01, ones, 0.f, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(p.s23, ones, s, false);
-  s = __builtin_amdgcn_fdot2_f32_bf16(p.s45, ones, s, false);
-  return __builtin_amdgcn_fdot2_f32_bf16(p.s67, ones, s, false);
-}
-
 // A chunk whose per-lane probability sum (relative to the running max)
 // exceeds this bound goes through the rescale path.
 constexpr float kPBound = 65536.0f;
@@ -459,9 +442,10 @@ __global__ __launch_bounds__(128) void attn_simt_kernel(const Geom g, const T* _
   __shared__ float ks[32][D], vs[32][D];
   float m = kNegInf, l = 0.f;
   const float c = g.scale_log2;
-  const int beg = row_ptr[row], end = row_ptr[row + 1];
+  // no lists: every key block (dense attention)
+  const int beg = row_ptr ? row_ptr[row] : 0, end = row_ptr ? row_ptr[row + 1] : g.nk;
   for (int p = beg; p < end; ++p) {
-    const int j = col_idx[p];
+    const int j = col_idx ? col_idx[p] : p;
     const int kend = min((j + 1) * g.C, g.N);
     for (int kb = j * g.C; kb < kend; kb += 32) {
       for (int idx = threadIdx.x; idx < 32 * D; idx += blockDim.x) {

@@ -1,0 +1,453 @@
+// Dense self-attention that also accumulates the exact block masses, in one
+// pass over K and V: the construction step of the LoSA page (Methodology
+// Summary: the pattern is built at one dense step from exact block masses;
+// Experiments Summary: the construction kernel is a dense-attention kernel
+// that accumulates exact block masses while computing full attention).
+//
+//   O(q)    = softmax over all valid keys of s = q.k * scale, times V;
+//   M[i,j]  = (1/valid rows of block i) * sum over rows q of block i and
+//             valid keys k of block j of exp(s_qk - lse_q)
+// (M is exactly what losa_block_mass computes).
+//
+// bf16 matrix-core path (d in {64, 128}, R in {64, 128}): the sparse
+// attention kernel's structure over the full key range.  One workgroup (four
+// waves, one per SIMD) per 64-query tile; wave kw takes the key BLOCKS
+// j = kw, kw+4, ... (all their 32-key chunks), so each block's sum comes from
+// one wave and one reference.  Per chunk a wave computes p = 2^(s*c - m)
+// against its fixed reference m (first chunk's maximum + 64, log2 units); p
+// rounded to bf16 feeds the P.V product and its normaliser, p in fp32 feeds
+// the block sums.  At the end of a block the wave stores the block sum of each
+// query to the workspace S (as the mass kernel does); after the four waves are
+// merged, lse is known and M follows from S.  The overflow rule and the exact
+// two-pass fallback are the sparse attention kernel's.
+//
+// Padding keys of the last block score exactly 0 against the zero rows of
+// the packed K and must leave the softmax: the wave that owns the last block
+// processes it first, its partly padded chunk at the very front (the first
+// chunk is masked explicitly), so the pipelined loop does no masking.
+#include "losa_device.hpp"
+#include "losa_internal.hpp"
+#include "losa_pack.hpp"
+
+namespace losa {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPBound = 65536.0f;  // per-lane chunk sum of the bf16 P: above it, the exact path
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
+                                                            const __bf16* __restrict__ Kp,
+                                                            const __bf16* __restrict__ Vp, int nch,
+                                                            float* __restrict__ S, float* __restrict__ Mout,
+                                                            void* O, int o_bf16) {
+  constexpr int DC = D / 32, DT = D / 16, kQT = 4;
+  constexpr int LD = D + 4;       // merge slot row stride (floats)
+  extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]
+  __shared__ float s_ref[4][64], s_tot[4][64];
+  const int qhalves = g.R / 64;
+  const int rows = g.rows();
+  const int tix = xcd_task(blockIdx.x, rows * qhalves);
+  const int row = tix / qhalves, qsub = tix - row * qhalves;
+  const int bh = row / g.nq, i = row - bh * g.nq;
+  const int b = bh / g.H, h = bh - b * g.H;
+  const int lane = threadIdx.x & 63, kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
+  const __bf16* Kbh = Kp + (int64_t)bh * nch * (32 * D);
+  const __bf16* Vbh = Vp + (int64_t)bh * nch * (32 * D);
+  const int row0 = i * g.R + qsub * 64;
+  float* Sg = S + (int64_t)tix * g.nk * 64;  // [nk][64] of this query tile
+
+  // Q as the B operand of S^T = K Q^T (padding rows -> 0), kept in AGPRs.
+  bf16x8 qop[kQT][DC];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int qrow = row0 + qt * 16 + lr;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      bf16x8 v = load_bf16x8(Qbh + (int64_t)qrow * g.qs[2] + dc * 32 + lg * 8);
+      if (qrow >= g.N) v = bf16x8{};
+      asm("" : "+a"(v));
+      qop[qt][dc] = v;
+    }
+  }
+
+  f32x4 o[DT][kQT];
+  float m[kQT], l[kQT], blk[kQT], tot = 0.f;
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    m[qt] = kNegInf;
+    l[qt] = 0.f;
+    blk[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c = g.scale_log2;
+
+  // This wave's chunk sequence: its blocks kw, kw+4, ... with all their valid
+  // chunks; the last block (partly padding unless N is a multiple of C) has
+  // sub_last valid chunks.  If its final chunk is partly padding, the last
+  // block goes first, that chunk at position 0.
+  const int sub = g.C / 32, sub_shift = __builtin_ctz(sub);
+  const int nb = g.nk > kw ? (g.nk - kw + 3) / 4 : 0;
+  const int last = g.nk - 1;
+  const int sub_last = (g.N - last * g.C + 31) / 32;
+  const bool own_last = nb > 0 && (last - kw) % 4 == 0;
+  const int nmine = own_last ? (nb - 1) * sub + sub_last : nb * sub;
+  const bool front = own_last && (g.N & 31) != 0;
+  // chunk t -> its first key; j and ends give its block and whether it closes it
+  // (both cases computed, then selected: no branch inside the loop body)
+  auto chunk_kb = [&](int t, int& j, bool& ends) -> int {
+    t = t < nmine ? t : nmine - 1;
+    const bool first_block = front && t < sub_last;
+    const int tt = front ? t - sub_last : t;  // negative (and unused) inside the first block
+    const int jn = kw + 4 * (tt >> sub_shift), scn = tt & (sub - 1);
+    j = first_block ? last : jn;
+    const int sc = first_block ? (t == 0 ? sub_last - 1 : t - 1) : scn;
+    ends = first_block ? t == sub_last - 1 : (scn == sub - 1 || (jn == last && scn == sub_last - 1));
+    return j * g.C + 32 * sc;
+  };
+  auto kb_of = [&](int t) {
+    int j;
+    bool e;
+    return chunk_kb(t, j, e);
+  };
+
+  auto load_k = [&](int kb, bf16x8 (&kop)[2][DC]) {
+    const __bf16* kc = Kbh + (int64_t)(kb >> 5) * (32 * D) + lane * 8;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) kop[kt][dc] = load_bf16x8(kc + (kt * DC + dc) * 512);
+  };
+  auto load_v = [&](int kb, bf16x8 (&vop)[DT]) {
+    const __bf16* vc = Vbh + (int64_t)(kb >> 5) * (32 * D) + lane * 8;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vop[dt] = load_bf16x8(vc + dt * 512);
+  };
+  // acc[kt][qt][r] = score of key kb + 8*lg + 4*kt + r for query qt*16 + lr.
+  auto scores = [&](const bf16x8 (&kop)[2][DC], f32x4 (&acc)[2][kQT]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = mfma_bf16(kop[kt][dc], qop[qt][dc], acc[kt][qt]);
+    }
+  };
+  auto mask_tail = [&](int kb, f32x4 (&acc)[2][kQT]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool dead = kb + lg * 8 + kt * 4 + r >= g.N;
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt)
+          if (dead) acc[kt][qt][r] = kNegInf;
+      }
+  };
+  // p = 2^(s*c - m): fp32 into the block sums, bf16 into P and the row sums.
+  auto probs = [&](const f32x4 (&acc)[2][kQT], bf16x8 (&pop)[kQT]) -> bool {
+    bool over = false;
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      const float nm = -m[qt];
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
+      blk[qt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pop[qt] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      const float rs = sum_bf16x8(pop[qt]);
+      over |= !(rs <= kPBound);
+      l[qt] += rs;
+    }
+    return over;
+  };
+  auto chunk_max = [&](const f32x4 (&acc)[2][kQT], float (&mx)[kQT]) {
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      float t = mx[qt];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t = fmaxf(t, acc[e >> 2][qt][e & 3]);
+      mx[qt] = t;
+    }
+  };
+  auto lanes_max = [&](float (&mx)[kQT]) {
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 16, kWave));
+      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32, kWave));
+    }
+  };
+  auto pv = [&](const bf16x8 (&vop)[DT], const bf16x8 (&pop)[kQT]) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt) o[dt][qt] = mfma_bf16(vop[dt], pop[qt], o[dt][qt]);
+  };
+  // Block end: lane (lg, lr) stores the block sum of query lg*16 + lr (sums
+  // over the four lane groups formed by a transpose-reduce: two values swapped
+  // with the lane 32 away, then one with the lane 16 away).
+  auto block_end = [&](int j) {
+    const bool lo2 = lg < 2, even = (lg & 1) == 0;
+    const float a = __shfl_xor(lo2 ? blk[2] : blk[0], 32, kWave);
+    const float a2 = __shfl_xor(lo2 ? blk[3] : blk[1], 32, kWave);
+    const float x0 = (lo2 ? blk[0] : blk[2]) + a, x1 = (lo2 ? blk[1] : blk[3]) + a2;
+    const float r = __shfl_xor(even ? x1 : x0, 16, kWave);
+    const float v = (even ? x0 : x1) + r;
+    tot += v;
+    Sg[(int64_t)j * 64 + lane] = v;
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) blk[qt] = 0.f;
+  };
+
+  constexpr float kHeadroom = 64.0f;
+  bool fallback = false;
+  bf16x8 kop[2][DC], vop[DT];
+  if (nmine > 0) {
+    int j0;
+    bool e0;
+    const int kb = chunk_kb(0, j0, e0);
+    load_k(kb, kop);
+    load_v(kb, vop);
+    f32x4 acc[2][kQT];
+    scores(kop, acc);
+    load_k(kb_of(1), kop);
+    if (kb + 32 > g.N) mask_tail(kb, acc);
+    {
+      float mx[kQT];
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt) mx[qt] = kNegInf;
+      chunk_max(acc, mx);
+      lanes_max(mx);
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt) m[qt] = mx[qt] * c + kHeadroom;  // finite: the chunk holds a valid key
+    }
+    bool over_any = false;
+    for (int t = 0; t < nmine; ++t) {
+      int jt;
+      bool ends;
+      chunk_kb(t, jt, ends);
+      f32x4 accn[2][kQT];
+      scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
+      load_k(kb_of(t + 2), kop);
+      bf16x8 pop[kQT];
+      const bool over = probs(acc, pop);  // chunk t
+      pv(vop, pop);
+      load_v(kb_of(t + 1), vop);
+#pragma unroll
+      for (int s = 0; s < 64; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // then two vector ALU ops
+      }
+      if (ends) block_end(jt);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = accn[kt][qt];
+      over_any |= over;
+    }
+    fallback = __any(over_any);
+  }
+  if (fallback) {
+    // Exact maximum over this wave's keys, then O, the row sums and the block
+    // sums again against it (all probabilities <= 1).
+    tot = 0.f;
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      l[qt] = 0.f;
+      m[qt] = kNegInf;
+      blk[qt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int t = 0; t < nmine; ++t) {
+      const int kb2 = kb_of(t);
+      load_k(kb2, kop);
+      f32x4 acc[2][kQT];
+      scores(kop, acc);
+      if (kb2 + 32 > g.N) mask_tail(kb2, acc);
+      chunk_max(acc, m);
+    }
+    lanes_max(m);
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) m[qt] *= c;
+    for (int t = 0; t < nmine; ++t) {
+      int jt;
+      bool ends;
+      const int kb2 = chunk_kb(t, jt, ends);
+      load_k(kb2, kop);
+      load_v(kb2, vop);
+      f32x4 acc[2][kQT];
+      scores(kop, acc);
+      if (kb2 + 32 > g.N) mask_tail(kb2, acc);
+      bf16x8 pop[kQT];
+      probs(acc, pop);
+      pv(vop, pop);
+      if (ends) block_end(jt);
+    }
+  }
+
+  // Row sums of P: combine the four lane groups that share each query.
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    l[qt] += __shfl_xor(l[qt], 16, kWave);
+    l[qt] += __shfl_xor(l[qt], 32, kWave);
+  }
+  // Reference and block-sum total of the query this lane stored (lg*16 + lr).
+  s_ref[kw][lane] = lg == 0 ? m[0] : lg == 1 ? m[1] : lg == 2 ? m[2] : m[3];
+  s_tot[kw][lane] = tot;
+
+  // Merge the key groups for O: 3 -> 2 -> 1 -> 0 through one LDS slot.
+  float* so = lds;
+  float* sm = lds + 64 * LD;
+  float* sl = sm + 64;
+  for (int src = 3; src >= 1; --src) {
+    __syncthreads();
+    if (kw == src) {
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt) {
+        const int qi = qt * 16 + lr;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<f32x4*>(so + qi * LD + dt * 16 + lg * 4) = o[dt][qt];
+        if (lg == 0) { sm[qi] = m[qt]; sl[qi] = l[qt]; }
+      }
+    }
+    __syncthreads();
+    if (kw == src - 1) {
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt) {
+        const int qi = qt * 16 + lr;
+        const float mo = sm[qi], lo = sl[qi];
+        const float mn = fmaxf(m[qt], mo);
+        const float a = m[qt] == kNegInf ? 0.f : fast_exp2(m[qt] - mn);
+        const float ao = mo == kNegInf ? 0.f : fast_exp2(mo - mn);
+        m[qt] = mn;
+        l[qt] = l[qt] * a + lo * ao;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4 oo = *reinterpret_cast<const f32x4*>(so + qi * LD + dt * 16 + lg * 4);
+          o[dt][qt] = o[dt][qt] * a + oo * ao;
+        }
+      }
+    }
+  }
+
+  // Masses: lse of the stored query, this wave's factor 2^(m - lse) (0 for
+  // padding rows), then M from S (s_ref/s_tot were written before the merge's
+  // first barrier).
+  {
+    float mm = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, s_ref[ww][lane]);
+    float lt = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww)
+      if (s_ref[ww][lane] != kNegInf) lt += s_tot[ww][lane] * fast_exp2(s_ref[ww][lane] - mm);
+    const float mine = s_ref[kw][lane];
+    const float f = (row0 + lane < g.N && mine != kNegInf) ? fast_exp2(mine - mm) / lt : 0.f;
+    const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
+    float* Mrow = Mout + ((int64_t)qsub * rows + row) * g.nk;
+    for (int bb = 0; bb < nb; ++bb) {
+      const int j = kw + 4 * bb;
+      const float v = wave_sum(Sg[(int64_t)j * 64 + lane] * f);
+      if (lane == 0) Mrow[j] = v * inv_rows;
+    }
+  }
+
+  if (kw == 0) {
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      const int qrow = row0 + qt * 16 + lr;
+      const float inv = (qrow < g.N && l[qt] > 0.f) ? 1.0f / l[qt] : 0.f;
+      const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 v = o[dt][qt] * inv;
+        const int d0 = dt * 16 + lg * 4;
+        if (o_bf16) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(v[0], v[1]);
+          pk[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(O) + obase + d0) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(O) + obase + d0) = v;
+        }
+      }
+    }
+  }
+}
+
+// M = Mh[0] + Mh[1]: the two 64-query halves of 128-row query blocks (two
+// addends, so the order of addition cannot change the result).
+__global__ __launch_bounds__(256) void add_halves_kernel(const float* __restrict__ Mh, float* __restrict__ M,
+                                                         int64_t n) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k < n) M[k] = Mh[k] + Mh[n + k];
+}
+
+struct DenseWs {
+  __bf16* Kp;
+  __bf16* Vp;
+  float* S;
+  float* Mh;  // R = 128 only
+};
+
+size_t dense_layout(const Geom& g, char* base, DenseWs* w) {
+  const size_t packed = (size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t);
+  const size_t s = align_up((size_t)g.B * g.H * g.nq * g.R * g.nk * sizeof(float), 256);
+  const size_t mh = g.R == 64 ? 0 : align_up((size_t)2 * g.rows() * g.nk * sizeof(float), 256);
+  if (w) {
+    w->Kp = reinterpret_cast<__bf16*>(base);
+    w->Vp = reinterpret_cast<__bf16*>(base + align_up(packed, 256));
+    w->S = reinterpret_cast<float*>(base + 2 * align_up(packed, 256));
+    w->Mh = reinterpret_cast<float*>(base + 2 * align_up(packed, 256) + s);
+  }
+  return 2 * align_up(packed, 256) + s + mh;
+}
+
+template <int D>
+hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O, int o_bf16,
+                       void* ws, hipStream_t st) {
+  DenseWs w;
+  dense_layout(g, reinterpret_cast<char*>(ws), &w);
+  const int nch = packed_chunks(g);
+  hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
+                     (const __bf16*)K, (const __bf16*)V, w.Kp, w.Vp, nch);
+  const int tiles = g.rows() * (g.R / 64);
+  const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float);
+  float* Mout = g.R == 64 ? M : w.Mh;
+  hipLaunchKernelGGL((dense_bf16_kernel<D>), dim3(tiles), dim3(256), lds, st, g, (const __bf16*)Q,
+                     (const __bf16*)w.Kp, (const __bf16*)w.Vp, nch, w.S, Mout, O, o_bf16);
+  if (g.R != 64) {
+    const int64_t n = (int64_t)g.rows() * g.nk;
+    hipLaunchKernelGGL(add_halves_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       (const float*)w.Mh, M, n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t dense_ws_bytes(const Geom& g) {
+  if (mfma_path(g)) return dense_layout(g, nullptr, nullptr);
+  return mass_ws_bytes(g);  // the separate mass and attention kernels
+}
+
+hipError_t launch_dense_attn_mass(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O,
+                                  int o_bf16, void* ws, hipStream_t stream) {
+  if (mfma_path(g))
+    return g.D == 128 ? launch_mfma<128>(g, Q, K, V, M, O, o_bf16, ws, stream)
+                      : launch_mfma<64>(g, Q, K, V, M, O, o_bf16, ws, stream);
+  // Other shapes: the SIMT mass kernels, then the SIMT attention kernel over
+  // every key block (no lists).
+  hipError_t e = launch_block_mass(g, Q, K, M, ws, stream);
+  if (e != hipSuccess) return e;
+  return launch_sparse_attn(g, Q, K, V, nullptr, nullptr, nullptr, O, o_bf16, nullptr, stream);
+}
+
+}  // namespace losa

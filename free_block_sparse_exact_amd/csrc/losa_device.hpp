@@ -37,6 +37,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
 
+// Eight fp32 values -> bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                        float a7) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  return __builtin_convertvector((f32x8{a0, a1, a2, a3, a4, a5, a6, a7}), bf16x8);
+}
+
+// Sum of eight bf16 probabilities exactly as they enter a P.V product, so a
+// softmax normaliser matches its numerator (v_dot2 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float s = __builtin_amdgcn_fdot2_f32_bf16(p.s01, ones, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.s23, ones, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(p.s45, ones, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(p.s67, ones, s, false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_sum(float v) {

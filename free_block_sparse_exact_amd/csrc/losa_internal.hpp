@@ -14,7 +14,7 @@ struct Geom {
   float scale;       // softmax scale (1/sqrt(d) by default)
   float scale_log2;  // scale * log2(e): scores in log2 units
   int64_t qs[3], ks[3], vs[3], os[3];
-  int rows() const { return B * H * nq; }
+  __host__ __device__ int rows() const { return B * H * nq; }
 };
 
 // Per-head fixed-point selection thresholds P = floor(p * 2^32 + 1/2),
@@ -58,5 +58,10 @@ size_t attn_ws_bytes(const Geom& g);
 hipError_t launch_sparse_attn(const Geom& g, const void* Q, const void* K, const void* V,
                               const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
                               void* O, int o_bf16, void* ws, hipStream_t stream);
+
+// Dense attention with exact block masses in one pass (construction step).
+size_t dense_ws_bytes(const Geom& g);
+hipError_t launch_dense_attn_mass(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O,
+                                  int o_bf16, void* ws, hipStream_t stream);
 
 }  // namespace losa

@@ -180,6 +180,30 @@ losa_status losa_sparse_attn(const losa_shape* shape, const void* Q, const void*
                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Dense attention with exact block masses, in one pass (the construction
+ * step).  LoSA page, Methodology Summary: the pattern is built once, at a
+ * dense step, from exact block masses; Experiments Summary: the
+ * construction kernel is a dense-attention kernel that accumulates the exact
+ * block masses while it computes full attention.
+ * O(q) = softmax over all valid keys of s = q.k * scale, times V (rows in
+ * [tokens, n_q*q_block) written as 0, rows beyond not touched); M = exactly
+ * what losa_block_mass computes.
+ *
+ * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
+ * O: [batch, heads, tokens_alloc, head_dim] with shape->o_stride, element
+ *    type o_dtype (LOSA_BF16 or LOSA_F32).
+ * ws: at least *bytes from losa_dense_attn_mass_workspace.  bf16
+ *    matrix-core path: packed K and V, per-(query row, key block) partial
+ *    sums (4 * batch*heads*n_q*q_block*n_k bytes) and, for q_block = 128, two
+ *    partial copies of M; other paths: the losa_block_mass workspace.
+ * Arithmetic as losa_sparse_attn for O and as losa_block_mass for M.
+ * ------------------------------------------------------------------------ */
+losa_status losa_dense_attn_mass_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_dense_attn_mass(const losa_shape* shape, const void* Q, const void* K, const void* V,
+                                 float* M, void* O, losa_dtype o_dtype, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Retained mass of a pattern (for Recall, Motivation Summary).
  * kept: fp32 [2 * batch*heads*n_q]: kept[2r] = sum of M[r, j] over the
  * listed blocks of row r, kept[2r+1] = sum of M[r, j] over all j.  Recall

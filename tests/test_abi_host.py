@@ -147,3 +147,23 @@ def test_sparse_attn_errors(lib):
     assert attn(O=FAKE + 8) == INVALID
     assert attn(ws_bytes=1) == WORKSPACE
     assert attn(ws=None) == NULL
+
+
+@no_gpu_only
+def test_dense_attn_mass_errors(lib):
+    s = shape()
+    n = ctypes.c_size_t()
+    assert lib.losa_dense_attn_mass_workspace(ctypes.byref(s), ctypes.byref(n)) == OK and n.value > 0
+
+    def dense(M=FAKE, O=FAKE, o_dtype=F.LOSA_BF16, ws=FAKE, ws_bytes=1 << 40, V=FAKE):
+        return lib.losa_dense_attn_mass(ctypes.byref(s), FAKE, FAKE, V, M, O, o_dtype, ws, ws_bytes, None)
+
+    assert dense(M=None) == NULL
+    assert dense(O=None) == NULL
+    assert dense(V=None) == NULL
+    assert dense(ws=None) == NULL
+    assert dense(o_dtype=3) == INVALID
+    assert dense(M=FAKE + 4) == INVALID
+    assert dense(ws_bytes=n.value - 1) == WORKSPACE
+    assert lib.losa_dense_attn_mass(ctypes.byref(shape(head_dim=96)), FAKE, FAKE, FAKE, FAKE, FAKE, F.LOSA_BF16,
+                                    FAKE, 1 << 40, None) == UNSUPPORTED

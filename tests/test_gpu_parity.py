@@ -253,6 +253,44 @@ def test_retained_mass_matches_recall():
     assert abs(rec_gpu - rec_ref) < 1e-5
 
 
+def negative_logit_inputs(rng, shift, H, Na, d):
+    """bf16 bit patterns of Q, K, V whose raw scores all lie near -shift: keys
+    share one large direction u and queries point against it."""
+    a = float(np.sqrt(shift))
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = -a * u + rng.standard_normal((1, H, Na, d)) * 0.7
+    k = a * u + rng.standard_normal((1, H, Na, d)) * 0.7
+    v = rng.standard_normal((1, H, Na, d))
+    return [S.bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
+
+
+def score_gap_inputs(rng, H, Na, d):
+    """bf16 bit patterns of Q, K, V where keys [0, 256) score at least ~170
+    (log2 units) below every later key."""
+    a = 27.0
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = a * u + rng.standard_normal((1, H, Na, d)) * 0.3
+    k = a * u + rng.standard_normal((1, H, Na, d)) * 0.3
+    k[:, :, :256] = -a * u + rng.standard_normal((1, H, 256, d)) * 0.3
+    v = rng.standard_normal((1, H, Na, d))
+    return [S.bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
+
+
+def check_masses_with_floor(M_gpu, M_ref, label):
+    """Relative error <= MASS_RTOL for masses in fp32's normal range; below
+    2^-126 (unrepresentable in the fp32 output) absolute error <= 2^-126."""
+    tiny = 2.0 ** -126
+    small = M_ref < tiny
+    if small.any():
+        assert np.abs(M_gpu[small] - M_ref[small]).max() <= tiny
+    rel = float((np.abs(M_gpu[~small] - M_ref[~small]) / M_ref[~small]).max())
+    say(f"{label}: mass rel err {rel:.2e} on {(~small).sum()} normal masses ({small.sum()} below 2^-126)")
+    assert rel <= MASS_RTOL
+    return small
+
+
 @pytest.mark.parametrize("shift", [225.0, 2500.0])
 @pytest.mark.parametrize("N", [1000, 970])
 @pytest.mark.parametrize("shuffle", [False, True])
@@ -266,17 +304,11 @@ def test_negative_logits_with_padded_tail(shift, N, shuffle):
     leaves the last 32-key chunk wholly padding; shuffled lists put the
     padded block anywhere in a row's list.
     """
-    rng = np.random.default_rng(int(shift) + N + 7 * shuffle)
     H, d, R = 2, 128, 64
     Na = -(-N // R) * R
     nq = Na // R
-    a = float(np.sqrt(shift))
-    u = rng.standard_normal(d)
-    u /= np.linalg.norm(u)
-    q = -a * u + rng.standard_normal((1, H, Na, d)) * 0.7
-    k = a * u + rng.standard_normal((1, H, Na, d)) * 0.7
-    v = rng.standard_normal((1, H, Na, d))
-    bits = [S.bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
+    rng = np.random.default_rng(int(shift) + N + 7 * shuffle)
+    bits = negative_logit_inputs(rng, shift, H, Na, d)
     q64, k64, v64 = (S.f64_from_bf16_bits(b) for b in bits)
     rows = H * nq
     lists = [np.arange(nq, dtype=np.int32) for _ in range(rows)]
@@ -309,28 +341,15 @@ def test_overflow_fallback_paths(R):
     below fp32's normal range: for reference masses under 2^-126 the check is
     |M_gpu - M_ref| <= 2^-126; above, relative error <= MASS_RTOL.
     """
-    rng = np.random.default_rng(2024 + R)
     H, d, N = 2, 128, 1000
     Na = -(-N // R) * R
-    a = 27.0
-    u = rng.standard_normal(d)
-    u /= np.linalg.norm(u)
-    q = a * u + rng.standard_normal((1, H, Na, d)) * 0.3
-    k = a * u + rng.standard_normal((1, H, Na, d)) * 0.3
-    k[:, :, :256] = -a * u + rng.standard_normal((1, H, 256, d)) * 0.3
-    v = rng.standard_normal((1, H, Na, d))
-    bits = [S.bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
+    bits = score_gap_inputs(np.random.default_rng(2024 + R), H, Na, d)
     q64, k64, v64 = (S.f64_from_bf16_bits(b) for b in bits)
     qd, kd, vd = (to_device(b, "bf16") for b in bits)
     M_ref = O.block_mass(q64, k64, N, R, R)
     M_gpu = F.losa_block_mass(qd, kd, N, R, R).cpu().numpy().astype(np.float64)
-    tiny = 2.0 ** -126
-    small = M_ref < tiny
+    small = check_masses_with_floor(M_gpu, M_ref, f"fallback R={R}")
     assert small.any() and (~small).any()
-    assert np.abs(M_gpu[small] - M_ref[small]).max() <= tiny
-    rel = float((np.abs(M_gpu[~small] - M_ref[~small]) / M_ref[~small]).max())
-    say(f"fallback R={R}: mass rel err {rel:.2e} on {(~small).sum()} normal masses")
-    assert rel <= MASS_RTOL
     nq = Na // R
     rows = H * nq
     rp = np.arange(rows + 1, dtype=np.int64) * nq
