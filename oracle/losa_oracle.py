@@ -40,6 +40,12 @@ notes of the repository):
   sum is >= T.  A plain fp64 argsort + cumsum is kept beside it as a cross-check.
 * Output lists are CSR with ascending block indices per row; the work order
   lists rows by kept-block count, descending, ties by row index ascending.
+* Pooled proxy masses (the coarse estimates the page contrasts with exact
+  masses -- Motivation Summary, SVG2 / SpargeAttn; the pages give no formula):
+  P[i, j] = |B_j| exp(qbar_i . kbar_j * scale) / sum_j' |B_j'| exp(qbar_i .
+  kbar_j' * scale), with qbar, kbar the means over the valid tokens of each
+  block and |B_j| the valid keys of key block j (each pooled key stands for
+  its block's keys).  Rows sum to 1, like M, so the same selector applies.
 
 Row numbering: row r = (b * H + h) * n_q + i for batch b, head h, query block i.
 Inputs are fp64 arrays [B, H, N_alloc, d] holding the exact values the GPU sees.
@@ -57,6 +63,7 @@ __all__ = [
     "dense_attention",
     "block_mass",
     "block_mass_rows",
+    "pooled_mass",
     "sanitize_masses",
     "select_contract",
     "select_contract_row",
@@ -156,6 +163,26 @@ def block_mass(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
         for h in range(H):
             M[b, h] = block_mass_rows(q, k, n_valid, R, C, [(b, h, i) for i in range(n_q)], scale)
     return M
+
+
+def pooled_mass(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
+                scale: Optional[float] = None) -> np.ndarray:
+    """Pooled proxy masses P [B, H, n_q, n_k] (fp64): a block-level softmax of
+    the block-mean query against the block-mean keys, each pooled key weighted
+    by its block's number of valid keys.  Coarse estimate of M (Motivation
+    Summary: coarse mass estimates); equals M exactly when the scores are
+    constant within every (query block, key block) pair."""
+    B, H, _, d = q.shape
+    sc = softmax_scale(d, scale)
+    n_q = -(-n_valid // R)
+    n_k = -(-n_valid // C)
+    qbar = np.stack([q[:, :, i * R:min((i + 1) * R, n_valid)].mean(axis=2) for i in range(n_q)], axis=2)
+    kbar = np.stack([k[:, :, j * C:min((j + 1) * C, n_valid)].mean(axis=2) for j in range(n_k)], axis=2)
+    size = np.array([min(C, n_valid - j * C) for j in range(n_k)], np.float64)
+    s = np.einsum("bhid,bhjd->bhij", qbar, kbar) * sc
+    s -= s.max(axis=3, keepdims=True)
+    w = size * np.exp(s)
+    return w / w.sum(axis=3, keepdims=True)
 
 
 def sanitize_masses(m: np.ndarray) -> np.ndarray:

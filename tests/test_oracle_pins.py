@@ -319,3 +319,75 @@ def test_bf16_rounding_nearest_even():
     assert got.tolist() == [1.0, 1.0, 1.0 + 4 * 2 ** -8, 1.0, -2.5]
     ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- pooled proxy masses
+# Reading (the pages name coarse, pooled estimates but print no formula):
+# P[i, j] = |B_j| exp(qbar_i . kbar_j * scale) / sum_j' |B_j'| exp(...).
+
+def _blockwise_constant(rng, H, N, Na, d, R, C):
+    """Q constant within every query block, K constant within every key block
+    (ragged last blocks included), padding rows left random."""
+    q = rng.standard_normal((1, H, Na, d))
+    k = rng.standard_normal((1, H, Na, d))
+    for i in range(-(-N // R)):
+        q[:, :, i * R:min((i + 1) * R, N)] = rng.standard_normal((1, H, 1, d)) * 1.5
+    for j in range(-(-N // C)):
+        k[:, :, j * C:min((j + 1) * C, N)] = rng.standard_normal((1, H, 1, d)) * 1.5
+    return q, k
+
+
+@pytest.mark.parametrize("N,R,C", [(1000, 64, 64), (1000, 64, 32), (777, 128, 32), (512, 64, 64)])
+def test_pooled_equals_exact_masses_for_blockwise_constant_scores(N, R, C):
+    """With scores constant on every (query block, key block) pair, the exact
+    block mass (the pinned definition) is the block-weighted softmax of the
+    pooled scores: the pooled proxy must equal it, ragged blocks included."""
+    rng = np.random.default_rng(N + R + C)
+    Na = max(-(-N // R) * R, -(-N // C) * C)
+    q, k = _blockwise_constant(rng, 2, N, Na, 16, R, C)
+    P = O.pooled_mass(q, k, N, R, C)
+    M = O.block_mass(q, k, N, R, C)
+    assert np.abs(P - M).max() <= 1e-12
+
+
+def test_pooled_zero_query_closed_form():
+    """Q = 0: every pooled score is 0, so P[i, j] = |B_j| / N (as for M)."""
+    N, R, C = 1000, 64, 32
+    rng = np.random.default_rng(3)
+    q = np.zeros((1, 2, 1024, 8))
+    k = rng.standard_normal((1, 2, 1024, 8))
+    P = O.pooled_mass(q, k, N, R, C)
+    size = np.array([min(C, N - j * C) for j in range(-(-N // C))], np.float64)
+    assert np.abs(P - size / N).max() <= 1e-15
+
+
+def test_pooled_rows_sum_to_one_and_differ_from_exact_in_general():
+    rng = np.random.default_rng(5)
+    N, R, C = 700, 64, 64
+    q = rng.standard_normal((1, 2, 704, 16)) * 2
+    k = rng.standard_normal((1, 2, 704, 16)) * 2
+    P = O.pooled_mass(q, k, N, R, C)
+    assert np.all(P >= 0)
+    assert np.abs(P.sum(axis=3) - 1).max() <= 1e-12
+    assert np.abs(P - O.block_mass(q, k, N, R, C)).max() > 1e-3  # a coarse estimate, not M
+
+
+def test_pooled_brute_force_loops():
+    """Explicit loops over tokens and blocks on a tiny case."""
+    rng = np.random.default_rng(11)
+    N, R, C, d = 70, 16, 8, 4
+    q = rng.standard_normal((1, 1, 80, d))
+    k = rng.standard_normal((1, 1, 80, d))
+    P = O.pooled_mass(q, k, N, R, C)
+    nq, nk = -(-N // R), -(-N // C)
+    sc = 1.0 / math.sqrt(d)
+    for i in range(nq):
+        rows = range(i * R, min((i + 1) * R, N))
+        qb = [sum(q[0, 0, t, e] for t in rows) / len(rows) for e in range(d)]
+        w = []
+        for j in range(nk):
+            keys = range(j * C, min((j + 1) * C, N))
+            kb = [sum(k[0, 0, t, e] for t in keys) / len(keys) for e in range(d)]
+            w.append(len(keys) * math.exp(sc * sum(qb[e] * kb[e] for e in range(d))))
+        for j in range(nk):
+            assert abs(P[0, 0, i, j] - w[j] / sum(w)) <= 1e-13
