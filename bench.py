@@ -292,6 +292,7 @@ def main():
                                   "frac_bf16_peak": construct_flop / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                   "launches": "pack_kv + dense (+ add_halves at R = 128)",
                                   "note": "construction step: dense O and exact M in one pass; not in ms_per_step"}
+    routing = pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev)
     cpu = None
     if args.cpu_rows > 0:
         log("timing the CPU oracle baseline ...")
@@ -321,9 +322,47 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "roofline_mass": roofline_mass,
+        "pooled_routing": routing,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
+
+
+ROUTING_P = (0.9, 0.95, 0.99, 0.995, 0.999)
+
+
+def pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev):
+    """Exact masses vs pooled proxy masses as the selector's input (LoSA page,
+    Motivation Summary: coarse estimates are miscalibrated near 99% recall):
+    for each p, the true recall (under the exact M) and the coverage of the
+    lists built from each.  M in bufs holds the exact masses of this layer."""
+    N, R, C = geom.tokens, geom.q_block, geom.k_block
+    nq, nk, rows = geom.n_q, geom.n_k, geom.rows
+    P = torch.empty_like(bufs.M)
+    ws_p = torch.empty(F.losa_pooled_mass_workspace(geom), dtype=torch.uint8, device=dev)
+    F.losa_pooled_mass(q, k, N, R, C, out=P, ws=ws_p, stream=stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        F.losa_pooled_mass(q, k, N, R, C, out=P, ws=ws_p, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    pooled_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    w = np.tile(np.array([min(R, N - i * R) for i in range(nq)], np.float64), rows // nq)
+    out = {"pooled_ms": pooled_ms, "p": list(ROUTING_P), "exact": {"recall": [], "coverage": []},
+           "pooled": {"recall": [], "coverage": []}}
+    for p in ROUTING_P:
+        for name, src in (("exact", bufs.M), ("pooled", P)):
+            F.losa_select(src, p, N, R, C, tokens_alloc=geom.tokens_alloc, row_ptr=bufs.row_ptr,
+                          col_idx=bufs.col_idx, order=bufs.order, ws=bufs.ws_sel, stream=stream)
+            F.losa_retained_mass(bufs.M, bufs.row_ptr, bufs.col_idx, N, R, C, out=bufs.kept, stream=stream)
+            kept = bufs.kept.cpu().numpy().astype(np.float64)
+            nnz = int(bufs.row_ptr[-1].item())
+            out[name]["recall"].append(float((kept[:, 0] * w).sum() / (kept[:, 1] * w).sum()))
+            out[name]["coverage"].append(nnz / float(rows * nk))
+    out["note"] = ("lists from exact masses vs from pooled proxy masses (block-mean Q/K, block-weighted softmax); "
+                   "recall measured under the exact masses")
+    return out
 
 
 def run_reuse(args, wl):

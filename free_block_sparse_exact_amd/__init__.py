@@ -38,6 +38,8 @@ __all__ = [
     "losa_retained_mass",
     "losa_dense_attn_mass_workspace",
     "losa_dense_attn_mass",
+    "losa_pooled_mass_workspace",
+    "losa_pooled_mass",
     "LOSA_F32",
     "LOSA_BF16",
     "STATUS",
@@ -112,6 +114,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "losa_retained_mass": ([S, P, P, P, P, P], i32),
         "losa_dense_attn_mass_workspace": ([S, sz], i32),
         "losa_dense_attn_mass": ([S, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
+        "losa_pooled_mass_workspace": ([S, sz], i32),
+        "losa_pooled_mass": ([S, P, P, P, P, ctypes.c_size_t, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -323,6 +327,29 @@ def losa_dense_attn_mass(q, k, v, tokens: int, q_block: int, k_block: int, softm
                                      _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "losa_dense_attn_mass")
     return out, M
+
+
+def losa_pooled_mass_workspace(geom: Geometry) -> int:
+    n = ctypes.c_size_t()
+    _check(_L().losa_pooled_mass_workspace(ctypes.byref(geom.shape()), ctypes.byref(n)), "losa_pooled_mass_workspace")
+    return n.value
+
+
+def losa_pooled_mass(q, k, tokens: int, q_block: int, k_block: int, softmax_scale: Optional[float] = None,
+                     out=None, ws=None, stream=None):
+    """Pooled proxy masses P [B, H, n_q, n_k] (fp32): block-mean Q against block-mean K,
+    block-weighted softmax over key blocks."""
+    import torch
+    g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
+    if out is None:
+        out = torch.empty((g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
+    shp = g.shape(q=q, k=k)
+    nbytes = ctypes.c_size_t()
+    _check(_L().losa_pooled_mass_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_pooled_mass_workspace")
+    ws = _workspace(nbytes.value, q.device, ws)
+    _check(_L().losa_pooled_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(out), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)), "losa_pooled_mass")
+    return out
 
 
 def losa_retained_mass(M, row_ptr, col_idx, tokens: int, q_block: int, k_block: int, out=None, stream=None):

@@ -195,6 +195,28 @@ losa_status losa_dense_attn_mass(const losa_shape* shape, const void* Q, const v
   return hip_status(losa::launch_dense_attn_mass(g, Q, K, V, M, O, o_dtype == LOSA_BF16, ws, stream));
 }
 
+losa_status losa_pooled_mass_workspace(const losa_shape* shape, size_t* bytes) {
+  Geom g;
+  if (!bytes) return LOSA_ERR_NULL;
+  const losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  *bytes = losa::pooled_ws_bytes(g);
+  return LOSA_OK;
+}
+
+losa_status losa_pooled_mass(const losa_shape* shape, const void* Q, const void* K, float* P, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if ((st = check_input(g, Q, g.qs)) != LOSA_OK) return st;
+  if ((st = check_input(g, K, g.ks)) != LOSA_OK) return st;
+  if (!P || !ws) return LOSA_ERR_NULL;
+  if (!aligned16(P)) return LOSA_ERR_INVALID_ARG;
+  if (ws_bytes < losa::pooled_ws_bytes(g) || !aligned16(ws)) return LOSA_ERR_WORKSPACE;
+  return hip_status(losa::launch_pooled_mass(g, Q, K, P, ws, stream));
+}
+
 losa_status losa_retained_mass(const losa_shape* shape, const float* M, const int32_t* row_ptr,
                                const int32_t* col_idx, float* kept, hipStream_t stream) {
   Geom g;

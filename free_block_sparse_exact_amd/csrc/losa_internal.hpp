@@ -64,4 +64,8 @@ size_t dense_ws_bytes(const Geom& g);
 hipError_t launch_dense_attn_mass(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O,
                                   int o_bf16, void* ws, hipStream_t stream);
 
+// Pooled proxy masses (block-mean Q and K, block-weighted softmax).
+size_t pooled_ws_bytes(const Geom& g);
+hipError_t launch_pooled_mass(const Geom& g, const void* Q, const void* K, float* P, void* ws, hipStream_t stream);
+
 }  // namespace losa

@@ -204,6 +204,27 @@ losa_status losa_dense_attn_mass(const losa_shape* shape, const void* Q, const v
                                  hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Pooled proxy masses: the coarse block-mass estimate of per-step top-p
+ * methods, which the LoSA page contrasts with exact masses (Motivation
+ * Summary: SVG2 and SpargeAttn rely on coarse estimates that are not
+ * accurate enough near 99% recall; the pages give no formula).  Reading:
+ *   P[b,h,i,j] = |B_j| exp(qbar_i . kbar_j * scale)
+ *                / sum_j' |B_j'| exp(qbar_i . kbar_j' * scale),
+ * qbar_i, kbar_j the means over the valid tokens of query block i and key
+ * block j, |B_j| the valid keys of block j.  Rows sum to 1 like losa_block_
+ * mass's M, so losa_select turns P into lists; P = M whenever the scores are
+ * constant on every (query block, key block) pair.
+ *
+ * P: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
+ * ws: at least *bytes from losa_pooled_mass_workspace (the block means, fp32).
+ * Arithmetic: fp32 means, dot products and softmax, for bf16 and f32 inputs
+ * and every supported block shape.
+ * ------------------------------------------------------------------------ */
+losa_status losa_pooled_mass_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_pooled_mass(const losa_shape* shape, const void* Q, const void* K, float* P, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Retained mass of a pattern (for Recall, Motivation Summary).
  * kept: fp32 [2 * batch*heads*n_q]: kept[2r] = sum of M[r, j] over the
  * listed blocks of row r, kept[2r+1] = sum of M[r, j] over all j.  Recall

@@ -167,3 +167,19 @@ def test_dense_attn_mass_errors(lib):
     assert dense(ws_bytes=n.value - 1) == WORKSPACE
     assert lib.losa_dense_attn_mass(ctypes.byref(shape(head_dim=96)), FAKE, FAKE, FAKE, FAKE, FAKE, F.LOSA_BF16,
                                     FAKE, 1 << 40, None) == UNSUPPORTED
+
+
+@no_gpu_only
+def test_pooled_mass_errors(lib):
+    s = shape()
+    n = ctypes.c_size_t()
+    assert lib.losa_pooled_mass_workspace(ctypes.byref(s), ctypes.byref(n)) == OK and n.value > 0
+
+    def pooled(P=FAKE, ws=FAKE, ws_bytes=1 << 40, K=FAKE):
+        return lib.losa_pooled_mass(ctypes.byref(s), FAKE, K, P, ws, ws_bytes, None)
+
+    assert pooled(P=None) == NULL
+    assert pooled(K=None) == NULL
+    assert pooled(ws=None) == NULL
+    assert pooled(P=FAKE + 4) == INVALID
+    assert pooled(ws_bytes=n.value - 1) == WORKSPACE
