@@ -528,9 +528,12 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
 # kernel name fragment -> (short name, call it belongs to)
 TRACE_KERNELS = [
     ("attn_bf16_kernel", "attn_bf16_kernel", "losa_sparse_attn"),
-    ("pack_kv_kernelILi128ELb1", "pack_kv_kernel (K and V)", "losa_sparse_attn"),
+    ("pack_kv_kernelILi128ELb1", "pack_kv_kernel (K and V)", "losa_sparse_attn, losa_dense_attn_mass"),
     ("pack_kv_kernelILi128ELb0", "pack_kv_kernel (K only)", "losa_block_mass"),
     ("mass_bf16_kernel", "mass_bf16_kernel", "losa_block_mass"),
+    ("dense_bf16_kernel", "dense_bf16_kernel", "losa_dense_attn_mass"),
+    ("pool_kernel", "pool_kernel", "losa_pooled_mass"),
+    ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
     ("cut_kernel", "cut_kernel", "losa_select"),
     ("scan_kernel", "scan_kernel", "losa_select"),
     ("compact_kernel", "compact_kernel", "losa_select"),
@@ -561,7 +564,8 @@ def summarize_trace(trace_dir, name, command):
         avg = float(r["AverageNs"]) / 1e3
         lines.append(f"| {short} | {call} | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-        per_call[call] = per_call.get(call, 0.0) + avg
+        for c in call.split(", "):
+            per_call[c] = per_call.get(c, 0.0) + avg
     lines += ["", "Average per library call (sum of its kernels' average durations):", ""]
     lines += [f"* {call}: {us / 1e3:.3f} ms" for call, us in per_call.items()]
     lines.append("")
