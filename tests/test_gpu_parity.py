@@ -361,3 +361,38 @@ def test_overflow_fallback_paths(R):
     err = float(np.abs(Og.cpu().numpy()[:, :, :N] - ref[:, :, :N]).max())
     say(f"fallback R={R}: O max abs err {err:.3e}")
     assert err <= ATTN_ATOL
+
+
+def test_batch_two_strided_all_calls():
+    """batch = 2 with token-major storage [B, N, H, d] viewed as [B, H, N, d]:
+    masses, lists, sparse attention, the construction call and the pooled
+    proxy against the oracle (each batch entry is independent)."""
+    rng = np.random.default_rng(77)
+    B, H, N, d, R, C, p = 2, 2, 700, 128, 64, 64, 0.95
+    Na = 704
+    vals = [rng.standard_normal((B, Na, H, d)) * s for s in (1.5, 1.5, 1.0)]
+    bits = [S.bf16_bits_from_f32(x.astype(np.float32)) for x in vals]
+    x64 = [S.f64_from_bf16_bits(b).transpose(0, 2, 1, 3) for b in bits]  # [B, H, Na, d]
+    dev = [to_device(b, "bf16").permute(0, 2, 1, 3) for b in bits]        # strided views
+    q, k, v = dev
+    assert not q.is_contiguous()
+    M = F.losa_block_mass(q, k, N, R, C)
+    M_ref = O.block_mass(x64[0], x64[1], N, R, C)
+    assert mass_rel_err(M.cpu().numpy(), M_ref) <= MASS_RTOL
+    rp, ci, order = F.losa_select(torch.from_numpy(M_ref.astype(np.float32)).cuda(), p, N, R, C, tokens_alloc=Na)
+    rp_ref, ci_ref = O.select_contract(M_ref.astype(np.float32), p)
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rp_h, rp_ref)
+    assert np.array_equal(ci[:int(rp_h[-1])].cpu().numpy(), ci_ref)
+    Og = F.losa_sparse_attn(q, k, v, rp, ci, order, N, R, C, out_dtype=torch.float32)
+    ref = O.sparse_attention(x64[0], x64[1], x64[2], N, R, C, rp_ref, ci_ref)
+    assert float(np.abs(Og.cpu().numpy()[:, :, :N] - ref[:, :, :N]).max()) <= ATTN_ATOL
+    Od, Md = F.losa_dense_attn_mass(q, k, v, N, R, C, out_dtype=torch.float32)
+    dense = O.dense_attention(x64[0], x64[1], x64[2], N)
+    assert float(np.abs(Od.cpu().numpy()[:, :, :N] - dense[:, :, :N]).max()) <= ATTN_ATOL
+    assert mass_rel_err(Md.cpu().numpy(), M_ref) <= MASS_RTOL
+    P = F.losa_pooled_mass(q, k, N, R, C).cpu().numpy().astype(np.float64)
+    P_ref = O.pooled_mass(x64[0], x64[1], N, R, C)
+    assert float((np.abs(P - P_ref) / P_ref).max()) <= MASS_RTOL
+    torch.cuda.synchronize()
+    say("batch 2, strided: all calls match the oracle")
