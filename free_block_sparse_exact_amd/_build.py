@@ -27,11 +27,12 @@ FLAGS = [
 ]
 
 
-# Per-source additions.  Sparse attention: matrix instructions take the form
-# whose result and accumulator live in vector registers.  Its scores feed
-# vector arithmetic straight away, and with one wave per SIMD the O
-# accumulators fit beside them; the default form parks results in AGPRs and
-# spends ~100 register moves per 32-key chunk copying them back and forth.
+# Per-source additions.  Sparse attention and the construction kernel: matrix
+# instructions take the form whose result and accumulator live in vector
+# registers.  Their scores feed vector arithmetic straight away, and with one
+# wave per SIMD the O accumulators fit beside them; the default form parks
+# results in AGPRs and spends ~100 register moves per 32-key chunk copying
+# them back and forth.
 EXTRA_FLAGS = {"losa_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "losa_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -9,12 +9,13 @@
 //     operand load is 64 lanes x 16 contiguous bytes -- with K and V read in
 //     their natural layouts each 1 KB load split into ~48 cache accesses and
 //     the texture data path, not the matrix cores, set the pace;
-//   * one workgroup per 64-query tile of a row (two per row when R = 128),
-//     dispatched in the caller's budget order.  Its waves split the row's
-//     32-key chunks (wave kw of each query group takes chunks kw, kw+4, ...),
-//     each keeping its own online-softmax state for its queries; the four key
-//     groups are merged through LDS at the end.  Each wave holds its Q tile
-//     as MFMA B operands in registers;
+//   * one workgroup (four waves, one per SIMD) per 64-query tile of a row
+//     (two per row when R = 128), dispatched in the caller's budget order
+//     with an XCD-aware mapping.  The waves split the row's 32-key chunks
+//     (wave kw takes chunks kw, kw+4, ...), each keeping its own online-
+//     softmax state for all 64 queries; the four key groups are merged
+//     through LDS at the end.  Each wave holds its Q tile as MFMA B operands
+//     in AGPRs (only matrix instructions read it);
 //   * S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA.  K rows are fed
 //     in the permuted order kappa(kt, rho) = 8*(rho>>2) + 4*kt + (rho&3), so
 //     lane l ends up holding the eight consecutive keys 8*(l>>4)+[0,8) of
@@ -23,8 +24,9 @@
 //   * no per-score maximum and no rescaling of O inside the loop (see the
 //     main loop); row sums use the bf16-rounded probabilities, matching the
 //     numerator;
-//   * the next chunk's K is requested as soon as the score MFMAs have read
-//     the current one, and V likewise after the P.V MFMAs.
+//   * a two-stage software pipeline (scores of chunk t+1 beside the softmax
+//     and P.V of chunk t), chunk keys read from registers, and the MFMA form
+//     with vector-register results (built with -amdgpu-mfma-vgpr-form).
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
 #include "losa_pack.hpp"
@@ -34,27 +36,22 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// A chunk whose per-lane probability sum (relative to the running max)
-// exceeds this bound goes through the rescale path.
+// A chunk whose per-lane probability sum against the wave's reference
+// exceeds this bound sends the wave to the exact two-pass path.
 constexpr float kPBound = 65536.0f;
 
-// Workgroup: 8 waves = 2 query halves (32 queries each) x 4 key groups.
-// Wave (qh, kw) keeps the running state of its 32 queries over the chunks
-// kw, kw+4, kw+8, ... of the row; at the end the four key groups of each
-// query half are merged through LDS.  32 queries per wave keep the state
-// within 256 registers, so two waves share each SIMD (one wave alone issues
-// vector instructions at about half the SIMD's rate).  The two query halves
-// of a key group read the same K and V chunks at about the same time.
-template <int kQT>
-constexpr int attn_waves() { return 4 * (4 / kQT); }
-
-template <int D, int kQT>
-__global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
+// Workgroup: 4 waves (one per SIMD), one per key group.  Wave kw keeps the
+// running state of all 64 queries of the tile (4 query tiles of 16: every
+// K and V operand feeds four MFMAs) over the chunks kw, kw+4, kw+8, ... of
+// the row; the four key groups are merged through LDS at the end.  (With 32
+// queries per wave two waves fit a SIMD, but each K/V chunk is then read by
+// two waves and the texture path saturates: measured slower.)
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     const Geom g, const __bf16* __restrict__ Q, const __bf16* __restrict__ Kp, const __bf16* __restrict__ Vp,
     int nch, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ order, void* O, int o_bf16) {
-  constexpr int DC = D / 32, DT = D / 16;
-  constexpr int kAttnWaves = attn_waves<kQT>();
+  constexpr int DC = D / 32, DT = D / 16, kQT = 4;
   constexpr int LD = D + 4;   // merge slot row stride (floats)
   extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]
   const int qhalves = g.R / 64;
@@ -63,8 +60,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   const int row = order ? order[ridx] : ridx;
   const int bh = row / g.nq, i = row - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kw = w & 3, qh = w >> 2;
+  const int lane = threadIdx.x & 63, kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
   const __bf16* Kbh = Kp + (int64_t)bh * nch * (32 * D);
@@ -76,7 +72,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   bf16x8 qop[kQT][DC];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    const int qrow = row0 + (qh * kQT + qt) * 16 + lr;
+    const int qrow = row0 + qt * 16 + lr;
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc) {
       bf16x8 v = load_bf16x8(Qbh + (int64_t)qrow * g.qs[2] + dc * 32 + lg * 8);
@@ -119,7 +115,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
     for (int dt = 0; dt < DT; ++dt) vop[dt] = load_bf16x8(vc + dt * 512);
   };
   // S^T for one chunk: acc[kt][qt][r] = score of key kb + 8*lg + 4*kt + r for
-  // query qh*32 + qt*16 + lr.
+  // query qt*16 + lr.
   auto scores = [&](const bf16x8 (&kop)[2][DC], f32x4 (&acc)[2][kQT]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -356,9 +352,9 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   }
 
   // Merge the key groups of each query group: 3 -> 2 -> 1 -> 0 through one LDS slot per group.
-  float* so = lds + qh * kQT * 16 * LD;
-  float* sm = lds + 64 * LD + qh * kQT * 16;
-  float* sl = lds + 64 * LD + 64 + qh * kQT * 16;
+  float* so = lds;
+  float* sm = lds + 64 * LD;
+  float* sl = sm + 64;
   for (int src = 3; src >= 1; --src) {
     __syncthreads();
     if (kw == src) {
@@ -394,7 +390,7 @@ __global__ __launch_bounds__(64 * attn_waves<kQT>(), 1) void attn_bf16_kernel(
   if (kw == 0) {
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
-      const int qrow = row0 + (qh * kQT + qt) * 16 + lr;
+      const int qrow = row0 + qt * 16 + lr;
       const float inv = (qrow < g.N && l[qt] > 0.f) ? 1.0f / l[qt] : 0.f;
       const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
 #pragma unroll
@@ -485,25 +481,19 @@ __global__ __launch_bounds__(128) void attn_simt_kernel(const Geom g, const T* _
   }
 }
 
-// 16-query tiles per wave: 4 (4 waves per workgroup, one wave per SIMD).  With
-// 2 (8 waves, two per SIMD) the two query halves read every K/V chunk twice,
-// which saturates the texture path; 4 measured faster.
-constexpr int kAttnQueryTiles = 4;
-
 int vt_chunks(const Geom& g) { return packed_chunks(g); }
 
 template <int D>
 hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* V, const int32_t* row_ptr,
                        const int32_t* col_idx, const int32_t* order, void* O, int o_bf16, void* ws,
                        hipStream_t st) {
-  constexpr int QT = kAttnQueryTiles;
   const int nch = vt_chunks(g);
   __bf16* Kp = reinterpret_cast<__bf16*>(ws);
   __bf16* Vp = Kp + (size_t)g.B * g.H * nch * 32 * D;
   hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)V, Kp, Vp, nch);
   const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float);
-  hipLaunchKernelGGL((attn_bf16_kernel<D, QT>), dim3(g.rows() * (g.R / 64)), dim3(64 * attn_waves<QT>()), lds, st,
+  hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st,
                      g, (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, row_ptr, col_idx, order, O,
                      o_bf16);
   return hipGetLastError();

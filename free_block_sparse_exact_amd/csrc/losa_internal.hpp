@@ -32,8 +32,8 @@ inline bool mfma_path(const Geom& g) {
   return g.bf16 && (g.D == 64 || g.D == 128) && (g.R == 64 || g.R == 128);
 }
 
-// Block masses.  Workspace: row log-sum-exp (B*H*Na floats) and, on the
-// matrix-core path, a packed copy of K.
+// Block masses.  Workspace: on the matrix-core path the per-(query row, key
+// block) partial sums and a packed copy of K; otherwise the row log-sum-exp.
 size_t mass_ws_bytes(const Geom& g);
 hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, void* ws,
                              hipStream_t stream);
@@ -53,7 +53,8 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
 hipError_t launch_retained_mass(const Geom& g, const float* M, const int32_t* row_ptr,
                                 const int32_t* col_idx, float* kept, hipStream_t stream);
 
-// Sparse attention; vt is workspace of B*H*D*Na bf16 on the matrix-core path.
+// Sparse attention.  Workspace: packed K and V on the matrix-core path, none
+// otherwise.  Null row_ptr/col_idx (SIMT path only) means every key block.
 size_t attn_ws_bytes(const Geom& g);
 hipError_t launch_sparse_attn(const Geom& g, const void* Q, const void* K, const void* V,
                               const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
