@@ -145,3 +145,51 @@ def test_select_bit_exact_full_shape(wid):
     assert np.array_equal(rp, rp_ref)
     assert np.array_equal(ci[:int(rp[-1])].cpu().numpy(), ci_ref)
     assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref))
+
+
+def test_maximum_key_block_count():
+    """n_k = 4096 (the largest the ABI accepts): one head of 131072 tokens with
+    128-token query and 32-token key blocks through masses, selection and
+    sparse attention; sampled rows against the oracle, and the selector
+    bit-exact on synthetic masses of the full [1, 1, 1024, 4096] shape."""
+    wl = S.Workload("max", "max_key_blocks", 1, 128, (32, 64, 64), 128, "bf16", 0.99, seed=12, k_block=32)
+    R, C = wl.block, wl.key_block
+    N, Na = wl.tokens, wl.tokens_alloc
+    assert wl.n_key_blocks == 4096
+    with Timer("generate"):
+        layer = S.make_layer(wl)
+    q, k, v = layer_to_device(layer)
+    M = F.losa_block_mass(q, k, N, R, C)
+    rp, ci, order = F.losa_select(M, wl.p, N, R, C, tokens_alloc=Na)
+    Og = F.losa_sparse_attn(q, k, v, rp, ci, order, N, R, C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:int(rp_h[-1])].cpu().numpy()
+    qh, kh, vh = (_head_f64(getattr(layer, n), wl.dtype, 0, 0) for n in ("q", "k", "v"))
+    iis = [0, 511, 1023] + list(np.random.default_rng(12).choice(1023, 5, replace=False))
+    Mref = O.block_mass_rows(qh, kh, N, R, C, [(0, 0, i) for i in iis])
+    Mg = M[0, 0].cpu().numpy()
+    worst_m = max(mass_rel_err(Mg[i], Mref[s_]) for s_, i in enumerate(iis))
+    worst_o, n_cmp = 0.0, 0
+    for s_, i in enumerate(iis):
+        lst = O.select_contract_row(Mref[s_].astype(np.float32), wl.p)[0]
+        if not np.array_equal(lst, row_csr(rp_h, ci_h, i)):
+            continue
+        n_cmp += 1
+        keys = np.concatenate([np.arange(j * C, min((j + 1) * C, N)) for j in lst])
+        r0, r1 = i * R, min((i + 1) * R, N)
+        a = O.attention_probs(qh[0, 0, r0:r1], kh[0, 0, keys], O.softmax_scale(wl.head_dim))
+        worst_o = max(worst_o, float(np.abs(Og[0, 0, r0:r1].cpu().numpy() - a @ vh[0, 0, keys]).max()))
+    say(f"n_k = 4096: mass rel err {worst_m:.2e}; O err {worst_o:.2e} on {n_cmp} of {len(iis)} rows")
+    assert worst_m <= MASS_RTOL
+    assert worst_o <= ATTN_ATOL
+    assert n_cmp >= len(iis) - 1
+    # the selector at the full width, bit-exact
+    Msyn = _synthetic_masses(np.random.default_rng(13), (1, 1, 1024, 4096))
+    rp2, ci2, order2 = F.losa_select(torch.from_numpy(Msyn).cuda(), wl.p, N, R, C, tokens_alloc=Na)
+    torch.cuda.synchronize()
+    rp_ref, ci_ref = O.select_contract(Msyn, wl.p)
+    rp2 = rp2.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rp2, rp_ref)
+    assert np.array_equal(ci2[:int(rp2[-1])].cpu().numpy(), ci_ref)
+    assert np.array_equal(order2.cpu().numpy(), O.budget_order(rp_ref))
