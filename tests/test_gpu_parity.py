@@ -396,3 +396,43 @@ def test_batch_two_strided_all_calls():
     assert float((np.abs(P - P_ref) / P_ref).max()) <= MASS_RTOL
     torch.cuda.synchronize()
     say("batch 2, strided: all calls match the oracle")
+
+
+@pytest.mark.parametrize("RC", [(64, 64), (128, 32), (128, 128)])
+@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 63, 64, 65, 96, 97, 127, 128, 129, 160])
+def test_small_token_counts_all_calls(N, RC):
+    """Token counts around every chunk and block boundary (one head, bf16, d = 128)
+    through masses, selection, sparse attention on the oracle's lists in
+    shuffled order, the construction call and the pooled proxy."""
+    R, C = RC
+    rng = np.random.default_rng(1000 * R + N)
+    H, d = 1, 128
+    Na = max(-(-N // R) * R, -(-N // C) * C)
+    bits = [S.bf16_bits_from_f32((rng.standard_normal((1, H, Na, d)) * s).astype(np.float32))
+            for s in (1.5, 1.5, 1.0)]
+    q64, k64, v64 = (S.f64_from_bf16_bits(b) for b in bits)
+    q, k, v = (to_device(b, "bf16") for b in bits)
+    M_ref = O.block_mass(q64, k64, N, R, C)
+    assert mass_rel_err(F.losa_block_mass(q, k, N, R, C).cpu().numpy(), M_ref) <= MASS_RTOL
+    rp_ref, ci_ref = O.select_contract(M_ref.astype(np.float32), 0.95)
+    rp, ci, order = F.losa_select(torch.from_numpy(M_ref.astype(np.float32)).cuda(), 0.95, N, R, C,
+                                  tokens_alloc=Na)
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rp_h, rp_ref)
+    assert np.array_equal(ci[:int(rp_h[-1])].cpu().numpy(), ci_ref)
+    # lists with the last (padded) block placed anywhere: shuffle each row
+    lists = [row_csr(rp_ref, ci_ref, r).copy() for r in range(len(rp_ref) - 1)]
+    for l in lists:
+        rng.shuffle(l)
+    ci_sh = np.concatenate(lists).astype(np.int32)
+    rp_d, ci_d = csr_to_device(rp_ref, ci_sh)
+    Og = F.losa_sparse_attn(q, k, v, rp_d, ci_d, None, N, R, C, out_dtype=torch.float32).cpu().numpy()
+    ref = O.sparse_attention(q64, k64, v64, N, R, C, rp_ref, ci_ref)
+    nqR = -(-N // R) * R
+    assert float(np.abs(Og[:, :, :nqR] - ref[:, :, :nqR]).max()) <= ATTN_ATOL
+    Od, Md = F.losa_dense_attn_mass(q, k, v, N, R, C, out_dtype=torch.float32)
+    dense = O.dense_attention(q64, k64, v64, N)
+    assert float(np.abs(Od.cpu().numpy()[:, :, :nqR] - dense[:, :, :nqR]).max()) <= ATTN_ATOL
+    assert mass_rel_err(Md.cpu().numpy(), M_ref) <= MASS_RTOL
+    P = F.losa_pooled_mass(q, k, N, R, C).cpu().numpy().astype(np.float64)
+    assert float((np.abs(P - O.pooled_mass(q64, k64, N, R, C)) / P).max()) <= MASS_RTOL
