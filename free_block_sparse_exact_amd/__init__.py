@@ -10,7 +10,12 @@ The functions carry the C names:
     losa_block_mass(q, k, tokens, q_block, k_block)            -> M
     losa_select(M, p, tokens, q_block, k_block, ...)          -> (row_ptr, col_idx, order)
     losa_sparse_attn(q, k, v, row_ptr, col_idx, order, ...)   -> O
+    losa_dense_attn_mass(q, k, v, tokens, q_block, k_block)   -> (O, M)
+    losa_pooled_mass(q, k, tokens, q_block, k_block)          -> P
     losa_retained_mass(M, row_ptr, col_idx, ...)              -> kept [rows, 2]
+
+Workspaces are allocated per call unless a tensor is passed as ``ws`` (any
+dtype; its size in bytes is what counts).
 
 Tensors are [batch, heads, tokens_alloc, head_dim] CUDA tensors (bf16 or
 fp32) whose last axis is contiguous.
@@ -200,6 +205,11 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _nbytes(ws) -> int:
+    """Size in bytes of a workspace tensor (any dtype), 0 for none."""
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
 def _workspace(nbytes: int, device, ws=None):
     import torch
     if nbytes == 0:
@@ -231,7 +241,7 @@ def losa_block_mass(q, k, tokens: int, q_block: int, k_block: int, softmax_scale
     if out is None:
         out = torch.empty((g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
     _check(_L().losa_block_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(out), _ptr(ws),
-                                0 if ws is None else ws.numel(), _stream(stream)), "losa_block_mass")
+                                _nbytes(ws), _stream(stream)), "losa_block_mass")
     return out
 
 
@@ -271,7 +281,7 @@ def losa_select(M, p: Union[float, Sequence[float]], tokens: int, q_block: int, 
     if not want_order:
         order = None
     _check(_L().losa_select(ctypes.byref(shp), _ptr(M), parr, len(pv), _ptr(row_ptr), _ptr(col_idx),
-                            col_idx.numel(), _ptr(order), _ptr(ws), 0 if ws is None else ws.numel(),
+                            col_idx.numel(), _ptr(order), _ptr(ws), _nbytes(ws),
                             _stream(stream)), "losa_select")
     return row_ptr, col_idx, order
 
@@ -296,7 +306,7 @@ def losa_sparse_attn(q, k, v, row_ptr, col_idx, order, tokens: int, q_block: int
     _check(_L().losa_sparse_attn_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_sparse_attn_workspace")
     ws = _workspace(nbytes.value, q.device, ws)
     _check(_L().losa_sparse_attn(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
-                                 _ptr(order), _ptr(out), odt, _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _ptr(order), _ptr(out), odt, _ptr(ws), _nbytes(ws),
                                  _stream(stream)), "losa_sparse_attn")
     return out
 
@@ -324,7 +334,7 @@ def losa_dense_attn_mass(q, k, v, tokens: int, q_block: int, k_block: int, softm
            "losa_dense_attn_mass_workspace")
     ws = _workspace(nbytes.value, q.device, ws)
     _check(_L().losa_dense_attn_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(M), _ptr(out), odt,
-                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+                                     _ptr(ws), _nbytes(ws), _stream(stream)),
            "losa_dense_attn_mass")
     return out, M
 
@@ -348,7 +358,7 @@ def losa_pooled_mass(q, k, tokens: int, q_block: int, k_block: int, softmax_scal
     _check(_L().losa_pooled_mass_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_pooled_mass_workspace")
     ws = _workspace(nbytes.value, q.device, ws)
     _check(_L().losa_pooled_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(out), _ptr(ws),
-                                 0 if ws is None else ws.numel(), _stream(stream)), "losa_pooled_mass")
+                                 _nbytes(ws), _stream(stream)), "losa_pooled_mass")
     return out
 
 
