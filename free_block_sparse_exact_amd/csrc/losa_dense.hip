@@ -25,6 +25,7 @@
 // the packed K and must leave the softmax: the wave that owns the last block
 // processes it first, its partly padded chunk at the very front (the first
 // chunk is masked explicitly), so the pipelined loop does no masking.
+#include "losa_blocksum.hpp"
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
 #include "losa_pack.hpp"
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   constexpr int DC = D / 32, DT = D / 16, kQT = 4;
   constexpr int LD = D + 4;       // merge slot row stride (floats)
   extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]
-  __shared__ float s_ref[4][64], s_tot[4][64];
+  __shared__ float s_ref[4][64], s_tot[4][64], s_f[4][64];
   const int qhalves = g.R / 64;
   const int rows = g.rows();
   const int tix = xcd_task(blockIdx.x, rows * qhalves);
@@ -349,14 +350,11 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
     for (int ww = 0; ww < 4; ++ww)
       if (s_ref[ww][lane] != kNegInf) lt += s_tot[ww][lane] * fast_exp2(s_ref[ww][lane] - mm);
     const float mine = s_ref[kw][lane];
-    const float f = (row0 + lane < g.N && mine != kNegInf) ? fast_exp2(mine - mm) / lt : 0.f;
+    s_f[kw][lane] = (row0 + lane < g.N && mine != kNegInf) ? fast_exp2(mine - mm) / lt : 0.f;
+    __syncthreads();  // every lane reads all 64 factors of its wave
     const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
     float* Mrow = Mout + ((int64_t)qsub * rows + row) * g.nk;
-    for (int bb = 0; bb < nb; ++bb) {
-      const int j = kw + 4 * bb;
-      const float v = wave_sum(Sg[(int64_t)j * 64 + lane] * f);
-      if (lane == 0) Mrow[j] = v * inv_rows;
-    }
+    blocks_from_sums(Sg, s_f[kw], kw, nb, inv_rows, Mrow, lane);
   }
 
   if (kw == 0) {

@@ -22,6 +22,7 @@
 //
 // fp32 inputs (and bf16 shapes outside the matrix-core path) take a SIMT
 // two-pass path: row log-sum-exp first, then the block sums.
+#include "losa_blocksum.hpp"
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
 #include "losa_pack.hpp"
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
                                                                      float* __restrict__ S, float* __restrict__ M) {
   constexpr float kHeadroom = 64.0f;
   constexpr float kSumBound = 1.2676506e30f;  // 2^100
-  __shared__ float s_ref[QG][4][64], s_tot[QG][4][64];
+  __shared__ float s_ref[QG][4][64], s_tot[QG][4][64], s_f[QG][4][64];
   extern __shared__ float part[];  // [QG][nk] per-group partial masses (QG > 1)
   const int rows = g.B * g.H * g.nq;
   const int task = xcd_task(blockIdx.x, rows);
@@ -239,16 +240,12 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
     const float mine = s_ref[grp][kw][lane];
     if (row0 + lane < g.N && mine != kNegInf) f = fast_exp2(mine - mm) / l;
   }
+  s_f[grp][kw][lane] = f;
+  __syncthreads();  // every lane reads all 64 factors of its wave
   const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
   float* Mrow = M + (int64_t)task * g.nk;
-  for (int bb = 0; bb < nb; ++bb) {
-    const int j = kw + 4 * bb;
-    const float v = wave_sum(Sg[(int64_t)j * 64 + lane] * f);
-    if (lane == 0) {
-      if (QG == 1) Mrow[j] = v * inv_rows;
-      else part[grp * g.nk + j] = v;
-    }
-  }
+  if (QG == 1) blocks_from_sums(Sg, s_f[grp][kw], kw, nb, inv_rows, Mrow, lane);
+  else blocks_from_sums(Sg, s_f[grp][kw], kw, nb, 1.0f, part + grp * g.nk, lane);
   if (QG > 1) {
     __syncthreads();
     for (int j = threadIdx.x; j < g.nk; j += blockDim.x) {
