@@ -51,7 +51,7 @@ template <int D>
 __global__ __launch_bounds__(256) void proxy_kernel(const Geom g, const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar, float* __restrict__ P) {
   extern __shared__ float sc[];  // [nk] scores
-  __shared__ float qv[D];
+  __shared__ __attribute__((aligned(16))) float qv[D];
   __shared__ float red[256 / kWave];
   const int r = blockIdx.x;
   const int bh = r / g.nq;
@@ -61,10 +61,16 @@ __global__ __launch_bounds__(256) void proxy_kernel(const Geom g, const float* _
   const float* kb = kbar + (int64_t)bh * g.nk * D;
   float mx = -__builtin_huge_valf();
   for (int j = tid; j < g.nk; j += 256) {
-    const float* kj = kb + (int64_t)j * D;
+    const f32x4* kj = reinterpret_cast<const f32x4*>(kb + (int64_t)j * D);  // 16-byte loads of the row
     float s = 0.f;
 #pragma unroll 8
-    for (int e = 0; e < D; ++e) s = __builtin_fmaf(qv[e], kj[e], s);
+    for (int e = 0; e < D / 4; ++e) {
+      const f32x4 k4 = kj[e], q4 = *reinterpret_cast<const f32x4*>(qv + 4 * e);
+      s = __builtin_fmaf(q4[0], k4[0], s);
+      s = __builtin_fmaf(q4[1], k4[1], s);
+      s = __builtin_fmaf(q4[2], k4[2], s);
+      s = __builtin_fmaf(q4[3], k4[3], s);
+    }
     s *= g.scale_log2;
     sc[j] = s;
     mx = fmaxf(mx, s);
