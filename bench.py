@@ -28,7 +28,12 @@ Other modes (used to produce the committed profile summaries):
   --summarize-trace DIR NAME "CMD"
                         write profiles/NAME.md from the kernel statistics of a
                         rocprofv3 --kernel-trace --stats run (DIR) of the
-                        command CMD.
+                        command CMD;
+  --summarize-clock PMC TRACE NAME "CMDS"
+                        write profiles/NAME.md: busy cycles per dispatch
+                        (rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES run
+                        PMC) against the kernel-trace durations (run TRACE),
+                        i.e. the clock the matrix-core kernels sustain.
 """
 from __future__ import annotations
 
@@ -174,12 +179,16 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "NAME", "COMMAND"))
+    ap.add_argument("--summarize-clock", nargs=4, metavar=("PMC_DIR", "TRACE_DIR", "NAME", "COMMANDS"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_clock:
+        summarize_clock(*args.summarize_clock)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -587,6 +596,58 @@ def summarize_trace(trace_dir, name, command):
             per_call[c] = per_call.get(c, 0.0) + avg
     lines += ["", "Average per library call (sum of its kernels' average durations):", ""]
     lines += [f"* {call}: {us / 1e3:.3f} ms" for call, us in per_call.items()]
+    lines.append("")
+    out = os.path.join(ROOT, "profiles", name + ".md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+CLOCK_KERNELS = [("attn_bf16_kernel", "attn_bf16_kernel", "sparse_attn"),
+                 ("mass_bf16_kernel", "mass_bf16_kernel", "block_mass"),
+                 ("dense_bf16_kernel", "dense_bf16_kernel", "dense_attn_mass")]
+N_XCD, N_SE = 8, 32          # MI355X: 8 XCDs, 4 shader engines each
+PEAK_CLOCK_GHZ = 2.4         # the clock the published 2.5 PFLOP/s bf16 peak assumes
+
+
+def summarize_clock(pmc_dir, trace_dir, name, commands):
+    """Clock the matrix-core kernels actually run at: GRBM_GUI_ACTIVE counts
+    busy GPU-clock cycles (rocprofv3 sums it over the 8 XCDs), SQ_BUSY_CYCLES
+    the same per shader engine (summed over 32); busy cycles per XCD over the
+    kernel's unprofiled median duration give the sustained clock."""
+    import csv
+    pmc = {}
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
+        lab = next((k for frag, k, _ in CLOCK_KERNELS if frag in r["Kernel_Name"]), None)
+        if lab is None:
+            continue
+        d = pmc.setdefault(lab, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    durs = {}
+    for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
+        lab = next((k for frag, k, _ in CLOCK_KERNELS if frag in r["Kernel_Name"]), None)
+        if lab is not None:
+            durs.setdefault(lab, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    trace = {lab: float(np.median(v)) for lab, v in durs.items()}
+    lines = [f"# Sustained clock of the matrix-core kernels: {name}", "",
+             "Commands (run from the repository root, after building the library):", ""]
+    lines += ["    " + c for c in commands.split(" ;; ")]
+    lines += ["", "GRBM_GUI_ACTIVE is summed over the 8 XCDs and SQ_BUSY_CYCLES over the 32 shader "
+              "engines; both give the busy cycles of one XCD.  Clock = those cycles / the kernel's "
+              f"average duration in the kernel trace (no counters attached).  The published bf16 peak "
+              f"(2.5 PFLOP/s) assumes {PEAK_CLOCK_GHZ} GHz.", "",
+              "| kernel | dispatches | GRBM cycles per XCD (M) | SQ busy cycles per SE (M) | trace median us | "
+              "sustained clock GHz | share of the 2.4 GHz rate |",
+              "|---|---|---|---|---|---|---|"]
+    for _, lab, _ in CLOCK_KERNELS:
+        if lab not in pmc or lab not in trace:
+            continue
+        ds = list(pmc[lab].values())
+        grbm = sum(d.get("GRBM_GUI_ACTIVE", 0.0) for d in ds) / len(ds) / N_XCD
+        sq = sum(d.get("SQ_BUSY_CYCLES", 0.0) for d in ds) / len(ds) / N_SE
+        ghz = grbm / trace[lab]
+        lines.append(f"| {lab} | {len(ds)} | {grbm / 1e6:.2f} | {sq / 1e6:.2f} | {trace[lab] / 1e3:.1f} | "
+                     f"{ghz:.2f} | {ghz / PEAK_CLOCK_GHZ:.2f} |")
     lines.append("")
     out = os.path.join(ROOT, "profiles", name + ".md")
     with open(out, "w") as f:
