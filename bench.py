@@ -562,11 +562,12 @@ TRACE_KERNELS = [
     ("dense_bf16_kernel", "dense_bf16_kernel", "losa_dense_attn_mass"),
     ("pool_kernel", "pool_kernel", "losa_pooled_mass"),
     ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
+    ("cut_wave_kernel", "cut_wave_kernel", "losa_select"),
     ("cut_kernel", "cut_kernel", "losa_select"),
-    ("scan_kernel", "scan_kernel", "losa_select"),
+    ("chunk_kernel", "chunk_kernel", "losa_select"),
+    ("offsets_kernel", "offsets_kernel", "losa_select"),
     ("compact_kernel", "compact_kernel", "losa_select"),
     ("place_kernel", "place_kernel", "losa_select"),
-    ("fill_i32_kernel", "fill_i32_kernel", "losa_select"),
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
 ]
 

@@ -42,7 +42,10 @@ hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float*
 struct SelectWs {
   int32_t* counts;      // [rows]
   uint64_t* kappa;      // [rows] boundary sort key of the last kept block
-  int32_t* chunk_hist;  // [(nk + 1) * nchunk] histogram of counts per row chunk, then offsets
+  int32_t* chunk_hist;  // [nchunk][nk + 1] rows per (chunk, nk - count), then offsets within each count
+  int32_t* chunk_sum;   // [nchunk] kept blocks per row chunk, then the chunk's first CSR slot
+  int32_t* done;        // [1] finished workgroups of the offsets kernel
+  int32_t* bucket;      // [nk + 1] rows per nk - count, then the first order slot of that count
   int nchunk;
 };
 constexpr int kOrderChunk = 256;  // rows per placement chunk for the budget order

@@ -4,18 +4,24 @@
 // cumulative mass reaches p times the block's total).
 //
 // Kernels, in launch order:
-//   fill        zero the count histogram (a kernel, not a memset, so the
+//   cut         the cut in (mass desc, index asc) order over exact integer
+//               units, without sorting -> the kept count s and the sort key
+//               kappa of the last kept block: one wave per row by bisection
+//               (n_k <= 2048), or one workgroup per row by radix select;
+//   chunk       one workgroup per chunk of 256 rows: histogram of counts
+//               and kept total of the chunk (LDS, then plain stores: no
+//               global atomics, nothing to clear beforehand, so the
 //               sequence can sit inside a captured graph);
-//   cut         one workgroup per row: sort keys (mass desc, index asc) in
-//               LDS with a bitonic network, integer prefix sums, find the
-//               kept count s and the sort key kappa of the last kept block;
-//               bump the histogram of counts for the work order;
-//   scan        one workgroup: exclusive scan of counts -> row_ptr, and of
-//               the count histogram -> per-(count, row chunk) offsets;
+//   offsets     one thread per count: exclusive scan over the row chunks of
+//               that count's histogram column; the last workgroup to finish
+//               scans the per-count totals (-> first order slot per count)
+//               and the per-chunk kept totals (-> first CSR slot per chunk,
+//               and row_ptr[rows]);
+//   place       one workgroup per chunk of 256 rows: row_ptr of its rows
+//               (chunk base + scan of counts), and the stable placement of
+//               its rows by count, descending -> order;
 //   compact     one workgroup per row: block j is kept iff its sort key is
-//               <= kappa; write kept indices ascending at row_ptr[row];
-//   place       one workgroup per chunk of rows: stable placement of rows
-//               by count, descending -> order.
+//               <= kappa; write kept indices ascending at row_ptr[row].
 //
 // Sort key of block j with (sanitised) mass bits u: ((2^32-1-u) << 32) | j.
 // For non-negative floats the bit pattern orders like the value, so an
@@ -26,6 +32,7 @@
 // 1/2 <= f < 1), q_j = ceil(m_j * 2^(51-e)) as uint64 (<= 2^51 each, so a row
 // of up to 4096 blocks sums below 2^63), T = ceil(P * sum q / 2^32) with a
 // 128-bit product, s = least prefix length with sum >= T; P = 2^32 keeps all.
+#include "losa.h"
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
 
@@ -106,94 +113,338 @@ __device__ __forceinline__ int block_sum_i32(int v, int* wsum) {
   return all;
 }
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x)
-    p[t] = v;
+// One workgroup per chunk of kOrderChunk rows: the chunk's histogram of
+// nk - count (built in LDS, stored whole, zeros included) and its kept
+// total.  Workgroup 0 also clears the offsets kernel's done counter.  Plain
+// stores only, so nothing needs clearing beforehand.
+__global__ __launch_bounds__(kOrderChunk) void chunk_kernel(const int32_t* __restrict__ counts, int rows, int nk,
+                                                            int32_t* __restrict__ hist,
+                                                            int32_t* __restrict__ chunk_sum, int32_t* done) {
+  extern __shared__ int hl[];  // [nk + 1]
+  __shared__ int wsum[kOrderChunk / 64];
+  const int chunk = blockIdx.x;
+  for (int x = threadIdx.x; x <= nk; x += blockDim.x) hl[x] = 0;
+  __syncthreads();
+  const int row = chunk * kOrderChunk + threadIdx.x;
+  const int cnt = row < rows ? counts[row] : 0;
+  if (row < rows) atomicAdd(&hl[nk - cnt], 1);
+  int v = cnt;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int32_t* hrow = hist + (int64_t)chunk * (nk + 1);
+  for (int x = threadIdx.x; x <= nk; x += blockDim.x) hrow[x] = hl[x];
+  if (threadIdx.x == 0) {
+    int t = 0;
+#pragma unroll
+    for (int ww = 0; ww < kOrderChunk / 64; ++ww) t += wsum[ww];
+    chunk_sum[chunk] = t;
+    if (chunk == 0) *done = 0;
+  }
 }
 
-// One workgroup per row.  Dynamic LDS: npad uint64 keys.
+// Most key blocks one thread of the cut kernel owns.
+constexpr int kMaxPer = LOSA_MAX_KEY_BLOCKS / kSelThreads;
+static_assert(kMaxPer == 16, "the workgroup cut kernel serves rows of 2049 to 4096 blocks");
+
+// One workgroup per row.  Finds the kept count s and the sort key kappa of
+// the s-th block in (mass desc, index asc) order without sorting: a radix
+// select, most significant digit first, over the inverted mass bits
+// ku = 2^32-1-u (ascending ku = descending mass), four passes of 8 bits.
+// Each pass sums the fixed-point units q of the remaining candidates per
+// digit and keeps the first non-empty digit at which the running sum
+// (everything before it included) reaches T; after the last pass the
+// candidates share one mass, and the cut within them falls by index.
+// Thread t owns the contiguous blocks [t*per, t*per + per), so thread order
+// is index order; kPer >= per bounds the per-thread register arrays.
+template <int kPer>
 __global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const float* __restrict__ M,
-                                                          const PTable pt, int npad,
-                                                          int32_t* __restrict__ counts,
-                                                          uint64_t* __restrict__ kappa,
-                                                          int32_t* __restrict__ chunk_hist, int nchunk) {
-  extern __shared__ uint64_t keys[];
+                                                          const PTable pt, int32_t* __restrict__ counts,
+                                                          uint64_t* __restrict__ kappa) {
+  __shared__ uint64_t hsum[256];
+  __shared__ uint32_t hnz[256];
   __shared__ uint64_t wsum64[kSelThreads / 64];
   __shared__ int wsum32[kSelThreads / 64];
-  __shared__ uint32_t wmax[kSelThreads / 64];
-  const int row = blockIdx.x;
+  __shared__ uint32_t wred[kSelThreads / 64];
+  __shared__ uint64_t s_below;
+  __shared__ int s_jcut;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = (row / g.nq) % g.H;
   const uint64_t P = pt.P[pt.per_head ? h : 0];
   const int nk = g.nk;
   const float* Mrow = M + (int64_t)row * nk;
+  const int per = (nk + kSelThreads - 1) / kSelThreads;
+  const int j0 = tid * per;
+  const int mine = max(0, min(per, nk - j0));  // valid blocks of this thread
+  if (tid == 0) s_jcut = 0;
 
+  uint32_t ku[kPer];
   uint32_t umax = 0;
-  for (int j = threadIdx.x; j < npad; j += kSelThreads) {
-    uint64_t key = ~0ull;
-    if (j < nk) {
-      const uint32_t u = sanitized_bits(Mrow[j]);
-      umax = umax > u ? umax : u;
-      key = sort_key(u, j);
-    }
-    keys[j] = key;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const uint32_t u = t < mine ? sanitized_bits(Mrow[j0 + t]) : 0u;
+    ku[t] = 0xFFFFFFFFu - u;
+    umax = umax > u ? umax : u;
   }
   umax = wave_max_u32(umax);
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = umax;
+  if (lane == 0) wred[w] = umax;
   __syncthreads();
 #pragma unroll
-  for (int ww = 0; ww < kSelThreads / 64; ++ww) umax = umax > wmax[ww] ? umax : wmax[ww];
-
-  // Bitonic sort, ascending.
-  for (int k = 2; k <= npad; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int t = threadIdx.x; t < (npad >> 1); t += kSelThreads) {
-        const int a = ((t & ~(jj - 1)) << 1) | (t & (jj - 1));
-        const int bb = a + jj;
-        const uint64_t ka = keys[a], kb = keys[bb];
-        const bool up = (a & k) == 0;
-        if ((ka > kb) == up) { keys[a] = kb; keys[bb] = ka; }
-      }
-      __syncthreads();
-    }
-  }
+  for (int ww = 0; ww < kSelThreads / 64; ++ww) umax = umax > wred[ww] ? umax : wred[ww];
+  __syncthreads();
 
   int s;
-  if (P == (1ull << 32)) {
+  uint64_t kap;
+  if (P == (1ull << 32)) {  // keep everything
     s = nk;
+    kap = ~0ull;
   } else {
     const int e = umax ? frexp_exp(umax) : 0;
-    // Each thread owns a contiguous run of sorted positions.
-    const int per = (npad + kSelThreads - 1) / kSelThreads;
-    const int p0 = threadIdx.x * per;
+    uint64_t q[kPer];
     uint64_t run = 0;
-    for (int t = 0; t < per; ++t) {
-      const int pos = p0 + t;
-      if (pos < nk) run += fixed_units(0xFFFFFFFFu - (uint32_t)(keys[pos] >> 32), e);
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      q[t] = t < mine ? fixed_units(0xFFFFFFFFu - ku[t], e) : 0;
+      run += q[t];
     }
     uint64_t total;
-    const uint64_t incl = block_inclusive_scan_u64(run, wsum64, &total);
+    block_inclusive_scan_u64(run, wsum64, &total);
     const uint64_t T = threshold(P, total);
-    uint64_t pre = incl - run;
-    int below = 0;
-    for (int t = 0; t < per; ++t) {
-      const int pos = p0 + t;
-      if (pos < nk) {
-        pre += fixed_units(0xFFFFFFFFu - (uint32_t)(keys[pos] >> 32), e);
-        below += pre < T ? 1 : 0;
+
+    uint32_t prefix = 0;  // digits fixed so far
+    uint64_t below = 0;   // units of all blocks ordered before the candidates
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hsum[tid] = 0;
+      hnz[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) {
+        if (t < mine && ((uint64_t)ku[t] >> (shift + 8)) == prefix) {
+          const int d = (ku[t] >> shift) & 255;
+          atomicAdd(reinterpret_cast<unsigned long long*>(&hsum[d]), (unsigned long long)q[t]);
+          hnz[d] = 1;
+        }
+      }
+      __syncthreads();
+      const uint64_t hs = hsum[tid];
+      uint64_t all;
+      const uint64_t cum = block_inclusive_scan_u64(hs, wsum64, &all);  // bins in ascending digit order
+      const bool hit = hnz[tid] != 0 && below + cum >= T;
+      const uint64_t bal = __ballot(hit);
+      if (lane == 0) wred[w] = bal ? (uint32_t)(w * 64 + __builtin_ctzll(bal)) : 0xFFFFFFFFu;
+      __syncthreads();
+      uint32_t bin = wred[0];
+#pragma unroll
+      for (int ww = 1; ww < kSelThreads / 64; ++ww) bin = bin < wred[ww] ? bin : wred[ww];
+      bin = bin < 255u ? bin : 255u;  // a hit always exists: the candidates' units reach T
+      if ((uint32_t)tid == bin) s_below = below + cum - hs;
+      __syncthreads();
+      below = s_below;
+      prefix = (prefix << 8) | bin;
+    }
+    // The cut lies among the blocks whose inverted bits equal prefix (all
+    // with units qu): the need-th of them in index order.
+    const uint64_t qu = fixed_units(0xFFFFFFFFu - prefix, e);
+    uint64_t need = 1;
+    if (below < T && qu > 0) need = (T - below + qu - 1) / qu;
+    int nbelow = 0, nties = 0;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      if (t < mine) {
+        nbelow += ku[t] < prefix ? 1 : 0;
+        nties += ku[t] == prefix ? 1 : 0;
       }
     }
-    below = block_sum_i32(below, wsum32);
-    s = below + 1;
-    if (s > nk) s = nk;
+    nbelow = block_sum_i32(nbelow, wsum32);
+    uint64_t tie_all;
+    const uint64_t tie_incl = block_inclusive_scan_u64((uint64_t)nties, wsum64, &tie_all);
+    uint64_t rank = tie_incl - (uint64_t)nties;  // ties owned by earlier threads
+    if (need > rank && need <= tie_incl) {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) {
+        if (t < mine && ku[t] == prefix) {
+          ++rank;
+          if (rank == need) s_jcut = j0 + t;
+        }
+      }
+    }
+    __syncthreads();
+    s = nbelow + (int)need;
+    kap = sort_key(0xFFFFFFFFu - prefix, s_jcut);
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     counts[row] = s;
-    kappa[row] = keys[s - 1];
-    if (chunk_hist) atomicAdd(&chunk_hist[(int64_t)(nk - s) * nchunk + row / kOrderChunk], 1);
+    kappa[row] = kap;
   }
 }
 
-// Single workgroup of 1024 threads: exclusive scans.
+// Wave reductions with a wave-uniform result: DPP within each 16-lane row
+// (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror 4, row_ror 8 leave
+// every lane with its row's total), then the four row totals read from
+// lanes 0, 16, 32, 48.  All 64 lanes must be active.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t add_dpp_u64(uint64_t x) {
+  return x + (((uint64_t)dpp_u32<kCtrl>((uint32_t)(x >> 32)) << 32) | dpp_u32<kCtrl>((uint32_t)x));
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  v = add_dpp_u64<kDppXor1>(v);
+  v = add_dpp_u64<kDppXor2>(v);
+  v = add_dpp_u64<kDppRor4>(v);
+  v = add_dpp_u64<kDppRor8>(v);
+  uint64_t t = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) t += ((uint64_t)lane_u32((uint32_t)(v >> 32), 16 * r) << 32) | lane_u32((uint32_t)v, 16 * r);
+  return t;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += (int)dpp_u32<kDppXor1>((uint32_t)v);
+  v += (int)dpp_u32<kDppXor2>((uint32_t)v);
+  v += (int)dpp_u32<kDppRor4>((uint32_t)v);
+  v += (int)dpp_u32<kDppRor8>((uint32_t)v);
+  return (int)(lane_u32(v, 0) + lane_u32(v, 16) + lane_u32(v, 32) + lane_u32(v, 48));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppXor1>(v));
+  v = min(v, dpp_u32<kDppXor2>(v));
+  v = min(v, dpp_u32<kDppRor4>(v));
+  v = min(v, dpp_u32<kDppRor8>(v));
+  return min(min(lane_u32(v, 0), lane_u32(v, 16)), min(lane_u32(v, 32), lane_u32(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppRor4>(v));
+  v = max(v, dpp_u32<kDppRor8>(v));
+  return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
+}
+
+// One wave per row (four rows per workgroup), no workgroup barriers.  The
+// cut is the least inverted-bits value v with F(v) = sum of the units q of
+// the blocks with ku <= v reaching T, found by bisection over the range of
+// the blocks' ku (F only steps at those values, so v is one of them, and
+// F(v - 1) < T).  Among the blocks with ku = v (equal masses, equal units)
+// the cut falls on the need-th in index order.  Lane l owns the contiguous
+// blocks [l*per, l*per + per), per <= kPer, so lane order is index order.
+template <int kPer>
+__global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float* __restrict__ M, const PTable pt,
+                                                       int32_t* __restrict__ counts,
+                                                       uint64_t* __restrict__ kappa) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= g.rows()) return;  // whole waves only
+  const int h = (row / g.nq) % g.H;
+  const uint64_t P = pt.P[pt.per_head ? h : 0];
+  const int nk = g.nk;
+  const float* Mrow = M + (int64_t)row * nk;
+  const int per = (nk + kWave - 1) / kWave;
+  const int j0 = lane * per;
+  const int mine = max(0, min(per, nk - j0));
+
+  uint32_t ku[kPer];
+  uint32_t umax = 0;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const uint32_t u = t < mine ? sanitized_bits(Mrow[j0 + t]) : 0u;
+    ku[t] = 0xFFFFFFFFu - u;
+    umax = umax > u ? umax : u;
+  }
+  umax = wave_max_u32_uniform(umax);
+
+  int s;
+  uint64_t kap;
+  if (P == (1ull << 32)) {  // keep everything
+    s = nk;
+    kap = ~0ull;
+  } else {
+    const int e = umax ? frexp_exp(umax) : 0;
+    uint64_t q[kPer];
+    uint64_t run = 0;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      q[t] = t < mine ? fixed_units(0xFFFFFFFFu - ku[t], e) : 0;
+      run += q[t];
+      if (t < mine) kmin = kmin < ku[t] ? kmin : ku[t];
+      if (q[t] > 0) {
+        lo = lo < ku[t] ? lo : ku[t];
+        hi = hi > ku[t] ? hi : ku[t];
+      }
+    }
+    const uint64_t T = threshold(P, wave_sum_u64(run));
+    uint32_t v;
+    if (T == 0) {
+      v = wave_min_u32(kmin);  // the first block in sorted order
+    } else {  // T > 0: some block has units, and F(max ku of those) = total >= T
+      lo = wave_min_u32(lo);
+      hi = wave_max_u32_uniform(hi);
+      while (lo < hi) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        uint64_t f = 0;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) f += ku[t] <= mid ? q[t] : 0;
+        if (wave_sum_u64(f) >= T) hi = mid;
+        else lo = mid + 1;
+      }
+      v = lo;
+    }
+    uint64_t below = 0;
+    int nbelow = 0, nties = 0;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      if (t < mine) {
+        below += ku[t] < v ? q[t] : 0;
+        nbelow += ku[t] < v ? 1 : 0;
+        nties += ku[t] == v ? 1 : 0;
+      }
+    }
+    below = wave_sum_u64(below);
+    const uint64_t qu = fixed_units(0xFFFFFFFFu - v, e);
+    uint64_t need = 1;
+    if (below < T && qu > 0) need = (T - below + qu - 1) / qu;
+    int incl = nties;  // ties owned by lanes <= this one
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int x = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += x;
+    }
+    int jcut = -1;
+    int rank = incl - nties;
+    if ((int64_t)need > rank && (int64_t)need <= incl) {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) {
+        if (t < mine && ku[t] == v) {
+          ++rank;
+          if (rank == (int)need) jcut = j0 + t;
+        }
+      }
+    }
+    const uint64_t owner = __ballot(jcut >= 0);
+    jcut = __builtin_amdgcn_readlane(jcut, owner ? __builtin_ctzll(owner) : 0);
+    s = wave_sum_i32(nbelow) + (int)need;
+    kap = sort_key(0xFFFFFFFFu - v, jcut < 0 ? 0 : jcut);
+  }
+  if (lane == 0) {
+    counts[row] = s;
+    kappa[row] = kap;
+  }
+}
+
+// Exclusive scan of data[0, n) into out by one workgroup (a multiple of 64
+// threads, wsum holding one int per wave); in place is allowed.
 __device__ void block_exclusive_scan_i32(int32_t* data, int n, int32_t* out, int32_t* out_total,
                                          int* wsum) {
   const int nt = blockDim.x;
@@ -233,12 +484,45 @@ __device__ void block_exclusive_scan_i32(int32_t* data, int n, int32_t* out, int
   __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int rows,
-                                                    int32_t* __restrict__ row_ptr, int32_t* chunk_hist,
-                                                    int hist_len) {
-  __shared__ int wsum[16];
-  block_exclusive_scan_i32(const_cast<int32_t*>(counts), rows, row_ptr, row_ptr + rows, wsum);
-  if (chunk_hist) block_exclusive_scan_i32(chunk_hist, hist_len, chunk_hist, nullptr, wsum);
+// One thread per count bucket b = nk - count: the column hist[.][b] becomes
+// its exclusive scan over the row chunks and bucket[b] its total.  The last
+// workgroup to finish (counted in *done) turns bucket into the first order
+// slot of each count (descending count = ascending b) and chunk_sum into the
+// first CSR slot of each chunk, and writes row_ptr[rows].
+__global__ __launch_bounds__(256) void offsets_kernel(int nk, int nchunk, int rows, int32_t* __restrict__ hist,
+                                                      int32_t* chunk_sum, int32_t* bucket, int32_t* done,
+                                                      int32_t* __restrict__ row_ptr) {
+  __shared__ int wsum[256 / 64];
+  __shared__ int last;
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b <= nk) {
+    int run = 0;
+    int c = 0;
+    for (; c + 8 <= nchunk; c += 8) {  // eight loads in flight per thread
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)(c + u) * (nk + 1) + b];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        hist[(int64_t)(c + u) * (nk + 1) + b] = run;
+        run += v[u];
+      }
+    }
+    for (; c < nchunk; ++c) {
+      const int v = hist[(int64_t)c * (nk + 1) + b];
+      hist[(int64_t)c * (nk + 1) + b] = run;
+      run += v;
+    }
+    bucket[b] = run;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  block_exclusive_scan_i32(bucket, nk + 1, bucket, nullptr, wsum);
+  block_exclusive_scan_i32(chunk_sum, nchunk, chunk_sum, row_ptr + rows, wsum);
 }
 
 // One workgroup per row: ascending compaction of {j : key_j <= kappa}.
@@ -280,19 +564,41 @@ __global__ __launch_bounds__(kSelThreads) void compact_kernel(const Geom g, cons
     if (flags & (1u << t)) col_idx[pos++] = j0 + t;
 }
 
-// One workgroup (kOrderChunk threads) per chunk of rows: stable placement by
-// count descending.  chunk_hist holds, after the scan, the first output slot
-// of each (nk - count, chunk) pair; waves take turns so that rows keep their
-// index order within a count.
-__global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __restrict__ counts, int rows,
-                                                            int nk, const int32_t* __restrict__ chunk_hist,
-                                                            int nchunk, int32_t* __restrict__ order) {
+// One workgroup (kOrderChunk threads) per chunk of rows.  row_ptr of the
+// chunk's rows: the chunk's first CSR slot plus the scan of their counts.
+// Then (if order is wanted) stable placement by count descending: the first
+// slot of a row with count c is bucket[nk - c] + hist[chunk][nk - c] plus the
+// rows of that count already placed by earlier waves of this chunk; waves
+// take turns so that rows keep their index order within a count.
+__global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __restrict__ counts, int rows, int nk,
+                                                            const int32_t* __restrict__ hist,
+                                                            const int32_t* __restrict__ bucket,
+                                                            const int32_t* __restrict__ chunk_base,
+                                                            int32_t* __restrict__ row_ptr,
+                                                            int32_t* __restrict__ order) {
   extern __shared__ int run[];  // [nk + 1] slots already used by earlier waves of this chunk
+  __shared__ int wsum[kOrderChunk / 64];
   const int chunk = blockIdx.x;
-  for (int v = threadIdx.x; v <= nk; v += blockDim.x) run[v] = 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int row = chunk * kOrderChunk + threadIdx.x;
-  const int bucket = row < rows ? nk - counts[row] : 0;
+  const int cnt = row < rows ? counts[row] : 0;
+  int v = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) wsum[w] = v;
+  for (int x = threadIdx.x; x <= nk; x += blockDim.x) run[x] = 0;
+  __syncthreads();
+  int before = chunk_base[chunk];
+#pragma unroll
+  for (int ww = 0; ww < kOrderChunk / 64; ++ww)
+    if (ww < w) before += wsum[ww];
+  if (row < rows) row_ptr[row] = before + v - cnt;
+  if (!order) return;
+  const int32_t* hrow = hist + (int64_t)chunk * (nk + 1);
+  const int bkt = nk - cnt;
   for (int turn = 0; turn < kOrderChunk / 64; ++turn) {
     __syncthreads();
     if (w == turn) {
@@ -301,10 +607,10 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
         const uint64_t am = __ballot(todo);
         if (am == 0) break;
         const int leader = __ffsll((unsigned long long)am) - 1;
-        const int b0 = __shfl(bucket, leader, kWave);
-        const bool match = todo && bucket == b0;
+        const int b0 = __shfl(bkt, leader, kWave);
+        const bool match = todo && bkt == b0;
         const uint64_t mm = __ballot(match);
-        const int base = chunk_hist[(int64_t)b0 * nchunk + chunk] + run[b0];
+        const int base = bucket[b0] + hrow[b0] + run[b0];
         if (match) {
           const int rank = __popcll(mm & ((1ull << lane) - 1));
           order[base + rank] = row;
@@ -332,12 +638,6 @@ __global__ __launch_bounds__(64) void retained_kernel(const Geom g, const float*
   if (threadIdx.x == 0) { kept[2 * row] = k; kept[2 * row + 1] = a; }
 }
 
-int next_pow2(int n) {
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
-}
-
 }  // namespace
 
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
@@ -348,12 +648,17 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
   off = align_up(off + (size_t)rows * sizeof(int32_t), 256);
   const size_t kappa_off = off;
   off = align_up(off + (size_t)rows * sizeof(uint64_t), 256);
-  const size_t hist_off = off;
-  off = align_up(off + (size_t)(g.nk + 1) * nchunk * sizeof(int32_t), 256);
+  const size_t hist_off = off;  // then chunk_sum and done
+  off = align_up(off + ((size_t)(g.nk + 1) * nchunk + nchunk + 1) * sizeof(int32_t), 256);
+  const size_t bucket_off = off;
+  off = align_up(off + (size_t)(g.nk + 1) * sizeof(int32_t), 256);
   if (layout) {
     layout->counts = reinterpret_cast<int32_t*>(base + counts_off);
     layout->kappa = reinterpret_cast<uint64_t*>(base + kappa_off);
     layout->chunk_hist = reinterpret_cast<int32_t*>(base + hist_off);
+    layout->chunk_sum = layout->chunk_hist + (size_t)(g.nk + 1) * nchunk;
+    layout->done = layout->chunk_sum + nchunk;
+    layout->bucket = reinterpret_cast<int32_t*>(base + bucket_off);
     layout->nchunk = nchunk;
   }
   return off;
@@ -362,22 +667,30 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
 hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr, int32_t* col_idx,
                          int32_t* order, const SelectWs& ws, hipStream_t st) {
   const int rows = g.rows();
-  const int npad = next_pow2(g.nk < 2 ? 2 : g.nk);
-  const int hist_len = (g.nk + 1) * ws.nchunk;
-  int32_t* hist = order ? ws.chunk_hist : nullptr;
-  if (hist) {
-    const int blocks = (hist_len + 255) / 256 < 1024 ? (hist_len + 255) / 256 : 1024;
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks), dim3(256), 0, st, hist, (int64_t)hist_len, 0);
+  // Up to 2048 key blocks a wave per row (bisection); beyond, a workgroup
+  // per row (radix select), which spreads a long row over 256 threads.  The
+  // per-thread arrays are unrolled, so the instance fits the row closely.
+  const int per = (g.nk + kWave - 1) / kWave;
+  if (per <= 32) {
+    auto cut = per <= 2 ? cut_wave_kernel<2> : per <= 4 ? cut_wave_kernel<4> : per <= 8 ? cut_wave_kernel<8>
+             : per <= 12 ? cut_wave_kernel<12> : per <= 16 ? cut_wave_kernel<16> : per <= 20 ? cut_wave_kernel<20>
+             : per <= 24 ? cut_wave_kernel<24> : cut_wave_kernel<32>;
+    hipLaunchKernelGGL(cut, dim3((rows + 3) / 4), dim3(256), 0, st, g, M, pt, ws.counts, ws.kappa);
+  } else {
+    const int per_t = (g.nk + kSelThreads - 1) / kSelThreads;
+    auto cut = per_t <= 12 ? cut_kernel<12> : cut_kernel<kMaxPer>;
+    hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.kappa);
   }
-  hipLaunchKernelGGL(cut_kernel, dim3(rows), dim3(kSelThreads), (size_t)npad * sizeof(uint64_t), st, g, M, pt,
-                     npad, ws.counts, ws.kappa, hist, ws.nchunk);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, (const int32_t*)ws.counts, rows, row_ptr, hist,
-                     hist_len);
+  const size_t hist_lds = (size_t)(g.nk + 1) * sizeof(int);
+  hipLaunchKernelGGL(chunk_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
+                     rows, g.nk, ws.chunk_hist, ws.chunk_sum, ws.done);
+  hipLaunchKernelGGL(offsets_kernel, dim3((g.nk + 1 + 255) / 256), dim3(256), 0, st, g.nk, ws.nchunk, rows,
+                     ws.chunk_hist, ws.chunk_sum, ws.bucket, ws.done, row_ptr);
+  hipLaunchKernelGGL(place_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
+                     rows, g.nk, (const int32_t*)ws.chunk_hist, (const int32_t*)ws.bucket,
+                     (const int32_t*)ws.chunk_sum, row_ptr, order);
   hipLaunchKernelGGL(compact_kernel, dim3(rows), dim3(kSelThreads), 0, st, g, M, (const uint64_t*)ws.kappa,
                      (const int32_t*)row_ptr, col_idx);
-  if (order)
-    hipLaunchKernelGGL(place_kernel, dim3(ws.nchunk), dim3(kOrderChunk), (size_t)(g.nk + 1) * sizeof(int), st,
-                       (const int32_t*)ws.counts, rows, g.nk, (const int32_t*)hist, ws.nchunk, order);
   return hipGetLastError();
 }
 
