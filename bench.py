@@ -29,6 +29,10 @@ Other modes (used to produce the committed profile summaries):
                         write profiles/NAME.md from the kernel statistics of a
                         rocprofv3 --kernel-trace --stats run (DIR) of the
                         command CMD;
+  --summarize-mfma PMC NAME "CMD"
+                        write profiles/NAME.md: rocprofv3's MfmaUtil (matrix
+                        cores busy, share of SIMD cycles) and MfmaFlopsBF16
+                        (bf16 MFMA flops executed) per dispatch;
   --summarize-clock PMC TRACE NAME "CMDS"
                         write profiles/NAME.md: busy cycles per dispatch
                         (rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES run
@@ -180,6 +184,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "NAME", "COMMAND"))
     ap.add_argument("--summarize-clock", nargs=4, metavar=("PMC_DIR", "TRACE_DIR", "NAME", "COMMANDS"))
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_DIR", "NAME", "COMMAND"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -189,6 +194,9 @@ def main():
         return
     if args.summarize_clock:
         summarize_clock(*args.summarize_clock)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -649,6 +657,38 @@ def summarize_clock(pmc_dir, trace_dir, name, commands):
         ghz = grbm / trace[lab]
         lines.append(f"| {lab} | {len(ds)} | {grbm / 1e6:.2f} | {sq / 1e6:.2f} | {trace[lab] / 1e3:.1f} | "
                      f"{ghz:.2f} | {ghz / PEAK_CLOCK_GHZ:.2f} |")
+    lines.append("")
+    out = os.path.join(ROOT, "profiles", name + ".md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_mfma(pmc_dir, name, command):
+    """Matrix-core utilisation from rocprofv3's derived counters: MfmaUtil =
+    MFMA-busy SIMD cycles / (busy GPU cycles x SIMDs), clock-independent;
+    MfmaFlopsBF16 = bf16 MFMA flops the hardware executed (padding and
+    recomputed chunks included), to set beside the algorithmic count."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
+        lab = next((k for frag, k, _ in CLOCK_KERNELS if frag in r["Kernel_Name"]), None)
+        if lab is None:
+            continue
+        d = per.setdefault(lab, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = [f"# Matrix-core utilisation: {name}", "", "Command (run from the repository root, after building the library):",
+             "", "    " + command, "",
+             "MfmaUtil = MFMA-busy SIMD cycles / (busy GPU cycles x SIMDs), in percent: the matrix cores' share "
+             "of the cycles the kernel ran, independent of the clock.  MfmaFlopsBF16 = bf16 MFMA flops executed.",
+             "", "| kernel | dispatches | MfmaUtil % | bf16 MFMA TFLOP executed per dispatch |", "|---|---|---|---|"]
+    for _, lab, _ in CLOCK_KERNELS:
+        if lab not in per:
+            continue
+        ds = list(per[lab].values())
+        util = sum(d.get("MfmaUtil", 0.0) for d in ds) / len(ds)
+        fl = sum(d.get("MfmaFlopsBF16", 0.0) for d in ds) / len(ds)
+        lines.append(f"| {lab} | {len(ds)} | {util:.1f} | {fl / 1e12:.3f} |")
     lines.append("")
     out = os.path.join(ROOT, "profiles", name + ".md")
     with open(out, "w") as f:
