@@ -1,0 +1,131 @@
+"""The selector's two sort-free searches against the sorted-prefix rule (CPU).
+
+The retained-mass rule (LoSA page, Methodology Summary, one-time pattern
+construction) sorts a row's key blocks by decreasing mass (ties: lower index
+first) and keeps the shortest prefix whose exact integer units reach the
+target T.  The GPU selector reaches the same cut without sorting: with
+ku = 2^32 - 1 - (float bits of the mass) and F(v) = sum of the units of the
+blocks with ku <= v, the cut value is the least v with F(v) >= T, found by
+bisection (one wave per row) or by a most-significant-digit radix select
+(one workgroup per row); among the blocks with ku = v (equal masses, equal
+units) the cut falls on the ceil((T - F(v-1)) / q)-th in index order.
+
+This file restates both searches in plain Python integers, written from that
+description and not from the kernels, and checks that their kept sets equal
+the oracle's on rows with ties, zeros, denormals, non-finite values and a
+one-hot row.  It does not run the GPU code: the GPU tests compare the library
+with the oracle directly; this pins the search schemes themselves.
+"""
+import math
+import struct
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+def _bits(m: float) -> int:
+    """Float bits of a sanitised fp32 mass (NaN, inf, negatives and -0 count as 0)."""
+    if not (m > 0.0 and math.isfinite(m)):
+        return 0
+    return struct.unpack("<I", struct.pack("<f", m))[0]
+
+
+def _units(u: int, e: int) -> int:
+    """ceil(m * 2^(51 - e)) for the fp32 value with bits u (exact rational arithmetic)."""
+    if u == 0:
+        return 0
+    m = struct.unpack("<f", struct.pack("<I", u))[0]
+    num, den = float(m).as_integer_ratio()
+    sh = 51 - e
+    if sh >= 0:
+        num <<= sh
+    else:
+        den <<= -sh
+    return -((-num) // den)
+
+
+def _row_setup(m32, p):
+    u = [_bits(float(x)) for x in m32]
+    ku = [0xFFFFFFFF - x for x in u]
+    umax = max(u)
+    e = math.frexp(struct.unpack("<f", struct.pack("<I", umax))[0])[1] if umax else 0
+    q = [_units(x, e) for x in u]
+    P = O.p_fixed(p)
+    T = -((-P * sum(q)) >> 32)
+    return ku, q, T, P, e
+
+
+def _finish(ku, q, T, v, e):
+    """Kept set once the cut value v is known: blocks before v, then the ties by index."""
+    below = sum(x for k, x in zip(ku, q) if k < v)
+    qu = _units(0xFFFFFFFF - v, e)
+    need = -((below - T) // qu) if (below < T and qu > 0) else 1
+    ties = [j for j, k in enumerate(ku) if k == v]
+    keep = [j for j, k in enumerate(ku) if k < v] + ties[:need]
+    return np.array(sorted(keep))
+
+
+def cut_bisection(m32, p):
+    ku, q, T, P, e = _row_setup(m32, p)
+    if P == 1 << 32:
+        return np.arange(len(ku))
+    if T == 0:
+        v = min(ku)
+    else:
+        pos = [k for k, x in zip(ku, q) if x > 0]
+        lo, hi = min(pos), max(pos)
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if sum(x for k, x in zip(ku, q) if k <= mid) >= T:
+                hi = mid
+            else:
+                lo = mid + 1
+        v = lo
+    return _finish(ku, q, T, v, e)
+
+
+def cut_radix(m32, p):
+    ku, q, T, P, e = _row_setup(m32, p)
+    if P == 1 << 32:
+        return np.arange(len(ku))
+    prefix, below = 0, 0
+    for pas in range(4):
+        shift = 24 - 8 * pas
+        hs, nz = [0] * 256, [False] * 256
+        for k, x in zip(ku, q):
+            if k >> (shift + 8) == prefix:
+                d = (k >> shift) & 255
+                hs[d] += x
+                nz[d] = True
+        cum = 0
+        for d in range(256):
+            cum += hs[d]
+            if nz[d] and below + cum >= T:
+                break
+        below += cum - hs[d]
+        prefix = (prefix << 8) | d
+    return _finish(ku, q, T, prefix, e)
+
+
+def _rows(rng, nk):
+    rows = [rng.random(nk), rng.exponential(size=nk) ** 4, np.full(nk, 1.0 / nk),
+            rng.integers(0, 4, nk) * 0.25, np.where(rng.random(nk) < 0.5, 0.0, rng.random(nk)),
+            np.zeros(nk), np.eye(1, nk, int(rng.integers(nk)))[0]]
+    out = [(r / max(r.sum(), 1e-300)).astype(np.float32) for r in rows]
+    out.append((rng.random(nk) * 1e-38).astype(np.float32))  # denormal masses
+    bad = rng.random(nk).astype(np.float32)
+    bad[rng.integers(nk, size=3)] = [np.nan, np.inf, -1.0]
+    out.append(bad)
+    return out
+
+
+@pytest.mark.parametrize("nk", [1, 2, 5, 64, 300])
+@pytest.mark.parametrize("p", [1e-9, 0.5, 0.9, 0.99, 0.995, 1.0])
+def test_sort_free_cuts_equal_sorted_prefix_rule(nk, p):
+    rng = np.random.default_rng(nk * 1000 + int(p * 1000))
+    for m in _rows(rng, nk):
+        ref = O.select_contract_row(m, p)[0]
+        assert np.array_equal(cut_bisection(m, p), ref)
+        assert np.array_equal(cut_radix(m, p), ref)
