@@ -46,6 +46,14 @@ notes of the repository):
   kbar_j' * scale), with qbar, kbar the means over the valid tokens of each
   block and |B_j| the valid keys of key block j (each pooled key stands for
   its block's keys).  Rows sum to 1, like M, so the same selector applies.
+* Masses within a candidate set (the reduced search of the GSRS card: later
+  top-p searches restricted to an earlier candidate set, with exact
+  attention weights computed inside the attention pass; the card gives no
+  formula): for a row's listed blocks L, the softmax runs over the valid
+  tokens of L only (the frozen-pattern attention's softmax) and
+  M_L(i, j) = mean over valid rows of block i of the sum over block j's
+  tokens of it, for j in L; 0 for blocks outside L.  A row with a non-empty
+  list sums to 1; with every block listed M_L = M.
 
 Row numbering: row r = (b * H + h) * n_q + i for batch b, head h, query block i.
 Inputs are fp64 arrays [B, H, N_alloc, d] holding the exact values the GPU sees.
@@ -64,6 +72,8 @@ __all__ = [
     "block_mass",
     "block_mass_rows",
     "pooled_mass",
+    "restricted_mass",
+    "restricted_mass_rows",
     "sanitize_masses",
     "select_contract",
     "select_contract_row",
@@ -341,6 +351,47 @@ def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_valid: int,
     for (b, h, i), o in zip(rows, res):
         O[b, h, i * R:i * R + o.shape[0]] = o
     return O
+
+
+def restricted_mass_rows(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
+                         row_ptr: np.ndarray, col_idx: np.ndarray, rows: Iterable[Tuple[int, int, int]],
+                         scale: Optional[float] = None) -> np.ndarray:
+    """Block masses within each listed row's candidate blocks -> [len(rows), n_k].
+
+    GSRS card (reduced search with exact attention weights inside the
+    attention pass): the softmax of the frozen-pattern attention, i.e. over
+    the valid tokens of the listed blocks only; M_L(i, j) = mean over valid
+    rows q of block i of the sum over the valid tokens of block j of it, for
+    listed j, and 0 for the rest.
+    """
+    B, H, Na, d = q.shape
+    sc = softmax_scale(d, scale)
+    n_q = -(-n_valid // R)
+    n_k = -(-n_valid // C)
+    rows = list(rows)
+    out = np.zeros((len(rows), n_k), np.float64)
+    for t, (b, h, i) in enumerate(rows):
+        r = row_id(b, h, i, H, n_q)
+        blocks = [int(j) for j in col_idx[int(row_ptr[r]):int(row_ptr[r + 1])]]
+        r0, r1 = i * R, min((i + 1) * R, n_valid)
+        keys = _kept_tokens(blocks, C, n_valid)
+        if keys.size == 0 or r1 <= r0:
+            continue
+        a = attention_probs(q[b, h, r0:r1], k[b, h, keys], sc)  # [rows_i, kept keys]
+        owner = keys // C                                         # key block of each kept token
+        for j in blocks:
+            out[t, j] = a[:, owner == j].sum(axis=1).mean()
+    return out
+
+
+def restricted_mass(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
+                    row_ptr: np.ndarray, col_idx: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """Masses within the candidate lists for every row -> [B, H, n_q, n_k] (fp64)."""
+    B, H = q.shape[:2]
+    n_q = -(-n_valid // R)
+    n_k = -(-n_valid // C)
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(n_q)]
+    return restricted_mass_rows(q, k, n_valid, R, C, row_ptr, col_idx, rows, scale).reshape(B, H, n_q, n_k)
 
 
 def budget_order(row_ptr: np.ndarray) -> np.ndarray:

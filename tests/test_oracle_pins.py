@@ -391,3 +391,77 @@ def test_pooled_brute_force_loops():
             w.append(len(keys) * math.exp(sc * sum(qb[e] * kb[e] for e in range(d))))
         for j in range(nk):
             assert abs(P[0, 0, i, j] - w[j] / sum(w)) <= 1e-13
+
+
+# ---------------------------------------------------------------- masses within candidate lists
+# Reading (GSRS card: reduced search with exact weights inside the attention
+# pass; no formula printed): the softmax over the listed blocks' valid tokens,
+# summed per listed block and averaged over the query block's valid rows.
+
+def _random_lists(rng, rows, n_k, keep):
+    row_ptr, cols = [0], []
+    for _ in range(rows):
+        sel = np.flatnonzero(rng.random(n_k) < keep)
+        cols.append(sel)
+        row_ptr.append(row_ptr[-1] + sel.size)
+    return np.asarray(row_ptr, np.int64), (np.concatenate(cols) if cols else np.zeros(0, np.int64))
+
+
+@pytest.mark.parametrize("N,R,C", [(1000, 64, 64), (777, 128, 32), (512, 64, 64)])
+def test_restricted_mass_with_every_block_listed_is_the_block_mass(N, R, C):
+    """Listing every block leaves the softmax unrestricted: M_L must equal the
+    pinned block mass M."""
+    rng = np.random.default_rng(N + C)
+    Na = max(-(-N // R) * R, -(-N // C) * C)
+    q, k, _ = _rand_qkv(rng, 1, 2, Na, 16, N, scale_q=2.0)
+    n_q, n_k = -(-N // R), -(-N // C)
+    rows = 2 * n_q
+    row_ptr = np.arange(rows + 1, dtype=np.int64) * n_k
+    col_idx = np.tile(np.arange(n_k), rows)
+    ML = O.restricted_mass(q, k, N, R, C, row_ptr, col_idx)
+    assert np.abs(ML - O.block_mass(q, k, N, R, C)).max() <= 1e-12
+
+
+def test_restricted_mass_zero_query_closed_form_and_row_sums():
+    """Q = 0: the restricted softmax is uniform over the listed valid tokens,
+    so M_L[i, j] = |B_j| / (sum of |B_j'| over the list) for listed j, else 0."""
+    N, R, C = 1000, 64, 32
+    rng = np.random.default_rng(8)
+    q = np.zeros((1, 2, 1024, 8))
+    k = rng.standard_normal((1, 2, 1024, 8))
+    n_q, n_k = -(-N // R), -(-N // C)
+    row_ptr, col_idx = _random_lists(rng, 2 * n_q, n_k, 0.4)
+    ML = O.restricted_mass(q, k, N, R, C, row_ptr, col_idx).reshape(2 * n_q, n_k)
+    size = np.array([min(C, N - j * C) for j in range(n_k)], np.float64)
+    for r in range(2 * n_q):
+        lst = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        want = np.zeros(n_k)
+        if lst.size:
+            want[lst] = size[lst] / size[lst].sum()
+            assert abs(ML[r].sum() - 1.0) <= 1e-12
+        assert np.abs(ML[r] - want).max() <= 1e-15
+
+
+def test_restricted_mass_brute_force_loops():
+    """Explicit loops over queries, listed blocks and tokens on a tiny case."""
+    rng = np.random.default_rng(21)
+    N, R, C, d = 70, 16, 8, 4
+    q = rng.standard_normal((1, 1, 80, d)) * 1.5
+    k = rng.standard_normal((1, 1, 80, d)) * 1.5
+    n_q, n_k = -(-N // R), -(-N // C)
+    row_ptr, col_idx = _random_lists(rng, n_q, n_k, 0.5)
+    ML = O.restricted_mass(q, k, N, R, C, row_ptr, col_idx)[0, 0]
+    sc = 1.0 / math.sqrt(d)
+    for i in range(n_q):
+        lst = [int(j) for j in col_idx[row_ptr[i]:row_ptr[i + 1]]]
+        rows_i = range(i * R, min((i + 1) * R, N))
+        want = [0.0] * n_k
+        for qq in rows_i:
+            w = {}
+            for j in lst:
+                for kk in range(j * C, min((j + 1) * C, N)):
+                    w[kk] = math.exp(sum(q[0, 0, qq, e] * k[0, 0, kk, e] for e in range(d)) * sc)
+            z = sum(w.values())
+            for j in lst:
+                want[j] += sum(w[kk] for kk in range(j * C, min((j + 1) * C, N))) / z / len(rows_i)
+        assert np.abs(ML[i] - np.asarray(want)).max() <= 1e-12
