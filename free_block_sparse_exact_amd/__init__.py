@@ -11,6 +11,7 @@ The functions carry the C names:
     losa_select(M, p, tokens, q_block, k_block, ...)          -> (row_ptr, col_idx, order)
     losa_sparse_attn(q, k, v, row_ptr, col_idx, order, ...)   -> O
     losa_dense_attn_mass(q, k, v, tokens, q_block, k_block)   -> (O, M)
+    losa_sparse_attn_mass(q, k, v, row_ptr, col_idx, order, ...) -> (O, M within the lists)
     losa_pooled_mass(q, k, tokens, q_block, k_block)          -> P
     losa_retained_mass(M, row_ptr, col_idx, ...)              -> kept [rows, 2]
 
@@ -43,6 +44,8 @@ __all__ = [
     "losa_retained_mass",
     "losa_dense_attn_mass_workspace",
     "losa_dense_attn_mass",
+    "losa_sparse_attn_mass_workspace",
+    "losa_sparse_attn_mass",
     "losa_pooled_mass_workspace",
     "losa_pooled_mass",
     "LOSA_F32",
@@ -119,6 +122,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "losa_retained_mass": ([S, P, P, P, P, P], i32),
         "losa_dense_attn_mass_workspace": ([S, sz], i32),
         "losa_dense_attn_mass": ([S, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
+        "losa_sparse_attn_mass_workspace": ([S, sz], i32),
+        "losa_sparse_attn_mass": ([S, P, P, P, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
         "losa_pooled_mass_workspace": ([S, sz], i32),
         "losa_pooled_mass": ([S, P, P, P, P, ctypes.c_size_t, P], i32),
     }
@@ -336,6 +341,36 @@ def losa_dense_attn_mass(q, k, v, tokens: int, q_block: int, k_block: int, softm
     _check(_L().losa_dense_attn_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(M), _ptr(out), odt,
                                      _ptr(ws), _nbytes(ws), _stream(stream)),
            "losa_dense_attn_mass")
+    return out, M
+
+
+def losa_sparse_attn_mass_workspace(geom: Geometry) -> int:
+    n = ctypes.c_size_t()
+    _check(_L().losa_sparse_attn_mass_workspace(ctypes.byref(geom.shape()), ctypes.byref(n)),
+           "losa_sparse_attn_mass_workspace")
+    return n.value
+
+
+def losa_sparse_attn_mass(q, k, v, row_ptr, col_idx, order, tokens: int, q_block: int, k_block: int,
+                          softmax_scale: Optional[float] = None, out=None, out_dtype=None, M=None, ws=None,
+                          stream=None):
+    """Sparse attention over the lists and the exact masses within them ->
+    (O [B, H, tokens_alloc, d], M [B, H, n_q, n_k], 0 outside the lists)."""
+    import torch
+    g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if M is None:
+        M = torch.empty((g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
+    odt = {torch.bfloat16: LOSA_BF16, torch.float32: LOSA_F32}[out.dtype]
+    shp = g.shape(q=q, k=k, v=v, o=out)
+    nbytes = ctypes.c_size_t()
+    _check(_L().losa_sparse_attn_mass_workspace(ctypes.byref(shp), ctypes.byref(nbytes)),
+           "losa_sparse_attn_mass_workspace")
+    ws = _workspace(nbytes.value, q.device, ws)
+    _check(_L().losa_sparse_attn_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
+                                      _ptr(order), _ptr(M), _ptr(out), odt, _ptr(ws), _nbytes(ws),
+                                      _stream(stream)), "losa_sparse_attn_mass")
     return out, M
 
 

@@ -195,6 +195,36 @@ losa_status losa_dense_attn_mass(const losa_shape* shape, const void* Q, const v
   return hip_status(losa::launch_dense_attn_mass(g, Q, K, V, M, O, o_dtype == LOSA_BF16, ws, stream));
 }
 
+losa_status losa_sparse_attn_mass_workspace(const losa_shape* shape, size_t* bytes) {
+  Geom g;
+  if (!bytes) return LOSA_ERR_NULL;
+  const losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if (!losa::mfma_path(g)) return LOSA_ERR_UNSUPPORTED;
+  *bytes = losa::sparse_mass_ws_bytes(g);
+  return LOSA_OK;
+}
+
+losa_status losa_sparse_attn_mass(const losa_shape* shape, const void* Q, const void* K, const void* V,
+                                  const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
+                                  float* M, void* O, losa_dtype o_dtype, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  Geom g;
+  losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if (!losa::mfma_path(g)) return LOSA_ERR_UNSUPPORTED;
+  if ((st = check_input(g, Q, g.qs)) != LOSA_OK) return st;
+  if ((st = check_input(g, K, g.ks)) != LOSA_OK) return st;
+  if ((st = check_input(g, V, g.vs)) != LOSA_OK) return st;
+  if (!row_ptr || !col_idx || !M || !O || !ws) return LOSA_ERR_NULL;
+  if (o_dtype != LOSA_F32 && o_dtype != LOSA_BF16) return LOSA_ERR_INVALID_ARG;
+  if (!aligned16(M)) return LOSA_ERR_INVALID_ARG;
+  if (!aligned16(O) || !strides_ok(g.os, g.D, o_dtype == LOSA_BF16 ? 8 : 4)) return LOSA_ERR_INVALID_ARG;
+  if (ws_bytes < losa::sparse_mass_ws_bytes(g) || !aligned16(ws)) return LOSA_ERR_WORKSPACE;
+  return hip_status(losa::launch_sparse_attn_mass(g, Q, K, V, row_ptr, col_idx, order, M, O,
+                                                  o_dtype == LOSA_BF16, ws, stream));
+}
+
 losa_status losa_pooled_mass_workspace(const losa_shape* shape, size_t* bytes) {
   Geom g;
   if (!bytes) return LOSA_ERR_NULL;

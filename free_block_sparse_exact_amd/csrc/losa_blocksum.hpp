@@ -9,16 +9,18 @@
 
 namespace losa {
 
-// Lane l takes block kw + 4*(b0 + l): its 64 sums are 256 contiguous bytes,
-// read as 16 independent 16-byte loads, against f from LDS (the same address
-// in every lane, so the reads broadcast).  One memory round trip per 64
-// blocks and no cross-lane reduction.  dst[j] = scale * mass of block j.
-__device__ __forceinline__ void blocks_from_sums(const float* __restrict__ Sg, const float* f, int kw, int nb,
-                                                 float scale, float* dst, int lane) {
+// Lane l takes the wave's block number b0 + l (block j = block_of(b0 + l)):
+// its 64 sums are 256 contiguous bytes, read as 16 independent 16-byte loads,
+// against f from LDS (the same address in every lane, so the reads
+// broadcast).  One memory round trip per 64 blocks and no cross-lane
+// reduction.  dst[j] = scale * mass of block j.
+template <typename BlockOf>
+__device__ __forceinline__ void blocks_from_sums(const float* __restrict__ Sg, const float* f, int nb, float scale,
+                                                 float* dst, int lane, BlockOf block_of) {
   for (int b0 = 0; b0 < nb; b0 += kWave) {
     const int bb = b0 + lane;
     if (bb < nb) {
-      const int j = kw + 4 * bb;
+      const int j = block_of(bb);
       const f32x4* src = reinterpret_cast<const f32x4*>(Sg + (int64_t)j * 64);
       f32x4 s4[16];
 #pragma unroll
@@ -33,6 +35,12 @@ __device__ __forceinline__ void blocks_from_sums(const float* __restrict__ Sg, c
       dst[j] = acc * scale;
     }
   }
+}
+
+// The wave's blocks are kw, kw+4, ... (every key block in turn).
+__device__ __forceinline__ void blocks_from_sums(const float* __restrict__ Sg, const float* f, int kw, int nb,
+                                                 float scale, float* dst, int lane) {
+  blocks_from_sums(Sg, f, nb, scale, dst, lane, [kw](int bb) { return kw + 4 * bb; });
 }
 
 }  // namespace losa

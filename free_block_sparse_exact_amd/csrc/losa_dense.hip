@@ -36,10 +36,13 @@ namespace {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kPBound = 65536.0f;  // per-lane chunk sum of the bf16 P: above it, the exact path
 
-template <int D>
+template <int D, bool kLists>
 __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
                                                             const __bf16* __restrict__ Kp,
                                                             const __bf16* __restrict__ Vp, int nch,
+                                                            const int32_t* __restrict__ row_ptr,
+                                                            const int32_t* __restrict__ col_idx,
+                                                            const int32_t* __restrict__ order,
                                                             float* __restrict__ S, float* __restrict__ Mout,
                                                             void* O, int o_bf16) {
   constexpr int DC = D / 32, DT = D / 16, kQT = 4;
@@ -48,8 +51,12 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   __shared__ float s_ref[4][64], s_tot[4][64], s_f[4][64];
   const int qhalves = g.R / 64;
   const int rows = g.rows();
-  const int tix = xcd_task(blockIdx.x, rows * qhalves);
-  const int row = tix / qhalves, qsub = tix - row * qhalves;
+  // Lists come in the caller's work order (rows by budget), dealt to the XCDs
+  // in blocks of 32 tasks like the sparse attention; dense rows are spread
+  // in contiguous ranges per XCD.
+  const int tix = kLists ? xcd_block_task(blockIdx.x, gridDim.x) : xcd_task(blockIdx.x, rows * qhalves);
+  const int ridx = tix / qhalves, qsub = tix - ridx * qhalves;
+  const int row = (kLists && order) ? order[ridx] : ridx;
   const int bh = row / g.nq, i = row - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
   const int lane = threadIdx.x & 63, kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -86,34 +93,63 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   }
   const float c = g.scale_log2;
 
-  // This wave's chunk sequence: its blocks kw, kw+4, ... with all their valid
-  // chunks; the last block (partly padding unless N is a multiple of C) has
-  // sub_last valid chunks.  If its final chunk is partly padding, the last
-  // block goes first, that chunk at position 0.
-  const int sub = g.C / 32, sub_shift = __builtin_ctz(sub);
-  const int nb = g.nk > kw ? (g.nk - kw + 3) / 4 : 0;
+  // The row's blocks: every block (dense), or the listed ones.  Wave kw owns
+  // list positions kw, kw+4, ... with all their valid chunks.  The last key
+  // block (nk - 1) is partly padding unless N = nk*C: the wave that owns it
+  // takes it first, its final (partly padded) chunk at the very front, and
+  // drops its wholly padded chunks, so only the first chunk needs masking.
+  const int beg = kLists ? row_ptr[row] : 0;
+  const int n = kLists ? row_ptr[row + 1] - beg : g.nk;
+  auto block_at = [&](int pos) -> int { return kLists ? col_idx[beg + pos] : pos; };
+  const int sub = g.C / 32, sub_shift = __builtin_ctz(sub), c_shift = __builtin_ctz(g.C);
+  const int nb = n > kw ? (n - kw + 3) / 4 : 0;
   const int last = g.nk - 1;
-  const int sub_last = (g.N - last * g.C + 31) / 32;
-  const bool own_last = nb > 0 && (last - kw) % 4 == 0;
+  const int sub_last = (g.N - last * g.C + 31) / 32;  // valid chunks of the last block
+  int lp = -1;                                        // position of the last block in the row
+  if (g.N != g.nk * g.C) {
+    if (!kLists) {
+      lp = last;
+    } else {
+      for (int base = 0; base < n; base += 4 * kWave) {
+        uint64_t hit[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int x = base + jj * kWave + lane;
+          hit[jj] = __ballot(x < n && col_idx[beg + x] == last);
+        }
+#pragma unroll
+        for (int jj = 3; jj >= 0; --jj)
+          if (hit[jj]) lp = base + jj * kWave + __builtin_ctzll(hit[jj]);
+        if (lp >= 0) break;
+      }
+    }
+  }
+  const bool own_last = lp >= 0 && (lp & 3) == kw;
+  const int o_last = lp >> 2;  // ordinal of the last block among this wave's blocks (when own_last)
   const int nmine = own_last ? (nb - 1) * sub + sub_last : nb * sub;
-  const bool front = own_last && (g.N & 31) != 0;
-  // chunk t -> its first key; j and ends give its block and whether it closes it
-  // (both cases computed, then selected: no branch inside the loop body)
-  auto chunk_kb = [&](int t, int& j, bool& ends) -> int {
+  // Chunk t of the wave -> its first key, with bit 0 set if it closes its block.
+  auto seq_key = [&](int t) -> int {
     t = t < nmine ? t : nmine - 1;
-    const bool first_block = front && t < sub_last;
-    const int tt = front ? t - sub_last : t;  // negative (and unused) inside the first block
-    const int jn = kw + 4 * (tt >> sub_shift), scn = tt & (sub - 1);
-    j = first_block ? last : jn;
-    const int sc = first_block ? (t == 0 ? sub_last - 1 : t - 1) : scn;
-    ends = first_block ? t == sub_last - 1 : (scn == sub - 1 || (jn == last && scn == sub_last - 1));
-    return j * g.C + 32 * sc;
+    int j, sc;
+    bool ends;
+    if (own_last && t < sub_last) {
+      j = last;
+      sc = t == 0 ? sub_last - 1 : t - 1;
+      ends = t == sub_last - 1;
+    } else {
+      const int tt = own_last ? t - sub_last : t;
+      int ord = tt >> sub_shift;
+      ord += (own_last && ord >= o_last) ? 1 : 0;
+      j = block_at(kw + 4 * ord);
+      sc = tt & (sub - 1);
+      ends = sc == sub - 1;
+    }
+    return (j * g.C + 32 * sc) | (ends ? 1 : 0);
   };
-  auto kb_of = [&](int t) {
-    int j;
-    bool e;
-    return chunk_kb(t, j, e);
-  };
+  // The loop reads chunk keys from registers: lane x of a window holds
+  // seq_key(base + x), so a key costs one lane read (two windows cover 128
+  // chunks; the next is loaded 64 iterations before it is needed).
+  auto key_window = [&](int base) -> int { return seq_key(base + lane); };
 
   auto load_k = [&](int kb, bf16x8 (&kop)[2][DC]) {
     const __bf16* kc = Kbh + (int64_t)(kb >> 5) * (32 * D) + lane * 8;
@@ -209,14 +245,12 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   bool fallback = false;
   bf16x8 kop[2][DC], vop[DT];
   if (nmine > 0) {
-    int j0;
-    bool e0;
-    const int kb = chunk_kb(0, j0, e0);
+    const int kb = seq_key(0) & ~1;
     load_k(kb, kop);
     load_v(kb, vop);
     f32x4 acc[2][kQT];
     scores(kop, acc);
-    load_k(kb_of(1), kop);
+    load_k(seq_key(1) & ~1, kop);
     if (kb + 32 > g.N) mask_tail(kb, acc);
     {
       float mx[kQT];
@@ -228,17 +262,29 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       for (int qt = 0; qt < kQT; ++qt) m[qt] = mx[qt] * c + kHeadroom;  // finite: the chunk holds a valid key
     }
     bool over_any = false;
+    int win_base = 0;
+    int win0 = key_window(0), win1 = key_window(64);
     for (int t = 0; t < nmine; ++t) {
-      int jt;
-      bool ends;
-      chunk_kb(t, jt, ends);
+      if (t == win_base + 64) {  // keys t..t+2 now lie in [win_base + 64, win_base + 128)
+        win_base += 64;
+        win0 = win1;
+        win1 = key_window(win_base + 64);
+      }
+      auto key_at = [&](int x) {  // both windows read, then a select: no branch inside the body
+        const int r = x - win_base;
+        const int k0 = __builtin_amdgcn_readlane(win0, r & 63), k1 = __builtin_amdgcn_readlane(win1, r & 63);
+        return r < 64 ? k0 : k1;
+      };
+      const int kt_cur = key_at(t);
+      const int jt = kt_cur >> c_shift;
+      const bool ends = (kt_cur & 1) != 0;
       f32x4 accn[2][kQT];
       scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
-      load_k(kb_of(t + 2), kop);
+      load_k(key_at(t + 2) & ~1, kop);
       bf16x8 pop[kQT];
       const bool over = probs(acc, pop);  // chunk t
       pv(vop, pop);
-      load_v(kb_of(t + 1), vop);
+      load_v(key_at(t + 1) & ~1, vop);
 #pragma unroll
       for (int s = 0; s < 64; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -266,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     for (int t = 0; t < nmine; ++t) {
-      const int kb2 = kb_of(t);
+      const int kb2 = seq_key(t) & ~1;
       load_k(kb2, kop);
       f32x4 acc[2][kQT];
       scores(kop, acc);
@@ -277,9 +323,9 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) m[qt] *= c;
     for (int t = 0; t < nmine; ++t) {
-      int jt;
-      bool ends;
-      const int kb2 = chunk_kb(t, jt, ends);
+      const int key = seq_key(t);
+      const int kb2 = key & ~1, jt = key >> c_shift;
+      const bool ends = (key & 1) != 0;
       load_k(kb2, kop);
       load_v(kb2, vop);
       f32x4 acc[2][kQT];
@@ -354,7 +400,13 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
     __syncthreads();  // every lane reads all 64 factors of its wave
     const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
     float* Mrow = Mout + ((int64_t)qsub * rows + row) * g.nk;
-    blocks_from_sums(Sg, s_f[kw], kw, nb, inv_rows, Mrow, lane);
+    if (kLists) {  // blocks outside the list get 0, then the listed ones their mass
+      for (int x = threadIdx.x; x < g.nk; x += blockDim.x) Mrow[x] = 0.f;
+      __syncthreads();
+      blocks_from_sums(Sg, s_f[kw], nb, inv_rows, Mrow, lane, [&](int bb) { return block_at(kw + 4 * bb); });
+    } else {
+      blocks_from_sums(Sg, s_f[kw], kw, nb, inv_rows, Mrow, lane);
+    }
   }
 
   if (kw == 0) {
@@ -409,8 +461,9 @@ size_t dense_layout(const Geom& g, char* base, DenseWs* w) {
 }
 
 template <int D>
-hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O, int o_bf16,
-                       void* ws, hipStream_t st) {
+hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* V, const int32_t* row_ptr,
+                       const int32_t* col_idx, const int32_t* order, float* M, void* O, int o_bf16, void* ws,
+                       hipStream_t st) {
   DenseWs w;
   dense_layout(g, reinterpret_cast<char*>(ws), &w);
   const int nch = packed_chunks(g);
@@ -419,8 +472,14 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* 
   const int tiles = g.rows() * (g.R / 64);
   const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float);
   float* Mout = g.R == 64 ? M : w.Mh;
-  hipLaunchKernelGGL((dense_bf16_kernel<D>), dim3(tiles), dim3(256), lds, st, g, (const __bf16*)Q,
-                     (const __bf16*)w.Kp, (const __bf16*)w.Vp, nch, w.S, Mout, O, o_bf16);
+  if (row_ptr)
+    hipLaunchKernelGGL((dense_bf16_kernel<D, true>), dim3(tiles), dim3(256), lds, st, g, (const __bf16*)Q,
+                       (const __bf16*)w.Kp, (const __bf16*)w.Vp, nch, row_ptr, col_idx, order, w.S, Mout, O,
+                       o_bf16);
+  else
+    hipLaunchKernelGGL((dense_bf16_kernel<D, false>), dim3(tiles), dim3(256), lds, st, g, (const __bf16*)Q,
+                       (const __bf16*)w.Kp, (const __bf16*)w.Vp, nch, nullptr, nullptr, nullptr, w.S, Mout, O,
+                       o_bf16);
   if (g.R != 64) {
     const int64_t n = (int64_t)g.rows() * g.nk;
     hipLaunchKernelGGL(add_halves_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
@@ -439,13 +498,22 @@ size_t dense_ws_bytes(const Geom& g) {
 hipError_t launch_dense_attn_mass(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O,
                                   int o_bf16, void* ws, hipStream_t stream) {
   if (mfma_path(g))
-    return g.D == 128 ? launch_mfma<128>(g, Q, K, V, M, O, o_bf16, ws, stream)
-                      : launch_mfma<64>(g, Q, K, V, M, O, o_bf16, ws, stream);
+    return g.D == 128 ? launch_mfma<128>(g, Q, K, V, nullptr, nullptr, nullptr, M, O, o_bf16, ws, stream)
+                      : launch_mfma<64>(g, Q, K, V, nullptr, nullptr, nullptr, M, O, o_bf16, ws, stream);
   // Other shapes: the SIMT mass kernels, then the SIMT attention kernel over
   // every key block (no lists).
   hipError_t e = launch_block_mass(g, Q, K, M, ws, stream);
   if (e != hipSuccess) return e;
   return launch_sparse_attn(g, Q, K, V, nullptr, nullptr, nullptr, O, o_bf16, nullptr, stream);
+}
+
+size_t sparse_mass_ws_bytes(const Geom& g) { return mfma_path(g) ? dense_layout(g, nullptr, nullptr) : 0; }
+
+hipError_t launch_sparse_attn_mass(const Geom& g, const void* Q, const void* K, const void* V,
+                                   const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
+                                   float* M, void* O, int o_bf16, void* ws, hipStream_t stream) {
+  return g.D == 128 ? launch_mfma<128>(g, Q, K, V, row_ptr, col_idx, order, M, O, o_bf16, ws, stream)
+                    : launch_mfma<64>(g, Q, K, V, row_ptr, col_idx, order, M, O, o_bf16, ws, stream);
 }
 
 }  // namespace losa

@@ -65,6 +65,12 @@ hipError_t launch_sparse_attn(const Geom& g, const void* Q, const void* K, const
 
 // Dense attention with exact block masses in one pass (construction step).
 size_t dense_ws_bytes(const Geom& g);
+// The same kernel over a row's listed blocks only (matrix-core shapes only):
+// sparse attention plus the masses within the lists.
+size_t sparse_mass_ws_bytes(const Geom& g);
+hipError_t launch_sparse_attn_mass(const Geom& g, const void* Q, const void* K, const void* V,
+                                   const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
+                                   float* M, void* O, int o_bf16, void* ws, hipStream_t stream);
 hipError_t launch_dense_attn_mass(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O,
                                   int o_bf16, void* ws, hipStream_t stream);
 

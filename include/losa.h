@@ -204,6 +204,40 @@ losa_status losa_dense_attn_mass(const losa_shape* shape, const void* Q, const v
                                  hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Frozen-pattern sparse attention with the exact masses within the lists.
+ * GSRS card (Sparse Attention for Video Generation Acceleration via Growing
+ * Sparsity and Reduced Search): later top-p searches are restricted to an
+ * early candidate set, and the attention weights they need are computed
+ * exactly inside the attention pass.  Reading (the card gives no formula):
+ * O is exactly losa_sparse_attn's, and for each row i with listed blocks L
+ *   M[b,h,i,j] = (1/valid rows of block i) * sum over valid rows q of block i
+ *                and valid keys k of block j of
+ *                exp(s_qk) / sum over the valid keys k' of L of exp(s_qk')
+ * for j in L (the softmax of the sparse attention itself, summed per block),
+ * and 0 for j outside L.  A row with a non-empty list sums to 1; with every
+ * block listed M is losa_block_mass's.  losa_select on M with a target p'
+ * then keeps a subset of L (for p' < 1) -- the reduced search.
+ *
+ * Supported: bf16, head_dim 64 or 128, q_block 64 or 128 (the matrix-core
+ *    shapes); other shapes return LOSA_ERR_UNSUPPORTED before any HIP call,
+ *    from this call and from its workspace query.
+ * row_ptr/col_idx/order: as losa_sparse_attn (indices in [0, n_k), each at
+ *    most once in a row -- a repeated index gives an unspecified O and M,
+ *    never an access outside the buffers).
+ * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
+ * O: [batch, heads, tokens_alloc, head_dim] with shape->o_stride, element
+ *    type o_dtype (LOSA_BF16 or LOSA_F32).
+ * ws: at least *bytes from losa_sparse_attn_mass_workspace (the sizes of
+ *    losa_dense_attn_mass's matrix-core path).
+ * Arithmetic as losa_dense_attn_mass.
+ * ------------------------------------------------------------------------ */
+losa_status losa_sparse_attn_mass_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_sparse_attn_mass(const losa_shape* shape, const void* Q, const void* K, const void* V,
+                                  const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
+                                  float* M, void* O, losa_dtype o_dtype, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Pooled proxy masses: the coarse block-mass estimate of per-step top-p
  * methods, which the LoSA page contrasts with exact masses (Motivation
  * Summary: SVG2 and SpargeAttn rely on coarse estimates that are not

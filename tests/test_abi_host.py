@@ -183,3 +183,28 @@ def test_pooled_mass_errors(lib):
     assert pooled(ws=None) == NULL
     assert pooled(P=FAKE + 4) == INVALID
     assert pooled(ws_bytes=n.value - 1) == WORKSPACE
+
+
+@no_gpu_only
+def test_sparse_attn_mass_errors(lib):
+    s = shape()
+    n = ctypes.c_size_t()
+    assert lib.losa_sparse_attn_mass_workspace(ctypes.byref(s), ctypes.byref(n)) == OK and n.value > 0
+
+    def call(shp=s, rp=FAKE, ci=FAKE, M=FAKE, O=FAKE, o_dtype=F.LOSA_BF16, ws=FAKE, ws_bytes=1 << 40, V=FAKE):
+        return lib.losa_sparse_attn_mass(ctypes.byref(shp), FAKE, FAKE, V, rp, ci, None, M, O, o_dtype, ws,
+                                         ws_bytes, None)
+
+    assert call(rp=None) == NULL
+    assert call(ci=None) == NULL
+    assert call(M=None) == NULL
+    assert call(O=None) == NULL
+    assert call(V=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(o_dtype=3) == INVALID
+    assert call(M=FAKE + 4) == INVALID
+    assert call(ws_bytes=n.value - 1) == WORKSPACE
+    # matrix-core shapes only: f32 inputs and 32-row query blocks are refused, query included
+    for kw in (dict(dtype=F.LOSA_F32), dict(q_block=32)):
+        assert lib.losa_sparse_attn_mass_workspace(ctypes.byref(shape(**kw)), ctypes.byref(n)) == UNSUPPORTED
+        assert call(shp=shape(**kw)) == UNSUPPORTED
