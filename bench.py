@@ -309,6 +309,24 @@ def main():
                                   "frac_bf16_peak": construct_flop / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                   "launches": "pack_kv + dense (+ add_halves at R = 128)",
                                   "note": "construction step: dense O and exact M in one pass; not in ms_per_step"}
+    # Sparse attention that also returns the masses within the lists (the
+    # reduced search's evaluation), on the step's lists; not part of ms_per_step.
+    ws_sm = torch.empty(F.losa_sparse_attn_mass_workspace(geom), dtype=torch.uint8, device=dev)
+    M_list = torch.empty_like(bufs.M)
+    sm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(6)]
+    for t, (e0, e1) in enumerate(sm_ev):
+        e0.record(stream)
+        F.losa_sparse_attn_mass(q, k, v, bufs.row_ptr, bufs.col_idx, bufs.order, N, R, C, out=bufs.out,
+                                M=M_list, ws=ws_sm, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    sm_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in sm_ev[1:]]))
+    del ws_sm, M_list
+    kernels["sparse_attn_mass"] = {"ms": sm_ms, "tflops": kept_flop / (sm_ms * 1e-3) / 1e12,
+                                   "frac_bf16_peak": kept_flop / (sm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                   "launches": "pack_kv + dense over the lists (+ add_halves at R = 128)",
+                                   "note": "sparse attention plus the exact masses within the lists (reduced "
+                                           "search); kept-block flops; not in ms_per_step"}
     routing = pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev)
     cpu = None
     if args.cpu_rows > 0:
@@ -464,6 +482,31 @@ def run_reuse(args, wl):
         kept = bufs.kept.cpu().numpy().astype(np.float64)
         recalls.append(float((kept[:, 0] * w).sum() / (kept[:, 1] * w).sum()))
         log(f"step {s}: recall {recalls[-1]:.6f}" + (f", sparse {sparse_ms[-1]:.3f} ms" if s != wl.construct_step else ""))
+    # Reduced search at the last step (GSRS card: a later top-p search within the
+    # earlier candidate set, on exact weights computed inside the attention
+    # pass): the masses within the frozen lists from this step's Q/K, then the
+    # same per-head p within them.  bufs.M still holds this step's exact masses.
+    ws_sm = torch.empty(F.losa_sparse_attn_mass_workspace(geom), dtype=torch.uint8, device=dev)
+    M_list = torch.empty_like(bufs.M)
+    out2 = torch.empty_like(bufs.out)
+    for warm in (True, False):
+        ev[2].record(stream)
+        F.losa_sparse_attn_mass(q, k, v, bufs.row_ptr, bufs.col_idx, bufs.order, N, R, C, out=out2, M=M_list,
+                                ws=ws_sm, stream=stream)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+    reduced_ms = ev[2].elapsed_time(ev[3])
+    rp2, ci2, _ = F.losa_select(M_list, p_heads, N, R, C, tokens_alloc=Na)
+    F.losa_retained_mass(bufs.M, rp2, ci2, N, R, C, out=bufs.kept, stream=stream)
+    kept2 = bufs.kept.cpu().numpy().astype(np.float64)
+    reduced = {"step": wl.steps - 1, "sparse_attn_mass_ms": reduced_ms,
+               "candidate_blocks": int(bufs.row_ptr[-1].item()), "kept_blocks": int(rp2[-1].item()),
+               "recall_frozen_lists": recalls[-1],
+               "recall_reduced_lists": float((kept2[:, 0] * w).sum() / (kept2[:, 1] * w).sum()),
+               "p": "the per-head p, applied within the candidates"}
+    del ws_sm, M_list, out2
+    log(f"reduced search at step {wl.steps - 1}: {reduced['kept_blocks']} of {reduced['candidate_blocks']} blocks, "
+        f"recall {reduced['recall_reduced_lists']:.4f} (frozen {recalls[-1]:.4f}), {reduced_ms:.3f} ms")
     rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
     counts = np.diff(rp)
     nnz = int(rp[-1])
@@ -496,6 +539,7 @@ def run_reuse(args, wl):
         "coverage_per_head": (per_head / (nq * nk)).tolist(),
         "imbalance_per_head_max_over_mean": float(per_head.max() / per_head.mean()),
         "imbalance_per_xcd_max_over_mean": float(per_xcd.max() / per_xcd.mean()),
+        "reduced_search": reduced,
     }
     print(json.dumps(res))
 
@@ -564,9 +608,12 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
 # kernel name fragment -> (short name, call it belongs to)
 TRACE_KERNELS = [
     ("attn_bf16_kernel", "attn_bf16_kernel", "losa_sparse_attn"),
-    ("pack_kv_kernelILi128ELb1", "pack_kv_kernel (K and V)", "losa_sparse_attn, losa_dense_attn_mass"),
+    ("pack_kv_kernelILi128ELb1", "pack_kv_kernel (K and V)",
+     "losa_sparse_attn, losa_dense_attn_mass, losa_sparse_attn_mass"),
     ("pack_kv_kernelILi128ELb0", "pack_kv_kernel (K only)", "losa_block_mass"),
     ("mass_bf16_kernel", "mass_bf16_kernel", "losa_block_mass"),
+    ("dense_bf16_kernel<128, true>", "dense_bf16_kernel (lists)", "losa_sparse_attn_mass"),
+    ("dense_bf16_kernelILi128ELb1", "dense_bf16_kernel (lists)", "losa_sparse_attn_mass"),
     ("dense_bf16_kernel", "dense_bf16_kernel", "losa_dense_attn_mass"),
     ("pool_kernel", "pool_kernel", "losa_pooled_mass"),
     ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
@@ -614,7 +661,8 @@ def summarize_trace(trace_dir, name, command):
 
 CLOCK_KERNELS = [("attn_bf16_kernel", "attn_bf16_kernel", "sparse_attn"),
                  ("mass_bf16_kernel", "mass_bf16_kernel", "block_mass"),
-                 ("dense_bf16_kernel", "dense_bf16_kernel", "dense_attn_mass")]
+                 ("dense_bf16_kernel<128, false>", "dense_bf16_kernel", "dense_attn_mass"),
+                 ("dense_bf16_kernelILi128ELb0", "dense_bf16_kernel", "dense_attn_mass")]
 N_XCD, N_SE = 8, 32          # MI355X: 8 XCDs, 4 shader engines each
 PEAK_CLOCK_GHZ = 2.4         # the clock the published 2.5 PFLOP/s bf16 peak assumes
 
@@ -648,7 +696,7 @@ def summarize_clock(pmc_dir, trace_dir, name, commands):
               "| kernel | dispatches | GRBM cycles per XCD (M) | SQ busy cycles per SE (M) | trace median us | "
               "sustained clock GHz | share of the 2.4 GHz rate |",
               "|---|---|---|---|---|---|---|"]
-    for _, lab, _ in CLOCK_KERNELS:
+    for lab in dict.fromkeys(k for _, k, _ in CLOCK_KERNELS):
         if lab not in pmc or lab not in trace:
             continue
         ds = list(pmc[lab].values())
@@ -682,7 +730,7 @@ def summarize_mfma(pmc_dir, name, command):
              "MfmaUtil = MFMA-busy SIMD cycles / (busy GPU cycles x SIMDs), in percent: the matrix cores' share "
              "of the cycles the kernel ran, independent of the clock.  MfmaFlopsBF16 = bf16 MFMA flops executed.",
              "", "| kernel | dispatches | MfmaUtil % | bf16 MFMA TFLOP executed per dispatch |", "|---|---|---|---|"]
-    for _, lab, _ in CLOCK_KERNELS:
+    for lab in dict.fromkeys(k for _, k, _ in CLOCK_KERNELS):
         if lab not in per:
             continue
         ds = list(per[lab].values())
