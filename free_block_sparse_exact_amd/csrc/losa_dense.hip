@@ -25,6 +25,13 @@
 // the packed K and must leave the softmax: the wave that owns the last block
 // processes it first, its partly padded chunk at the very front (the first
 // chunk is masked explicitly), so the pipelined loop does no masking.
+//
+// With CSR lists (kLists) the same kernel runs over each row's listed blocks
+// only: O is then the frozen-pattern sparse attention, and M the masses
+// within the lists -- the softmax of that attention summed per listed block
+// (0 outside the list), the exact weights a reduced search (GSRS card: later
+// top-p searches within an early candidate set, evaluated inside the
+// attention pass) selects from.
 #include "losa_blocksum.hpp"
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
