@@ -64,7 +64,7 @@ CALL_SOURCES = {
     "losa_sparse_attn": [_CSRC + "losa_attn.hip", _CSRC + "losa_pack.hpp", _CSRC + "losa_device.hpp",
                          "free_block_sparse_exact_amd/_build.py"],
     "losa_block_mass": [_CSRC + "losa_mass.hip", _CSRC + "losa_pack.hpp", _CSRC + "losa_device.hpp",
-                        "free_block_sparse_exact_amd/_build.py"],
+                        _CSRC + "losa_blocksum.hpp", "free_block_sparse_exact_amd/_build.py"],
 }
 # kernel name fragment -> (part, call) for the traffic summary
 PMC_KERNELS = [("attn_bf16_kernel", "attn", "losa_sparse_attn"),
