@@ -282,9 +282,6 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
         const int k0 = __builtin_amdgcn_readlane(win0, r & 63), k1 = __builtin_amdgcn_readlane(win1, r & 63);
         return r < 64 ? k0 : k1;
       };
-      const int kt_cur = key_at(t);
-      const int jt = kt_cur >> c_shift;
-      const bool ends = (kt_cur & 1) != 0;
       f32x4 accn[2][kQT];
       scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
       load_k(key_at(t + 2) & ~1, kop);
@@ -292,12 +289,16 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       const bool over = probs(acc, pop);  // chunk t
       pv(vop, pop);
       load_v(key_at(t + 1) & ~1, vop);
+      // Three vector instructions per MFMA: the block sums add 32 to the
+      // sparse attention loop's ~110 per 64 MFMAs, and with two per MFMA the
+      // rest bunched up in one stretch (config 3: 179 against 170 ms).
 #pragma unroll
       for (int s = 0; s < 64; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // then two vector ALU ops
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then three vector ALU ops
       }
-      if (ends) block_end(jt);
+      const int kt_cur = key_at(t);
+      if (kt_cur & 1) block_end(kt_cur >> c_shift);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
