@@ -19,23 +19,27 @@ inline int packed_chunks(const Geom& g) { return (int)(align_up((size_t)g.nk * g
 //   Vp[bh][c][dt][lane][8]: V[32c + (lane>>4)*8 + e][dt*16 + (lane&15)]
 //       for e in [0,8) (the A operand of O^T += V^T P^T for dim tile dt).
 // Tokens >= N are written as zeros.  Grid: (nch / 2, B*H) with nch even;
-// each workgroup packs 64 tokens (two chunks), V through an LDS tile.
+// each workgroup packs 64 tokens (two chunks), V through an LDS tile (rows
+// read and staged 16 bytes at a time, then gathered column-wise).
 // kWithV = false packs K only (Vp unused).
 template <int D, bool kWithV>
 __global__ __launch_bounds__(256) void pack_kv_kernel(const Geom g, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V, __bf16* __restrict__ Kp,
                                                       __bf16* __restrict__ Vp, int nch) {
   constexpr int DC = D / 32, DT = D / 16;
-  __shared__ uint16_t vt[64][D + 2];
+  constexpr int VP = D + 8;  // LDS row pitch (elements): rows stay 16-byte aligned
+  __shared__ __attribute__((aligned(16))) uint16_t vt[64][VP];
   const int t0 = blockIdx.x * 64, bh = blockIdx.y;
   const int b = bh / g.H, h = bh - b * g.H;
   const __bf16* Kbh = K + b * g.ks[0] + h * g.ks[1];
-  const uint16_t* Vbh = kWithV ? reinterpret_cast<const uint16_t*>(V + b * g.vs[0] + h * g.vs[1]) : nullptr;
+  const __bf16* Vbh = kWithV ? V + b * g.vs[0] + h * g.vs[1] : nullptr;
   if (kWithV) {
-    for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
-      const int tt = idx / D, dd = idx - tt * D;
+    for (int idx = threadIdx.x; idx < 64 * D / 8; idx += 256) {
+      const int tt = idx / (D / 8), d8 = idx - tt * (D / 8);
       const int tok = t0 + tt;
-      vt[tt][dd] = tok < g.N ? Vbh[(int64_t)tok * g.vs[2] + dd] : (uint16_t)0;
+      bf16x8 v = bf16x8{};
+      if (tok < g.N) v = load_bf16x8(Vbh + (int64_t)tok * g.vs[2] + d8 * 8);
+      *reinterpret_cast<bf16x8*>(&vt[tt][d8 * 8]) = v;
     }
   }
   const int64_t cbase = (int64_t)bh * nch + (t0 >> 5);
