@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     const int32_t* __restrict__ order, void* O, int o_bf16) {
   constexpr int DC = D / 32, DT = D / 16, kQT = 4;
   constexpr int LD = D + 4;   // merge slot row stride (floats)
-  extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]
+  extern __shared__ float lds[];  // merge slots [4][64][LD] f32, maxima [4][64], row sums [4][64]
   const int qhalves = g.R / 64;
   const int tix = xcd_block_task(blockIdx.x, gridDim.x);
   const int ridx = tix / qhalves, qsub = tix - ridx * qhalves;
@@ -351,60 +351,59 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     l[qt] += __shfl_xor(l[qt], 32, kWave);
   }
 
-  // Merge the key groups of each query group: 3 -> 2 -> 1 -> 0 through one LDS slot per group.
-  float* so = lds;
-  float* sm = lds + 64 * LD;
-  float* sl = sm + 64;
-  for (int src = 3; src >= 1; --src) {
-    __syncthreads();
-    if (kw == src) {
+  // Merge the four key groups in one step: every wave parks its partial O,
+  // maxima and row sums in its own LDS slot, then wave kw combines dims
+  // [kw*D/4, (kw+1)*D/4) of all 64 queries from the four slots and stores
+  // them (a chain of three pairwise merges through one slot took ~5 us per
+  // workgroup, measured with one-block lists).
+  constexpr int DTW = DT / 4;  // dim tiles merged and stored per wave
+  float* slot = lds + kw * (64 * LD);
+  float* sm = lds + 4 * 64 * LD;  // [4][64] maxima
+  float* sl = sm + 4 * 64;        // [4][64] row sums
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) {
-        const int qi = qt * 16 + lr;
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int qi = qt * 16 + lr;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(so + qi * LD + dt * 16 + lg * 4) = o[dt][qt];
-        if (lg == 0) { sm[qi] = m[qt]; sl[qi] = l[qt]; }
-      }
-    }
-    __syncthreads();
-    if (kw == src - 1) {
-#pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) {
-        const int qi = qt * 16 + lr;
-        const float mo = sm[qi], lo = sl[qi];
-        const float mn = fmaxf(m[qt], mo);
-        const float a = m[qt] == kNegInf ? 0.f : fast_exp2(m[qt] - mn);
-        const float ao = mo == kNegInf ? 0.f : fast_exp2(mo - mn);
-        m[qt] = mn;
-        l[qt] = l[qt] * a + lo * ao;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const f32x4 oo = *reinterpret_cast<const f32x4*>(so + qi * LD + dt * 16 + lg * 4);
-          o[dt][qt] = o[dt][qt] * a + oo * ao;
-        }
-      }
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(slot + qi * LD + dt * 16 + lg * 4) = o[dt][qt];
+    if (lg == 0) {
+      sm[kw * 64 + qi] = m[qt];
+      sl[kw * 64 + qi] = l[qt];
     }
   }
-
-  if (kw == 0) {
+  __syncthreads();
 #pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-      const int qrow = row0 + qt * 16 + lr;
-      const float inv = (qrow < g.N && l[qt] > 0.f) ? 1.0f / l[qt] : 0.f;
-      const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int qi = qt * 16 + lr;
+    float mw[4], a[4], mm = kNegInf, lt = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = o[dt][qt] * inv;
-        const int d0 = dt * 16 + lg * 4;
-        if (o_bf16) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(v[0], v[1]);
-          pk[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(O) + obase + d0) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(O) + obase + d0) = v;
-        }
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = sm[w * 64 + qi];
+      mm = fmaxf(mm, mw[w]);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      a[w] = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - mm);
+      lt += a[w] * sl[w * 64 + qi];
+    }
+    const int qrow = row0 + qi;
+    const float inv = (qrow < g.N && lt > 0.f) ? 1.0f / lt : 0.f;
+    const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
+#pragma unroll
+    for (int dd = 0; dd < DTW; ++dd) {
+      const int dt = kw * DTW + dd;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        v += *reinterpret_cast<const f32x4*>(lds + w * (64 * LD) + qi * LD + dt * 16 + lg * 4) * a[w];
+      v *= inv;
+      const int d0 = dt * 16 + lg * 4;
+      if (o_bf16) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(v[0], v[1]);
+        pk[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(O) + obase + d0) = pk;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(O) + obase + d0) = v;
       }
     }
   }
@@ -492,7 +491,7 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* 
   __bf16* Vp = Kp + (size_t)g.B * g.H * nch * 32 * D;
   hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)V, Kp, Vp, nch);
-  const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float);
+  const size_t lds = (size_t)(4 * 64 * (D + 4) + 512) * sizeof(float);  // 137 KB at d = 128
   hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st,
                      g, (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, row_ptr, col_idx, order, O,
                      o_bf16);
