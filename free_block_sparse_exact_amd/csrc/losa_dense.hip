@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
                                                             void* O, int o_bf16) {
   constexpr int DC = D / 32, DT = D / 16, kQT = 4;
   constexpr int LD = D + 4;       // merge slot row stride (floats)
-  extern __shared__ float lds[];  // merge slot [64][LD] f32, m[64], l[64]
+  extern __shared__ float lds[];  // merge slots [4][64][LD] f32, maxima [4][64], row sums [4][64]
   __shared__ float s_ref[4][64], s_tot[4][64], s_f[4][64];
   const int qhalves = g.R / 64;
   const int rows = g.rows();
@@ -356,37 +356,58 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   s_ref[kw][lane] = lg == 0 ? m[0] : lg == 1 ? m[1] : lg == 2 ? m[2] : m[3];
   s_tot[kw][lane] = tot;
 
-  // Merge the key groups for O: 3 -> 2 -> 1 -> 0 through one LDS slot.
-  float* so = lds;
-  float* sm = lds + 64 * LD;
-  float* sl = sm + 64;
-  for (int src = 3; src >= 1; --src) {
-    __syncthreads();
-    if (kw == src) {
+  // Merge the four key groups for O in one step: every wave parks its partial
+  // O, maxima and row sums in its own LDS slot, then wave kw combines dims
+  // [kw*D/4, (kw+1)*D/4) of all 64 queries from the four slots and stores them.
+  {
+    constexpr int DTW = DT / 4;
+    float* slot = lds + kw * (64 * LD);
+    float* sm = lds + 4 * 64 * LD;  // [4][64] maxima
+    float* sl = sm + 4 * 64;        // [4][64] row sums
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) {
-        const int qi = qt * 16 + lr;
+    for (int qt = 0; qt < kQT; ++qt) {
+      const int qi = qt * 16 + lr;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(so + qi * LD + dt * 16 + lg * 4) = o[dt][qt];
-        if (lg == 0) { sm[qi] = m[qt]; sl[qi] = l[qt]; }
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(slot + qi * LD + dt * 16 + lg * 4) = o[dt][qt];
+      if (lg == 0) {
+        sm[kw * 64 + qi] = m[qt];
+        sl[kw * 64 + qi] = l[qt];
       }
     }
     __syncthreads();
-    if (kw == src - 1) {
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) {
-        const int qi = qt * 16 + lr;
-        const float mo = sm[qi], lo = sl[qi];
-        const float mn = fmaxf(m[qt], mo);
-        const float a = m[qt] == kNegInf ? 0.f : fast_exp2(m[qt] - mn);
-        const float ao = mo == kNegInf ? 0.f : fast_exp2(mo - mn);
-        m[qt] = mn;
-        l[qt] = l[qt] * a + lo * ao;
+    for (int qt = 0; qt < kQT; ++qt) {
+      const int qi = qt * 16 + lr;
+      float mw[4], a[4], mm = kNegInf, lt = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const f32x4 oo = *reinterpret_cast<const f32x4*>(so + qi * LD + dt * 16 + lg * 4);
-          o[dt][qt] = o[dt][qt] * a + oo * ao;
+      for (int w = 0; w < 4; ++w) {
+        mw[w] = sm[w * 64 + qi];
+        mm = fmaxf(mm, mw[w]);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        a[w] = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - mm);
+        lt += a[w] * sl[w * 64 + qi];
+      }
+      const int qrow = row0 + qi;
+      const float inv = (qrow < g.N && lt > 0.f) ? 1.0f / lt : 0.f;
+      const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
+#pragma unroll
+      for (int dd = 0; dd < DTW; ++dd) {
+        const int dt = kw * DTW + dd;
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          v += *reinterpret_cast<const f32x4*>(lds + w * (64 * LD) + qi * LD + dt * 16 + lg * 4) * a[w];
+        v *= inv;
+        const int d0 = dt * 16 + lg * 4;
+        if (o_bf16) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(v[0], v[1]);
+          pk[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(O) + obase + d0) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(O) + obase + d0) = v;
         }
       }
     }
@@ -394,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
 
   // Masses: lse of the stored query, this wave's factor 2^(m - lse) (0 for
   // padding rows), then M from S (s_ref/s_tot were written before the merge's
-  // first barrier).
+  // barrier).
   {
     float mm = kNegInf;
 #pragma unroll
@@ -414,28 +435,6 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       blocks_from_sums(Sg, s_f[kw], nb, inv_rows, Mrow, lane, [&](int bb) { return block_at(kw + 4 * bb); });
     } else {
       blocks_from_sums(Sg, s_f[kw], kw, nb, inv_rows, Mrow, lane);
-    }
-  }
-
-  if (kw == 0) {
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-      const int qrow = row0 + qt * 16 + lr;
-      const float inv = (qrow < g.N && l[qt] > 0.f) ? 1.0f / l[qt] : 0.f;
-      const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = o[dt][qt] * inv;
-        const int d0 = dt * 16 + lg * 4;
-        if (o_bf16) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(v[0], v[1]);
-          pk[1] = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(O) + obase + d0) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(O) + obase + d0) = v;
-        }
-      }
     }
   }
 }
@@ -478,7 +477,7 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* 
   hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)V, w.Kp, w.Vp, nch);
   const int tiles = g.rows() * (g.R / 64);
-  const size_t lds = (size_t)(64 * (D + 4) + 128) * sizeof(float);
+  const size_t lds = (size_t)(4 * 64 * (D + 4) + 512) * sizeof(float);  // 137 KB at d = 128
   float* Mout = g.R == 64 ? M : w.Mh;
   if (row_ptr)
     hipLaunchKernelGGL((dense_bf16_kernel<D, true>), dim3(tiles), dim3(256), lds, st, g, (const __bf16*)Q,
