@@ -363,10 +363,18 @@ def test_overflow_fallback_paths(R):
     assert err <= ATTN_ATOL
 
 
+def _check_list_masses(Mg: np.ndarray, Mref: np.ndarray):
+    """Masses within the lists: listed blocks (Mref > 0) within MASS_RTOL, the rest exactly 0."""
+    listed = Mref > 0
+    assert np.all(Mg[~listed] == 0.0)
+    assert float((np.abs(Mg[listed] - Mref[listed]) / Mref[listed]).max()) <= MASS_RTOL
+
+
 def test_batch_two_strided_all_calls():
     """batch = 2 with token-major storage [B, N, H, d] viewed as [B, H, N, d]:
-    masses, lists, sparse attention, the construction call and the pooled
-    proxy against the oracle (each batch entry is independent)."""
+    masses, lists, sparse attention, the construction call, the pooled proxy
+    and the masses within the lists against the oracle (each batch entry is
+    independent)."""
     rng = np.random.default_rng(77)
     B, H, N, d, R, C, p = 2, 2, 700, 128, 64, 64, 0.95
     Na = 704
@@ -394,6 +402,9 @@ def test_batch_two_strided_all_calls():
     P = F.losa_pooled_mass(q, k, N, R, C).cpu().numpy().astype(np.float64)
     P_ref = O.pooled_mass(x64[0], x64[1], N, R, C)
     assert float((np.abs(P - P_ref) / P_ref).max()) <= MASS_RTOL
+    Os, Ms = F.losa_sparse_attn_mass(q, k, v, rp, ci, order, N, R, C, out_dtype=torch.float32)
+    assert float(np.abs(Os.cpu().numpy()[:, :, :N] - ref[:, :, :N]).max()) <= ATTN_ATOL
+    _check_list_masses(Ms.cpu().numpy(), O.restricted_mass(x64[0], x64[1], N, R, C, rp_ref, ci_ref))
     torch.cuda.synchronize()
     say("batch 2, strided: all calls match the oracle")
 
@@ -403,7 +414,8 @@ def test_batch_two_strided_all_calls():
 def test_small_token_counts_all_calls(N, RC):
     """Token counts around every chunk and block boundary (one head, bf16, d = 128)
     through masses, selection, sparse attention on the oracle's lists in
-    shuffled order, the construction call and the pooled proxy."""
+    shuffled order, the construction call, the pooled proxy and the masses
+    within the (shuffled) lists."""
     R, C = RC
     rng = np.random.default_rng(1000 * R + N)
     H, d = 1, 128
@@ -436,3 +448,6 @@ def test_small_token_counts_all_calls(N, RC):
     assert mass_rel_err(Md.cpu().numpy(), M_ref) <= MASS_RTOL
     P = F.losa_pooled_mass(q, k, N, R, C).cpu().numpy().astype(np.float64)
     assert float((np.abs(P - O.pooled_mass(q64, k64, N, R, C)) / P).max()) <= MASS_RTOL
+    Os, Ms = F.losa_sparse_attn_mass(q, k, v, rp_d, ci_d, None, N, R, C, out_dtype=torch.float32)
+    assert float(np.abs(Os.cpu().numpy()[:, :, :nqR] - ref[:, :, :nqR]).max()) <= ATTN_ATOL
+    _check_list_masses(Ms.cpu().numpy(), O.restricted_mass(q64, k64, N, R, C, rp_ref, ci_ref))
