@@ -39,7 +39,8 @@ notes of the repository):
   T = ceil(P * sum_j q_j / 2^32), s = the least prefix length whose integer
   sum is >= T.  A plain fp64 argsort + cumsum is kept beside it as a cross-check.
 * Output lists are CSR with ascending block indices per row; the work order
-  lists rows by kept-block count, descending, ties by row index ascending.
+  keeps each head's n_q rows together (heads in index order) and lists them
+  by kept-block count, descending, ties by row index ascending.
 * Pooled proxy masses (the coarse estimates the page contrasts with exact
   masses -- Motivation Summary, SVG2 / SpargeAttn; the pages give no formula):
   P[i, j] = |B_j| exp(qbar_i . kbar_j * scale) / sum_j' |B_j'| exp(qbar_i .
@@ -394,10 +395,19 @@ def restricted_mass(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
     return restricted_mass_rows(q, k, n_valid, R, C, row_ptr, col_idx, rows, scale).reshape(B, H, n_q, n_k)
 
 
-def budget_order(row_ptr: np.ndarray) -> np.ndarray:
-    """Work order: rows by kept-block count descending, ties by row index ascending."""
+def budget_order(row_ptr: np.ndarray, n_q: int) -> np.ndarray:
+    """Work order: the rows of each (batch, head), n_q consecutive rows, stay
+    together, heads in index order; within a head, rows by kept-block count
+    descending, ties by row index ascending.
+
+    The pages ask for work ordered by budget because per-head budgets are
+    uneven (HASTE page, head-wise adaptive top-p; Sol-Attn page, dynamic but
+    imbalanced budgets); keeping each head's rows contiguous lets the
+    workgroups that run at the same time share that head's keys and values.
+    """
     counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
-    return np.argsort(-counts, kind="stable").astype(np.int64)
+    rows = np.arange(counts.size, dtype=np.int64)
+    return np.lexsort((rows, -counts, rows // int(n_q))).astype(np.int64)
 
 
 def recall(M: np.ndarray, row_ptr: np.ndarray, col_idx: np.ndarray, n_valid: int, R: int) -> float:

@@ -294,9 +294,29 @@ def test_recall_at_construction_and_coverage():
 
 
 def test_budget_order():
-    rp = np.array([0, 3, 5, 8, 9, 11])
-    order = O.budget_order(rp)
-    assert order.tolist() == [0, 2, 1, 4, 3]
+    # two heads of three rows, counts (3, 2, 3) and (1, 2, 2): each head's
+    # rows stay together; inside a head, longest first, equal counts by index
+    rp = np.array([0, 3, 5, 8, 9, 11, 13])
+    assert O.budget_order(rp, 3).tolist() == [0, 2, 1, 4, 5, 3]
+    # one head holding every row: the plain count-descending order
+    assert O.budget_order(rp, 6).tolist() == [0, 2, 1, 4, 5, 3]
+    assert O.budget_order(np.array([0, 3, 5, 8, 9, 11]), 5).tolist() == [0, 2, 1, 4, 3]
+    # one row per head: the natural order whatever the counts
+    assert O.budget_order(rp, 1).tolist() == list(range(6))
+
+
+def test_budget_order_brute_force():
+    rng = np.random.default_rng(5)
+    for n_q, heads in ((1, 7), (4, 3), (17, 5), (64, 2)):
+        counts = rng.integers(0, 6, size=n_q * heads)
+        rp = np.concatenate([[0], np.cumsum(counts)])
+        order = O.budget_order(rp, n_q)
+        ref = sorted(range(counts.size), key=lambda r: (r // n_q, -counts[r], r))
+        assert order.tolist() == ref
+        for h in range(heads):  # a permutation of each head's rows, non-increasing counts
+            part = order[h * n_q:(h + 1) * n_q]
+            assert sorted(part.tolist()) == list(range(h * n_q, (h + 1) * n_q))
+            assert np.all(np.diff(counts[part]) <= 0)
 
 
 # ---------------------------------------------------------------- generator
