@@ -42,11 +42,13 @@ hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float*
 struct SelectWs {
   int32_t* counts;      // [rows]
   uint64_t* kappa;      // [rows] boundary sort key of the last kept block
-  int32_t* chunk_hist;  // [nchunk][nk + 1] rows per (chunk, nk - count), then offsets within each count
+  int32_t* chunk_hist;  // [nchunk][nk + 1] rows per (chunk, nk - count), then that count's rows in the
+                        // head's earlier chunks
   int32_t* chunk_sum;   // [nchunk] kept blocks per row chunk, then the chunk's first CSR slot
   int32_t* done;        // [1] finished workgroups of the offsets kernel
-  int32_t* bucket;      // [nk + 1] rows per nk - count, then the first order slot of that count
-  int nchunk;
+  int32_t* bucket;      // [B*H][nk + 1] the head's rows per nk - count
+  int nchunk;           // B*H*cph row chunks, each inside one head
+  int cph;              // chunks per head: ceil(nq / kOrderChunk)
 };
 constexpr int kOrderChunk = 256;  // rows per placement chunk for the budget order
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base);

@@ -8,20 +8,23 @@
 //               units, without sorting -> the kept count s and the sort key
 //               kappa of the last kept block: one wave per row by bisection
 //               (n_k <= 2048), or one workgroup per row by radix select;
-//   chunk       one workgroup per chunk of 256 rows: histogram of counts
-//               and kept total of the chunk (LDS, then plain stores: no
-//               global atomics, nothing to clear beforehand, so the
-//               sequence can sit inside a captured graph);
-//   offsets     one thread per count: exclusive scan over the row chunks of
-//               that count's histogram column; the last workgroup to finish
-//               scans the per-count totals (-> first order slot per count)
-//               and the per-chunk kept totals (-> first CSR slot per chunk,
-//               and row_ptr[rows]);
-//   place       one workgroup per chunk of 256 rows: row_ptr of its rows
-//               (chunk base + scan of counts), and the stable placement of
-//               its rows by count, descending -> order;
+//   chunk       one workgroup per chunk of up to 256 rows of one head:
+//               histogram of counts and kept total of the chunk (LDS, then
+//               plain stores: no global atomics, nothing to clear
+//               beforehand, so the sequence can sit inside a captured graph);
+//   offsets     one thread per count: exclusive scan, head by head, over
+//               the head's row chunks of that count's histogram column
+//               (-> the head's rows of that count); the last workgroup to
+//               finish scans the per-chunk kept totals (-> first CSR slot
+//               per chunk, and row_ptr[rows]);
+//   place       one workgroup per chunk: row_ptr of its rows (chunk base +
+//               scan of counts), and the stable placement of its rows by
+//               count, descending, inside its head's n_q slots -> order;
 //   compact     one workgroup per row: block j is kept iff its sort key is
 //               <= kappa; write kept indices ascending at row_ptr[row].
+//
+// Work order: the n_q rows of each (batch, head) keep their range, heads in
+// index order; inside it, rows by kept count descending, ties by row index.
 //
 // Sort key of block j with (sanitised) mass bits u: ((2^32-1-u) << 32) | j.
 // For non-negative floats the bit pattern orders like the value, so an
@@ -113,21 +116,33 @@ __device__ __forceinline__ int block_sum_i32(int v, int* wsum) {
   return all;
 }
 
-// One workgroup per chunk of kOrderChunk rows: the chunk's histogram of
-// nk - count (built in LDS, stored whole, zeros included) and its kept
-// total.  Workgroup 0 also clears the offsets kernel's done counter.  Plain
-// stores only, so nothing needs clearing beforehand.
-__global__ __launch_bounds__(kOrderChunk) void chunk_kernel(const int32_t* __restrict__ counts, int rows, int nk,
-                                                            int32_t* __restrict__ hist,
+// Chunk c covers rows h * nq + k * kOrderChunk + [0, kOrderChunk) of head
+// h = c / cph, k = c % cph (cph chunks per head), cut at the head's end.
+struct ChunkRows {
+  int row, valid, head;
+  __device__ ChunkRows(int chunk, int nq, int cph) {
+    head = chunk / cph;
+    const int local = (chunk - head * cph) * kOrderChunk + (int)threadIdx.x;
+    valid = local < nq;
+    row = head * nq + local;
+  }
+};
+
+// One workgroup per chunk: the chunk's histogram of nk - count (built in
+// LDS, stored whole, zeros included) and its kept total.  Workgroup 0 also
+// clears the offsets kernel's done counter.  Plain stores only, so nothing
+// needs clearing beforehand.
+__global__ __launch_bounds__(kOrderChunk) void chunk_kernel(const int32_t* __restrict__ counts, int nq, int cph,
+                                                            int nk, int32_t* __restrict__ hist,
                                                             int32_t* __restrict__ chunk_sum, int32_t* done) {
   extern __shared__ int hl[];  // [nk + 1]
   __shared__ int wsum[kOrderChunk / 64];
   const int chunk = blockIdx.x;
   for (int x = threadIdx.x; x <= nk; x += blockDim.x) hl[x] = 0;
   __syncthreads();
-  const int row = chunk * kOrderChunk + threadIdx.x;
-  const int cnt = row < rows ? counts[row] : 0;
-  if (row < rows) atomicAdd(&hl[nk - cnt], 1);
+  const ChunkRows cr(chunk, nq, cph);
+  const int cnt = cr.valid ? counts[cr.row] : 0;
+  if (cr.valid) atomicAdd(&hl[nk - cnt], 1);
   int v = cnt;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -445,7 +460,7 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
 
 // Exclusive scan of data[0, n) into out by one workgroup (a multiple of 64
 // threads, wsum holding one int per wave); in place is allowed.
-__device__ void block_exclusive_scan_i32(int32_t* data, int n, int32_t* out, int32_t* out_total,
+__device__ void block_exclusive_scan_i32(const int32_t* data, int n, int32_t* out, int32_t* out_total,
                                          int* wsum) {
   const int nt = blockDim.x;
   const int per = (n + nt - 1) / nt;
@@ -484,36 +499,39 @@ __device__ void block_exclusive_scan_i32(int32_t* data, int n, int32_t* out, int
   __syncthreads();
 }
 
-// One thread per count bucket b = nk - count: the column hist[.][b] becomes
-// its exclusive scan over the row chunks and bucket[b] its total.  The last
-// workgroup to finish (counted in *done) turns bucket into the first order
-// slot of each count (descending count = ascending b) and chunk_sum into the
-// first CSR slot of each chunk, and writes row_ptr[rows].
-__global__ __launch_bounds__(256) void offsets_kernel(int nk, int nchunk, int rows, int32_t* __restrict__ hist,
-                                                      int32_t* chunk_sum, int32_t* bucket, int32_t* done,
+// One thread per count bucket b = nk - count: within each head, the column
+// hist[.][b] over the head's cph chunks becomes its exclusive scan, and
+// bucket[head][b] the head's total.  The last workgroup to finish (counted
+// in *done) turns chunk_sum into the first CSR slot of each chunk and writes
+// row_ptr[rows].
+__global__ __launch_bounds__(256) void offsets_kernel(int nk, int nchunk, int cph, int rows,
+                                                      int32_t* __restrict__ hist, int32_t* chunk_sum,
+                                                      int32_t* __restrict__ bucket, int32_t* done,
                                                       int32_t* __restrict__ row_ptr) {
   __shared__ int wsum[256 / 64];
   __shared__ int last;
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b <= nk) {
-    int run = 0;
+    int run = 0, k = 0, h = 0;  // running total, chunk within the head, head
+    auto step = [&](int c, int v) {
+      if (k == 0) run = 0;
+      hist[(int64_t)c * (nk + 1) + b] = run;
+      run += v;
+      if (++k == cph) {
+        bucket[(int64_t)h * (nk + 1) + b] = run;
+        k = 0;
+        ++h;
+      }
+    };
     int c = 0;
     for (; c + 8 <= nchunk; c += 8) {  // eight loads in flight per thread
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)(c + u) * (nk + 1) + b];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        hist[(int64_t)(c + u) * (nk + 1) + b] = run;
-        run += v[u];
-      }
+      for (int u = 0; u < 8; ++u) step(c + u, v[u]);
     }
-    for (; c < nchunk; ++c) {
-      const int v = hist[(int64_t)c * (nk + 1) + b];
-      hist[(int64_t)c * (nk + 1) + b] = run;
-      run += v;
-    }
-    bucket[b] = run;
+    for (; c < nchunk; ++c) step(c, hist[(int64_t)c * (nk + 1) + b]);
   }
   __threadfence();
   __syncthreads();
@@ -521,7 +539,6 @@ __global__ __launch_bounds__(256) void offsets_kernel(int nk, int nchunk, int ro
   __syncthreads();
   if (!last) return;
   __threadfence();
-  block_exclusive_scan_i32(bucket, nk + 1, bucket, nullptr, wsum);
   block_exclusive_scan_i32(chunk_sum, nchunk, chunk_sum, row_ptr + rows, wsum);
 }
 
@@ -566,22 +583,26 @@ __global__ __launch_bounds__(kSelThreads) void compact_kernel(const Geom g, cons
 
 // One workgroup (kOrderChunk threads) per chunk of rows.  row_ptr of the
 // chunk's rows: the chunk's first CSR slot plus the scan of their counts.
-// Then (if order is wanted) stable placement by count descending: the first
-// slot of a row with count c is bucket[nk - c] + hist[chunk][nk - c] plus the
-// rows of that count already placed by earlier waves of this chunk; waves
-// take turns so that rows keep their index order within a count.
-__global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __restrict__ counts, int rows, int nk,
-                                                            const int32_t* __restrict__ hist,
+// Then (if order is wanted) stable placement by count descending inside the
+// head's slots [h * nq, (h + 1) * nq): the first slot of a row with count c
+// is h * nq + (rows of the head with a larger count: the exclusive scan of
+// bucket[h]) + hist[chunk][nk - c] (rows of count c in earlier chunks of the
+// head) plus the rows of that count already placed by earlier waves of this
+// chunk; waves take turns so that rows keep their index order within a count.
+__global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __restrict__ counts, int nq, int cph,
+                                                            int nk, const int32_t* __restrict__ hist,
                                                             const int32_t* __restrict__ bucket,
                                                             const int32_t* __restrict__ chunk_base,
                                                             int32_t* __restrict__ row_ptr,
                                                             int32_t* __restrict__ order) {
-  extern __shared__ int run[];  // [nk + 1] slots already used by earlier waves of this chunk
+  extern __shared__ int run[];  // [nk + 1] next free slot of each count, relative to the head's first
   __shared__ int wsum[kOrderChunk / 64];
+  __shared__ int wscan[kOrderChunk / 64];
   const int chunk = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = chunk * kOrderChunk + threadIdx.x;
-  const int cnt = row < rows ? counts[row] : 0;
+  const ChunkRows cr(chunk, nq, cph);
+  const int row = cr.row;
+  const int cnt = cr.valid ? counts[row] : 0;
   int v = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -589,20 +610,21 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
     if (lane >= o) v += t;
   }
   if (lane == 63) wsum[w] = v;
-  for (int x = threadIdx.x; x <= nk; x += blockDim.x) run[x] = 0;
   __syncthreads();
   int before = chunk_base[chunk];
 #pragma unroll
   for (int ww = 0; ww < kOrderChunk / 64; ++ww)
     if (ww < w) before += wsum[ww];
-  if (row < rows) row_ptr[row] = before + v - cnt;
+  if (cr.valid) row_ptr[row] = before + v - cnt;
   if (!order) return;
+  block_exclusive_scan_i32(bucket + (int64_t)cr.head * (nk + 1), nk + 1, run, nullptr, wscan);
   const int32_t* hrow = hist + (int64_t)chunk * (nk + 1);
+  const int head0 = cr.head * nq;
   const int bkt = nk - cnt;
   for (int turn = 0; turn < kOrderChunk / 64; ++turn) {
     __syncthreads();
     if (w == turn) {
-      bool todo = row < rows;
+      bool todo = cr.valid;
       while (true) {
         const uint64_t am = __ballot(todo);
         if (am == 0) break;
@@ -610,7 +632,7 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
         const int b0 = __shfl(bkt, leader, kWave);
         const bool match = todo && bkt == b0;
         const uint64_t mm = __ballot(match);
-        const int base = bucket[b0] + hrow[b0] + run[b0];
+        const int base = head0 + hrow[b0] + run[b0];
         if (match) {
           const int rank = __popcll(mm & ((1ull << lane) - 1));
           order[base + rank] = row;
@@ -642,7 +664,9 @@ __global__ __launch_bounds__(64) void retained_kernel(const Geom g, const float*
 
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
   const int rows = g.rows();
-  const int nchunk = (rows + kOrderChunk - 1) / kOrderChunk;
+  const int heads = g.B * g.H;
+  const int cph = (g.nq + kOrderChunk - 1) / kOrderChunk;
+  const int nchunk = heads * cph;
   size_t off = 0;
   const size_t counts_off = off;
   off = align_up(off + (size_t)rows * sizeof(int32_t), 256);
@@ -651,7 +675,7 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
   const size_t hist_off = off;  // then chunk_sum and done
   off = align_up(off + ((size_t)(g.nk + 1) * nchunk + nchunk + 1) * sizeof(int32_t), 256);
   const size_t bucket_off = off;
-  off = align_up(off + (size_t)(g.nk + 1) * sizeof(int32_t), 256);
+  off = align_up(off + (size_t)heads * (g.nk + 1) * sizeof(int32_t), 256);
   if (layout) {
     layout->counts = reinterpret_cast<int32_t*>(base + counts_off);
     layout->kappa = reinterpret_cast<uint64_t*>(base + kappa_off);
@@ -660,6 +684,7 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
     layout->done = layout->chunk_sum + nchunk;
     layout->bucket = reinterpret_cast<int32_t*>(base + bucket_off);
     layout->nchunk = nchunk;
+    layout->cph = cph;
   }
   return off;
 }
@@ -683,11 +708,11 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
   }
   const size_t hist_lds = (size_t)(g.nk + 1) * sizeof(int);
   hipLaunchKernelGGL(chunk_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
-                     rows, g.nk, ws.chunk_hist, ws.chunk_sum, ws.done);
-  hipLaunchKernelGGL(offsets_kernel, dim3((g.nk + 1 + 255) / 256), dim3(256), 0, st, g.nk, ws.nchunk, rows,
-                     ws.chunk_hist, ws.chunk_sum, ws.bucket, ws.done, row_ptr);
+                     g.nq, ws.cph, g.nk, ws.chunk_hist, ws.chunk_sum, ws.done);
+  hipLaunchKernelGGL(offsets_kernel, dim3((g.nk + 1 + 255) / 256), dim3(256), 0, st, g.nk, ws.nchunk, ws.cph,
+                     rows, ws.chunk_hist, ws.chunk_sum, ws.bucket, ws.done, row_ptr);
   hipLaunchKernelGGL(place_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
-                     rows, g.nk, (const int32_t*)ws.chunk_hist, (const int32_t*)ws.bucket,
+                     g.nq, ws.cph, g.nk, (const int32_t*)ws.chunk_hist, (const int32_t*)ws.bucket,
                      (const int32_t*)ws.chunk_sum, row_ptr, order);
   hipLaunchKernelGGL(compact_kernel, dim3(rows), dim3(kSelThreads), 0, st, g, M, (const uint64_t*)ws.kappa,
                      (const int32_t*)row_ptr, col_idx);

@@ -138,9 +138,13 @@ losa_status losa_block_mass(const losa_shape* shape, const void* Q, const void* 
  *    col_idx[row_ptr[r] .. row_ptr[r+1]-1], in ascending block order.
  * col_idx: int32, col_capacity >= batch*heads*n_q*n_k entries (the worst
  *    case; the used length is row_ptr[last], read back by the caller).
- * order: int32 [batch*heads*n_q] or NULL.  When given, receives the rows
- *    sorted by kept-block count, descending, ties by row index ascending
- *    (the work order losa_sparse_attn takes).
+ * order: int32 [batch*heads*n_q] or NULL.  When given, receives the work
+ *    order losa_sparse_attn takes: slots [g*n_q, (g+1)*n_q) hold the rows
+ *    of head g = b*heads + h, sorted by kept-block count, descending, ties
+ *    by row index ascending.  Per-head budgets are uneven (HASTE page,
+ *    head-wise adaptive top-p; Sol-Attn page, imbalanced dynamic budgets),
+ *    so the longest rows go first; keeping a head's rows together lets the
+ *    workgroups running at one time share that head's keys and values.
  * ws: at least *bytes from losa_select_workspace.
  * ------------------------------------------------------------------------ */
 losa_status losa_select_workspace(const losa_shape* shape, size_t* bytes);

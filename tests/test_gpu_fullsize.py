@@ -53,10 +53,11 @@ def test_fullsize_pipeline_sampled_rows(wid):
     rp_h = rp.cpu().numpy().astype(np.int64)
     ci_h = ci[:int(rp_h[-1])].cpu().numpy()
     order_h = order.cpu().numpy()
-    # the work order is a permutation, by count descending, stable
+    # the work order is a permutation: each head's rows in its own range, by
+    # count descending, equal counts by row index
     cnt = np.diff(rp_h)
     assert np.array_equal(np.sort(order_h), np.arange(len(cnt)))
-    assert np.array_equal(order_h, np.argsort(-cnt, kind="stable"))
+    assert np.array_equal(order_h, O.budget_order(rp_h, nq))
     say(f"  nnz={int(rp_h[-1])} coverage={rp_h[-1] / (len(cnt) * nk):.4f} budgets {cnt.min()}..{cnt.max()}")
 
     by_head = {}
@@ -144,7 +145,7 @@ def test_select_bit_exact_full_shape(wid):
     rp = rp.cpu().numpy().astype(np.int64)
     assert np.array_equal(rp, rp_ref)
     assert np.array_equal(ci[:int(rp[-1])].cpu().numpy(), ci_ref)
-    assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref))
+    assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref, M.shape[2]))
 
 
 def test_maximum_key_block_count():
@@ -192,4 +193,4 @@ def test_maximum_key_block_count():
     rp2 = rp2.cpu().numpy().astype(np.int64)
     assert np.array_equal(rp2, rp_ref)
     assert np.array_equal(ci2[:int(rp2[-1])].cpu().numpy(), ci_ref)
-    assert np.array_equal(order2.cpu().numpy(), O.budget_order(rp_ref))
+    assert np.array_equal(order2.cpu().numpy(), O.budget_order(rp_ref, Msyn.shape[2]))

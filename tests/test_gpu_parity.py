@@ -63,7 +63,7 @@ def _case(name):
     M = O.block_mass(q64, k64, N, R, C)
     M32 = M.astype(np.float32)
     rp, ci = O.select_contract(M32, p)
-    order = O.budget_order(rp)
+    order = O.budget_order(rp, M.shape[2])
     Oref = O.sparse_attention(q64, k64, v64, N, R, C, rp, ci)
     d = dict(layer=layer, N=N, Na=Na, R=R, C=C, p=p, M=M, M32=M32, rp=rp, ci=ci, order=order, O=Oref)
     _cache[name] = d

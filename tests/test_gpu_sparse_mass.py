@@ -106,7 +106,7 @@ def test_sparse_mass_random_lists(N, R, C, use_order):
     layer.q, layer.k, layer.v = pad(layer.q), pad(layer.k), pad(layer.v)
     n_q, n_k = -(-N // R), -(-N // C)
     rp, ci = _random_lists(np.random.default_rng(N + R + C), 2 * n_q, n_k, 0.5)
-    order = O.budget_order(rp) if use_order else None
+    order = O.budget_order(rp, n_q) if use_order else None
     q64, k64, v64 = layer.f64("q"), layer.f64("k"), layer.f64("v")
     Og, Mg = run(layer, N, R, C, rp, ci, order)
     ref = O.sparse_attention(q64, k64, v64, N, R, C, rp, ci)
