@@ -55,6 +55,13 @@ notes of the repository):
   M_L(i, j) = mean over valid rows of block i of the sum over block j's
   tokens of it, for j in L; 0 for blocks outside L.  A row with a non-empty
   list sums to 1; with every block listed M_L = M.
+* Drift-triggered refresh (the HASTE page's temporal mask reuse: mask
+  prediction is skipped while queries and keys have drifted little since it
+  was last made; the page gives no measure): per (batch, head), the drift of
+  Q is ||Q - Q_ref||_F / ||Q_ref||_F over the valid tokens, Q_ref being the
+  queries of the step at which the head's lists were built, likewise for K
+  (0/0 = 0, x/0 = inf for x > 0); a head's lists are rebuilt when the larger
+  of its two drifts exceeds a threshold tau, and kept otherwise.
 
 Row numbering: row r = (b * H + h) * n_q + i for batch b, head h, query block i.
 Inputs are fp64 arrays [B, H, N_alloc, d] holding the exact values the GPU sees.
@@ -84,6 +91,9 @@ __all__ = [
     "sparse_attention",
     "sparse_attention_rows",
     "budget_order",
+    "qk_drift",
+    "refresh_heads",
+    "merge_lists",
     "recall",
     "coverage",
     "row_id",
@@ -408,6 +418,41 @@ def budget_order(row_ptr: np.ndarray, n_q: int) -> np.ndarray:
     counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
     rows = np.arange(counts.size, dtype=np.int64)
     return np.lexsort((rows, -counts, rows // int(n_q))).astype(np.int64)
+
+
+def qk_drift(q: np.ndarray, k: np.ndarray, q_ref: np.ndarray, k_ref: np.ndarray, n_valid: int) -> np.ndarray:
+    """Relative Frobenius drift of Q and K per (batch, head) since the reference
+    step, over the valid tokens: out[b, h] = (dQ, dK) (HASTE page, temporal
+    mask reuse, as read in this module's header)."""
+    out = np.zeros(q.shape[:2] + (2,), np.float64)
+    for t, (x, xr) in enumerate(((q, q_ref), (k, k_ref))):
+        diff = np.asarray(x, np.float64)[:, :, :n_valid] - np.asarray(xr, np.float64)[:, :, :n_valid]
+        num = np.sqrt(np.sum(diff * diff, axis=(2, 3)))
+        den = np.sqrt(np.sum(np.asarray(xr, np.float64)[:, :, :n_valid] ** 2, axis=(2, 3)))
+        with np.errstate(divide="ignore", invalid="ignore"):
+            out[:, :, t] = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
+    return out
+
+
+def refresh_heads(drift: np.ndarray, tau: float) -> np.ndarray:
+    """Heads whose lists are rebuilt: the larger of the two drifts exceeds tau."""
+    return np.max(drift, axis=-1) > tau
+
+
+def merge_lists(rp_a: np.ndarray, ci_a: np.ndarray, rp_b: np.ndarray, ci_b: np.ndarray,
+                take_b: np.ndarray, n_q: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Row r's list from set b when its head (r // n_q) is refreshed, from set a
+    otherwise; CSR in row order."""
+    take = np.asarray(take_b).reshape(-1)
+    rows = len(rp_a) - 1
+    rp, parts = [0], []
+    for r in range(rows):
+        src_rp, src_ci = (rp_b, ci_b) if take[r // n_q] else (rp_a, ci_a)
+        lst = np.asarray(src_ci[int(src_rp[r]):int(src_rp[r + 1])], np.int64)
+        parts.append(lst)
+        rp.append(rp[-1] + len(lst))
+    ci = np.concatenate(parts) if parts else np.zeros(0, np.int64)
+    return np.asarray(rp, np.int64), ci
 
 
 def recall(M: np.ndarray, row_ptr: np.ndarray, col_idx: np.ndarray, n_valid: int, R: int) -> float:

@@ -485,3 +485,69 @@ def test_restricted_mass_brute_force_loops():
             for j in lst:
                 want[j] += sum(w[kk] for kk in range(j * C, min((j + 1) * C, N))) / z / len(rows_i)
         assert np.abs(ML[i] - np.asarray(want)).max() <= 1e-12
+
+
+# ------------------------------------------------------- drift-triggered refresh
+
+def test_qk_drift_closed_forms():
+    rng = np.random.default_rng(21)
+    B, H, N, Na, d = 2, 3, 10, 16, 8
+    q_ref = rng.standard_normal((B, H, Na, d))
+    k_ref = rng.standard_normal((B, H, Na, d))
+    # a scaled copy drifts by the scale change; an unchanged tensor by 0
+    dr = O.qk_drift(1.25 * q_ref, k_ref, q_ref, k_ref, N)
+    assert np.allclose(dr[..., 0], 0.25, rtol=0, atol=1e-14) and np.all(dr[..., 1] == 0)
+    # an orthogonal change: rows 3 e_0 moved by 4 e_1 drift by 4/3
+    a = np.zeros((B, H, Na, d))
+    a[:, :, :, 0] = 3.0
+    b = a.copy()
+    b[:, :, :, 1] = 4.0
+    assert np.allclose(O.qk_drift(a, b, a, a, N)[..., 1], 4.0 / 3.0, rtol=1e-15)
+    # padding rows are not tokens
+    qp, qrp = q_ref.copy(), q_ref.copy()
+    qp[:, :, N:] = np.nan
+    qrp[:, :, N:] = 1e30
+    assert np.array_equal(O.qk_drift(qp, k_ref, qrp, k_ref, N), O.qk_drift(q_ref, k_ref, q_ref, k_ref, N))
+    # a zero reference: 0 if still zero, inf otherwise
+    z = np.zeros_like(q_ref)
+    dz = O.qk_drift(z, q_ref, z, z, N)
+    assert np.all(dz[..., 0] == 0) and np.all(np.isinf(dz[..., 1]))
+    # heads are measured separately
+    q2 = q_ref.copy()
+    q2[1, 0, :N] += 0.5
+    d2 = O.qk_drift(q2, k_ref, q_ref, k_ref, N)
+    assert d2[1, 0, 0] > 0 and np.count_nonzero(d2) == 1
+
+
+def test_qk_drift_brute_force():
+    rng = np.random.default_rng(22)
+    B, H, N, Na, d = 1, 2, 5, 8, 4
+    x = [rng.standard_normal((B, H, Na, d)) for _ in range(4)]
+    got = O.qk_drift(x[0], x[1], x[2], x[3], N)
+    for h in range(H):
+        for t, (cur, ref) in enumerate(((x[0], x[2]), (x[1], x[3]))):
+            num = den = 0.0
+            for n in range(N):
+                for c in range(d):
+                    num += (cur[0, h, n, c] - ref[0, h, n, c]) ** 2
+                    den += ref[0, h, n, c] ** 2
+            assert abs(got[0, h, t] - math.sqrt(num) / math.sqrt(den)) <= 1e-14 * got[0, h, t]
+
+
+def test_refresh_rule():
+    dr = np.array([[[0.1, 0.3], [0.3, 0.1], [0.2, 0.2], [0.0, np.inf]]])
+    assert O.refresh_heads(dr, 0.2).tolist() == [[True, True, False, True]]
+    assert O.refresh_heads(dr, 0.3).tolist() == [[False, False, False, True]]
+
+
+def test_merge_lists():
+    # two heads of two rows each
+    rp_a, ci_a = np.array([0, 2, 3, 3, 5]), np.array([0, 1, 2, 0, 3])
+    rp_b, ci_b = np.array([0, 1, 1, 4, 5]), np.array([3, 0, 1, 2, 1])
+    rp, ci = O.merge_lists(rp_a, ci_a, rp_b, ci_b, np.array([False, True]), 2)
+    assert rp.tolist() == [0, 2, 3, 6, 7] and ci.tolist() == [0, 1, 2, 0, 1, 2, 1]
+    rp, ci = O.merge_lists(rp_a, ci_a, rp_b, ci_b, np.array([True, False]), 2)
+    assert rp.tolist() == [0, 1, 1, 1, 3] and ci.tolist() == [3, 0, 3]
+    for take, (r0, c0) in (([0, 0], (rp_a, ci_a)), ([1, 1], (rp_b, ci_b))):
+        rp, ci = O.merge_lists(rp_a, ci_a, rp_b, ci_b, np.array(take, bool), 2)
+        assert np.array_equal(rp, r0) and np.array_equal(ci, c0)
