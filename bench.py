@@ -180,6 +180,8 @@ def main():
     ap.add_argument("--workload", default="1")
     ap.add_argument("--cpu-rows", type=int, default=16, help="query blocks in the oracle CPU baseline (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--refresh-tau", type=float, default=0.75,
+                    help="drift threshold of the drift-triggered refresh leg of the reuse workload")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "NAME", "COMMAND"))
@@ -327,6 +329,7 @@ def main():
                                    "launches": "pack_kv + dense over the lists (+ add_halves at R = 128)",
                                    "note": "sparse attention plus the exact masses within the lists (reduced "
                                            "search); kept-block flops; not in ms_per_step"}
+    kernels.update(refresh_calls(F, torch, q, k, bufs, geom, wl, stream, dev))
     routing = pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev)
     cpu = None
     if args.cpu_rows > 0:
@@ -407,6 +410,127 @@ def _drift_step(s):
     """One step's drifted Q/K (bf16 bit patterns) from the layer set before the fork."""
     import synthetic as S
     return S.drift_qk(_REUSE_LAYER, s)
+
+
+def refresh_calls(F, torch, q, k, bufs, geom, wl, stream, dev):
+    """The drift-triggered refresh's two calls on this layer, timed on their own
+    (not part of ms_per_step): the query-key drift against a reference copy of
+    Q and K (HBM-bound: the four tensors' valid tokens read once), and the
+    per-head merge of two list sets (here the step's lists with themselves,
+    every other head taken from the second set)."""
+    N, R, C = wl.tokens, wl.block, wl.key_block
+    q_ref, k_ref = q.clone(), k.clone()
+    ws = torch.empty(F.losa_qk_drift_workspace(geom), dtype=torch.uint8, device=dev)
+    drift = torch.empty((geom.batch, geom.heads, 2), dtype=torch.float64, device=dev)
+    flags = torch.empty((geom.batch, geom.heads), dtype=torch.int32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        F.losa_qk_drift(q, k, q_ref, k_ref, N, 0.5, R, C, drift=drift, refresh=flags, ws=ws, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    drift_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[1:]]))
+    drift_bytes = 4.0 * geom.batch * geom.heads * N * geom.head_dim * q.element_size()
+    del q_ref, k_ref, ws
+    take = (torch.arange(geom.batch * geom.heads, device=dev, dtype=torch.int32) % 2).view(geom.batch, geom.heads)
+    rows, nk = geom.rows, geom.n_k
+    rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(rows * nk, dtype=torch.int32, device=dev)
+    order = torch.empty(rows, dtype=torch.int32, device=dev)
+    ws = torch.empty(F.losa_merge_lists_workspace(geom), dtype=torch.uint8, device=dev)
+    for e0, e1 in evs:
+        e0.record(stream)
+        F.losa_merge_lists(take, bufs.row_ptr, bufs.col_idx, bufs.row_ptr, bufs.col_idx, N, R, C,
+                           tokens_alloc=geom.tokens_alloc, row_ptr=rp, col_idx=ci, order=order, ws=ws, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    merge_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[1:]]))
+    nnz = int(bufs.row_ptr[-1].item())
+    merge_bytes = 8.0 * nnz + 4.0 * 5 * rows  # indices read and written; row offsets of both sets, counts, order
+    del rp, ci, order, ws
+    return {
+        "qk_drift": {"ms": drift_ms, "gbs": drift_bytes / (drift_ms * 1e-3) / 1e9,
+                     "frac_hbm_peak": drift_bytes / (drift_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "bytes": drift_bytes, "launches": "drift_partial + drift_final",
+                     "note": "Q, K and their references read once; not in ms_per_step"},
+        "merge_lists": {"ms": merge_ms, "gbs": merge_bytes / (merge_ms * 1e-3) / 1e9, "bytes": merge_bytes,
+                        "launches": "pick_counts + chunk + offsets + place + copy_lists",
+                        "note": "launch-latency bound at this size; not in ms_per_step"},
+    }
+
+
+def refresh_trajectory(F, torch, wl, tau, steps_qk, q, k, v, bufs, geom, p_heads, w, stream, dev, frozen_recalls):
+    """The reuse trajectory with a drift-triggered refresh (HASTE page, temporal
+    mask reuse): at every sparse step, each head's Q and K drift against the
+    step its lists were built at; when either exceeds tau the head's lists are
+    rebuilt from that step's exact masses with its p (the masses of every head
+    are computed, the merge keeps the other heads' lists) and the step's Q and
+    K become its reference.  Drift, rebuild and sparse attention are timed."""
+    N, R, C, Na = wl.tokens, wl.block, wl.key_block, wl.tokens_alloc
+    H, rows, nk = geom.heads, geom.rows, geom.n_k
+    q.copy_(steps_qk[wl.construct_step][0])
+    k.copy_(steps_qk[wl.construct_step][1])
+    q_ref, k_ref = q.clone(), k.clone()
+    cur = [bufs.row_ptr.clone(), bufs.col_idx.clone(), bufs.order.clone()]
+    new = [torch.empty_like(cur[0]), torch.empty_like(cur[1]), None]
+    nxt = [torch.empty_like(t) for t in cur]
+    M_new = torch.empty_like(bufs.M)
+    ws_d = torch.empty(F.losa_qk_drift_workspace(geom), dtype=torch.uint8, device=dev)
+    drift = torch.empty((1, H, 2), dtype=torch.float64, device=dev)
+    flags = torch.empty((1, H), dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    drift_ms, rebuild_ms, sparse_ms, recalls, refreshed, drift_max = [], [], [], [], [], []
+    for s in range(wl.steps):
+        if s == wl.construct_step:
+            recalls.append(frozen_recalls[s])
+            refreshed.append(0)
+            drift_max.append(0.0)
+            continue
+        q.copy_(steps_qk[s][0])
+        k.copy_(steps_qk[s][1])
+        ev[0].record(stream)
+        F.losa_qk_drift(q, k, q_ref, k_ref, N, tau, R, C, drift=drift, refresh=flags, ws=ws_d, stream=stream)
+        ev[1].record(stream)
+        f = flags.cpu().numpy()[0]          # the host decides which heads to rebuild
+        drift_ms.append(ev[0].elapsed_time(ev[1]))
+        drift_max.append(float(drift.cpu().numpy().max()))
+        refreshed.append(int(f.sum()))
+        if f.any():
+            ev[2].record(stream)
+            F.losa_block_mass(q, k, N, R, C, out=M_new, ws=bufs.ws_mass, stream=stream)
+            F.losa_select(M_new, p_heads, N, R, C, tokens_alloc=Na, want_order=False, row_ptr=new[0],
+                          col_idx=new[1], ws=bufs.ws_sel, stream=stream)
+            F.losa_merge_lists(flags, cur[0], cur[1], new[0], new[1], N, R, C, tokens_alloc=Na, row_ptr=nxt[0],
+                               col_idx=nxt[1], order=nxt[2], ws=bufs.ws_sel, stream=stream)
+            ev[3].record(stream)
+            cur, nxt = nxt, cur
+            for h in np.flatnonzero(f):
+                q_ref[:, h].copy_(q[:, h])
+                k_ref[:, h].copy_(k[:, h])
+            torch.cuda.synchronize()
+            rebuild_ms.append(ev[2].elapsed_time(ev[3]))
+        ev[4].record(stream)
+        F.losa_sparse_attn(q, k, v, cur[0], cur[1], cur[2], N, R, C, out=bufs.out, ws=bufs.ws_attn, stream=stream)
+        ev[5].record(stream)
+        torch.cuda.synchronize()
+        sparse_ms.append(ev[4].elapsed_time(ev[5]))
+        # recall of the lists in use under this step's exact masses, not timed
+        F.losa_block_mass(q, k, N, R, C, out=bufs.M, ws=bufs.ws_mass, stream=stream)
+        F.losa_retained_mass(bufs.M, cur[0], cur[1], N, R, C, out=bufs.kept, stream=stream)
+        kept = bufs.kept.cpu().numpy().astype(np.float64)
+        recalls.append(float((kept[:, 0] * w).sum() / (kept[:, 1] * w).sum()))
+        log(f"refresh leg step {s}: max drift {drift_max[-1]:.3f}, {refreshed[-1]} heads rebuilt, "
+            f"recall {recalls[-1]:.6f}")
+    total = float(np.sum(drift_ms) + np.sum(rebuild_ms) + np.sum(sparse_ms))
+    return {"tau": tau, "measure": "per head, ||X - X_ref||_F / ||X_ref||_F for X = Q and K over the valid tokens",
+            "heads_rebuilt_per_step": refreshed, "drift_max_per_step": drift_max,
+            "rebuild_steps": int(sum(1 for x in refreshed if x)), "recall_per_step": recalls,
+            "mean_recall": float(np.mean(recalls)), "mean_recall_frozen": float(np.mean(frozen_recalls)),
+            "min_recall": float(np.min(recalls)), "min_recall_frozen": float(np.min(frozen_recalls)),
+            "drift_ms_mean": float(np.mean(drift_ms)),
+            "rebuild_ms_mean": float(np.mean(rebuild_ms)) if rebuild_ms else None,
+            "sparse_attn_ms_mean": float(np.mean(sparse_ms)),
+            "steps_ms_excluding_construction": total}
 
 
 def run_reuse(args, wl):
@@ -507,6 +631,8 @@ def run_reuse(args, wl):
     del ws_sm, M_list, out2
     log(f"reduced search at step {wl.steps - 1}: {reduced['kept_blocks']} of {reduced['candidate_blocks']} blocks, "
         f"recall {reduced['recall_reduced_lists']:.4f} (frozen {recalls[-1]:.4f}), {reduced_ms:.3f} ms")
+    refresh = refresh_trajectory(F, torch, wl, args.refresh_tau, steps_qk, q, k, v, bufs, geom, p_heads, w, stream,
+                                 dev, recalls)
     rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
     counts = np.diff(rp)
     nnz = int(rp[-1])
@@ -540,6 +666,7 @@ def run_reuse(args, wl):
         "imbalance_per_head_max_over_mean": float(per_head.max() / per_head.mean()),
         "imbalance_per_xcd_max_over_mean": float(per_xcd.max() / per_xcd.mean()),
         "reduced_search": reduced,
+        "drift_refresh": refresh,
     }
     print(json.dumps(res))
 

@@ -48,6 +48,10 @@ __all__ = [
     "losa_sparse_attn_mass",
     "losa_pooled_mass_workspace",
     "losa_pooled_mass",
+    "losa_qk_drift_workspace",
+    "losa_qk_drift",
+    "losa_merge_lists_workspace",
+    "losa_merge_lists",
     "LOSA_F32",
     "LOSA_BF16",
     "STATUS",
@@ -126,6 +130,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "losa_sparse_attn_mass": ([S, P, P, P, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
         "losa_pooled_mass_workspace": ([S, sz], i32),
         "losa_pooled_mass": ([S, P, P, P, P, ctypes.c_size_t, P], i32),
+        "losa_qk_drift_workspace": ([S, sz], i32),
+        "losa_qk_drift": ([S, P, P, P, P, ctypes.c_double, P, P, P, ctypes.c_size_t, P], i32),
+        "losa_merge_lists_workspace": ([S, sz], i32),
+        "losa_merge_lists": ([S, P, P, P, P, P, P, P, ctypes.c_int64, P, P, ctypes.c_size_t, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -407,3 +415,68 @@ def losa_retained_mass(M, row_ptr, col_idx, tokens: int, q_block: int, k_block: 
     _check(_L().losa_retained_mass(ctypes.byref(g.shape()), _ptr(M), _ptr(row_ptr), _ptr(col_idx), _ptr(out),
                                    _stream(stream)), "losa_retained_mass")
     return out
+
+
+def losa_qk_drift_workspace(geom: Geometry) -> int:
+    n = ctypes.c_size_t()
+    _check(_L().losa_qk_drift_workspace(ctypes.byref(geom.shape()), ctypes.byref(n)), "losa_qk_drift_workspace")
+    return n.value
+
+
+def losa_qk_drift(q, k, q_ref, k_ref, tokens: int, tau: float, q_block: int = 64, k_block: int = 64,
+                  drift=None, refresh=None, ws=None, stream=None):
+    """Drift of Q and K per (batch, head) since the reference step and the heads
+    to refresh: (drift fp64 [B, H, 2], refresh int32 [B, H])."""
+    import torch
+    if q_ref.shape != q.shape or k_ref.shape != k.shape or q_ref.stride() != q.stride() \
+            or k_ref.stride() != k.stride() or {q_ref.dtype, k_ref.dtype, k.dtype} != {q.dtype}:
+        raise ValueError("q_ref/k_ref must match q/k in shape, strides and dtype")
+    g = Geometry.of(q, tokens, q_block, k_block)
+    shp = g.shape(q=q, k=k)
+    nbytes = ctypes.c_size_t()
+    _check(_L().losa_qk_drift_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_qk_drift_workspace")
+    ws = _workspace(nbytes.value, q.device, ws)
+    if drift is None:
+        drift = torch.empty((g.batch, g.heads, 2), dtype=torch.float64, device=q.device)
+    if refresh is None:
+        refresh = torch.empty((g.batch, g.heads), dtype=torch.int32, device=q.device)
+    _check(_L().losa_qk_drift(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(q_ref), _ptr(k_ref), float(tau),
+                              _ptr(drift), _ptr(refresh), _ptr(ws), _nbytes(ws), _stream(stream)), "losa_qk_drift")
+    return drift, refresh
+
+
+def losa_merge_lists_workspace(geom: Geometry) -> int:
+    n = ctypes.c_size_t()
+    _check(_L().losa_merge_lists_workspace(ctypes.byref(geom.shape()), ctypes.byref(n)),
+           "losa_merge_lists_workspace")
+    return n.value
+
+
+def losa_merge_lists(take_b, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, tokens: int, q_block: int, k_block: int,
+                     tokens_alloc: Optional[int] = None, want_order: bool = True, row_ptr=None, col_idx=None,
+                     order=None, ws=None, stream=None):
+    """Lists of the heads flagged in take_b [B, H] from set b, the others from
+    set a: (row_ptr, col_idx, order or None), as losa_select returns them."""
+    import torch
+    B, H = take_b.shape
+    n_q, n_k = -(-int(tokens) // q_block), -(-int(tokens) // k_block)
+    Na = tokens_alloc if tokens_alloc is not None else max(n_q * q_block, n_k * k_block)
+    g = Geometry(B, H, int(tokens), Na, 128, int(q_block), int(k_block), LOSA_BF16)
+    shp = g.shape()
+    nbytes = ctypes.c_size_t()
+    _check(_L().losa_merge_lists_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_merge_lists_workspace")
+    dev = take_b.device
+    ws = _workspace(nbytes.value, dev, ws)
+    rows = g.rows
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(rows * n_k, dtype=torch.int32, device=dev)
+    if want_order and order is None:
+        order = torch.empty(rows, dtype=torch.int32, device=dev)
+    if not want_order:
+        order = None
+    _check(_L().losa_merge_lists(ctypes.byref(shp), _ptr(take_b), _ptr(row_ptr_a), _ptr(col_idx_a),
+                                 _ptr(row_ptr_b), _ptr(col_idx_b), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                 _ptr(order), _ptr(ws), _nbytes(ws), _stream(stream)), "losa_merge_lists")
+    return row_ptr, col_idx, order

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblosa.so")
-SOURCES = ["losa_api.cpp", "losa_mass.hip", "losa_select.hip", "losa_attn.hip", "losa_dense.hip", "losa_pooled.hip"]
+SOURCES = ["losa_api.cpp", "losa_mass.hip", "losa_select.hip", "losa_attn.hip", "losa_dense.hip", "losa_pooled.hip",
+           "losa_drift.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

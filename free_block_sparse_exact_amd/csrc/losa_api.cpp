@@ -256,4 +256,52 @@ losa_status losa_retained_mass(const losa_shape* shape, const float* M, const in
   return hip_status(losa::launch_retained_mass(g, M, row_ptr, col_idx, kept, stream));
 }
 
+losa_status losa_qk_drift_workspace(const losa_shape* shape, size_t* bytes) {
+  Geom g;
+  if (!bytes) return LOSA_ERR_NULL;
+  const losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  *bytes = losa::drift_ws_bytes(g);
+  return LOSA_OK;
+}
+
+losa_status losa_qk_drift(const losa_shape* shape, const void* Q, const void* K, const void* Q_ref,
+                          const void* K_ref, double tau, double* drift, int32_t* refresh, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  Geom g;
+  losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if ((st = check_input(g, Q, g.qs)) != LOSA_OK) return st;
+  if ((st = check_input(g, K, g.ks)) != LOSA_OK) return st;
+  if ((st = check_input(g, Q_ref, g.qs)) != LOSA_OK) return st;
+  if ((st = check_input(g, K_ref, g.ks)) != LOSA_OK) return st;
+  if (!drift || !ws) return LOSA_ERR_NULL;
+  if (!(tau == tau)) return LOSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(drift) & 7u) != 0 || (reinterpret_cast<uintptr_t>(refresh) & 3u) != 0)
+    return LOSA_ERR_INVALID_ARG;
+  if (ws_bytes < losa::drift_ws_bytes(g) || !aligned16(ws)) return LOSA_ERR_WORKSPACE;
+  return hip_status(losa::launch_qk_drift(g, Q, K, Q_ref, K_ref, tau, drift, refresh, ws, stream));
+}
+
+losa_status losa_merge_lists_workspace(const losa_shape* shape, size_t* bytes) {
+  return losa_select_workspace(shape, bytes);
+}
+
+losa_status losa_merge_lists(const losa_shape* shape, const int32_t* take_b, const int32_t* row_ptr_a,
+                             const int32_t* col_idx_a, const int32_t* row_ptr_b, const int32_t* col_idx_b,
+                             int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if (!take_b || !row_ptr_a || !col_idx_a || !row_ptr_b || !col_idx_b || !row_ptr || !col_idx || !ws)
+    return LOSA_ERR_NULL;
+  if (col_capacity < (int64_t)g.rows() * g.nk) return LOSA_ERR_CAPACITY;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return LOSA_ERR_WORKSPACE;
+  losa::SelectWs layout;
+  if (ws_bytes < losa::select_ws_bytes(g, &layout, reinterpret_cast<char*>(ws))) return LOSA_ERR_WORKSPACE;
+  return hip_status(losa::launch_merge_lists(g, take_b, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, row_ptr,
+                                             col_idx, order, layout, stream));
+}
+
 }  // extern "C"

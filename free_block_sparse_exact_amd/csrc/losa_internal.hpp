@@ -54,6 +54,19 @@ constexpr int kOrderChunk = 256;  // rows per placement chunk for the budget ord
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base);
 hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr,
                          int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t stream);
+// Row offsets and work order from the kept counts in ws.counts (shared by
+// the selector and the list merge).
+void launch_offsets_and_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, int32_t* order,
+                              hipStream_t stream);
+// Per-head choice between two list sets (selector workspace).
+hipError_t launch_merge_lists(const Geom& g, const int32_t* take_b, const int32_t* rpa, const int32_t* cia,
+                              const int32_t* rpb, const int32_t* cib, int32_t* row_ptr, int32_t* col_idx,
+                              int32_t* order, const SelectWs& ws, hipStream_t stream);
+
+// Query-key drift per head since a reference step.
+size_t drift_ws_bytes(const Geom& g);
+hipError_t launch_qk_drift(const Geom& g, const void* Q, const void* K, const void* Qr, const void* Kr, double tau,
+                           double* drift, int32_t* refresh, void* ws, hipStream_t stream);
 
 hipError_t launch_retained_mass(const Geom& g, const float* M, const int32_t* row_ptr,
                                 const int32_t* col_idx, float* kept, hipStream_t stream);

@@ -646,6 +646,37 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
   }
 }
 
+// List merge: row r takes its count from set b when its head is flagged,
+// from set a otherwise (clamped to [0, nk], so a malformed count cannot
+// place a row outside the output).
+__global__ __launch_bounds__(256) void pick_counts_kernel(int rows, int nq, int nk, const int32_t* __restrict__ take_b,
+                                                          const int32_t* __restrict__ rpa,
+                                                          const int32_t* __restrict__ rpb,
+                                                          int32_t* __restrict__ counts) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const int32_t* rp = take_b[r / nq] ? rpb : rpa;
+  counts[r] = min(max(rp[r + 1] - rp[r], 0), nk);
+}
+
+// One wave per row: copy the chosen set's indices to row_ptr[r].
+__global__ __launch_bounds__(256) void copy_lists_kernel(int rows, int nq, const int32_t* __restrict__ take_b,
+                                                         const int32_t* __restrict__ rpa,
+                                                         const int32_t* __restrict__ cia,
+                                                         const int32_t* __restrict__ rpb,
+                                                         const int32_t* __restrict__ cib,
+                                                         const int32_t* __restrict__ counts,
+                                                         const int32_t* __restrict__ row_ptr,
+                                                         int32_t* __restrict__ col_idx) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const bool b = take_b[r / nq] != 0;
+  const int32_t* src = (b ? cib : cia) + (b ? rpb : rpa)[r];
+  int32_t* dst = col_idx + row_ptr[r];
+  const int n = counts[r];
+  for (int t = threadIdx.x & 63; t < n; t += 64) dst[t] = src[t];
+}
+
 __global__ __launch_bounds__(64) void retained_kernel(const Geom g, const float* __restrict__ M,
                                                       const int32_t* __restrict__ row_ptr,
                                                       const int32_t* __restrict__ col_idx,
@@ -706,6 +737,27 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
     auto cut = per_t <= 12 ? cut_kernel<12> : cut_kernel<kMaxPer>;
     hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.kappa);
   }
+  launch_offsets_and_order(g, ws, row_ptr, order, st);
+  hipLaunchKernelGGL(compact_kernel, dim3(rows), dim3(kSelThreads), 0, st, g, M, (const uint64_t*)ws.kappa,
+                     (const int32_t*)row_ptr, col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_lists(const Geom& g, const int32_t* take_b, const int32_t* rpa, const int32_t* cia,
+                              const int32_t* rpb, const int32_t* cib, int32_t* row_ptr, int32_t* col_idx,
+                              int32_t* order, const SelectWs& ws, hipStream_t st) {
+  const int rows = g.rows();
+  hipLaunchKernelGGL(pick_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, g.nq, g.nk, take_b, rpa,
+                     rpb, ws.counts);
+  launch_offsets_and_order(g, ws, row_ptr, order, st);
+  hipLaunchKernelGGL(copy_lists_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, rows, g.nq, take_b, rpa, cia, rpb,
+                     cib, (const int32_t*)ws.counts, (const int32_t*)row_ptr, col_idx);
+  return hipGetLastError();
+}
+
+// From the kept counts in ws.counts: row_ptr, and (order != NULL) the work order.
+void launch_offsets_and_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, int32_t* order, hipStream_t st) {
+  const int rows = g.rows();
   const size_t hist_lds = (size_t)(g.nk + 1) * sizeof(int);
   hipLaunchKernelGGL(chunk_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
                      g.nq, ws.cph, g.nk, ws.chunk_hist, ws.chunk_sum, ws.done);
@@ -714,9 +766,6 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
   hipLaunchKernelGGL(place_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
                      g.nq, ws.cph, g.nk, (const int32_t*)ws.chunk_hist, (const int32_t*)ws.bucket,
                      (const int32_t*)ws.chunk_sum, row_ptr, order);
-  hipLaunchKernelGGL(compact_kernel, dim3(rows), dim3(kSelThreads), 0, st, g, M, (const uint64_t*)ws.kappa,
-                     (const int32_t*)row_ptr, col_idx);
-  return hipGetLastError();
 }
 
 hipError_t launch_retained_mass(const Geom& g, const float* M, const int32_t* row_ptr, const int32_t* col_idx,

@@ -13,10 +13,16 @@
  *                     (Methodology Summary, sparse attention with a frozen
  *                     pattern)
  *
+ * The further calls below (each cites the page it follows) build the
+ * patterns in other ways or maintain them: dense attention with the masses
+ * in one pass, masses within given lists, pooled proxy masses, the query-key
+ * drift that triggers a refresh, and the per-head merge of refreshed lists.
+ *
  * Conventions shared by every call
  * --------------------------------
- * Memory.  Every pointer named Q, K, V, O, M, row_ptr, col_idx, order, ws,
- *   kept is DEVICE memory owned by the caller; the library allocates nothing
+ * Memory.  Every pointer named Q, K, V, O, M, P, row_ptr, col_idx, order,
+ *   ws, kept, Q_ref, K_ref, drift, refresh, take_b (and the _a/_b list sets)
+ *   is DEVICE memory owned by the caller; the library allocates nothing
  *   and keeps no pointer after a call returns.  The only host pointers are the
  *   losa_shape, the p array of losa_select and the size_t out-parameters.
  * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
@@ -270,6 +276,55 @@ losa_status losa_pooled_mass(const losa_shape* shape, const void* Q, const void*
  * ------------------------------------------------------------------------ */
 losa_status losa_retained_mass(const losa_shape* shape, const float* M, const int32_t* row_ptr,
                                const int32_t* col_idx, float* kept, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Query-key drift since a reference step, and the heads to refresh.
+ * HASTE page (temporal mask reuse): mask prediction is skipped while the
+ * queries and keys have drifted little since it was last made.  The page
+ * gives no measure; read here as, for head g = b*heads + h over its valid
+ * tokens,
+ *   drift[2g]     = ||Q_g - Q_ref_g||_F / ||Q_ref_g||_F,
+ *   drift[2g + 1] = ||K_g - K_ref_g||_F / ||K_ref_g||_F
+ * (0/0 = 0, x/0 = +inf for x > 0, NaN when a valid token holds NaN), and
+ * refresh[g] = 1 when drift[2g] > tau or drift[2g + 1] > tau, else 0.
+ * Q_ref/K_ref are the queries and keys of the step at which head g's lists
+ * were built; a refreshed head takes the current ones as its new reference
+ * (a device copy by the caller).
+ *
+ * Q, K, Q_ref, K_ref: as for losa_block_mass; Q_ref uses q_stride and K_ref
+ *    k_stride.  Padding rows are not read.
+ * tau: any value but NaN (LOSA_ERR_INVALID_ARG).
+ * drift: fp64 [2 * batch*heads], 8-byte aligned.
+ * refresh: int32 [batch*heads], or NULL (not written).
+ * ws: at least *bytes from losa_qk_drift_workspace (per-workgroup partial
+ *    sums, 32 bytes per 8192 elements of each tensor).
+ * Arithmetic: differences, squares and sums in fp64, in a fixed order (no
+ * atomics): the result is the same on every run.
+ * ------------------------------------------------------------------------ */
+losa_status losa_qk_drift_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_qk_drift(const losa_shape* shape, const void* Q, const void* K, const void* Q_ref,
+                          const void* K_ref, double tau, double* drift, int32_t* refresh, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-head merge of two list sets: the lists of the heads refreshed by a
+ * drift-triggered rebuild (set b) replace theirs in the frozen set (set a);
+ * the other heads keep set a's lists.  Row r of head g = r / n_q takes its
+ * list from set b when take_b[g] != 0, from set a otherwise.
+ *
+ * take_b: int32 [batch*heads] (e.g. losa_qk_drift's refresh).
+ * row_ptr_a/col_idx_a, row_ptr_b/col_idx_b: CSR lists as losa_select writes
+ *    them (counts outside [0, n_k] are clamped to it); neither may overlap
+ *    the outputs.
+ * row_ptr/col_idx/col_capacity/order: outputs, as for losa_select; order
+ *    receives the work order of the merged lists.
+ * ws: at least *bytes from losa_merge_lists_workspace.
+ * ------------------------------------------------------------------------ */
+losa_status losa_merge_lists_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_merge_lists(const losa_shape* shape, const int32_t* take_b, const int32_t* row_ptr_a,
+                             const int32_t* col_idx_a, const int32_t* row_ptr_b, const int32_t* col_idx_b,
+                             int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -60,8 +60,8 @@ notes of the repository):
   was last made; the page gives no measure): per (batch, head), the drift of
   Q is ||Q - Q_ref||_F / ||Q_ref||_F over the valid tokens, Q_ref being the
   queries of the step at which the head's lists were built, likewise for K
-  (0/0 = 0, x/0 = inf for x > 0); a head's lists are rebuilt when the larger
-  of its two drifts exceeds a threshold tau, and kept otherwise.
+  (0/0 = 0, x/0 = inf for x > 0, NaN stays NaN); a head's lists are rebuilt
+  when either drift exceeds a threshold tau, and kept otherwise.
 
 Row numbering: row r = (b * H + h) * n_q + i for batch b, head h, query block i.
 Inputs are fp64 arrays [B, H, N_alloc, d] holding the exact values the GPU sees.
@@ -429,14 +429,20 @@ def qk_drift(q: np.ndarray, k: np.ndarray, q_ref: np.ndarray, k_ref: np.ndarray,
         diff = np.asarray(x, np.float64)[:, :, :n_valid] - np.asarray(xr, np.float64)[:, :, :n_valid]
         num = np.sqrt(np.sum(diff * diff, axis=(2, 3)))
         den = np.sqrt(np.sum(np.asarray(xr, np.float64)[:, :, :n_valid] ** 2, axis=(2, 3)))
-        with np.errstate(divide="ignore", invalid="ignore"):
-            out[:, :, t] = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
+        for idx in np.ndindex(num.shape):
+            n, m = num[idx], den[idx]
+            if m > 0:
+                out[idx + (t,)] = n / m
+            elif m == 0:
+                out[idx + (t,)] = math.inf if n > 0 else n  # 0/0 = 0; NaN stays NaN
+            else:
+                out[idx + (t,)] = m  # NaN
     return out
 
 
 def refresh_heads(drift: np.ndarray, tau: float) -> np.ndarray:
-    """Heads whose lists are rebuilt: the larger of the two drifts exceeds tau."""
-    return np.max(drift, axis=-1) > tau
+    """Heads whose lists are rebuilt: either drift exceeds tau (a NaN drift never does)."""
+    return np.any(drift > tau, axis=-1)
 
 
 def merge_lists(rp_a: np.ndarray, ci_a: np.ndarray, rp_b: np.ndarray, ci_b: np.ndarray,

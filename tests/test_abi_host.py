@@ -208,3 +208,57 @@ def test_sparse_attn_mass_errors(lib):
     for kw in (dict(dtype=F.LOSA_F32), dict(q_block=32)):
         assert lib.losa_sparse_attn_mass_workspace(ctypes.byref(shape(**kw)), ctypes.byref(n)) == UNSUPPORTED
         assert call(shp=shape(**kw)) == UNSUPPORTED
+
+
+@no_gpu_only
+def test_qk_drift_errors(lib):
+    s = shape()
+    n = ctypes.c_size_t()
+    assert lib.losa_qk_drift_workspace(ctypes.byref(s), ctypes.byref(n)) == OK and n.value > 0
+
+    def drift(Qr=FAKE, Kr=FAKE, tau=0.1, d=FAKE, refresh=FAKE, ws=FAKE, ws_bytes=1 << 40, shp=s):
+        return lib.losa_qk_drift(ctypes.byref(shp), FAKE, FAKE, Qr, Kr, tau, d, refresh, ws, ws_bytes, None)
+
+    assert drift(Qr=None) == NULL
+    assert drift(Kr=None) == NULL
+    assert drift(d=None) == NULL
+    assert drift(ws=None) == NULL
+    assert drift(Qr=FAKE + 2) == INVALID          # not 16-byte aligned
+    assert drift(tau=float("nan")) == INVALID
+    assert drift(d=FAKE + 4) == INVALID           # fp64 output not 8-byte aligned
+    assert drift(refresh=FAKE + 2) == INVALID
+    assert drift(ws_bytes=n.value - 1) == WORKSPACE
+    bad = shape()
+    bad.q_stride[2] = 100                         # token stride not a multiple of 8 elements
+    assert drift(shp=bad) == INVALID
+
+
+@no_gpu_only
+def test_merge_lists_errors(lib):
+    s = shape()
+    rows, nk = 2 * 16, 16
+    n = ctypes.c_size_t()
+    assert lib.losa_merge_lists_workspace(ctypes.byref(s), ctypes.byref(n)) == OK
+    sel = ctypes.c_size_t()
+    assert lib.losa_select_workspace(ctypes.byref(s), ctypes.byref(sel)) == OK and n.value == sel.value
+
+    def merge(take=FAKE, rpa=FAKE, cib=FAKE, rp=FAKE, cap=rows * nk, ws=0x100000, ws_bytes=1 << 40):
+        return lib.losa_merge_lists(ctypes.byref(s), take, rpa, FAKE, FAKE, cib, rp, FAKE, cap, None, ws, ws_bytes,
+                                    None)
+
+    assert merge(take=None) == NULL
+    assert merge(rpa=None) == NULL
+    assert merge(cib=None) == NULL
+    assert merge(rp=None) == NULL
+    assert merge(cap=rows * nk - 1) == CAPACITY
+    assert merge(ws=0x100010) == WORKSPACE
+    assert merge(ws_bytes=n.value - 1) == WORKSPACE
+
+
+def test_binding_names_match_header():
+    """Every call the header declares has a Python binding of the same name."""
+    for n in declared_functions():
+        if n != "losa_status_string":
+            assert hasattr(F, n), n
+    for n in F.__all__:
+        assert hasattr(F, n), n

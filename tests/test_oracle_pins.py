@@ -535,9 +535,19 @@ def test_qk_drift_brute_force():
 
 
 def test_refresh_rule():
-    dr = np.array([[[0.1, 0.3], [0.3, 0.1], [0.2, 0.2], [0.0, np.inf]]])
-    assert O.refresh_heads(dr, 0.2).tolist() == [[True, True, False, True]]
-    assert O.refresh_heads(dr, 0.3).tolist() == [[False, False, False, True]]
+    dr = np.array([[[0.1, 0.3], [0.3, 0.1], [0.2, 0.2], [0.0, np.inf], [np.nan, 0.25], [np.nan, 0.0]]])
+    assert O.refresh_heads(dr, 0.2).tolist() == [[True, True, False, True, True, False]]
+    assert O.refresh_heads(dr, 0.3).tolist() == [[False, False, False, True, False, False]]
+
+
+def test_qk_drift_nan_tokens():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((1, 2, 6, 4))
+    q2 = q.copy()
+    q2[0, 0, 1, 2] = np.nan  # a NaN in a valid token of head 0 only
+    d = O.qk_drift(q2, q, q, q, 6)
+    assert np.isnan(d[0, 0, 0]) and d[0, 1, 0] == 0 and np.all(d[..., 1] == 0)
+    assert np.isnan(O.qk_drift(q, q, q2, q, 6)[0, 0, 0])
 
 
 def test_merge_lists():
