@@ -751,6 +751,10 @@ TRACE_KERNELS = [
     ("compact_kernel", "compact_kernel", "losa_select"),
     ("place_kernel", "place_kernel", "losa_select"),
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
+    ("drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),
+    ("drift_final_kernel", "drift_final_kernel", "losa_qk_drift"),
+    ("pick_counts_kernel", "pick_counts_kernel", "losa_merge_lists"),
+    ("copy_lists_kernel", "copy_lists_kernel", "losa_merge_lists"),
 ]
 
 
