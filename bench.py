@@ -746,10 +746,10 @@ TRACE_KERNELS = [
     ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
     ("cut_wave_kernel", "cut_wave_kernel", "losa_select"),
     ("cut_kernel", "cut_kernel", "losa_select"),
-    ("chunk_kernel", "chunk_kernel", "losa_select"),
-    ("offsets_kernel", "offsets_kernel", "losa_select"),
+    ("chunk_kernel", "chunk_kernel", "losa_select, losa_merge_lists"),
+    ("offsets_kernel", "offsets_kernel", "losa_select, losa_merge_lists"),
     ("compact_kernel", "compact_kernel", "losa_select"),
-    ("place_kernel", "place_kernel", "losa_select"),
+    ("place_kernel", "place_kernel", "losa_select, losa_merge_lists"),
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
     ("drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),
     ("drift_final_kernel", "drift_final_kernel", "losa_qk_drift"),
