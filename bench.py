@@ -234,20 +234,20 @@ def main():
     stream = torch.cuda.current_stream()
     p = wl.p
 
-    def step(ev=None):
+    def step(ev=None, st=stream):
         if ev:
-            ev[0].record(stream)
-        F.losa_block_mass(q, k, N, R, C, out=bufs.M, ws=bufs.ws_mass, stream=stream)
+            ev[0].record(st)
+        F.losa_block_mass(q, k, N, R, C, out=bufs.M, ws=bufs.ws_mass, stream=st)
         if ev:
-            ev[1].record(stream)
+            ev[1].record(st)
         F.losa_select(bufs.M, p, N, R, C, tokens_alloc=Na, row_ptr=bufs.row_ptr, col_idx=bufs.col_idx,
-                      order=bufs.order, ws=bufs.ws_sel, stream=stream)
+                      order=bufs.order, ws=bufs.ws_sel, stream=st)
         if ev:
-            ev[2].record(stream)
+            ev[2].record(st)
         F.losa_sparse_attn(q, k, v, bufs.row_ptr, bufs.col_idx, bufs.order, N, R, C, out=bufs.out,
-                           ws=bufs.ws_attn, stream=stream)
+                           ws=bufs.ws_attn, stream=st)
         if ev:
-            ev[3].record(stream)
+            ev[3].record(st)
 
     for _ in range(args.warmup):
         step()
@@ -262,6 +262,7 @@ def main():
     t1 = time.perf_counter()
     log(f"timed {args.steps} steps")
     ms_step = (t1 - t0) * 1e3 / args.steps
+    graph_ms = graph_step_ms(torch, step, stream, args.steps)
     mass_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     sel_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
@@ -343,6 +344,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "graph_ms_per_step": graph_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -410,6 +412,30 @@ def _drift_step(s):
     """One step's drifted Q/K (bf16 bit patterns) from the layer set before the fork."""
     import synthetic as S
     return S.drift_qk(_REUSE_LAYER, s)
+
+
+def graph_step_ms(torch, step, stream, steps):
+    """The same step captured once in a HIP graph and replayed: every call is
+    capture-safe (no allocation, no memset, state only in the caller's
+    buffers), so the replay drops the host's per-call work and launch gaps."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(st=side)              # one eager run on the capture stream first
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(st=torch.cuda.current_stream())
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def refresh_calls(F, torch, q, k, bufs, geom, wl, stream, dev):
