@@ -55,6 +55,14 @@ notes of the repository):
   M_L(i, j) = mean over valid rows of block i of the sum over block j's
   tokens of it, for j in L; 0 for blocks outside L.  A row with a non-empty
   list sums to 1; with every block listed M_L = M.
+* Online block thresholding (the Sol-Attn page: critical blocks are picked
+  by comparing block proxy scores against a threshold during the online
+  softmax pass, giving dynamic budgets; the page gives no rule): visiting a
+  row's key blocks in index order, as an online-softmax pass does, block j
+  is kept when its mass (exact or proxy, sanitised as for top-p) is at least
+  theta times the largest mass seen so far, block j included -- in scores,
+  within ln(1/theta) of the running maximum.  theta in (0, 1]; the
+  comparison is made in fp64 on the fp32 masses.
 * Drift-triggered refresh (the HASTE page's temporal mask reuse: mask
   prediction is skipped while queries and keys have drifted little since it
   was last made; the page gives no measure): per (batch, head), the drift of
@@ -91,6 +99,8 @@ __all__ = [
     "sparse_attention",
     "sparse_attention_rows",
     "budget_order",
+    "select_threshold_row",
+    "select_threshold",
     "qk_drift",
     "refresh_heads",
     "merge_lists",
@@ -295,6 +305,36 @@ def select_contract(M32: np.ndarray, p) -> Tuple[np.ndarray, np.ndarray]:
     np.cumsum(counts, out=row_ptr[1:])
     col_idx = np.concatenate(cols) if cols else np.zeros(0, np.int32)
     return row_ptr, col_idx
+
+
+def select_threshold_row(m32: np.ndarray, theta: float) -> np.ndarray:
+    """Kept blocks of one row under online thresholding (module header): in
+    index order, keep j when m_j >= theta * max(m_0 .. m_j)."""
+    m = sanitize_masses(m32).astype(np.float64)
+    kept = []
+    running = 0.0
+    for j in range(m.size):
+        running = max(running, float(m[j]))
+        if float(m[j]) >= float(theta) * running:
+            kept.append(j)
+    return np.asarray(kept, np.int64)
+
+
+def select_threshold(M32: np.ndarray, theta) -> Tuple[np.ndarray, np.ndarray]:
+    """CSR lists of online thresholding for every row of M32 [B, H, n_q, n_k];
+    ``theta`` is a scalar or one value per head."""
+    B, H, n_q, n_k = M32.shape
+    t_h = np.broadcast_to(np.asarray(theta, dtype=np.float64), (H,))
+    row_ptr = [0]
+    cols: List[np.ndarray] = []
+    for b in range(B):
+        for h in range(H):
+            for i in range(n_q):
+                kept = select_threshold_row(M32[b, h, i], float(t_h[h]))
+                cols.append(kept.astype(np.int32))
+                row_ptr.append(row_ptr[-1] + kept.size)
+    col_idx = np.concatenate(cols) if cols else np.zeros(0, np.int32)
+    return np.asarray(row_ptr, np.int64), col_idx
 
 
 def select_float(M: np.ndarray, p) -> Tuple[np.ndarray, np.ndarray, List[Tuple[int, float]]]:

@@ -561,3 +561,52 @@ def test_merge_lists():
     for take, (r0, c0) in (([0, 0], (rp_a, ci_a)), ([1, 1], (rp_b, ci_b))):
         rp, ci = O.merge_lists(rp_a, ci_a, rp_b, ci_b, np.array(take, bool), 2)
         assert np.array_equal(rp, r0) and np.array_equal(ci, c0)
+
+
+# ------------------------------------------------------------ online thresholding
+
+def test_threshold_hand_worked():
+    m = np.array([0.1, 0.5, 0.2, 0.6, 0.05], np.float32)
+    assert O.select_threshold_row(m, 0.5).tolist() == [0, 1, 3]     # 0.2 < 0.25, 0.05 < 0.3
+    assert O.select_threshold_row(m, 0.3).tolist() == [0, 1, 2, 3]  # 0.2 >= 0.15
+    assert O.select_threshold_row(m, 1.0).tolist() == [0, 1, 3]     # the running maxima
+    assert O.select_threshold_row(m, 1e-9).tolist() == [0, 1, 2, 3, 4]
+    # sanitised: NaN and negatives count as 0; equality keeps
+    bad = np.array([np.nan, 0.0, 0.2, -1.0, 0.1], np.float32)
+    assert O.select_threshold_row(bad, 0.5).tolist() == [0, 1, 2, 4]
+    # a flat row keeps everything, a one-hot row keeps the blocks up to its peak
+    assert O.select_threshold_row(np.full(6, 0.25, np.float32), 0.9).tolist() == list(range(6))
+    assert O.select_threshold_row(np.eye(1, 6, 3, dtype=np.float32)[0], 0.5).tolist() == [0, 1, 2, 3]
+
+
+def test_threshold_log_domain_and_monotone():
+    """On softmax masses, keeping m_j >= theta * running max is keeping scores
+    within ln(1/theta) of the running maximum score; a larger theta keeps a
+    subset."""
+    rng = np.random.default_rng(41)
+    for _ in range(50):
+        n = int(rng.integers(1, 200))
+        s = rng.standard_normal(n) * rng.uniform(0.5, 6.0)
+        m = np.exp(s - s.max())
+        m32 = (m / m.sum()).astype(np.float32)
+        s32 = np.log(m32.astype(np.float64))            # the scores the fp32 masses carry
+        for theta in (0.01, 0.1, 0.5):
+            run = np.maximum.accumulate(s32)
+            margin = s32 - (run + math.log(theta))
+            if np.min(np.abs(margin)) < 1e-9:
+                continue
+            assert O.select_threshold_row(m32, theta).tolist() == np.flatnonzero(margin > 0).tolist()
+        a, b = O.select_threshold_row(m32, 0.05), O.select_threshold_row(m32, 0.4)
+        assert set(b.tolist()) <= set(a.tolist()) and 0 in b.tolist()
+
+
+def test_threshold_csr_and_per_head():
+    rng = np.random.default_rng(42)
+    M = rng.random((2, 3, 4, 7)).astype(np.float32)
+    rp, ci = O.select_threshold(M, [0.2, 0.6, 0.9])
+    assert rp[0] == 0 and len(rp) == 2 * 3 * 4 + 1
+    for b in range(2):
+        for h in range(3):
+            for i in range(4):
+                r = O.row_id(b, h, i, 3, 4)
+                assert ci[rp[r]:rp[r + 1]].tolist() == O.select_threshold_row(M[b, h, i], [0.2, 0.6, 0.9][h]).tolist()
