@@ -369,6 +369,7 @@ def main():
 
 
 ROUTING_P = (0.9, 0.95, 0.99, 0.995, 0.999)
+ROUTING_THETA = (0.1, 0.03, 0.01, 0.003, 0.001)
 
 
 def pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev):
@@ -400,8 +401,30 @@ def pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev):
             nnz = int(bufs.row_ptr[-1].item())
             out[name]["recall"].append(float((kept[:, 0] * w).sum() / (kept[:, 1] * w).sum()))
             out[name]["coverage"].append(nnz / float(rows * nk))
-    out["note"] = ("lists from exact masses vs from pooled proxy masses (block-mean Q/K, block-weighted softmax); "
-                   "recall measured under the exact masses")
+    # Online block thresholding (the Sol-Attn page's block thresholding during
+    # the online pass): the same two inputs, kept when at least theta times the
+    # running maximum.
+    thr = {"theta": list(ROUTING_THETA), "exact": {"recall": [], "coverage": []},
+           "pooled": {"recall": [], "coverage": []}}
+    for theta in ROUTING_THETA:
+        for name, src in (("exact", bufs.M), ("pooled", P)):
+            F.losa_select_threshold(src, theta, N, R, C, tokens_alloc=geom.tokens_alloc, row_ptr=bufs.row_ptr,
+                                    col_idx=bufs.col_idx, order=bufs.order, ws=bufs.ws_sel, stream=stream)
+            F.losa_retained_mass(bufs.M, bufs.row_ptr, bufs.col_idx, N, R, C, out=bufs.kept, stream=stream)
+            kept = bufs.kept.cpu().numpy().astype(np.float64)
+            nnz = int(bufs.row_ptr[-1].item())
+            thr[name]["recall"].append(float((kept[:, 0] * w).sum() / (kept[:, 1] * w).sum()))
+            thr[name]["coverage"].append(nnz / float(rows * nk))
+    for e0, e1 in evs:
+        e0.record(stream)
+        F.losa_select_threshold(P, ROUTING_THETA[2], N, R, C, tokens_alloc=geom.tokens_alloc, row_ptr=bufs.row_ptr,
+                                col_idx=bufs.col_idx, order=bufs.order, ws=bufs.ws_sel, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    thr["select_threshold_ms"] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[1:]]))
+    out["threshold"] = thr
+    out["note"] = ("lists from exact masses vs from pooled proxy masses (block-mean Q/K, block-weighted softmax), "
+                   "by top-p and by online thresholding; recall measured under the exact masses")
     return out
 
 
@@ -772,13 +795,14 @@ TRACE_KERNELS = [
     ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
     ("cut_wave_kernel", "cut_wave_kernel", "losa_select"),
     ("cut_kernel", "cut_kernel", "losa_select"),
-    ("chunk_kernel", "chunk_kernel", "losa_select, losa_merge_lists"),
-    ("offsets_kernel", "offsets_kernel", "losa_select, losa_merge_lists"),
+    ("chunk_kernel", "chunk_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
+    ("offsets_kernel", "offsets_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("compact_kernel", "compact_kernel", "losa_select"),
-    ("place_kernel", "place_kernel", "losa_select, losa_merge_lists"),
+    ("place_kernel", "place_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
     ("drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),
     ("drift_final_kernel", "drift_final_kernel", "losa_qk_drift"),
+    ("threshold_kernel", "threshold_kernel", "losa_select_threshold"),
     ("pick_counts_kernel", "pick_counts_kernel", "losa_merge_lists"),
     ("copy_lists_kernel", "copy_lists_kernel", "losa_merge_lists"),
 ]

@@ -48,6 +48,8 @@ __all__ = [
     "losa_sparse_attn_mass",
     "losa_pooled_mass_workspace",
     "losa_pooled_mass",
+    "losa_select_threshold_workspace",
+    "losa_select_threshold",
     "losa_qk_drift_workspace",
     "losa_qk_drift",
     "losa_merge_lists_workspace",
@@ -130,6 +132,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "losa_sparse_attn_mass": ([S, P, P, P, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
         "losa_pooled_mass_workspace": ([S, sz], i32),
         "losa_pooled_mass": ([S, P, P, P, P, ctypes.c_size_t, P], i32),
+        "losa_select_threshold_workspace": ([S, sz], i32),
+        "losa_select_threshold": ([S, P, ctypes.POINTER(ctypes.c_double), i32, P, P, ctypes.c_int64, P, P,
+                                   ctypes.c_size_t, P], i32),
         "losa_qk_drift_workspace": ([S, sz], i32),
         "losa_qk_drift": ([S, P, P, P, P, ctypes.c_double, P, P, P, ctypes.c_size_t, P], i32),
         "losa_merge_lists_workspace": ([S, sz], i32),
@@ -415,6 +420,48 @@ def losa_retained_mass(M, row_ptr, col_idx, tokens: int, q_block: int, k_block: 
     _check(_L().losa_retained_mass(ctypes.byref(g.shape()), _ptr(M), _ptr(row_ptr), _ptr(col_idx), _ptr(out),
                                    _stream(stream)), "losa_retained_mass")
     return out
+
+
+def losa_select_threshold_workspace(geom: Geometry) -> int:
+    n = ctypes.c_size_t()
+    _check(_L().losa_select_threshold_workspace(ctypes.byref(geom.shape()), ctypes.byref(n)),
+           "losa_select_threshold_workspace")
+    return n.value
+
+
+def losa_select_threshold(M, theta: Union[float, Sequence[float]], tokens: int, q_block: int, k_block: int,
+                          tokens_alloc: Optional[int] = None, want_order: bool = True, row_ptr=None, col_idx=None,
+                          order=None, ws=None, stream=None):
+    """Online block thresholding lists (block j kept when its mass is at least
+    theta times the running maximum): (row_ptr, col_idx, order or None), as
+    losa_select returns them."""
+    import torch
+    B, H, nq, nk = M.shape
+    Na = tokens_alloc if tokens_alloc is not None else max(nq * q_block, nk * k_block)
+    g = Geometry(B, H, int(tokens), Na, 128, int(q_block), int(k_block), LOSA_BF16)
+    if g.n_q != nq or g.n_k != nk:
+        raise ValueError("M does not match tokens/q_block/k_block")
+    shp = g.shape()
+    tv = [float(theta)] if isinstance(theta, (int, float)) else [float(x) for x in theta]
+    tarr = (ctypes.c_double * len(tv))(*tv)
+    nbytes = ctypes.c_size_t()
+    _check(_L().losa_select_threshold_workspace(ctypes.byref(shp), ctypes.byref(nbytes)),
+           "losa_select_threshold_workspace")
+    dev = M.device
+    ws = _workspace(nbytes.value, dev, ws)
+    rows = g.rows
+    if row_ptr is None:
+        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(rows * nk, dtype=torch.int32, device=dev)
+    if want_order and order is None:
+        order = torch.empty(rows, dtype=torch.int32, device=dev)
+    if not want_order:
+        order = None
+    _check(_L().losa_select_threshold(ctypes.byref(shp), _ptr(M), tarr, len(tv), _ptr(row_ptr), _ptr(col_idx),
+                                      col_idx.numel(), _ptr(order), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "losa_select_threshold")
+    return row_ptr, col_idx, order
 
 
 def losa_qk_drift_workspace(geom: Geometry) -> int:

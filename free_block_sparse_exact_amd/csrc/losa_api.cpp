@@ -256,6 +256,33 @@ losa_status losa_retained_mass(const losa_shape* shape, const float* M, const in
   return hip_status(losa::launch_retained_mass(g, M, row_ptr, col_idx, kept, stream));
 }
 
+losa_status losa_select_threshold_workspace(const losa_shape* shape, size_t* bytes) {
+  return losa_select_workspace(shape, bytes);
+}
+
+losa_status losa_select_threshold(const losa_shape* shape, const float* M, const double* theta, int32_t n_theta,
+                                  int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  Geom g;
+  losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if (!M || !theta || !row_ptr || !col_idx || !ws) return LOSA_ERR_NULL;
+  if (n_theta != 1 && n_theta != g.H) return LOSA_ERR_INVALID_ARG;
+  if (n_theta > 1 && n_theta > LOSA_MAX_HEADS_P) return LOSA_ERR_UNSUPPORTED;
+  losa::ThetaTable tt;
+  memset(&tt, 0, sizeof tt);
+  tt.per_head = n_theta > 1;
+  for (int t = 0; t < n_theta; ++t) {
+    if (!(theta[t] > 0.0 && theta[t] <= 1.0)) return LOSA_ERR_INVALID_ARG;
+    tt.t[t] = theta[t];
+  }
+  if (col_capacity < (int64_t)g.rows() * g.nk) return LOSA_ERR_CAPACITY;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return LOSA_ERR_WORKSPACE;
+  losa::SelectWs layout;
+  if (ws_bytes < losa::select_ws_bytes(g, &layout, reinterpret_cast<char*>(ws))) return LOSA_ERR_WORKSPACE;
+  return hip_status(losa::launch_select_threshold(g, M, tt, row_ptr, col_idx, order, layout, stream));
+}
+
 losa_status losa_qk_drift_workspace(const losa_shape* shape, size_t* bytes) {
   Geom g;
   if (!bytes) return LOSA_ERR_NULL;

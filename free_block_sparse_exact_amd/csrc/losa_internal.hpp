@@ -54,6 +54,13 @@ constexpr int kOrderChunk = 256;  // rows per placement chunk for the budget ord
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base);
 hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr,
                          int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t stream);
+// Online block thresholding: per-head theta (or one for all) by value.
+struct ThetaTable {
+  double t[kMaxHeadsP];
+  int per_head;  // 0: t[0] for every head
+};
+hipError_t launch_select_threshold(const Geom& g, const float* M, const ThetaTable& tt, int32_t* row_ptr,
+                                   int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t stream);
 // Row offsets and work order from the kept counts in ws.counts (shared by
 // the selector and the list merge).
 void launch_offsets_and_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, int32_t* order,

@@ -646,6 +646,46 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
   }
 }
 
+// Online block thresholding (the Sol-Attn page's block thresholding during
+// the online-softmax pass): visiting the row's key blocks in index order,
+// block j is kept when m_j >= theta * max(m_0 .. m_j), on the sanitised fp32
+// masses, compared in fp64.  One wave per row, 64 blocks per step: coalesced
+// loads, an inclusive max scan across the wave, and the running maximum
+// carried from the previous step.  kWrite = false: the kept count into
+// counts[row]; true: the kept indices, ascending, from row_ptr[row].
+template <bool kWrite>
+__global__ __launch_bounds__(256) void threshold_kernel(const Geom g, const float* __restrict__ M, const ThetaTable tt,
+                                                        int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ row_ptr,
+                                                        int32_t* __restrict__ col_idx) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= g.rows()) return;  // the whole wave
+  const int nk = g.nk;
+  const double theta = tt.t[tt.per_head ? (row / g.nq) % g.H : 0];
+  const float* Mrow = M + (int64_t)row * nk;
+  int32_t* dst = kWrite ? col_idx + row_ptr[row] : nullptr;
+  float carry = 0.f;  // largest mass before this step's blocks
+  int kept = 0;
+  for (int j0 = 0; j0 < nk; j0 += kWave) {
+    const int j = j0 + lane;
+    const float x = j < nk ? __uint_as_float(sanitized_bits(Mrow[j])) : 0.f;
+    float run = x;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float y = __shfl_up(run, o, kWave);
+      if (lane >= o) run = fmaxf(run, y);
+    }
+    run = fmaxf(run, carry);
+    const bool keep = j < nk && (double)x >= theta * (double)run;
+    const uint64_t bal = __ballot(keep);
+    if (kWrite && keep) dst[kept + __popcll(bal & ((1ull << lane) - 1))] = j;
+    kept += __popcll(bal);
+    carry = __shfl(run, kWave - 1, kWave);
+  }
+  if (!kWrite && lane == 0) counts[row] = kept;
+}
+
 // List merge: row r takes its count from set b when its head is flagged,
 // from set a otherwise (clamped to [0, nk], so a malformed count cannot
 // place a row outside the output).
@@ -739,6 +779,18 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
   }
   launch_offsets_and_order(g, ws, row_ptr, order, st);
   hipLaunchKernelGGL(compact_kernel, dim3(rows), dim3(kSelThreads), 0, st, g, M, (const uint64_t*)ws.kappa,
+                     (const int32_t*)row_ptr, col_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_threshold(const Geom& g, const float* M, const ThetaTable& tt, int32_t* row_ptr,
+                                   int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t st) {
+  const int rows = g.rows();
+  const dim3 grid((rows + 3) / 4);
+  hipLaunchKernelGGL(threshold_kernel<false>, grid, dim3(256), 0, st, g, M, tt, ws.counts, (const int32_t*)nullptr,
+                     (int32_t*)nullptr);
+  launch_offsets_and_order(g, ws, row_ptr, order, st);
+  hipLaunchKernelGGL(threshold_kernel<true>, grid, dim3(256), 0, st, g, M, tt, (int32_t*)nullptr,
                      (const int32_t*)row_ptr, col_idx);
   return hipGetLastError();
 }

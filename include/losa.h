@@ -15,8 +15,9 @@
  *
  * The further calls below (each cites the page it follows) build the
  * patterns in other ways or maintain them: dense attention with the masses
- * in one pass, masses within given lists, pooled proxy masses, the query-key
- * drift that triggers a refresh, and the per-head merge of refreshed lists.
+ * in one pass, masses within given lists, pooled proxy masses, online block
+ * thresholding, the query-key drift that triggers a refresh, and the
+ * per-head merge of refreshed lists.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -24,7 +25,8 @@
  *   ws, kept, Q_ref, K_ref, drift, refresh, take_b (and the _a/_b list sets)
  *   is DEVICE memory owned by the caller; the library allocates nothing
  *   and keeps no pointer after a call returns.  The only host pointers are the
- *   losa_shape, the p array of losa_select and the size_t out-parameters.
+ *   losa_shape, the p array of losa_select, the theta array of
+ *   losa_select_threshold and the size_t out-parameters.
  * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
  *   returns without waiting.  Outputs are valid once the stream reaches them.
  * Errors.  Argument checks run on the host before any HIP call; a failed
@@ -276,6 +278,30 @@ losa_status losa_pooled_mass(const losa_shape* shape, const void* Q, const void*
  * ------------------------------------------------------------------------ */
 losa_status losa_retained_mass(const losa_shape* shape, const float* M, const int32_t* row_ptr,
                                const int32_t* col_idx, float* kept, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Online block thresholding.
+ * Sol-Attn page: critical blocks are picked by comparing block proxy scores
+ * against a threshold during the online-softmax pass, which gives dynamic
+ * per-row budgets; the page gives no rule.  Read here as: visiting a row's
+ * key blocks in index order (the order an online pass visits them), block j
+ * is kept when M[r, j] >= theta * max(M[r, 0 .. j]) -- in scores, within
+ * ln(1/theta) of the running maximum.  Masses are sanitised as in
+ * losa_select (NaN, inf, negatives and -0 count as 0); the comparison is
+ * made in fp64, so the lists are exact.  Block 0 is always kept.
+ *
+ * M: fp32 [batch, heads, n_q, n_k], contiguous: exact masses
+ *    (losa_block_mass) or proxies (losa_pooled_mass).
+ * theta: host array of n_theta values in (0, 1]; n_theta = 1 (all heads) or
+ *    heads (head h uses theta[h]; heads <= LOSA_MAX_HEADS_P).
+ * row_ptr/col_idx/col_capacity/order: as losa_select (indices ascending;
+ *    the same per-head work order).
+ * ws: at least *bytes from losa_select_threshold_workspace.
+ * ------------------------------------------------------------------------ */
+losa_status losa_select_threshold_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_select_threshold(const losa_shape* shape, const float* M, const double* theta, int32_t n_theta,
+                                  int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Query-key drift since a reference step, and the heads to refresh.

@@ -262,3 +262,25 @@ def test_binding_names_match_header():
             assert hasattr(F, n), n
     for n in F.__all__:
         assert hasattr(F, n), n
+
+
+@no_gpu_only
+def test_select_threshold_errors(lib):
+    s = shape()
+    rows, nk = 2 * 16, 16
+    n = ctypes.c_size_t()
+    assert lib.losa_select_threshold_workspace(ctypes.byref(s), ctypes.byref(n)) == OK and n.value > 0
+    t1 = (ctypes.c_double * 1)(0.1)
+
+    def sel(t=t1, n_t=1, cap=rows * nk, ws=0x100000, ws_bytes=1 << 40, M=FAKE):
+        return lib.losa_select_threshold(ctypes.byref(s), M, t, n_t, FAKE, FAKE, cap, None, ws, ws_bytes, None)
+
+    assert sel(M=None) == NULL
+    assert sel(t=None) == NULL
+    assert sel(cap=rows * nk - 1) == CAPACITY
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        assert sel(t=(ctypes.c_double * 1)(bad)) == INVALID
+    assert sel(n_t=3) == INVALID
+    assert sel(t=(ctypes.c_double * 2)(0.1, 0.0), n_t=2) == INVALID
+    assert sel(ws=0x100010) == WORKSPACE
+    assert sel(ws_bytes=n.value - 1) == WORKSPACE
