@@ -91,7 +91,7 @@ def cpu_baseline(layer, wl, rows_wanted, p, budget_s=20.0):
     import oracle as O
     import synthetic as S
     R, C = wl.block, wl.key_block
-    N, H, d = wl.tokens, wl.heads, wl.head_dim
+    N, H, d = wl.tokens, layer.q.shape[1], wl.head_dim
     nq = wl.n_blocks
     rng = np.random.default_rng(7)
     t_mass = t_sel = t_attn = 0.0
@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="1")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="run only the first HEADS heads of the workload (one GPU's share under head sharding)")
     ap.add_argument("--cpu-rows", type=int, default=16, help="query blocks in the oracle CPU baseline (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--refresh-tau", type=float, default=0.75,
@@ -216,9 +218,12 @@ def main():
         return run_reuse(args, wl)
     R, C = wl.block, wl.key_block
     N, Na, H, d = wl.tokens, wl.tokens_alloc, wl.heads, wl.head_dim
-    log(f"workload {wl.wid} {wl.name}: H={H} d={d} N={N} block={R} p={wl.p}")
+    share = 0 < args.heads < wl.heads
+    if share:
+        H = args.heads
+    log(f"workload {wl.wid} {wl.name}: H={H}{f' of {wl.heads}' if share else ''} d={d} N={N} block={R} p={wl.p}")
     t0 = time.time()
-    layer = S.make_layer(wl)
+    layer = S.make_layer(wl, heads=list(range(H)) if share else None)
     log(f"generated in {time.time() - t0:.1f}s")
     dev = torch.device("cuda:0")
 
@@ -283,7 +288,7 @@ def main():
                    "frac_hbm_peak": sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
     def traffic_of(call):
-        return load_traffic(call) if wl.wid == "1" else (None, "measured for the Wan2.1-1.3B shape only")
+        return load_traffic(call) if wl.wid == "1" and not share else (None, "measured for the Wan2.1-1.3B shape only")
 
     # The dominant kernel is attn_bf16_kernel (the mass call splits its time over two kernels).
     traffic, traffic_src = traffic_of("losa_sparse_attn")
@@ -350,7 +355,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic (seeded random-Fourier-feature Q/K + N(0,1) noise and sinks, N(0,1) V; no trained weights)",
-        "config": {"workload": wl.name, "batch": 1, "heads": H, "head_dim": d, "tokens": N, "tokens_alloc": Na,
+        "config": {"workload": wl.name + (f" (heads 0-{H - 1} of {wl.heads})" if share else ""), "batch": 1,
+                   "heads": H, "head_dim": d, "tokens": N, "tokens_alloc": Na,
                    "block": R, "k_block": C, "p": wl.p, "parallelism": "single GPU"},
         "sparse_attn_ms": attn_ms,
         "mass_select_ms": mass_ms + sel_ms,
