@@ -808,7 +808,10 @@ TRACE_KERNELS = [
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
     ("drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),
     ("drift_final_kernel", "drift_final_kernel", "losa_qk_drift"),
-    ("threshold_kernel", "threshold_kernel", "losa_select_threshold"),
+    ("threshold_kernel<false>", "threshold_kernel (counts)", "losa_select_threshold"),
+    ("threshold_kernelILb0", "threshold_kernel (counts)", "losa_select_threshold"),
+    ("threshold_kernel<true>", "threshold_kernel (indices)", "losa_select_threshold"),
+    ("threshold_kernelILb1", "threshold_kernel (indices)", "losa_select_threshold"),
     ("pick_counts_kernel", "pick_counts_kernel", "losa_merge_lists"),
     ("copy_lists_kernel", "copy_lists_kernel", "losa_merge_lists"),
 ]
