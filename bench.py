@@ -203,7 +203,7 @@ def main():
         summarize_mfma(*args.summarize_mfma)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs the path on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
