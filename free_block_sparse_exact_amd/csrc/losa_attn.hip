@@ -169,8 +169,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   auto lanes_max = [&](float (&mx)[kQT]) {
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
-      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 16, kWave));
-      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32, kWave));
+      mx[qt] = rows_max(mx[qt]);
     }
   };
   auto pv = [&](const bf16x8 (&vop)[DT], const bf16x8 (&pop)[kQT]) {
@@ -347,8 +346,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   // Row sums: combine the four lane groups that share each query.
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    l[qt] += __shfl_xor(l[qt], 16, kWave);
-    l[qt] += __shfl_xor(l[qt], 32, kWave);
+    l[qt] = rows_sum(l[qt]);
   }
 
   // Merge the four key groups in one step: every wave parks its partial O,

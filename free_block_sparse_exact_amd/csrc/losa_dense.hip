@@ -222,8 +222,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   auto lanes_max = [&](float (&mx)[kQT]) {
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
-      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 16, kWave));
-      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32, kWave));
+      mx[qt] = rows_max(mx[qt]);
     }
   };
   auto pv = [&](const bf16x8 (&vop)[DT], const bf16x8 (&pop)[kQT]) {
@@ -236,12 +235,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   // over the four lane groups formed by a transpose-reduce: two values swapped
   // with the lane 32 away, then one with the lane 16 away).
   auto block_end = [&](int j) {
-    const bool lo2 = lg < 2, even = (lg & 1) == 0;
-    const float a = __shfl_xor(lo2 ? blk[2] : blk[0], 32, kWave);
-    const float a2 = __shfl_xor(lo2 ? blk[3] : blk[1], 32, kWave);
-    const float x0 = (lo2 ? blk[0] : blk[2]) + a, x1 = (lo2 ? blk[1] : blk[3]) + a2;
-    const float r = __shfl_xor(even ? x1 : x0, 16, kWave);
-    const float v = (even ? x0 : x1) + r;
+    const float v = rows_sum_own(blk);
     tot += v;
     Sg[(int64_t)j * 64 + lane] = v;
 #pragma unroll
@@ -349,8 +343,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   // Row sums of P: combine the four lane groups that share each query.
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
-    l[qt] += __shfl_xor(l[qt], 16, kWave);
-    l[qt] += __shfl_xor(l[qt], 32, kWave);
+    l[qt] = rows_sum(l[qt]);
   }
   // Reference and block-sum total of the query this lane stored (lg*16 + lr).
   s_ref[kw][lane] = lg == 0 ? m[0] : lg == 1 ? m[1] : lg == 2 ? m[2] : m[3];

@@ -57,6 +57,41 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over the four 16-lane rows of a wave (lane = 16 * row + column)
+// on gfx950's lane swaps, vector instructions that need no LDS permute:
+// v_permlane32_swap(a, b) returns (a.lo, b.lo) and (a.hi, b.hi) by 32-lane
+// halves, v_permlane16_swap(a, b) returns (a.r0, b.r0, a.r2, b.r2) and
+// (a.r1, b.r1, a.r3, b.r3) by 16-lane rows.  Every lane must be active.
+// The sums add the same pairs in the same grouping as the xor-16-then-32
+// (or 32-then-16) exchange they replace, so results are bit-identical.
+__device__ __forceinline__ float swap_sum32(float a, float b) {  // lower lanes: a + a', upper: b' + b
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {  // even rows: a + a', odd rows: b' + b
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lane (row g, column c) gets v[g] summed over the four rows at column c:
+// each lane ends with the total of "its own" value of the four.
+__device__ __forceinline__ float rows_sum_own(const float (&v)[4]) {
+  return swap_sum16(swap_sum32(v[0], v[2]), swap_sum32(v[1], v[3]));
+}
+
+// x summed (maximised) over the four rows: every lane gets its column's total.
+__device__ __forceinline__ float rows_sum(float x) {
+  const float y = swap_sum16(x, x);
+  return swap_sum32(y, y);
+}
+
+__device__ __forceinline__ float rows_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -135,14 +135,7 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
   // that lane (lg, lr) ends with the one for query lg*16 + lr (the one it
   // stores): two values swapped with the lane 32 away, then one with the lane
   // 16 away.
-  auto reduce_mine = [&](const float (&v)[4]) -> float {
-    const bool lo2 = lg < 2, even = (lg & 1) == 0;
-    const float a = __shfl_xor(lo2 ? v[2] : v[0], 32, kWave);
-    const float b2 = __shfl_xor(lo2 ? v[3] : v[1], 32, kWave);
-    const float x0 = (lo2 ? v[0] : v[2]) + a, x1 = (lo2 ? v[1] : v[3]) + b2;
-    const float r = __shfl_xor(even ? x1 : x0, 16, kWave);
-    return (even ? x0 : x1) + r;
-  };
+  auto reduce_mine = [&](const float (&v)[4]) -> float { return rows_sum_own(v); };
 
   // One sweep over my chunks against the reference m (fixed_from_first: m is
   // set from the first chunk).  tot = this lane's query's total.  Returns
@@ -168,8 +161,7 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
           float mx = acc[0][qt][0];
 #pragma unroll
           for (int e = 1; e < 8; ++e) mx = fmaxf(mx, acc[e >> 2][qt][e & 3]);
-          mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+          mx = rows_max(mx);
           m[qt] = mx * c + kHeadroom;  // finite: the first chunk holds a valid key
         }
       }
@@ -216,8 +208,7 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
     }
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
-      m[qt] = fmaxf(m[qt], __shfl_xor(m[qt], 16, kWave));
-      m[qt] = fmaxf(m[qt], __shfl_xor(m[qt], 32, kWave));
+      m[qt] = rows_max(m[qt]);
       m[qt] *= c;
     }
     sweep(false);
