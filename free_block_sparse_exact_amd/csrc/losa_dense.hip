@@ -1,8 +1,8 @@
 // Dense self-attention that also accumulates the exact block masses, in one
 // pass over K and V: the construction step of the LoSA page (Methodology
 // Summary: the pattern is built at one dense step from exact block masses;
-// Experiments Summary: the construction kernel is a dense-attention kernel
-// that accumulates exact block masses while computing full attention).
+// Experiments Summary: the construction step's kernel is a full attention
+// pass that also sums the exact block masses).
 //
 //   O(q)    = softmax over all valid keys of s = q.k * scale, times V;
 //   M[i,j]  = (1/valid rows of block i) * sum over rows q of block i and
@@ -29,9 +29,9 @@
 // With CSR lists (kLists) the same kernel runs over each row's listed blocks
 // only: O is then the frozen-pattern sparse attention, and M the masses
 // within the lists -- the softmax of that attention summed per listed block
-// (0 outside the list), the exact weights a reduced search (GSRS card: later
-// top-p searches within an early candidate set, evaluated inside the
-// attention pass) selects from.
+// (0 outside the list), the exact weights a reduced search (GSRS card: a
+// top-p search that, after the first, looks only among blocks an earlier
+// search kept, its weights taken from the attention pass) selects from.
 #include "losa_blocksum.hpp"
 #include "losa_device.hpp"
 #include "losa_internal.hpp"

@@ -1,7 +1,7 @@
 // Pooled proxy masses: the coarse block-mass estimate that per-step top-p
 // methods rely on and that the LoSA page contrasts with exact masses
-// (Motivation Summary: SVG2 and SpargeAttn use coarse mass estimates that are
-// not accurate enough near 99% recall).  The pages give no formula; this
+// (Motivation Summary: the estimates SVG2 and SpargeAttn use lose accuracy
+// just where 99% recall is wanted).  The pages give no formula; this
 // library takes the plainest block-pooled reading:
 //
 //   P[b,h,i,j] = |B_j| exp(qbar_i . kbar_j * scale) / sum_j' |B_j'| exp(qbar_i . kbar_j' * scale),

@@ -23,6 +23,11 @@
 //   compact     one workgroup per row: block j is kept iff its sort key is
 //               <= kappa; write kept indices ascending at row_ptr[row].
 //
+// The same chunk / offsets / place kernels also serve two other list
+// builders here: online block thresholding (threshold kernel: counts, then
+// the kept indices) and the per-head merge of two list sets (pick_counts,
+// then copy_lists).
+//
 // Work order: the n_q rows of each (batch, head) keep their range, heads in
 // index order; inside it, rows by kept count descending, ties by row index.
 //

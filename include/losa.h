@@ -218,9 +218,9 @@ losa_status losa_dense_attn_mass(const losa_shape* shape, const void* Q, const v
 /* ------------------------------------------------------------------------
  * Frozen-pattern sparse attention with the exact masses within the lists.
  * GSRS card (Sparse Attention for Video Generation Acceleration via Growing
- * Sparsity and Reduced Search): later top-p searches are restricted to an
- * early candidate set, and the attention weights they need are computed
- * exactly inside the attention pass.  Reading (the card gives no formula):
+ * Sparsity and Reduced Search): after the first top-p search, later ones
+ * look only among the blocks an earlier search kept, and the weights they
+ * rank are the exact ones the attention pass itself produces.  Reading (the card gives no formula):
  * O is exactly losa_sparse_attn's, and for each row i with listed blocks L
  *   M[b,h,i,j] = (1/valid rows of block i) * sum over valid rows q of block i
  *                and valid keys k of block j of
@@ -252,8 +252,8 @@ losa_status losa_sparse_attn_mass(const losa_shape* shape, const void* Q, const 
 /* ------------------------------------------------------------------------
  * Pooled proxy masses: the coarse block-mass estimate of per-step top-p
  * methods, which the LoSA page contrasts with exact masses (Motivation
- * Summary: SVG2 and SpargeAttn rely on coarse estimates that are not
- * accurate enough near 99% recall; the pages give no formula).  Reading:
+ * Summary: the estimates SVG2 and SpargeAttn use lose accuracy just where
+ * 99% recall is wanted; the pages give no formula).  Reading:
  *   P[b,h,i,j] = |B_j| exp(qbar_i . kbar_j * scale)
  *                / sum_j' |B_j'| exp(qbar_i . kbar_j' * scale),
  * qbar_i, kbar_j the means over the valid tokens of query block i and key
@@ -281,9 +281,9 @@ losa_status losa_retained_mass(const losa_shape* shape, const float* M, const in
 
 /* ------------------------------------------------------------------------
  * Online block thresholding.
- * Sol-Attn page: critical blocks are picked by comparing block proxy scores
- * against a threshold during the online-softmax pass, which gives dynamic
- * per-row budgets; the page gives no rule.  Read here as: visiting a row's
+ * Sol-Attn page: which blocks matter is decided while the online softmax
+ * runs, each block's proxy score tested against a threshold, so the budget
+ * varies by row; the page gives no rule.  Read here as: visiting a row's
  * key blocks in index order (the order an online pass visits them), block j
  * is kept when M[r, j] >= theta * max(M[r, 0 .. j]) -- in scores, within
  * ln(1/theta) of the running maximum.  Masses are sanitised as in

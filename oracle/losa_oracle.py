@@ -55,9 +55,9 @@ notes of the repository):
   M_L(i, j) = mean over valid rows of block i of the sum over block j's
   tokens of it, for j in L; 0 for blocks outside L.  A row with a non-empty
   list sums to 1; with every block listed M_L = M.
-* Online block thresholding (the Sol-Attn page: critical blocks are picked
-  by comparing block proxy scores against a threshold during the online
-  softmax pass, giving dynamic budgets; the page gives no rule): visiting a
+* Online block thresholding (the Sol-Attn page decides which blocks matter
+  while its online softmax runs, each block's proxy score tested against a
+  threshold, so budgets vary by row; the page gives no rule): visiting a
   row's key blocks in index order, as an online-softmax pass does, block j
   is kept when its mass (exact or proxy, sanitised as for top-p) is at least
   theta times the largest mass seen so far, block j included -- in scores,

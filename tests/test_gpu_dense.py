@@ -2,8 +2,8 @@
 masses in one pass (the construction step) -- against the fp64 oracle.
 
 LoSA page: Methodology Summary (the pattern is constructed once, at a dense
-step, from exact block masses); Experiments Summary (the construction kernel
-accumulates exact block masses while computing full attention).  O is checked
+step, from exact block masses); Experiments Summary (the construction step's
+kernel is a full attention pass that also sums the exact block masses).  O is checked
 against the oracle's dense attention (absolute 1e-2), M against the oracle's
 block masses (relative 1e-3), on the small seeded cases of the sparse
 parity tests, on rows whose logits all lie far below zero, on rows that drive

@@ -59,8 +59,8 @@ def test_attention_two_key_closed_form():
 
 @pytest.mark.parametrize("n_valid,R,C", [(300, 64, 64), (256, 32, 64), (333, 128, 32), (64, 64, 64)])
 def test_mass_rows_sum_to_one_and_nonnegative(n_valid, R, C):
-    """Methodology Summary: each query row of A sums to one, so a query block of size R holds mass R
-    (row-mean form: each row of blocks sums to 1)."""
+    """Methodology Summary: every query row's probabilities add up to 1, so a block of R query
+    rows carries mass R (row-mean form: each row of blocks sums to 1)."""
     rng = np.random.default_rng(2)
     Na = max(-(-n_valid // R) * R, -(-n_valid // C) * C)
     q, k, _ = _rand_qkv(rng, 2, 2, Na, 16, n_valid, scale_q=3.0)
