@@ -38,9 +38,10 @@ notes of the repository):
   positive mass is at least one unit), P = floor(p * 2^32 + 1/2),
   T = ceil(P * sum_j q_j / 2^32), s = the least prefix length whose integer
   sum is >= T.  A plain fp64 argsort + cumsum is kept beside it as a cross-check.
-* Output lists are CSR with ascending block indices per row; the work order
-  keeps each head's n_q rows together (heads in index order) and lists them
-  by kept-block count, descending, ties by row index ascending.
+* Output lists are CSR with ascending block indices per row.  The work order
+  ranks each head's n_q rows by kept-block count (descending, ties by row
+  index), cuts the ranks into groups of 32, and runs the groups longest
+  first (by their first row's count; ties by head, then group).
 * Pooled proxy masses (the coarse estimates the page contrasts with exact
   masses -- Motivation Summary, SVG2 / SpargeAttn; the pages give no formula):
   P[i, j] = |B_j| exp(qbar_i . kbar_j * scale) / sum_j' |B_j'| exp(qbar_i .
@@ -99,6 +100,7 @@ __all__ = [
     "sparse_attention",
     "sparse_attention_rows",
     "budget_order",
+    "ORDER_GROUP",
     "select_threshold_row",
     "select_threshold",
     "qk_drift",
@@ -445,19 +447,35 @@ def restricted_mass(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
     return restricted_mass_rows(q, k, n_valid, R, C, row_ptr, col_idx, rows, scale).reshape(B, H, n_q, n_k)
 
 
+ORDER_GROUP = 32  # rows per work group in the work order
+
+
 def budget_order(row_ptr: np.ndarray, n_q: int) -> np.ndarray:
-    """Work order: the rows of each (batch, head), n_q consecutive rows, stay
-    together, heads in index order; within a head, rows by kept-block count
-    descending, ties by row index ascending.
+    """Work order.  Within each (batch, head) -- n_q consecutive rows -- rows
+    are ranked by kept-block count, descending, ties by row index; the ranks
+    are cut into groups of ORDER_GROUP consecutive ranks (the head's last
+    group may be shorter); groups run longest first, by the count of their
+    first (largest) row, ties by head and then by group; rows within a group
+    keep their rank order.
 
     The pages ask for work ordered by budget because per-head budgets are
     uneven (HASTE page, head-wise adaptive top-p; Sol-Attn page, dynamic but
-    imbalanced budgets); keeping each head's rows contiguous lets the
-    workgroups that run at the same time share that head's keys and values.
+    imbalanced budgets); a group holds rows of one head, so the workgroups
+    that run it side by side share that head's keys and values.
     """
     counts = np.diff(np.asarray(row_ptr, dtype=np.int64))
     rows = np.arange(counts.size, dtype=np.int64)
-    return np.lexsort((rows, -counts, rows // int(n_q))).astype(np.int64)
+    head = rows // int(n_q)
+    ranked = np.lexsort((rows, -counts, head))          # head-major, count desc, row asc
+    rank = np.empty_like(rows)
+    rank[ranked] = np.arange(rows.size) - head[ranked] * int(n_q)
+    group = rank // ORDER_GROUP
+    first = {}
+    for r in rows:                                       # each group's first (largest) row
+        if rank[r] % ORDER_GROUP == 0:
+            first[(int(head[r]), int(group[r]))] = int(counts[r])
+    key = np.array([first[(int(head[r]), int(group[r]))] for r in rows], np.int64)
+    return np.lexsort((rank, head, -key)).astype(np.int64)
 
 
 def qk_drift(q: np.ndarray, k: np.ndarray, q_ref: np.ndarray, k_ref: np.ndarray, n_valid: int) -> np.ndarray:

@@ -294,29 +294,62 @@ def test_recall_at_construction_and_coverage():
 
 
 def test_budget_order():
-    # two heads of three rows, counts (3, 2, 3) and (1, 2, 2): each head's
-    # rows stay together; inside a head, longest first, equal counts by index
+    # two heads of three rows, counts (3, 2, 3) and (1, 2, 2); each head's
+    # three rows fit one group: head 0's group (first row: count 3) runs
+    # before head 1's (first row: count 2); inside a group, longest first,
+    # equal counts by index
     rp = np.array([0, 3, 5, 8, 9, 11, 13])
     assert O.budget_order(rp, 3).tolist() == [0, 2, 1, 4, 5, 3]
-    # one head holding every row: the plain count-descending order
-    assert O.budget_order(rp, 6).tolist() == [0, 2, 1, 4, 5, 3]
-    assert O.budget_order(np.array([0, 3, 5, 8, 9, 11]), 5).tolist() == [0, 2, 1, 4, 3]
-    # one row per head: the natural order whatever the counts
-    assert O.budget_order(rp, 1).tolist() == list(range(6))
+    # heads swapped: the heavier head still runs first
+    rp2 = np.array([0, 1, 3, 5, 8, 10, 13])  # counts (1, 2, 2) and (3, 2, 3)
+    assert O.budget_order(rp2, 3).tolist() == [3, 5, 4, 1, 2, 0]
+    # equal first counts: ties by head
+    rp3 = np.array([0, 2, 3, 5, 6])          # counts (2, 1) and (2, 1)
+    assert O.budget_order(rp3, 2).tolist() == [0, 1, 2, 3]
+    # one row per head: groups of one row, longest first, ties by index
+    assert O.budget_order(rp, 1).tolist() == [0, 2, 1, 4, 5, 3]
+
+
+def test_budget_order_groups_of_32():
+    """A head of 70 rows is three groups (32, 32 and 6 rows); the groups of
+    two heads interleave by their first counts."""
+    rng = np.random.default_rng(6)
+    n_q = 70
+    counts = np.concatenate([rng.integers(50, 100, n_q), rng.integers(0, 80, n_q)])
+    rp = np.concatenate([[0], np.cumsum(counts)])
+    groups = []
+    for h in range(2):
+        ranked = sorted(range(h * n_q, (h + 1) * n_q), key=lambda r: (-counts[r], r))
+        for g0 in range(0, n_q, 32):
+            groups.append((-counts[ranked[g0]], h, g0, ranked[g0:g0 + 32]))
+    ref = [r for g in sorted(groups, key=lambda t: t[:3]) for r in g[3]]
+    assert O.budget_order(rp, n_q).tolist() == ref
+    assert O.ORDER_GROUP == 32
 
 
 def test_budget_order_brute_force():
+    """Groups are up to 32 consecutive slots of one head, rows inside by
+    (-count, row), and the groups' first counts never increase."""
     rng = np.random.default_rng(5)
-    for n_q, heads in ((1, 7), (4, 3), (17, 5), (64, 2)):
+    for n_q, heads in ((1, 7), (4, 3), (17, 5), (64, 2), (100, 3)):
         counts = rng.integers(0, 6, size=n_q * heads)
         rp = np.concatenate([[0], np.cumsum(counts)])
         order = O.budget_order(rp, n_q)
-        ref = sorted(range(counts.size), key=lambda r: (r // n_q, -counts[r], r))
-        assert order.tolist() == ref
-        for h in range(heads):  # a permutation of each head's rows, non-increasing counts
-            part = order[h * n_q:(h + 1) * n_q]
-            assert sorted(part.tolist()) == list(range(h * n_q, (h + 1) * n_q))
-            assert np.all(np.diff(counts[part]) <= 0)
+        assert sorted(order.tolist()) == list(range(counts.size))
+        seen = {h: 0 for h in range(heads)}
+        pos, prev = 0, None
+        while pos < order.size:
+            h = int(order[pos] // n_q)
+            size = min(32, n_q - seen[h])
+            grp = order[pos:pos + size].tolist()
+            assert all(r // n_q == h for r in grp)
+            ranked = sorted(range(h * n_q, (h + 1) * n_q), key=lambda r: (-counts[r], r))
+            assert grp == ranked[seen[h]:seen[h] + size]
+            key = (-int(counts[grp[0]]), h)
+            assert prev is None or prev <= key
+            prev = key
+            seen[h] += size
+            pos += size
 
 
 # ---------------------------------------------------------------- generator
