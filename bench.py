@@ -804,6 +804,8 @@ TRACE_KERNELS = [
     ("chunk_kernel", "chunk_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("offsets_kernel", "offsets_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("compact_kernel", "compact_kernel", "losa_select"),
+    ("group_order_kernel", "group_order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
+    ("scatter_order_kernel", "scatter_order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("place_kernel", "place_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
     ("drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),

@@ -49,8 +49,13 @@ struct SelectWs {
   int32_t* bucket;      // [B*H][nk + 1] the head's rows per nk - count
   int nchunk;           // B*H*cph row chunks, each inside one head
   int cph;              // chunks per head: ceil(nq / kOrderChunk)
+  int32_t* ranked;      // [rows] row of rank r in head h at h * nq + r
+  int32_t* gkey;        // [B*H*ngh] count of each work group's first row
+  int32_t* gstart;      // [B*H*ngh] first order slot of each work group
+  int ngh;              // work groups per head: ceil(nq / kGroupRows)
 };
 constexpr int kOrderChunk = 256;  // rows per placement chunk for the budget order
+constexpr int kGroupRows = 32;    // rows per work group of the budget order (one XCD's CUs)
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base);
 hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr,
                          int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t stream);

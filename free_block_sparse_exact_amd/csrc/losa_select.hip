@@ -18,8 +18,11 @@
 //               finish scans the per-chunk kept totals (-> first CSR slot
 //               per chunk, and row_ptr[rows]);
 //   place       one workgroup per chunk: row_ptr of its rows (chunk base +
-//               scan of counts), and the stable placement of its rows by
-//               count, descending, inside its head's n_q slots -> order;
+//               scan of counts), and each row's stable rank by count,
+//               descending, inside its head (-> ranked rows, group keys);
+//   group_order one workgroup: the work groups (32 ranks of one head) by
+//               their first count, descending, stable -> each group's slot;
+//   scatter     one thread per rank: the row into its group's slots -> order;
 //   compact     one workgroup per row: block j is kept iff its sort key is
 //               <= kappa; write kept indices ascending at row_ptr[row].
 //
@@ -28,8 +31,10 @@
 // the kept indices) and the per-head merge of two list sets (pick_counts,
 // then copy_lists).
 //
-// Work order: the n_q rows of each (batch, head) keep their range, heads in
-// index order; inside it, rows by kept count descending, ties by row index.
+// Work order: each (batch, head)'s n_q rows ranked by kept count,
+// descending, ties by row index; the ranks cut into groups of 32 (what one
+// XCD's CUs run side by side); groups longest first by their first row's
+// count, ties by head and group; ranks in order inside a group.
 //
 // Sort key of block j with (sanitised) mass bits u: ((2^32-1-u) << 32) | j.
 // For non-negative floats the bit pattern orders like the value, so an
@@ -588,18 +593,20 @@ __global__ __launch_bounds__(kSelThreads) void compact_kernel(const Geom g, cons
 
 // One workgroup (kOrderChunk threads) per chunk of rows.  row_ptr of the
 // chunk's rows: the chunk's first CSR slot plus the scan of their counts.
-// Then (if order is wanted) stable placement by count descending inside the
-// head's slots [h * nq, (h + 1) * nq): the first slot of a row with count c
-// is h * nq + (rows of the head with a larger count: the exclusive scan of
-// bucket[h]) + hist[chunk][nk - c] (rows of count c in earlier chunks of the
-// head) plus the rows of that count already placed by earlier waves of this
-// chunk; waves take turns so that rows keep their index order within a count.
+// Then (if the work order is wanted) each row's rank r in its head by count
+// descending, stable: h * nq + r is h * nq + (rows of the head with a larger
+// count: the exclusive scan of bucket[h]) + hist[chunk][nk - c] (rows of
+// count c in earlier chunks of the head) plus the rows of that count already
+// placed by earlier waves of this chunk; waves take turns so that rows keep
+// their index order within a count.  ranked[h * nq + r] = row, and the rows
+// of rank r = 0 mod kGroupRows record their count as their group's key.
 __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __restrict__ counts, int nq, int cph,
                                                             int nk, const int32_t* __restrict__ hist,
                                                             const int32_t* __restrict__ bucket,
                                                             const int32_t* __restrict__ chunk_base,
                                                             int32_t* __restrict__ row_ptr,
-                                                            int32_t* __restrict__ order) {
+                                                            int32_t* __restrict__ ranked, int ngh,
+                                                            int32_t* __restrict__ gkey) {
   extern __shared__ int run[];  // [nk + 1] next free slot of each count, relative to the head's first
   __shared__ int wsum[kOrderChunk / 64];
   __shared__ int wscan[kOrderChunk / 64];
@@ -621,7 +628,7 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
   for (int ww = 0; ww < kOrderChunk / 64; ++ww)
     if (ww < w) before += wsum[ww];
   if (cr.valid) row_ptr[row] = before + v - cnt;
-  if (!order) return;
+  if (!ranked) return;
   block_exclusive_scan_i32(bucket + (int64_t)cr.head * (nk + 1), nk + 1, run, nullptr, wscan);
   const int32_t* hrow = hist + (int64_t)chunk * (nk + 1);
   const int head0 = cr.head * nq;
@@ -639,8 +646,9 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
         const uint64_t mm = __ballot(match);
         const int base = head0 + hrow[b0] + run[b0];
         if (match) {
-          const int rank = __popcll(mm & ((1ull << lane) - 1));
-          order[base + rank] = row;
+          const int r = base + __popcll(mm & ((1ull << lane) - 1)) - head0;  // rank within the head
+          ranked[head0 + r] = row;
+          if (r % kGroupRows == 0) gkey[cr.head * ngh + r / kGroupRows] = cnt;  // the group's first count
           todo = false;
         }
         __builtin_amdgcn_wave_barrier();
@@ -649,6 +657,79 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
       }
     }
   }
+}
+
+// The work order's groups: group (h, k) holds ranks [k * kGroupRows,
+// (k + 1) * kGroupRows) of head h (the last group of a head holds
+// nq - (ngh - 1) * kGroupRows rows when nq is not a multiple of kGroupRows);
+// groups run by key descending, ties by group index (head, then k).  One
+// workgroup: a counting sort over the keys in LDS (all groups, and the short
+// head-last groups) and a stable placement in group-index order.  A group's
+// first slot is kGroupRows * R - (kGroupRows - last) * S, with R the groups
+// and S the short groups placed before it.
+__global__ __launch_bounds__(256) void group_order_kernel(int ngroups, int ngh, int last, int nk,
+                                                          const int32_t* __restrict__ gkey,
+                                                          int32_t* __restrict__ gstart) {
+  extern __shared__ int gl[];  // [2][nk + 1]: groups, then short groups, per key bucket nk - key
+  __shared__ int wsum[256 / 64];
+  int* all = gl;
+  int* shrt = gl + nk + 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int x = threadIdx.x; x < 2 * (nk + 1); x += 256) gl[x] = 0;
+  __syncthreads();
+  const bool has_short = last < kGroupRows;
+  for (int gi = threadIdx.x; gi < ngroups; gi += 256) {
+    const int b = nk - gkey[gi];
+    atomicAdd(&all[b], 1);
+    if (has_short && gi % ngh == ngh - 1) atomicAdd(&shrt[b], 1);
+  }
+  __syncthreads();
+  block_exclusive_scan_i32(all, nk + 1, all, nullptr, wsum);  // now the next slot per bucket
+  block_exclusive_scan_i32(shrt, nk + 1, shrt, nullptr, wsum);
+  for (int t0 = 0; t0 < ngroups; t0 += 256) {
+    const int gi = t0 + (int)threadIdx.x;
+    const bool valid = gi < ngroups;
+    const int b = valid ? nk - gkey[gi] : 0;
+    const bool is_short = valid && has_short && gi % ngh == ngh - 1;
+    for (int turn = 0; turn < 4; ++turn) {
+      __syncthreads();
+      if (w == turn) {
+        bool todo = valid;
+        while (true) {
+          const uint64_t am = __ballot(todo);
+          if (am == 0) break;
+          const int leader = __ffsll((unsigned long long)am) - 1;
+          const int b0 = __shfl(b, leader, kWave);
+          const bool match = todo && b == b0;
+          const uint64_t mm = __ballot(match), ms = __ballot(match && is_short);
+          const int r0 = all[b0], s0 = shrt[b0];
+          if (match) {
+            const uint64_t lt = (1ull << lane) - 1;
+            const int R = r0 + __popcll(mm & lt), S = s0 + __popcll(ms & lt);
+            gstart[gi] = kGroupRows * R - (kGroupRows - last) * S;
+            todo = false;
+          }
+          __builtin_amdgcn_wave_barrier();
+          if (lane == leader) {
+            all[b0] += __popcll(mm);
+            shrt[b0] += __popcll(ms);
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+    }
+  }
+}
+
+// order[first slot of the row's group + rank within the group] = row.
+__global__ __launch_bounds__(256) void scatter_order_kernel(int rows, int nq, int ngh,
+                                                            const int32_t* __restrict__ ranked,
+                                                            const int32_t* __restrict__ gstart,
+                                                            int32_t* __restrict__ order) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= rows) return;
+  const int h = p / nq, r = p - h * nq;
+  order[gstart[h * ngh + r / kGroupRows] + r % kGroupRows] = ranked[p];
 }
 
 // Online block thresholding (the Sol-Attn page's block thresholding during
@@ -752,6 +833,11 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
   off = align_up(off + ((size_t)(g.nk + 1) * nchunk + nchunk + 1) * sizeof(int32_t), 256);
   const size_t bucket_off = off;
   off = align_up(off + (size_t)heads * (g.nk + 1) * sizeof(int32_t), 256);
+  const int ngh = (g.nq + kGroupRows - 1) / kGroupRows;
+  const size_t ranked_off = off;
+  off = align_up(off + (size_t)rows * sizeof(int32_t), 256);
+  const size_t gkey_off = off;  // then gstart
+  off = align_up(off + (size_t)2 * heads * ngh * sizeof(int32_t), 256);
   if (layout) {
     layout->counts = reinterpret_cast<int32_t*>(base + counts_off);
     layout->kappa = reinterpret_cast<uint64_t*>(base + kappa_off);
@@ -761,6 +847,10 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
     layout->bucket = reinterpret_cast<int32_t*>(base + bucket_off);
     layout->nchunk = nchunk;
     layout->cph = cph;
+    layout->ranked = reinterpret_cast<int32_t*>(base + ranked_off);
+    layout->gkey = reinterpret_cast<int32_t*>(base + gkey_off);
+    layout->gstart = layout->gkey + (size_t)heads * ngh;
+    layout->ngh = ngh;
   }
   return off;
 }
@@ -822,7 +912,14 @@ void launch_offsets_and_order(const Geom& g, const SelectWs& ws, int32_t* row_pt
                      rows, ws.chunk_hist, ws.chunk_sum, ws.bucket, ws.done, row_ptr);
   hipLaunchKernelGGL(place_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
                      g.nq, ws.cph, g.nk, (const int32_t*)ws.chunk_hist, (const int32_t*)ws.bucket,
-                     (const int32_t*)ws.chunk_sum, row_ptr, order);
+                     (const int32_t*)ws.chunk_sum, row_ptr, order ? ws.ranked : nullptr, ws.ngh, ws.gkey);
+  if (!order) return;
+  const int ngroups = g.B * g.H * ws.ngh;
+  const int last = g.nq - (ws.ngh - 1) * kGroupRows;
+  hipLaunchKernelGGL(group_order_kernel, dim3(1), dim3(256), 2 * hist_lds, st, ngroups, ws.ngh, last, g.nk,
+                     (const int32_t*)ws.gkey, ws.gstart);
+  hipLaunchKernelGGL(scatter_order_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, g.nq, ws.ngh,
+                     (const int32_t*)ws.ranked, (const int32_t*)ws.gstart, order);
 }
 
 hipError_t launch_retained_mass(const Geom& g, const float* M, const int32_t* row_ptr, const int32_t* col_idx,

@@ -147,12 +147,15 @@ losa_status losa_block_mass(const losa_shape* shape, const void* Q, const void* 
  * col_idx: int32, col_capacity >= batch*heads*n_q*n_k entries (the worst
  *    case; the used length is row_ptr[last], read back by the caller).
  * order: int32 [batch*heads*n_q] or NULL.  When given, receives the work
- *    order losa_sparse_attn takes: slots [g*n_q, (g+1)*n_q) hold the rows
- *    of head g = b*heads + h, sorted by kept-block count, descending, ties
- *    by row index ascending.  Per-head budgets are uneven (HASTE page,
- *    head-wise adaptive top-p; Sol-Attn page, imbalanced dynamic budgets),
- *    so the longest rows go first; keeping a head's rows together lets the
- *    workgroups running at one time share that head's keys and values.
+ *    order losa_sparse_attn takes: the rows of each head g = b*heads + h are
+ *    ranked by kept-block count, descending, ties by row index; the ranks
+ *    are cut into groups of 32 (a head's last group may be shorter); the
+ *    groups run longest first by their first row's count, ties by head and
+ *    then group, each group's rows in rank order.  Per-head budgets are
+ *    uneven (HASTE page, head-wise adaptive top-p; Sol-Attn page,
+ *    imbalanced dynamic budgets), so long work starts first; a group is one
+ *    head's rows, which the workgroups running side by side on one XCD then
+ *    share keys and values for.
  * ws: at least *bytes from losa_select_workspace.
  * ------------------------------------------------------------------------ */
 losa_status losa_select_workspace(const losa_shape* shape, size_t* bytes);
