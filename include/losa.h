@@ -107,10 +107,14 @@ const char* losa_status_string(losa_status status);
  * in row-mean form: M[b, h, i, j] = that sum divided by the number of valid
  * rows of query block i, so each row of blocks sums to 1.
  *
- * Computed in two passes over K: a flash-style pass for each row's
- * log-sum-exp, then a second pass that accumulates exp(s - LSE) per key
- * block.  Arithmetic: products and sums in fp32 (bf16 inputs are exact in
- * fp32), exponentials in fp32.
+ * bf16 matrix-core path (head_dim 64/128, q_block 64/128): one pass over
+ * K -- per query row and key block, the sum of exp(s - m) against a fixed
+ * per-row reference m goes to the workspace, the row's log-sum-exp follows
+ * from those sums, and M from the sums scaled by exp(m - LSE); rows whose
+ * sums leave a safe range are redone against their exact maximum.  Other
+ * shapes: two passes over K (the row log-sum-exp, then exp(s - LSE) summed
+ * per key block).  Arithmetic: products and sums in fp32 (bf16 inputs are
+ * exact in fp32), exponentials in fp32.
  *
  * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
  * ws: at least *bytes from losa_block_mass_workspace.  bf16 matrix-core path:
