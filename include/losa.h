@@ -181,7 +181,7 @@ losa_status losa_select(const losa_shape* shape, const float* M, const double* p
  *    row -- a repeated index gives an unspecified O, never an access outside
  *    the buffers).
  * order: NULL (rows in index order) or a permutation of the rows giving the
- *    order in which work is dispatched (losa_select's budget order).  The
+ *    order in which work is dispatched (losa_select's work order).  The
  *    result does not depend on it.
  * O: [batch, heads, tokens_alloc, head_dim] with shape->o_stride, element
  *    type o_dtype (LOSA_BF16 or LOSA_F32).
@@ -202,8 +202,8 @@ losa_status losa_sparse_attn(const losa_shape* shape, const void* Q, const void*
  * Dense attention with exact block masses, in one pass (the construction
  * step).  LoSA page, Methodology Summary: the pattern is built once, at a
  * dense step, from exact block masses; Experiments Summary: the
- * construction kernel is a dense-attention kernel that accumulates the exact
- * block masses while it computes full attention.
+ * construction step's kernel is a full attention pass that also sums the
+ * exact block masses.
  * O(q) = softmax over all valid keys of s = q.k * scale, times V (rows in
  * [tokens, n_q*q_block) written as 0, rows beyond not touched); M = exactly
  * what losa_block_mass computes.
@@ -227,8 +227,8 @@ losa_status losa_dense_attn_mass(const losa_shape* shape, const void* Q, const v
  * GSRS card (Sparse Attention for Video Generation Acceleration via Growing
  * Sparsity and Reduced Search): after the first top-p search, later ones
  * look only among the blocks an earlier search kept, and the weights they
- * rank are the exact ones the attention pass itself produces.  Reading (the card gives no formula):
- * O is exactly losa_sparse_attn's, and for each row i with listed blocks L
+ * rank are the exact ones the attention pass itself produces.  Reading (the
+ * card gives no formula): O is exactly losa_sparse_attn's, and for each row i with listed blocks L
  *   M[b,h,i,j] = (1/valid rows of block i) * sum over valid rows q of block i
  *                and valid keys k of block j of
  *                exp(s_qk) / sum over the valid keys k' of L of exp(s_qk')
