@@ -99,3 +99,22 @@ def test_threshold_then_sparse_attention():
     err = float(np.abs(Og.cpu().numpy()[:, :, :N] - ref[:, :, :N]).max())
     say(f"sparse attention on thresholded lists: O max abs err {err:.2e}")
     assert err <= ATTN_ATOL
+
+
+def test_work_order_many_short_groups():
+    """1024 heads of 33 query blocks (a 32-row and a 1-row group each) and
+    nine key blocks: 2048 work groups, few distinct counts; the selector's
+    lists and its work order against the oracle, bit for bit."""
+    rng = np.random.default_rng(99)
+    H, R, C, N = 1024, 32, 128, 1049
+    nq, nk = -(-N // R), -(-N // C)
+    assert (nq, nk) == (33, 9)
+    M = rng.random((1, H, nq, nk)).astype(np.float32) ** 3
+    rp_ref, ci_ref = O.select_contract(M, 0.7)
+    rp, ci, order = F.losa_select(torch.from_numpy(M).cuda(), 0.7, N, R, C, tokens_alloc=max(nq * R, nk * C))
+    torch.cuda.synchronize()
+    rp = rp.cpu().numpy().astype(np.int64)
+    assert np.array_equal(rp, rp_ref)
+    assert np.array_equal(ci[:int(rp[-1])].cpu().numpy(), ci_ref)
+    assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref, nq))
+    say(f"{H} heads x {nq} rows: lists and work order bit-exact")
