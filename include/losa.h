@@ -302,7 +302,7 @@ losa_status losa_retained_mass(const losa_shape* shape, const float* M, const in
  * theta: host array of n_theta values in (0, 1]; n_theta = 1 (all heads) or
  *    heads (head h uses theta[h]; heads <= LOSA_MAX_HEADS_P).
  * row_ptr/col_idx/col_capacity/order: as losa_select (indices ascending;
- *    the same per-head work order).
+ *    the same work order).
  * ws: at least *bytes from losa_select_threshold_workspace.
  * ------------------------------------------------------------------------ */
 losa_status losa_select_threshold_workspace(const losa_shape* shape, size_t* bytes);
