@@ -6,8 +6,9 @@
 // Kernels, in launch order:
 //   cut         the cut in (mass desc, index asc) order over exact integer
 //               units, without sorting -> the kept count s and the sort key
-//               kappa of the last kept block: one wave per row by bisection
-//               (n_k <= 2048), or one workgroup per row by radix select;
+//               kappa of the last kept block: one wave per row
+//               (n_k <= 2048) by a radix select over the range of the
+//               row's keys, or one workgroup per row by radix select;
 //   chunk       one workgroup per chunk of up to 256 rows of one head:
 //               histogram of counts and kept total of the chunk (LDS, then
 //               plain stores: no global atomics, nothing to clear
@@ -341,6 +342,14 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   return (int)(lane_u32(v, 0) + lane_u32(v, 16) + lane_u32(v, 32) + lane_u32(v, 48));
 }
 
+// Orders this wave's LDS accesses across its lanes (the waves of a
+// workgroup work on different rows and do not meet).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp_u32<kDppXor1>(v));
   v = min(v, dpp_u32<kDppXor2>(v));
@@ -359,15 +368,16 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
 
 // One wave per row (four rows per workgroup), no workgroup barriers.  The
 // cut is the least inverted-bits value v with F(v) = sum of the units q of
-// the blocks with ku <= v reaching T, found by bisection over the range of
-// the blocks' ku (F only steps at those values, so v is one of them, and
-// F(v - 1) < T).  Among the blocks with ku = v (equal masses, equal units)
+// the blocks with ku <= v reaching T, found over the range of the blocks'
+// ku (F only steps at those values, so v is one of them, and F(v - 1) < T)
+// by a radix select.  Among the blocks with ku = v (equal masses, equal units)
 // the cut falls on the need-th in index order.  Lane l owns the contiguous
 // blocks [l*per, l*per + per), per <= kPer, so lane order is index order.
 template <int kPer>
 __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float* __restrict__ M, const PTable pt,
                                                        int32_t* __restrict__ counts,
                                                        uint64_t* __restrict__ kappa) {
+  __shared__ uint64_t cut_hist[4][256];  // per wave: units per digit of the radix select
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= g.rows()) return;  // whole waves only
@@ -414,17 +424,68 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
     if (T == 0) {
       v = wave_min_u32(kmin);  // the first block in sorted order
     } else {  // T > 0: some block has units, and F(max ku of those) = total >= T
+      // F steps only at keys of blocks with units, all in [lo, hi]: a radix
+      // select over rel = ku - lo, most significant 8-bit digit of the
+      // range first.  Each pass sums the units of the blocks still in the
+      // prefix's range per digit (this wave's histogram in LDS, exact u64
+      // sums) and keeps the least digit at which acc + the running sum
+      // reaches T.  At most four passes, against up to 32 bisection steps
+      // that each re-sum the whole row.
       lo = wave_min_u32(lo);
       hi = wave_max_u32_uniform(hi);
-      while (lo < hi) {
-        const uint32_t mid = lo + ((hi - lo) >> 1);
-        uint64_t f = 0;
+      const uint32_t width = hi - lo;
+      uint64_t* hist = cut_hist[threadIdx.x >> 6];
+      uint32_t rel[kPer];
 #pragma unroll
-        for (int t = 0; t < kPer; ++t) f += ku[t] <= mid ? q[t] : 0;
-        if (wave_sum_u64(f) >= T) hi = mid;
-        else lo = mid + 1;
+      for (int t = 0; t < kPer; ++t) rel[t] = ku[t] - lo;
+      uint32_t pre = 0;  // digits found so far
+      uint64_t acc = 0;  // units of the blocks below the prefix's range
+      for (int top = width ? 32 - __builtin_clz(width) : 0; top > 0;) {
+        const int shift = top > 8 ? top - 8 : 0;
+        const uint32_t dmask = (1u << (top - shift)) - 1u;
+        const uint32_t above = top >= 32 ? 0u : (0xFFFFFFFFu << top);
+        hist[4 * lane] = 0;
+        hist[4 * lane + 1] = 0;
+        hist[4 * lane + 2] = 0;
+        hist[4 * lane + 3] = 0;
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < kPer; ++t)
+          if (q[t] > 0 && ((rel[t] ^ pre) & above) == 0)
+            atomicAdd(reinterpret_cast<unsigned long long*>(hist + ((rel[t] >> shift) & dmask)),
+                      (unsigned long long)q[t]);
+        wave_lds_sync();
+        uint64_t c[4];  // inclusive sums of this lane's digits 4 lane .. 4 lane + 3
+        c[0] = hist[4 * lane];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) c[k] = c[k - 1] + hist[4 * lane + k];
+        uint64_t inc = c[3];  // inclusive scan over lanes
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t xl = __shfl_up((uint32_t)inc, o, kWave), xh = __shfl_up((uint32_t)(inc >> 32), o, kWave);
+          if (lane >= o) inc += ((uint64_t)xh << 32) | xl;
+        }
+        const uint64_t base = acc + (inc - c[3]);
+        // this lane's least digit reaching T (4: none), and the units below it
+        int k = 4;
+        uint64_t bel = 0;
+#pragma unroll
+        for (int kk = 3; kk >= 0; --kk)
+          if (base + c[kk] >= T) {
+            k = kk;
+            bel = kk ? c[kk - 1] : 0;
+          }
+        // some lane hits: acc plus all units in the prefix's range is F(end of the range) >= T
+        const uint64_t hit = __ballot(k < 4);
+        const int lf = __builtin_ctzll(hit);
+        const uint32_t digit = 4u * lf + (uint32_t)__builtin_amdgcn_readlane(k, lf);
+        const uint64_t add = (inc - c[3]) + bel;
+        acc += ((uint64_t)lane_u32((uint32_t)(add >> 32), lf) << 32) | lane_u32((uint32_t)add, lf);
+        pre |= digit << shift;
+        top = shift;
+        wave_lds_sync();  // every lane has read the histogram before the next pass clears it
       }
-      v = lo;
+      v = lo + pre;
     }
     uint64_t below = 0;
     int nbelow = 0, nties = 0;
@@ -858,7 +919,7 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
 hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr, int32_t* col_idx,
                          int32_t* order, const SelectWs& ws, hipStream_t st) {
   const int rows = g.rows();
-  // Up to 2048 key blocks a wave per row (bisection); beyond, a workgroup
+  // Up to 2048 key blocks a wave per row; beyond, a workgroup
   // per row (radix select), which spreads a long row over 256 threads.  The
   // per-thread arrays are unrolled, so the instance fits the row closely.
   const int per = (g.nk + kWave - 1) / kWave;

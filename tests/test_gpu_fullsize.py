@@ -148,6 +148,28 @@ def test_select_bit_exact_full_shape(wid):
     assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref, M.shape[2]))
 
 
+@pytest.mark.parametrize("nk", [1, 2, 63, 64, 65, 127, 129, 200, 1000, 1217, 2047, 2048])
+def test_select_widths_and_ties(nk):
+    """Row widths around every multiple of the 64-lane step up to the widest
+    one-wave row (2048 blocks), most rows adversarial (equal masses, exact
+    ties, zeros, one-hot, denormals, non-finite): lists and order bit-exact
+    for several p, ties cut in index order."""
+    rng = np.random.default_rng(300 + nk)
+    C, R = 32, 128
+    N = nk * C - 3 if nk > 1 else 20
+    nq = -(-N // R)
+    M = _synthetic_masses(rng, (1, 2, nq, nk))
+    for p in (0.5, 0.9, 0.99, 0.999):
+        rp_ref, ci_ref = O.select_contract(M, p)
+        rp, ci, order = F.losa_select(torch.from_numpy(M).cuda(), p, N, R, C, tokens_alloc=max(nq * R, nk * C))
+        torch.cuda.synchronize()
+        rp = rp.cpu().numpy().astype(np.int64)
+        assert np.array_equal(rp, rp_ref), (nk, p)
+        assert np.array_equal(ci[:int(rp[-1])].cpu().numpy(), ci_ref), (nk, p)
+        assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref, nq)), (nk, p)
+    say(f"n_k={nk}: lists bit-exact for p in 0.5 .. 0.999")
+
+
 def test_maximum_key_block_count():
     """n_k = 4096 (the largest the ABI accepts): one head of 131072 tokens with
     128-token query and 32-token key blocks through masses, selection and

@@ -6,8 +6,9 @@ first) and keeps the shortest prefix whose exact integer units reach the
 target T.  The GPU selector reaches the same cut without sorting: with
 ku = 2^32 - 1 - (float bits of the mass) and F(v) = sum of the units of the
 blocks with ku <= v, the cut value is the least v with F(v) >= T, found by
-bisection (one wave per row) or by a most-significant-digit radix select
-(one workgroup per row); among the blocks with ku = v (equal masses, equal
+a most-significant-digit radix select: over the range of the keys of the
+blocks with units, digits of at most 8 bits (one wave per row), or over the
+whole 32-bit key in four 8-bit digits (one workgroup per row); among the blocks with ku = v (equal masses, equal
 units) the cut falls on the ceil((T - F(v-1)) / q)-th in index order.
 
 This file restates both searches in plain Python integers, written from that
@@ -67,23 +68,35 @@ def _finish(ku, q, T, v, e):
     return np.array(sorted(keep))
 
 
-def cut_bisection(m32, p):
+def cut_range_radix(m32, p):
+    """One wave per row: the least v found by a radix select over rel = ku - lo in
+    [0, hi - lo] (lo, hi: least and greatest ku of the blocks with units), digits of at
+    most 8 bits taken from the top of the range down."""
     ku, q, T, P, e = _row_setup(m32, p)
     if P == 1 << 32:
         return np.arange(len(ku))
     if T == 0:
-        v = min(ku)
-    else:
-        pos = [k for k, x in zip(ku, q) if x > 0]
-        lo, hi = min(pos), max(pos)
-        while lo < hi:
-            mid = (lo + hi) // 2
-            if sum(x for k, x in zip(ku, q) if k <= mid) >= T:
-                hi = mid
-            else:
-                lo = mid + 1
-        v = lo
-    return _finish(ku, q, T, v, e)
+        return _finish(ku, q, T, min(ku), e)
+    pos = [k for k, x in zip(ku, q) if x > 0]
+    lo, hi = min(pos), max(pos)
+    top = (hi - lo).bit_length()
+    pre, acc = 0, 0
+    while top > 0:
+        shift = max(top - 8, 0)
+        hs = [0] * (1 << (top - shift))
+        for k, x in zip(ku, q):
+            r = k - lo
+            if x > 0 and r >> top == pre >> top:
+                hs[(r >> shift) & (len(hs) - 1)] += x
+        cum = 0
+        for d, h in enumerate(hs):
+            if acc + cum + h >= T:
+                break
+            cum += h
+        acc += cum
+        pre |= d << shift
+        top = shift
+    return _finish(ku, q, T, lo + pre, e)
 
 
 def cut_radix(m32, p):
@@ -115,6 +128,10 @@ def _rows(rng, nk):
             np.zeros(nk), np.eye(1, nk, int(rng.integers(nk)))[0]]
     out = [(r / max(r.sum(), 1e-300)).astype(np.float32) for r in rows]
     out.append((rng.random(nk) * 1e-38).astype(np.float32))  # denormal masses
+    # dyadic masses 1/2, 1/4, ..., with the last repeated (sum exactly 1), shuffled: the
+    # prefix sums hit the targets of p = 0.5, 0.75, ... exactly
+    dy = np.array([2.0 ** -min(k + 1, nk - 1) for k in range(nk)] if nk > 1 else [1.0])
+    out.append(rng.permutation(dy).astype(np.float32))
     bad = rng.random(nk).astype(np.float32)
     bad[rng.integers(nk, size=3)] = [np.nan, np.inf, -1.0]
     out.append(bad)
@@ -122,10 +139,10 @@ def _rows(rng, nk):
 
 
 @pytest.mark.parametrize("nk", [1, 2, 5, 64, 300])
-@pytest.mark.parametrize("p", [1e-9, 0.5, 0.9, 0.99, 0.995, 1.0])
+@pytest.mark.parametrize("p", [1e-9, 0.5, 0.75, 0.9, 0.99, 0.995, 1.0])
 def test_sort_free_cuts_equal_sorted_prefix_rule(nk, p):
     rng = np.random.default_rng(nk * 1000 + int(p * 1000))
     for m in _rows(rng, nk):
         ref = O.select_contract_row(m, p)[0]
-        assert np.array_equal(cut_bisection(m, p), ref)
+        assert np.array_equal(cut_range_radix(m, p), ref)
         assert np.array_equal(cut_radix(m, p), ref)
