@@ -127,6 +127,27 @@ __device__ __forceinline__ int block_sum_i32(int v, int* wsum) {
   return all;
 }
 
+// Orders this wave's LDS accesses across its lanes (the waves of a
+// workgroup work on different rows and do not meet).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The active lanes of this wave whose key equals this lane's (0 <= key <
+// 2^nbits): one ballot per key bit, so a wave of many distinct keys costs
+// no more than a wave of one.
+__device__ __forceinline__ uint64_t match_lanes(int key, bool active, int nbits) {
+  uint64_t eq = __ballot(active);
+  for (int i = 0; i < nbits; ++i) {
+    const bool bit = (key >> i) & 1;
+    const uint64_t bm = __ballot(bit);
+    eq &= bit ? bm : ~bm;
+  }
+  return eq;
+}
+
 // Chunk c covers rows h * nq + k * kOrderChunk + [0, kOrderChunk) of head
 // h = c / cph, k = c % cph (cph chunks per head), cut at the head's end.
 struct ChunkRows {
@@ -340,14 +361,6 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
   v += (int)dpp_u32<kDppRor4>((uint32_t)v);
   v += (int)dpp_u32<kDppRor8>((uint32_t)v);
   return (int)(lane_u32(v, 0) + lane_u32(v, 16) + lane_u32(v, 32) + lane_u32(v, 48));
-}
-
-// Orders this wave's LDS accesses across its lanes (the waves of a
-// workgroup work on different rows and do not meet).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
@@ -694,28 +707,19 @@ __global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __res
   const int32_t* hrow = hist + (int64_t)chunk * (nk + 1);
   const int head0 = cr.head * nq;
   const int bkt = nk - cnt;
-  for (int turn = 0; turn < kOrderChunk / 64; ++turn) {
+  const int nbits = 32 - __builtin_clz(nk);  // bkt <= nk
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int turn = 0; turn < kOrderChunk / 64; ++turn) {  // waves in row order: the ranks are stable
     __syncthreads();
     if (w == turn) {
-      bool todo = cr.valid;
-      while (true) {
-        const uint64_t am = __ballot(todo);
-        if (am == 0) break;
-        const int leader = __ffsll((unsigned long long)am) - 1;
-        const int b0 = __shfl(bkt, leader, kWave);
-        const bool match = todo && bkt == b0;
-        const uint64_t mm = __ballot(match);
-        const int base = head0 + hrow[b0] + run[b0];
-        if (match) {
-          const int r = base + __popcll(mm & ((1ull << lane) - 1)) - head0;  // rank within the head
-          ranked[head0 + r] = row;
-          if (r % kGroupRows == 0) gkey[cr.head * ngh + r / kGroupRows] = cnt;  // the group's first count
-          todo = false;
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (lane == leader) run[b0] += __popcll(mm);
-        __builtin_amdgcn_wave_barrier();
+      const uint64_t eq = match_lanes(bkt, cr.valid, nbits);
+      if (cr.valid) {
+        const int r = hrow[bkt] + run[bkt] + __popcll(eq & lt);  // rank within the head
+        ranked[head0 + r] = row;
+        if (r % kGroupRows == 0) gkey[cr.head * ngh + r / kGroupRows] = cnt;  // the group's first count
       }
+      wave_lds_sync();  // every lane has read run[] before the first lane of each key moves it on
+      if (cr.valid && (eq & lt) == 0) run[bkt] += __popcll(eq);
     }
   }
 }
@@ -739,6 +743,7 @@ __global__ __launch_bounds__(256) void group_order_kernel(int ngroups, int ngh, 
   for (int x = threadIdx.x; x < 2 * (nk + 1); x += 256) gl[x] = 0;
   __syncthreads();
   const bool has_short = last < kGroupRows;
+  const int nbits = 32 - __builtin_clz(nk);  // nk - key <= nk
   for (int gi = threadIdx.x; gi < ngroups; gi += 256) {
     const int b = nk - gkey[gi];
     atomicAdd(&all[b], 1);
@@ -752,30 +757,20 @@ __global__ __launch_bounds__(256) void group_order_kernel(int ngroups, int ngh, 
     const bool valid = gi < ngroups;
     const int b = valid ? nk - gkey[gi] : 0;
     const bool is_short = valid && has_short && gi % ngh == ngh - 1;
-    for (int turn = 0; turn < 4; ++turn) {
+    for (int turn = 0; turn < 4; ++turn) {  // waves in group order: the slots are stable
       __syncthreads();
       if (w == turn) {
-        bool todo = valid;
-        while (true) {
-          const uint64_t am = __ballot(todo);
-          if (am == 0) break;
-          const int leader = __ffsll((unsigned long long)am) - 1;
-          const int b0 = __shfl(b, leader, kWave);
-          const bool match = todo && b == b0;
-          const uint64_t mm = __ballot(match), ms = __ballot(match && is_short);
-          const int r0 = all[b0], s0 = shrt[b0];
-          if (match) {
-            const uint64_t lt = (1ull << lane) - 1;
-            const int R = r0 + __popcll(mm & lt), S = s0 + __popcll(ms & lt);
-            gstart[gi] = kGroupRows * R - (kGroupRows - last) * S;
-            todo = false;
-          }
-          __builtin_amdgcn_wave_barrier();
-          if (lane == leader) {
-            all[b0] += __popcll(mm);
-            shrt[b0] += __popcll(ms);
-          }
-          __builtin_amdgcn_wave_barrier();
+        const uint64_t eq = match_lanes(b, valid, nbits);
+        const uint64_t es = eq & __ballot(is_short);
+        const uint64_t lt = (1ull << lane) - 1ull;
+        if (valid) {
+          const int R = all[b] + __popcll(eq & lt), S = shrt[b] + __popcll(es & lt);
+          gstart[gi] = kGroupRows * R - (kGroupRows - last) * S;
+        }
+        wave_lds_sync();  // every lane has read the slots before the first lane of each key moves them on
+        if (valid && (eq & lt) == 0) {
+          all[b] += __popcll(eq);
+          shrt[b] += __popcll(es);
         }
       }
     }
