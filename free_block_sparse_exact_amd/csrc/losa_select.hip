@@ -24,7 +24,7 @@
 //   group_order one workgroup: the work groups (32 ranks of one head) by
 //               their first count, descending, stable -> each group's slot;
 //   scatter     one thread per rank: the row into its group's slots -> order;
-//   compact     one workgroup per row: block j is kept iff its sort key is
+//   compact     one wave per row: block j is kept iff its sort key is
 //               <= kappa; write kept indices ascending at row_ptr[row].
 //
 // The same chunk / offsets / place kernels also serve two other list
@@ -626,43 +626,36 @@ __global__ __launch_bounds__(256) void offsets_kernel(int nk, int nchunk, int cp
   block_exclusive_scan_i32(chunk_sum, nchunk, chunk_sum, row_ptr + rows, wsum);
 }
 
-// One workgroup per row: ascending compaction of {j : key_j <= kappa}.
-__global__ __launch_bounds__(kSelThreads) void compact_kernel(const Geom g, const float* __restrict__ M,
-                                                              const uint64_t* __restrict__ kappa,
-                                                              const int32_t* __restrict__ row_ptr,
-                                                              int32_t* __restrict__ col_idx) {
-  __shared__ int wsum[kSelThreads / 64];
-  const int row = blockIdx.x;
+// One wave per row (four rows per workgroup): lane l tests the blocks l,
+// l + 64, ... (coalesced loads, four in flight), and the kept ones -- sort
+// key <= kappa -- are written in index order at row_ptr[row] plus the
+// number kept before them (a ballot per 64 blocks).
+__global__ __launch_bounds__(256) void compact_kernel(const Geom g, const float* __restrict__ M,
+                                                      const uint64_t* __restrict__ kappa,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      int32_t* __restrict__ col_idx) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= g.rows()) return;  // whole waves only
   const int nk = g.nk;
   const float* Mrow = M + (int64_t)row * nk;
   const uint64_t kap = kappa[row];
-  const int per = (nk + kSelThreads - 1) / kSelThreads;
-  const int j0 = threadIdx.x * per;
-  unsigned flags = 0;  // per <= 16 since nk <= 4096
-  int cnt = 0;
-  for (int t = 0; t < per; ++t) {
-    const int j = j0 + t;
-    if (j < nk && sort_key(sanitized_bits(Mrow[j]), j) <= kap) {
-      flags |= 1u << t;
-      ++cnt;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int pos = row_ptr[row];
+  for (int j0 = 0; j0 < nk; j0 += 4 * kWave) {
+    bool keep[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * kWave + lane;
+      keep[u] = j < nk && sort_key(sanitized_bits(Mrow[j]), j) <= kap;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t m = __ballot(keep[u]);
+      if (keep[u]) col_idx[pos + __popcll(m & lt)] = j0 + u * kWave + lane;
+      pos += __popcll(m);
     }
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int v = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int ww = 0; ww < kSelThreads / 64; ++ww)
-    if (ww < w) before += wsum[ww];
-  int pos = row_ptr[row] + before + v - cnt;
-  for (int t = 0; t < per; ++t)
-    if (flags & (1u << t)) col_idx[pos++] = j0 + t;
 }
 
 // One workgroup (kOrderChunk threads) per chunk of rows.  row_ptr of the
@@ -929,7 +922,7 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
     hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.kappa);
   }
   launch_offsets_and_order(g, ws, row_ptr, order, st);
-  hipLaunchKernelGGL(compact_kernel, dim3(rows), dim3(kSelThreads), 0, st, g, M, (const uint64_t*)ws.kappa,
+  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, g, M, (const uint64_t*)ws.kappa,
                      (const int32_t*)row_ptr, col_idx);
   return hipGetLastError();
 }
