@@ -293,6 +293,99 @@ def test_recall_at_construction_and_coverage():
         assert O.coverage(rp, 1, 2, 16, 16) == rp[-1] / 512.0
 
 
+def test_recall_ragged_query_block_hand_worked():
+    """Motivation Summary (Recall): the page's block mass sums over a query
+    block's rows, so a block of 36 valid rows weighs 36/64 of a full one.
+    N = 100, R = 64 (rows 64 and 36), C = 50, two heads; masses in row-mean
+    form (dyadic, exact in fp64):
+      head 0: block 0 [3/4, 1/4] keeps {0}; block 1 [1/2, 1/2] keeps {1}
+      head 1: block 0 [1/8, 7/8] keeps {0, 1}; block 1 [1, 0] keeps {1}
+    kept = 64*3/4 + 36*1/2 + 64*1 + 36*0 = 130 of 2*(64 + 36) = 200 rows of
+    mass: recall = 13/20 (an unweighted mean of row recalls gives 9/16)."""
+    M = np.array([[[[0.75, 0.25], [0.5, 0.5]], [[0.125, 0.875], [1.0, 0.0]]]])
+    row_ptr = np.array([0, 1, 2, 4, 5])
+    col_idx = np.array([0, 1, 0, 1, 1], np.int32)
+    assert Fraction(O.recall(M, row_ptr, col_idx, 100, 64)).limit_denominator(1000) == Fraction(13, 20)
+    assert abs(O.recall(M, row_ptr, col_idx, 100, 64) - 0.65) < 1e-15
+    # a full last block (N = 128): equal weights, recall = (3/4 + 1/2 + 1 + 0) / 4
+    assert abs(O.recall(M, row_ptr, col_idx, 128, 64) - 0.5625) < 1e-15
+
+
+def test_recall_equals_kept_probability_over_queries():
+    """Recall from its definition on the attention itself: with the page's
+    un-normalised masses the total is one unit per valid query, so recall =
+    (1/(H*N)) * sum over valid queries q of the attention probability on the
+    keys of q's kept blocks -- computed here query by query with explicit
+    exponentials (ragged query and key blocks: N = 100, R = 64, C = 32)."""
+    rng = np.random.default_rng(21)
+    N, Na, R, C, H, d = 100, 128, 64, 32, 2, 8
+    q, k, _ = _rand_qkv(rng, 1, H, Na, d, N, scale_q=3.0)
+    M = O.block_mass(q, k, N, R, C)
+    rp, ci = O.select_contract(M.astype(np.float32), 0.6)
+    n_q = 2
+    kept_prob = 0.0
+    for h in range(H):
+        for qi in range(N):
+            r = h * n_q + qi // R
+            blocks = set(int(j) for j in ci[rp[r]:rp[r + 1]])
+            s = [sum(q[0, h, qi, t] * k[0, h, kk, t] for t in range(d)) / math.sqrt(d) for kk in range(N)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            z = sum(e)
+            kept_prob += sum(e[kk] for kk in range(N) if kk // C in blocks) / z
+    assert abs(O.recall(M, rp, ci, N, R) - kept_prob / (H * N)) < 1e-12
+
+
+def test_coverage_rectangular_blocks_hand_worked():
+    """Motivation Summary (Coverage): the kept share of the n_q x n_k block
+    pairs, averaged over heads.  N = 256, R = 128, C = 64: n_q = 2, n_k = 4;
+    head 0 keeps 3 and 1 blocks, head 1 keeps 4 and 2: (4/8 + 6/8) / 2 = 5/8."""
+    rp = np.array([0, 3, 4, 8, 10])
+    assert O.coverage(rp, 1, 2, 2, 4) == 0.625
+    # the same rows as two batches of one head: the average runs over both
+    assert O.coverage(rp, 2, 1, 2, 4) == 0.625
+    # one head, one query block of 4 key blocks, 1 kept: 1/4
+    assert O.coverage(np.array([0, 1]), 1, 1, 1, 4) == 0.25
+
+
+def test_p_fixed_hand_worked():
+    """The selection target's p in 32-bit fixed point, floor(p * 2^32 + 1/2)
+    (round half up), worked by hand from the exact binary values of p:
+      0.99  * 2^32 = 4252017623.04...  -> 4252017623
+      0.995 * 2^32 = 4273492459.52...  -> 4273492460 (floor would give ...459)
+      0.9   * 2^32 = 3865470566.4...   -> 3865470566
+      0.5   * 2^32 = 2^31 exactly
+      5 * 2^-33 * 2^32 = 2.5 exactly    -> 3 (half rounds up; half-to-even gives 2)
+      1.0 -> 2^32 (keep every block)."""
+    assert O.p_fixed(0.99) == 4252017623
+    assert O.p_fixed(0.995) == 4273492460
+    assert O.p_fixed(0.9) == 3865470566
+    assert O.p_fixed(0.5) == 2147483648
+    assert O.p_fixed(5.0 * 2.0 ** -33) == 3
+    assert O.p_fixed(1.0) == 4294967296
+    for bad in (0.0, -0.5, 1.0000001, float("nan")):
+        with pytest.raises(ValueError):
+            O.p_fixed(bad)
+
+
+def test_p_fixed_rounding_decides_a_cut():
+    """A row where rounding p * 2^32 (rather than flooring it) changes the cut.
+    p = 0.995: P = 4273492460, the floor 4273492459 = P_f.  Masses u_j * 2^-40
+    with units u = (4262754816, 10737643, 10737419, 10737418) (each exact in
+    fp32; sum 2^32).  The maximum lies in [2^-9, 2^-8), so e = -8 and the
+    contract rule's units are u_j * 2^19, total 2^51, T = P * 2^19.  The
+    first two blocks in mass order sum to exactly P_f * 2^19: they reach
+    the target when P = P_f and fall one unit of P short when P = P_f + 1."""
+    u = [4262754816, 10737643, 10737419, 10737418]
+    assert sum(u) == 1 << 32 and u[0] + u[1] == 4273492459
+    masses = np.array([x * 2.0 ** -40 for x in u], np.float32)
+    assert [int(float(m) * 2.0 ** 40) for m in masses] == u  # exact in fp32
+    kept, s = O.select_contract_row(masses, 0.995)
+    assert s == 3 and kept.tolist() == [0, 1, 2]
+    kept, s = O.select_contract_row(masses, 4273492459 / 2.0 ** 32)
+    assert s == 2 and kept.tolist() == [0, 1]
+
+
 def test_budget_order():
     # two heads of three rows, counts (3, 2, 3) and (1, 2, 2); each head's
     # three rows fit one group: head 0's group (first row: count 3) runs
