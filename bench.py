@@ -4,10 +4,12 @@ One step = one pass of the whole path over one synthetic layer:
   losa_block_mass (exact masses) -> losa_select (top-p lists + budget order)
   -> losa_sparse_attn (frozen-pattern attention).
 Inputs are resident in HBM before the timed region; every buffer and
-workspace is allocated before it.  Default workload: the Wan2.1-1.3B 480p
-layer shape (12 heads x 128, 21x30x52 = 32760 tokens, 64-token blocks,
-p = 0.99, bf16).  ``--workload 4`` runs the 50-step frozen-reuse trajectory
-(construction at step 2, per-head p, Q/K drift).
+workspace is allocated before it.  Default workload: the largest layer, the
+HunyuanVideo 720p shape (24 heads x 128, 33x45x80 = 118800 tokens,
+128-token blocks, p = 0.99, bf16); ``--workload 1`` is the Wan2.1-1.3B 480p
+shape (12 heads x 128, 32760 tokens, 64-token blocks), ``--workload 2`` the
+Wan2.1-14B 720p shape.  ``--workload 4`` runs the 50-step frozen-reuse
+trajectory (construction at step 2, per-head p, Q/K drift).
 
 Prints ONE JSON line.  value = kept-block TFLOP/s of the sparse attention
 (4 * d * R * C * kept blocks / time of one losa_sparse_attn call, measured
@@ -20,11 +22,11 @@ hash to the version that was measured (null otherwise).
 Other modes (used to produce the committed profile summaries):
   --copy-calibration    run a plain 1 GiB device copy three times (for
                         scaling rocprofv3 FETCH_SIZE/WRITE_SIZE);
-  --summarize-pmc F W CF CW
-                        write the traffic summary from the counter CSVs of a
-                        FETCH_SIZE run F and a WRITE_SIZE run W of this
-                        benchmark, and of the copy calibration under the same
-                        two counters (CF, CW);
+  --summarize-pmc WL F W CF CW
+                        write the traffic summary of workload WL from the
+                        counter CSVs of a FETCH_SIZE run F and a WRITE_SIZE
+                        run W of this benchmark, and of the copy calibration
+                        under the same two counters (CF, CW);
   --summarize-trace DIR NAME "CMD"
                         write profiles/NAME.md from the kernel statistics of a
                         rocprofv3 --kernel-trace --stats run (DIR) of the
@@ -57,7 +59,8 @@ sys.path.insert(0, ROOT)
 METRIC = "block-sparse attn ms & effective TFLOP/s at p=0.99 (1 GPU); mass+select ms"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_wan13b_480p.json")
+def traffic_file(workload_name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_name}.json")
 _CSRC = "free_block_sparse_exact_amd/csrc/"
 # sources each call's kernels are built from (a traffic figure is reported only while they are unchanged)
 CALL_SOURCES = {
@@ -66,11 +69,21 @@ CALL_SOURCES = {
     "losa_block_mass": [_CSRC + "losa_mass.hip", _CSRC + "losa_pack.hpp", _CSRC + "losa_device.hpp",
                         _CSRC + "losa_blocksum.hpp", "free_block_sparse_exact_amd/_build.py"],
 }
+CALL_SOURCES["losa_select"] = [_CSRC + "losa_select.hip", _CSRC + "losa_device.hpp", _CSRC + "losa_internal.hpp",
+                               "free_block_sparse_exact_amd/_build.py"]
 # kernel name fragment -> (part, call) for the traffic summary
 PMC_KERNELS = [("attn_bf16_kernel", "attn", "losa_sparse_attn"),
                ("pack_kv_kernelILi128ELb1", "pack_kv", "losa_sparse_attn"),
                ("mass_bf16_kernel", "mass", "losa_block_mass"),
-               ("pack_kv_kernelILi128ELb0", "pack_k", "losa_block_mass")]
+               ("pack_kv_kernelILi128ELb0", "pack_k", "losa_block_mass"),
+               ("cut_wave_kernel", "cut", "losa_select"),
+               ("cut_kernel", "cut_wg", "losa_select"),
+               ("chunk_kernel", "chunk", "losa_select"),
+               ("offsets_kernel", "offsets", "losa_select"),
+               ("place_kernel", "place", "losa_select"),
+               ("group_order_kernel", "group_order", "losa_select"),
+               ("scatter_order_kernel", "scatter_order", "losa_select"),
+               ("compact_kernel", "compact", "losa_select")]
 
 
 def log(*a):
@@ -136,16 +149,48 @@ def cpu_baseline(layer, wl, rows_wanted, p, budget_s=20.0):
         "ms_per_step_extrapolated": (t_mass + t_sel + t_attn) / done * rows_total * 1e3,
         "mass_ms_extrapolated": t_mass / done * rows_total * 1e3,
         "sparse_attn_ms_extrapolated": t_attn / done * rows_total * 1e3,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
 
 
-def load_traffic(call: str):
-    """HBM bytes per launch of one library call from the committed PMC summary,
-    if the call's kernel sources are unchanged since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None, "no PMC summary"
-    with open(TRAFFIC_FILE) as f:
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), with the logical CPU count."""
+    name = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name} ({os.cpu_count()} logical CPUs visible)"
+
+
+def xcd_loads(order, counts, qhalves, n_xcd=8, block=32):
+    """Kept blocks per XCD under the sparse attention's dispatch: workgroup
+    bid runs on XCD bid % n_xcd and takes task xcd_block_task(bid) (blocks of
+    32 consecutive tasks dealt to the XCDs round-robin; the tail past the last
+    whole round keeps the identity); task t is query tile t % qhalves of row
+    order[t // qhalves]."""
+    n = len(order) * qhalves
+    bid = np.arange(n)
+    group = n_xcd * block
+    full = n // group * group
+    xcd, local = bid % n_xcd, bid // n_xcd
+    task = np.where(bid >= full, bid, (local // block) * group + xcd * block + (local % block))
+    work = np.asarray(counts)[np.asarray(order)[task // qhalves]]
+    return np.bincount(xcd, weights=work, minlength=n_xcd)
+
+
+def load_traffic(call: str, workload_name: str):
+    """HBM bytes per launch of one library call from the committed PMC summary
+    of this workload, if the call's kernel sources are unchanged since the
+    counters were taken."""
+    path = traffic_file(workload_name)
+    if not os.path.exists(path):
+        return None, "no PMC summary for this workload"
+    with open(path) as f:
         t = json.load(f)
     c = t.get("calls", {}).get(call)
     if c is None:
@@ -177,15 +222,19 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="1")
+    ap.add_argument("--workload", default="3")
     ap.add_argument("--heads", type=int, default=0,
                     help="run only the first HEADS heads of the workload (one GPU's share under head sharding)")
     ap.add_argument("--cpu-rows", type=int, default=16, help="query blocks in the oracle CPU baseline (0: skip)")
+    ap.add_argument("--legs", choices=("all", "step"), default="all",
+                    help="step: time the step only (no construction, reduced-search, refresh, graph and routing "
+                         "legs), e.g. under a profiler")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--refresh-tau", type=float, default=0.75,
                     help="drift threshold of the drift-triggered refresh leg of the reuse workload")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    ap.add_argument("--summarize-pmc", nargs=5,
+                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "NAME", "COMMAND"))
     ap.add_argument("--summarize-clock", nargs=4, metavar=("PMC_DIR", "TRACE_DIR", "NAME", "COMMANDS"))
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_DIR", "NAME", "COMMAND"))
@@ -267,7 +316,8 @@ def main():
     t1 = time.perf_counter()
     log(f"timed {args.steps} steps")
     ms_step = (t1 - t0) * 1e3 / args.steps
-    graph_ms = graph_step_ms(torch, step, stream, args.steps)
+    all_legs = args.legs == "all"
+    graph_ms = graph_step_ms(torch, step, stream, args.steps) if all_legs else None
     mass_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     sel_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
@@ -288,7 +338,7 @@ def main():
                    "frac_hbm_peak": sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
     def traffic_of(call):
-        return load_traffic(call) if wl.wid == "1" and not share else (None, "measured for the Wan2.1-1.3B shape only")
+        return load_traffic(call, wl.name) if not share else (None, "measured for whole layers only")
 
     # The dominant kernel is attn_bf16_kernel (the mass call splits its time over two kernels).
     traffic, traffic_src = traffic_of("losa_sparse_attn")
@@ -299,6 +349,63 @@ def main():
     roofline_mass = {"kernel": "losa_block_mass (pack_kv_kernel + mass_bf16_kernel)",
                      "bound": "mfma", "achieved": mass_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": mass_tflops / PEAK_BF16_TFLOPS, "traffic": traffic, "traffic_source": traffic_src}
+    counts = np.diff(bufs.row_ptr.cpu().numpy().astype(np.int64))
+    per_xcd = xcd_loads(bufs.order.cpu().numpy(), counts, R // 64)
+    routing = None
+    if all_legs:
+        other_legs(F, torch, q, k, v, bufs, geom, wl, stream, dev, kernels, kept_flop)
+        routing = pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev)
+    cpu = None
+    if args.cpu_rows > 0:
+        log("timing the CPU oracle baseline ...")
+        cpu = cpu_baseline(layer, wl, args.cpu_rows, wl.p, args.cpu_budget)
+    sel_traffic, sel_src = traffic_of("losa_select")
+    roofline_select = {"kernel": "losa_select (all its kernels)", "bound": "hbm", "achieved": sel_bytes / (sel_ms * 1e-3) / 1e9,
+                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": sel_traffic,
+                       "traffic_source": sel_src,
+                       "algorithmic_bytes": "4 per mass read + 4 per kept index + 8 per row (row_ptr, order)"}
+    res = {
+        "metric": METRIC,
+        "value": attn_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "graph_ms_per_step": graph_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random-Fourier-feature Q/K + N(0,1) noise and sinks, N(0,1) V; no trained weights)",
+        "config": {"workload": wl.name + (f" (heads 0-{H - 1} of {wl.heads})" if share else ""), "batch": 1,
+                   "heads": H, "head_dim": d, "tokens": N, "tokens_alloc": Na,
+                   "block": R, "k_block": C, "p": wl.p, "parallelism": "single GPU"},
+        "sparse_attn_ms": attn_ms,
+        "mass_select_ms": mass_ms + sel_ms,
+        "mass_ms": mass_ms,
+        "select_ms": sel_ms,
+        "dense_equiv_tflops": dense_flop / (attn_ms * 1e-3) / 1e12,
+        "nnz_blocks": nnz,
+        "coverage": nnz / float(rows * nk),
+        "imbalance_per_xcd_max_over_mean": float(per_xcd.max() / per_xcd.mean()),
+        "kernels": kernels,
+        "roofline": roofline,
+        "roofline_mass": roofline_mass,
+        "roofline_select": roofline_select,
+        "pooled_routing": routing,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+def other_legs(F, torch, q, k, v, bufs, geom, wl, stream, dev, kernels, kept_flop):
+    """Calls timed after the steps, not part of ms_per_step: the construction
+    call, the sparse attention with the masses within its lists, and the
+    drift-triggered refresh's two calls."""
+    N, R, C = wl.tokens, wl.block, wl.key_block
+    H, d = geom.heads, geom.head_dim
     # The construction call (dense attention + exact masses in one pass), timed
     # on its own after the steps; not part of ms_per_step.
     ws_dense = torch.empty(F.losa_dense_attn_mass_workspace(geom), dtype=torch.uint8, device=dev)
@@ -336,42 +443,6 @@ def main():
                                    "note": "sparse attention plus the exact masses within the lists (reduced "
                                            "search); kept-block flops; not in ms_per_step"}
     kernels.update(refresh_calls(F, torch, q, k, bufs, geom, wl, stream, dev))
-    routing = pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev)
-    cpu = None
-    if args.cpu_rows > 0:
-        log("timing the CPU oracle baseline ...")
-        cpu = cpu_baseline(layer, wl, args.cpu_rows, wl.p, args.cpu_budget)
-    res = {
-        "metric": METRIC,
-        "value": attn_tflops,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "graph_ms_per_step": graph_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded random-Fourier-feature Q/K + N(0,1) noise and sinks, N(0,1) V; no trained weights)",
-        "config": {"workload": wl.name + (f" (heads 0-{H - 1} of {wl.heads})" if share else ""), "batch": 1,
-                   "heads": H, "head_dim": d, "tokens": N, "tokens_alloc": Na,
-                   "block": R, "k_block": C, "p": wl.p, "parallelism": "single GPU"},
-        "sparse_attn_ms": attn_ms,
-        "mass_select_ms": mass_ms + sel_ms,
-        "mass_ms": mass_ms,
-        "select_ms": sel_ms,
-        "dense_equiv_tflops": dense_flop / (attn_ms * 1e-3) / 1e12,
-        "nnz_blocks": nnz,
-        "coverage": nnz / float(rows * nk),
-        "kernels": kernels,
-        "roofline": roofline,
-        "roofline_mass": roofline_mass,
-        "pooled_routing": routing,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(res))
 
 
 ROUTING_P = (0.9, 0.95, 0.99, 0.995, 0.999)
@@ -693,9 +764,7 @@ def run_reuse(args, wl):
     nnz = int(rp[-1])
     per_head = counts.reshape(H, nq).sum(axis=1).astype(np.float64)
     order = bufs.order.cpu().numpy()
-    per_xcd = np.zeros(8)
-    for t, r in enumerate(order):
-        per_xcd[t % 8] += counts[r]
+    per_xcd = xcd_loads(order, counts, R // 64)
     mean_sparse = float(np.mean(sparse_ms))
     kept_flop = 4.0 * d * R * C * nnz
     res = {
@@ -720,6 +789,8 @@ def run_reuse(args, wl):
         "coverage_per_head": (per_head / (nq * nk)).tolist(),
         "imbalance_per_head_max_over_mean": float(per_head.max() / per_head.mean()),
         "imbalance_per_xcd_max_over_mean": float(per_xcd.max() / per_xcd.mean()),
+        "imbalance_per_xcd_note": "kept blocks dealt to each XCD by the sparse attention's workgroup mapping "
+                                  "(a static count, not measured busy time)",
         "reduced_search": reduced,
         "drift_refresh": refresh,
     }
@@ -740,10 +811,15 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "repeats": 3}))
 
 
-def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
-    """Per-launch HBM traffic of the mass and sparse-attention calls from
-    rocprofv3 CSVs, scaled by a plain copy of 1 GiB (FETCH_SIZE/WRITE_SIZE
-    are in KiB)."""
+def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Per-launch HBM traffic of the mass, selection and sparse-attention
+    calls of one workload from rocprofv3 CSVs, scaled by a plain copy of
+    1 GiB (FETCH_SIZE/WRITE_SIZE are in KiB).  Kernels launched by more than
+    one call (the selector's scan kernels also serve other list builders) are
+    counted over every launch of the run, so the run should time the plain
+    step only (--steps 1 --warmup 1 --legs step)."""
+    import synthetic as S
+    wl = S.get_workload(workload)
     import csv
 
     def read(d, counter):
@@ -769,20 +845,25 @@ def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     calls = {}
     for key, part, call in PMC_KERNELS:
         f_raw, w_raw = per_launch(fetch, key), per_launch(write, key)
+        if f_raw == 0.0 and w_raw == 0.0:
+            continue  # not launched for this shape
         c = calls.setdefault(call, {"sources_sha256_16": sources_hash(CALL_SOURCES[call]), "kernels": {}, "bytes": 0.0})
         b = f_raw * (ff or 1.0) + w_raw * (wf or 1.0)
         c["kernels"][part] = {"fetch_kib_raw": f_raw / 1024.0, "write_kib_raw": w_raw / 1024.0, "bytes": b}
         c["bytes"] += b
     out = {
-        "workload": "Wan2.1-1.3B 480p layer shape (12 heads x 128, 32760 tokens, 64-token blocks), p = 0.99",
+        "workload": f"{wl.name}: {wl.heads} heads x {wl.head_dim}, {wl.tokens} tokens, {wl.block}-token query "
+                    f"blocks, {wl.key_block}-token key blocks, p = {wl.p}",
         "copy_scale": {"FETCH_SIZE": ff, "WRITE_SIZE": wf},
         "calls": calls,
-        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -o run -- python -u "
-                   "bench.py --steps 1 --warmup 1 --cpu-rows 0; copy scale from rocprofv3 --pmc <same counter> -- "
-                   "python -u bench.py --copy-calibration; summary by python bench.py --summarize-pmc",
+        "command": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -o run -- python -u "
+                   f"bench.py --workload {workload} --steps 1 --warmup 1 --cpu-rows 0 --legs step; copy scale from "
+                   f"rocprofv3 --pmc <same counter> -- python -u bench.py --copy-calibration; summary by python "
+                   f"bench.py --summarize-pmc {workload} DIRS",
     }
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    path = traffic_file(wl.name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 

@@ -59,8 +59,8 @@ __all__ = [
     "STATUS",
 ]
 
-# LOSA_LIBRARY may name another build of the same library (e.g. for A/B timing).
-LIB_PATH = os.environ.get("LOSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblosa.so")
+# The library built next to this file (free_block_sparse_exact_amd._build); no other is ever loaded.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblosa.so")
 
 LOSA_F32 = 0
 LOSA_BF16 = 1
@@ -103,11 +103,12 @@ class losa_shape(ctypes.Structure):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+def load_library() -> ctypes.CDLL:
     """Load liblosa.so and declare its signatures (raises if it is not built)."""
     global _lib
-    if _lib is not None and path == LIB_PATH:
+    if _lib is not None:
         return _lib
+    path = LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m free_block_sparse_exact_amd._build`")
     lib = ctypes.CDLL(path)
@@ -144,8 +145,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res
-    if path == LIB_PATH:
-        _lib = lib
+    _lib = lib
     return lib
 
 
@@ -216,11 +216,28 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _tstream(stream):
+    """The stream a call runs on, as a torch stream: torch's current stream
+    by default, a torch stream as given, or a raw hipStream_t handle."""
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _stream(st) -> int:
+    return st.cuda_stream
+
+
+def _empty(st, *args, **kw):
+    """torch.empty on the call's stream: the caching allocator then ties the
+    memory to that stream, so a buffer freed when the call returns is not
+    handed to work on another stream while the kernels still use it."""
+    import torch
+    with torch.cuda.stream(st):
+        return torch.empty(*args, **kw)
 
 
 def _nbytes(ws) -> int:
@@ -228,13 +245,13 @@ def _nbytes(ws) -> int:
     return 0 if ws is None else ws.numel() * ws.element_size()
 
 
-def _workspace(nbytes: int, device, ws=None):
+def _workspace(nbytes: int, device, ws, st):
     import torch
     if nbytes == 0:
         return None
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _empty(st, nbytes, dtype=torch.uint8, device=device)
 
 
 def losa_abi_version() -> int:
@@ -251,15 +268,16 @@ def losa_block_mass(q, k, tokens: int, q_block: int, k_block: int, softmax_scale
                     out=None, ws=None, stream=None):
     """Exact block masses M [B, H, n_q, n_k] (fp32, row-mean form)."""
     import torch
+    st = _tstream(stream)
     g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
     shp = g.shape(q=q, k=k)
     nbytes = ctypes.c_size_t()
     _check(_L().losa_block_mass_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_block_mass_workspace")
-    ws = _workspace(nbytes.value, q.device, ws)
+    ws = _workspace(nbytes.value, q.device, ws, st)
     if out is None:
-        out = torch.empty((g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
+        out = _empty(st, (g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
     _check(_L().losa_block_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(out), _ptr(ws),
-                                _nbytes(ws), _stream(stream)), "losa_block_mass")
+                                _nbytes(ws), _stream(st)), "losa_block_mass")
     return out
 
 
@@ -277,6 +295,7 @@ def losa_select(M, p: Union[float, Sequence[float]], tokens: int, q_block: int, 
     col_idx has capacity rows*n_k; its used length is row_ptr[-1].
     """
     import torch
+    st = _tstream(stream)
     B, H, nq, nk = M.shape
     Na = tokens_alloc if tokens_alloc is not None else max(nq * q_block, nk * k_block)
     g = Geometry(B, H, int(tokens), Na, head_dim, int(q_block), int(k_block), dtype)
@@ -287,20 +306,20 @@ def losa_select(M, p: Union[float, Sequence[float]], tokens: int, q_block: int, 
     parr = (ctypes.c_double * len(pv))(*pv)
     nbytes = ctypes.c_size_t()
     _check(_L().losa_select_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_select_workspace")
-    ws = _workspace(nbytes.value, M.device, ws)
+    ws = _workspace(nbytes.value, M.device, ws, st)
     rows = g.rows
     dev = M.device
     if row_ptr is None:
-        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+        row_ptr = _empty(st, rows + 1, dtype=torch.int32, device=dev)
     if col_idx is None:
-        col_idx = torch.empty(rows * nk, dtype=torch.int32, device=dev)
+        col_idx = _empty(st, rows * nk, dtype=torch.int32, device=dev)
     if want_order and order is None:
-        order = torch.empty(rows, dtype=torch.int32, device=dev)
+        order = _empty(st, rows, dtype=torch.int32, device=dev)
     if not want_order:
         order = None
     _check(_L().losa_select(ctypes.byref(shp), _ptr(M), parr, len(pv), _ptr(row_ptr), _ptr(col_idx),
                             col_idx.numel(), _ptr(order), _ptr(ws), _nbytes(ws),
-                            _stream(stream)), "losa_select")
+                            _stream(st)), "losa_select")
     return row_ptr, col_idx, order
 
 
@@ -315,17 +334,18 @@ def losa_sparse_attn(q, k, v, row_ptr, col_idx, order, tokens: int, q_block: int
                      softmax_scale: Optional[float] = None, out=None, out_dtype=None, ws=None, stream=None):
     """Frozen-pattern sparse attention -> O [B, H, tokens_alloc, d] (bf16 by default for bf16 inputs)."""
     import torch
+    st = _tstream(stream)
     g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        out = _empty(st, q.shape, dtype=out_dtype or q.dtype, device=q.device)
     odt = {torch.bfloat16: LOSA_BF16, torch.float32: LOSA_F32}[out.dtype]
     shp = g.shape(q=q, k=k, v=v, o=out)
     nbytes = ctypes.c_size_t()
     _check(_L().losa_sparse_attn_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_sparse_attn_workspace")
-    ws = _workspace(nbytes.value, q.device, ws)
+    ws = _workspace(nbytes.value, q.device, ws, st)
     _check(_L().losa_sparse_attn(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
                                  _ptr(order), _ptr(out), odt, _ptr(ws), _nbytes(ws),
-                                 _stream(stream)), "losa_sparse_attn")
+                                 _stream(st)), "losa_sparse_attn")
     return out
 
 
@@ -340,19 +360,20 @@ def losa_dense_attn_mass(q, k, v, tokens: int, q_block: int, k_block: int, softm
                          out=None, out_dtype=None, M=None, ws=None, stream=None):
     """Dense attention and exact block masses in one pass -> (O [B, H, tokens_alloc, d], M [B, H, n_q, n_k])."""
     import torch
+    st = _tstream(stream)
     g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        out = _empty(st, q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if M is None:
-        M = torch.empty((g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
+        M = _empty(st, (g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
     odt = {torch.bfloat16: LOSA_BF16, torch.float32: LOSA_F32}[out.dtype]
     shp = g.shape(q=q, k=k, v=v, o=out)
     nbytes = ctypes.c_size_t()
     _check(_L().losa_dense_attn_mass_workspace(ctypes.byref(shp), ctypes.byref(nbytes)),
            "losa_dense_attn_mass_workspace")
-    ws = _workspace(nbytes.value, q.device, ws)
+    ws = _workspace(nbytes.value, q.device, ws, st)
     _check(_L().losa_dense_attn_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(M), _ptr(out), odt,
-                                     _ptr(ws), _nbytes(ws), _stream(stream)),
+                                     _ptr(ws), _nbytes(ws), _stream(st)),
            "losa_dense_attn_mass")
     return out, M
 
@@ -370,20 +391,21 @@ def losa_sparse_attn_mass(q, k, v, row_ptr, col_idx, order, tokens: int, q_block
     """Sparse attention over the lists and the exact masses within them ->
     (O [B, H, tokens_alloc, d], M [B, H, n_q, n_k], 0 outside the lists)."""
     import torch
+    st = _tstream(stream)
     g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+        out = _empty(st, q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if M is None:
-        M = torch.empty((g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
+        M = _empty(st, (g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
     odt = {torch.bfloat16: LOSA_BF16, torch.float32: LOSA_F32}[out.dtype]
     shp = g.shape(q=q, k=k, v=v, o=out)
     nbytes = ctypes.c_size_t()
     _check(_L().losa_sparse_attn_mass_workspace(ctypes.byref(shp), ctypes.byref(nbytes)),
            "losa_sparse_attn_mass_workspace")
-    ws = _workspace(nbytes.value, q.device, ws)
+    ws = _workspace(nbytes.value, q.device, ws, st)
     _check(_L().losa_sparse_attn_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx),
                                       _ptr(order), _ptr(M), _ptr(out), odt, _ptr(ws), _nbytes(ws),
-                                      _stream(stream)), "losa_sparse_attn_mass")
+                                      _stream(st)), "losa_sparse_attn_mass")
     return out, M
 
 
@@ -398,27 +420,29 @@ def losa_pooled_mass(q, k, tokens: int, q_block: int, k_block: int, softmax_scal
     """Pooled proxy masses P [B, H, n_q, n_k] (fp32): block-mean Q against block-mean K,
     block-weighted softmax over key blocks."""
     import torch
+    st = _tstream(stream)
     g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
     if out is None:
-        out = torch.empty((g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
+        out = _empty(st, (g.batch, g.heads, g.n_q, g.n_k), dtype=torch.float32, device=q.device)
     shp = g.shape(q=q, k=k)
     nbytes = ctypes.c_size_t()
     _check(_L().losa_pooled_mass_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_pooled_mass_workspace")
-    ws = _workspace(nbytes.value, q.device, ws)
+    ws = _workspace(nbytes.value, q.device, ws, st)
     _check(_L().losa_pooled_mass(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(out), _ptr(ws),
-                                 _nbytes(ws), _stream(stream)), "losa_pooled_mass")
+                                 _nbytes(ws), _stream(st)), "losa_pooled_mass")
     return out
 
 
 def losa_retained_mass(M, row_ptr, col_idx, tokens: int, q_block: int, k_block: int, out=None, stream=None):
     """Per-row (kept mass, total mass) of M under the lists -> fp32 [rows, 2]."""
     import torch
+    st = _tstream(stream)
     B, H, nq, nk = M.shape
     g = Geometry(B, H, int(tokens), max(nq * q_block, nk * k_block), 128, int(q_block), int(k_block), LOSA_BF16)
     if out is None:
-        out = torch.empty((g.rows, 2), dtype=torch.float32, device=M.device)
+        out = _empty(st, (g.rows, 2), dtype=torch.float32, device=M.device)
     _check(_L().losa_retained_mass(ctypes.byref(g.shape()), _ptr(M), _ptr(row_ptr), _ptr(col_idx), _ptr(out),
-                                   _stream(stream)), "losa_retained_mass")
+                                   _stream(st)), "losa_retained_mass")
     return out
 
 
@@ -436,6 +460,7 @@ def losa_select_threshold(M, theta: Union[float, Sequence[float]], tokens: int, 
     theta times the running maximum): (row_ptr, col_idx, order or None), as
     losa_select returns them."""
     import torch
+    st = _tstream(stream)
     B, H, nq, nk = M.shape
     Na = tokens_alloc if tokens_alloc is not None else max(nq * q_block, nk * k_block)
     g = Geometry(B, H, int(tokens), Na, 128, int(q_block), int(k_block), LOSA_BF16)
@@ -448,18 +473,18 @@ def losa_select_threshold(M, theta: Union[float, Sequence[float]], tokens: int, 
     _check(_L().losa_select_threshold_workspace(ctypes.byref(shp), ctypes.byref(nbytes)),
            "losa_select_threshold_workspace")
     dev = M.device
-    ws = _workspace(nbytes.value, dev, ws)
+    ws = _workspace(nbytes.value, dev, ws, st)
     rows = g.rows
     if row_ptr is None:
-        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+        row_ptr = _empty(st, rows + 1, dtype=torch.int32, device=dev)
     if col_idx is None:
-        col_idx = torch.empty(rows * nk, dtype=torch.int32, device=dev)
+        col_idx = _empty(st, rows * nk, dtype=torch.int32, device=dev)
     if want_order and order is None:
-        order = torch.empty(rows, dtype=torch.int32, device=dev)
+        order = _empty(st, rows, dtype=torch.int32, device=dev)
     if not want_order:
         order = None
     _check(_L().losa_select_threshold(ctypes.byref(shp), _ptr(M), tarr, len(tv), _ptr(row_ptr), _ptr(col_idx),
-                                      col_idx.numel(), _ptr(order), _ptr(ws), _nbytes(ws), _stream(stream)),
+                                      col_idx.numel(), _ptr(order), _ptr(ws), _nbytes(ws), _stream(st)),
            "losa_select_threshold")
     return row_ptr, col_idx, order
 
@@ -475,6 +500,7 @@ def losa_qk_drift(q, k, q_ref, k_ref, tokens: int, tau: float, q_block: int = 64
     """Drift of Q and K per (batch, head) since the reference step and the heads
     to refresh: (drift fp64 [B, H, 2], refresh int32 [B, H])."""
     import torch
+    st = _tstream(stream)
     if q_ref.shape != q.shape or k_ref.shape != k.shape or q_ref.stride() != q.stride() \
             or k_ref.stride() != k.stride() or {q_ref.dtype, k_ref.dtype, k.dtype} != {q.dtype}:
         raise ValueError("q_ref/k_ref must match q/k in shape, strides and dtype")
@@ -482,13 +508,13 @@ def losa_qk_drift(q, k, q_ref, k_ref, tokens: int, tau: float, q_block: int = 64
     shp = g.shape(q=q, k=k)
     nbytes = ctypes.c_size_t()
     _check(_L().losa_qk_drift_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_qk_drift_workspace")
-    ws = _workspace(nbytes.value, q.device, ws)
+    ws = _workspace(nbytes.value, q.device, ws, st)
     if drift is None:
-        drift = torch.empty((g.batch, g.heads, 2), dtype=torch.float64, device=q.device)
+        drift = _empty(st, (g.batch, g.heads, 2), dtype=torch.float64, device=q.device)
     if refresh is None:
-        refresh = torch.empty((g.batch, g.heads), dtype=torch.int32, device=q.device)
+        refresh = _empty(st, (g.batch, g.heads), dtype=torch.int32, device=q.device)
     _check(_L().losa_qk_drift(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(q_ref), _ptr(k_ref), float(tau),
-                              _ptr(drift), _ptr(refresh), _ptr(ws), _nbytes(ws), _stream(stream)), "losa_qk_drift")
+                              _ptr(drift), _ptr(refresh), _ptr(ws), _nbytes(ws), _stream(st)), "losa_qk_drift")
     return drift, refresh
 
 
@@ -505,6 +531,7 @@ def losa_merge_lists(take_b, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, tokens:
     """Lists of the heads flagged in take_b [B, H] from set b, the others from
     set a: (row_ptr, col_idx, order or None), as losa_select returns them."""
     import torch
+    st = _tstream(stream)
     B, H = take_b.shape
     n_q, n_k = -(-int(tokens) // q_block), -(-int(tokens) // k_block)
     Na = tokens_alloc if tokens_alloc is not None else max(n_q * q_block, n_k * k_block)
@@ -513,17 +540,17 @@ def losa_merge_lists(take_b, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, tokens:
     nbytes = ctypes.c_size_t()
     _check(_L().losa_merge_lists_workspace(ctypes.byref(shp), ctypes.byref(nbytes)), "losa_merge_lists_workspace")
     dev = take_b.device
-    ws = _workspace(nbytes.value, dev, ws)
+    ws = _workspace(nbytes.value, dev, ws, st)
     rows = g.rows
     if row_ptr is None:
-        row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+        row_ptr = _empty(st, rows + 1, dtype=torch.int32, device=dev)
     if col_idx is None:
-        col_idx = torch.empty(rows * n_k, dtype=torch.int32, device=dev)
+        col_idx = _empty(st, rows * n_k, dtype=torch.int32, device=dev)
     if want_order and order is None:
-        order = torch.empty(rows, dtype=torch.int32, device=dev)
+        order = _empty(st, rows, dtype=torch.int32, device=dev)
     if not want_order:
         order = None
     _check(_L().losa_merge_lists(ctypes.byref(shp), _ptr(take_b), _ptr(row_ptr_a), _ptr(col_idx_a),
                                  _ptr(row_ptr_b), _ptr(col_idx_b), _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
-                                 _ptr(order), _ptr(ws), _nbytes(ws), _stream(stream)), "losa_merge_lists")
+                                 _ptr(order), _ptr(ws), _nbytes(ws), _stream(st)), "losa_merge_lists")
     return row_ptr, col_idx, order

@@ -12,14 +12,21 @@
 // bf16 matrix-core path (d in {64, 128}, R in {64, 128}): the sparse
 // attention kernel's structure over the full key range.  One workgroup (four
 // waves, one per SIMD) per 64-query tile; wave kw takes the key BLOCKS
-// j = kw, kw+4, ... (all their 32-key chunks), so each block's sum comes from
-// one wave and one reference.  Per chunk a wave computes p = 2^(s*c - m)
-// against its fixed reference m (first chunk's maximum + 64, log2 units); p
-// rounded to bf16 feeds the P.V product and its normaliser, p in fp32 feeds
-// the block sums.  At the end of a block the wave stores the block sum of each
-// query to the workspace S (as the mass kernel does); after the four waves are
-// merged, lse is known and M follows from S.  The overflow rule and the exact
-// two-pass fallback are the sparse attention kernel's.
+// j = kw, kw+4, ... (all their 32-key chunks).  The four waves share one
+// fixed reference m per query: the largest score of their first chunks
+// (log2 units), exchanged through LDS before the main loop, with no
+// headroom.  Being an actual score of the row, m is at most its log-sum-exp,
+// so each term p = 2^(s*c - m) is at least the probability it stands for: a
+// key of probability >= 2^-126 is never flushed by the exponential, and the
+// block sums keep fp32's relative precision down to there (at most C * 2^-126
+// is lost per mass, from keys of smaller probability).  p rounded to bf16
+// feeds the P.V product and its normaliser, p in fp32 feeds the block sums.
+// At the end of a block the wave stores the block sum of each query to the
+// workspace S (as the mass kernel does); with one reference the partial O,
+// row sums and row totals of the four waves simply add, and M follows from S
+// divided by the row total.  If a chunk's probabilities grow too large (a
+// score more than ~77 above the first chunks' maximum) or O is not finite,
+// the whole workgroup recomputes against the exact maximum of the row.
 //
 // Padding keys of the last block score exactly 0 against the zero rows of
 // the packed K and must leave the softmax: the wave that owns the last block
@@ -41,7 +48,7 @@ namespace losa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kPBound = 65536.0f;  // per-lane chunk sum of the bf16 P: above it, the exact path
+constexpr float kPBound = 1.2089258e24f;  // 2^80: per-lane chunk sum of the bf16 P above it -> the exact path
 
 template <int D, bool kLists>
 __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
@@ -56,6 +63,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   constexpr int LD = D + 4;       // merge slot row stride (floats)
   extern __shared__ float lds[];  // merge slots [4][64][LD] f32, maxima [4][64], row sums [4][64]
   __shared__ float s_ref[4][64], s_tot[4][64], s_f[4][64];
+  __shared__ int s_over;
   const int qhalves = g.R / 64;
   const int rows = g.rows();
   // Lists come in the caller's work order (rows by budget), dealt to the XCDs
@@ -242,26 +250,41 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
     for (int qt = 0; qt < kQT; ++qt) blk[qt] = 0.f;
   };
 
-  constexpr float kHeadroom = 64.0f;
-  bool fallback = false;
-  bf16x8 kop[2][DC], vop[DT];
-  if (nmine > 0) {
-    const int kb = seq_key(0) & ~1;
-    load_k(kb, kop);
-    load_v(kb, vop);
-    f32x4 acc[2][kQT];
-    scores(kop, acc);
-    load_k(seq_key(1) & ~1, kop);
-    if (kb + 32 > g.N) mask_tail(kb, acc);
-    {
-      float mx[kQT];
+  // The query's common reference from the four waves' entries in s_ref.
+  auto common_ref = [&]() {
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) mx[qt] = kNegInf;
-      chunk_max(acc, mx);
-      lanes_max(mx);
+    for (int qt = 0; qt < kQT; ++qt) {
+      float mm = s_ref[0][qt * 16 + lr];
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt) m[qt] = mx[qt] * c + kHeadroom;  // finite: the chunk holds a valid key
+      for (int ww = 1; ww < 4; ++ww) mm = fmaxf(mm, s_ref[ww][qt * 16 + lr]);
+      m[qt] = mm;
     }
+  };
+  auto publish_ref = [&](const float (&mx)[kQT]) {  // lane (lg, lr) writes query lg*16 + lr's entry
+    s_ref[kw][lane] = (lg == 0 ? mx[0] : lg == 1 ? mx[1] : lg == 2 ? mx[2] : mx[3]) * c;
+  };
+  bf16x8 kop[2][DC], vop[DT];
+  f32x4 acc[2][kQT];
+  {
+    float mx[kQT];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) mx[qt] = kNegInf;
+    if (nmine > 0) {
+      const int kb = seq_key(0) & ~1;
+      load_k(kb, kop);
+      load_v(kb, vop);
+      scores(kop, acc);
+      load_k(seq_key(1) & ~1, kop);
+      if (kb + 32 > g.N) mask_tail(kb, acc);
+      chunk_max(acc, mx);
+      lanes_max(mx);  // finite: the chunk holds a valid key
+    }
+    publish_ref(mx);
+    if (threadIdx.x == 0) s_over = 0;
+  }
+  __syncthreads();
+  common_ref();
+  if (nmine > 0) {
     bool over_any = false;
     int win_base = 0;
     int win0 = key_window(0), win1 = key_window(64);
@@ -299,16 +322,25 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
         for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = accn[kt][qt];
       over_any |= over;
     }
-    fallback = __any(over_any);
+    // O itself must be finite (its probabilities may reach 2^80)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) over_any |= !(__builtin_fabsf(o[dt][qt][e]) <= 3.0e38f);
+    if (__any(over_any) && lane == 0) s_over = 1;
   }
-  if (fallback) {
-    // Exact maximum over this wave's keys, then O, the row sums and the block
-    // sums again against it (all probabilities <= 1).
+  __syncthreads();
+  if (s_over) {
+    // Exact maximum of the row over every wave's keys, then O, the row sums
+    // and the block sums again against it (all probabilities <= 1).
     tot = 0.f;
+    float mx[kQT];
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       l[qt] = 0.f;
-      m[qt] = kNegInf;
+      mx[qt] = kNegInf;
       blk[qt] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -316,25 +348,26 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
     for (int t = 0; t < nmine; ++t) {
       const int kb2 = seq_key(t) & ~1;
       load_k(kb2, kop);
-      f32x4 acc[2][kQT];
-      scores(kop, acc);
-      if (kb2 + 32 > g.N) mask_tail(kb2, acc);
-      chunk_max(acc, m);
+      f32x4 acc2[2][kQT];
+      scores(kop, acc2);
+      if (kb2 + 32 > g.N) mask_tail(kb2, acc2);
+      chunk_max(acc2, mx);
     }
-    lanes_max(m);
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) m[qt] *= c;
+    lanes_max(mx);
+    publish_ref(mx);  // every wave read the first references before the barrier above
+    __syncthreads();
+    common_ref();
     for (int t = 0; t < nmine; ++t) {
       const int key = seq_key(t);
       const int kb2 = key & ~1, jt = key >> c_shift;
       const bool ends = (key & 1) != 0;
       load_k(kb2, kop);
       load_v(kb2, vop);
-      f32x4 acc[2][kQT];
-      scores(kop, acc);
-      if (kb2 + 32 > g.N) mask_tail(kb2, acc);
+      f32x4 acc2[2][kQT];
+      scores(kop, acc2);
+      if (kb2 + 32 > g.N) mask_tail(kb2, acc2);
       bf16x8 pop[kQT];
-      probs(acc, pop);
+      probs(acc2, pop);
       pv(vop, pop);
       if (ends) block_end(jt);
     }
@@ -345,53 +378,39 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
   for (int qt = 0; qt < kQT; ++qt) {
     l[qt] = rows_sum(l[qt]);
   }
-  // Reference and block-sum total of the query this lane stored (lg*16 + lr).
-  s_ref[kw][lane] = lg == 0 ? m[0] : lg == 1 ? m[1] : lg == 2 ? m[2] : m[3];
+  // Block-sum total of the query this lane stored (lg*16 + lr).
   s_tot[kw][lane] = tot;
 
   // Merge the four key groups for O in one step: every wave parks its partial
-  // O, maxima and row sums in its own LDS slot, then wave kw combines dims
-  // [kw*D/4, (kw+1)*D/4) of all 64 queries from the four slots and stores them.
+  // O and row sums in its own LDS slot, then wave kw adds up dims
+  // [kw*D/4, (kw+1)*D/4) of all 64 queries from the four slots and stores
+  // them (one reference for all four: plain sums).
   {
     constexpr int DTW = DT / 4;
     float* slot = lds + kw * (64 * LD);
-    float* sm = lds + 4 * 64 * LD;  // [4][64] maxima
-    float* sl = sm + 4 * 64;        // [4][64] row sums
+    float* sl = lds + 4 * 64 * LD + 4 * 64;  // [4][64] row sums
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       const int qi = qt * 16 + lr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(slot + qi * LD + dt * 16 + lg * 4) = o[dt][qt];
-      if (lg == 0) {
-        sm[kw * 64 + qi] = m[qt];
-        sl[kw * 64 + qi] = l[qt];
-      }
+      if (lg == 0) sl[kw * 64 + qi] = l[qt];
     }
     __syncthreads();
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       const int qi = qt * 16 + lr;
-      float mw[4], a[4], mm = kNegInf, lt = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        mw[w] = sm[w * 64 + qi];
-        mm = fmaxf(mm, mw[w]);
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        a[w] = mw[w] == kNegInf ? 0.f : fast_exp2(mw[w] - mm);
-        lt += a[w] * sl[w * 64 + qi];
-      }
+      const float lt = (sl[qi] + sl[64 + qi]) + (sl[128 + qi] + sl[192 + qi]);
       const int qrow = row0 + qi;
       const float inv = (qrow < g.N && lt > 0.f) ? 1.0f / lt : 0.f;
       const int64_t obase = b * g.os[0] + h * g.os[1] + (int64_t)qrow * g.os[2];
 #pragma unroll
       for (int dd = 0; dd < DTW; ++dd) {
         const int dt = kw * DTW + dd;
-        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          v += *reinterpret_cast<const f32x4*>(lds + w * (64 * LD) + qi * LD + dt * 16 + lg * 4) * a[w];
+        const float* src = lds + qi * LD + dt * 16 + lg * 4;
+        f32x4 v = (*reinterpret_cast<const f32x4*>(src) + *reinterpret_cast<const f32x4*>(src + 64 * LD)) +
+                  (*reinterpret_cast<const f32x4*>(src + 2 * 64 * LD) +
+                   *reinterpret_cast<const f32x4*>(src + 3 * 64 * LD));
         v *= inv;
         const int d0 = dt * 16 + lg * 4;
         if (o_bf16) {
@@ -406,19 +425,12 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
     }
   }
 
-  // Masses: lse of the stored query, this wave's factor 2^(m - lse) (0 for
-  // padding rows), then M from S (s_ref/s_tot were written before the merge's
-  // barrier).
+  // Masses: the stored query's factor 1 / (its row total against the common
+  // reference; 0 for padding rows), then M from S (s_tot was written before
+  // the merge's barrier).
   {
-    float mm = kNegInf;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, s_ref[ww][lane]);
-    float lt = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww)
-      if (s_ref[ww][lane] != kNegInf) lt += s_tot[ww][lane] * fast_exp2(s_ref[ww][lane] - mm);
-    const float mine = s_ref[kw][lane];
-    s_f[kw][lane] = (row0 + lane < g.N && mine != kNegInf) ? fast_exp2(mine - mm) / lt : 0.f;
+    const float lt = (s_tot[0][lane] + s_tot[1][lane]) + (s_tot[2][lane] + s_tot[3][lane]);
+    s_f[kw][lane] = (row0 + lane < g.N && lt > 0.f) ? 1.0f / lt : 0.f;
     __syncthreads();  // every lane reads all 64 factors of its wave
     const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
     float* Mrow = Mout + ((int64_t)qsub * rows + row) * g.nk;

@@ -9,19 +9,19 @@
 // bf16 matrix-core path (d in {64, 128}, R in {64, 128}): ONE pass over K.
 // A workgroup owns one query block (R/64 groups of 64 rows, four waves per
 // group); the waves of a group split the KEY BLOCKS (wave w takes blocks
-// j = w, w+4, ...).  For every query a wave fixes a reference m at its first
-// chunk's maximum plus kHeadroom (log2 units; scores are pre-multiplied by
-// scale*log2(e)), sums 2^(s*c - m) per key block, writes that per-(query,
-// block) sum to a workspace S and keeps the row total.  Once the four waves
-// are merged, lse_q is known, and the workgroup reads S back:
-//   M[i,j] = (1/rows) * sum_q S[q,j] * 2^(m_q,w(j) - lse_q).
+// j = w, w+4, ...).  For every query the group fixes one reference m, the
+// largest score of the waves' first chunks (log2 units; scores are
+// pre-multiplied by scale*log2(e)); each wave sums 2^(s*c - m) per key block,
+// writes that per-(query, block) sum to a workspace S and keeps the row
+// total.  Once the four waves' totals are added, the workgroup reads S back:
+//   M[i,j] = (1/rows) * sum_q S[q,j] / total_q.
 // The scores and exponentials are computed once (a two-pass form computes
 // both twice); S costs 4 bytes per (query row, key block) of HBM traffic each
 // way.  S^T = K Q^T is formed with 16x16x32 bf16 MFMA: lane l owns query
 // (l & 15) of each 16-query tile and 4 keys per 16-key tile.
 //
 // fp32 inputs (and bf16 shapes outside the matrix-core path) take a SIMT
-// two-pass path: row log-sum-exp first, then the block sums.
+// two-pass path: row maximum and sum first, then the block sums.
 #include "losa_blocksum.hpp"
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
@@ -31,7 +31,6 @@ namespace losa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kPosInf = __builtin_huge_valf();
 
 // ------------------------------------------------------------------ bf16 MFMA
 
@@ -96,18 +95,31 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
 }
 
 // Grid: B*H*nq workgroups of 256*QG threads (QG = R/64 query groups), two
-// waves per SIMD.  A term 2^(s*c - m) can only overflow if a score exceeds the
-// wave's first-chunk maximum by more than ~190 (log2 units); terms more than
-// ~60 below the row maximum flush to 0, negligible against it.  If a block sum
-// or the row total leaves [0, 2^100] (or m is not finite), the wave recomputes
-// its blocks against its exact maximum instead, overwriting its S entries.
+// waves per SIMD.
+//
+// Reference.  The four waves of a query group share one reference per query:
+// the largest score of their first chunks, exchanged through LDS before the
+// sweep (no headroom).  It is an actual score of the row, so it is at most
+// the row's log-sum-exp: every term 2^(s*c - m) is at least the probability
+// it stands for.  A key whose probability is a normal fp32 number (>= 2^-126)
+// therefore never lands in the range the exponential flushes to zero, and the
+// masses keep fp32's relative precision down to that range; only keys of
+// probability below 2^-126 may be lost, at most C * 2^-126 per mass.  With
+// one reference per query the row total is a plain sum over the waves and the
+// per-query factor is 1 / total: no exponential of a reference difference,
+// which could itself flush when the waves' first chunks differ widely.
+//
+// A term can only exceed 1 when a later score exceeds the first chunks'
+// maximum; if a block sum or a row total leaves [0, 2^100] (a score ~83 above
+// it; or a non-finite input), the whole workgroup recomputes against the
+// exact maximum of the row (every term <= 1), overwriting its S entries.
 template <int D, int QG>
 __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
                                                                      const __bf16* __restrict__ Kp, int nch,
                                                                      float* __restrict__ S, float* __restrict__ M) {
-  constexpr float kHeadroom = 64.0f;
   constexpr float kSumBound = 1.2676506e30f;  // 2^100
   __shared__ float s_ref[QG][4][64], s_tot[QG][4][64], s_f[QG][4][64];
+  __shared__ int s_over;
   extern __shared__ float part[];  // [QG][nk] per-group partial masses (QG > 1)
   const int rows = g.B * g.H * g.nq;
   const int task = xcd_task(blockIdx.x, rows);
@@ -136,65 +148,103 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
   // stores): two values swapped with the lane 32 away, then one with the lane
   // 16 away.
   auto reduce_mine = [&](const float (&v)[4]) -> float { return rows_sum_own(v); };
+  // The query group's common reference for the queries of this lane's four
+  // tiles, from the four waves' entries in s_ref (scaled, log2 units).
+  float m[4];
+  auto common_ref = [&]() {
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      float mm = s_ref[grp][0][qt * 16 + lr];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) mm = fmaxf(mm, s_ref[grp][ww][qt * 16 + lr]);
+      m[qt] = mm;
+    }
+  };
+  auto publish_ref = [&](const float (&mx)[4]) {  // lane (lg, lr) holds query lg*16 + lr's entry
+    s_ref[grp][kw][lane] = (lg == 0 ? mx[0] : lg == 1 ? mx[1] : lg == 2 ? mx[2] : mx[3]) * c;
+  };
 
-  // One sweep over my chunks against the reference m (fixed_from_first: m is
-  // set from the first chunk).  tot = this lane's query's total.  Returns
-  // whether a sum left [0, 2^100].
-  float m[4], tot;
-  auto sweep = [&](bool fixed_from_first) -> bool {
-    bool over = false;
-    float blk[4];
+  // One sweep over my chunks against m (acc0: the scores of chunk 0 when
+  // have0).  tot = this lane's query's total.  Returns whether some sum left
+  // [0, 2^100].
+  float tot;
+  bool over;
+  float blk[4];
+  auto consume = [&](const f32x4 (&acc)[2][4], int u) {
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const float nm = -m[qt];
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
+      blk[qt] += sum;
+    }
+    if ((u & (sub - 1)) == sub - 1) {  // block complete: store this lane's query's sum, add it to the total
+      const int j = kw + 4 * (u >> sub_shift);
+      const float v = reduce_mine(blk);
+      tot += v;
+      over |= !(v <= kSumBound);
+      Sg[(int64_t)j * 64 + lane] = v;  // lane = query lg*16 + lr
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) blk[qt] = 0.f;
+    }
+  };
+  auto sweep = [&](const f32x4 (&acc0)[2][4], bool have0) -> bool {
+    over = false;
     tot = 0.f;
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) blk[qt] = 0.f;
+    if (have0) consume(acc0, 0);
+    const int u0 = have0 ? 1 : 0;
     bf16x8 kop[2][D / 32];
-    load_kchunk<D>(Kpbh, chunk_kb(0), lane, kop);
-    for (int u = 0; u < nu; ++u) {
+    if (u0 < nu) load_kchunk<D>(Kpbh, chunk_kb(u0), lane, kop);
+    for (int u = u0; u < nu; ++u) {
       const int kb = chunk_kb(u);
       f32x4 acc[2][4];
       chunk_scores<D>(q, kop, acc);
       if (u + 1 < nu) load_kchunk<D>(Kpbh, chunk_kb(u + 1), lane, kop);
       if (__builtin_expect(kb + 32 > g.N, 0)) mask_tail(kb, g.N, lg, acc);
-      if (fixed_from_first && u == 0) {
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          float mx = acc[0][qt][0];
-#pragma unroll
-          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, acc[e >> 2][qt][e & 3]);
-          mx = rows_max(mx);
-          m[qt] = mx * c + kHeadroom;  // finite: the first chunk holds a valid key
-        }
-      }
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const float nm = -m[qt];
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
-        blk[qt] += sum;
-      }
-      if ((u & (sub - 1)) == sub - 1) {  // block complete: store this lane's query's sum, add it to the total
-        const int j = kw + 4 * (u >> sub_shift);
-        const float v = reduce_mine(blk);
-        tot += v;
-        over |= !(v <= kSumBound);
-        Sg[(int64_t)j * 64 + lane] = v;  // lane = query lg*16 + lr
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) blk[qt] = 0.f;
-      }
+      consume(acc, u);
     }
     over |= !(tot <= kSumBound);
     return __any(over);
   };
 
+  // Chunk 0's scores and their maximum per query (-inf for a wave without key
+  // blocks), shared through LDS: the common reference.
+  f32x4 acc0[2][4];
+  {
+    float mx[4];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) m[qt] = kNegInf;
+    for (int qt = 0; qt < 4; ++qt) mx[qt] = kNegInf;
+    if (nu > 0) {
+      bf16x8 kop[2][D / 32];
+      load_kchunk<D>(Kpbh, chunk_kb(0), lane, kop);
+      chunk_scores<D>(q, kop, acc0);
+      if (chunk_kb(0) + 32 > g.N) mask_tail(chunk_kb(0), g.N, lg, acc0);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        float t = acc0[0][qt][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) t = fmaxf(t, acc0[e >> 2][qt][e & 3]);
+        mx[qt] = rows_max(t);  // finite: a key block's first chunk holds a valid key
+      }
+    }
+    publish_ref(mx);
+    if (threadIdx.x == 0) s_over = 0;
+  }
+  __syncthreads();
+  common_ref();
   tot = 0.f;
-  if (nu > 0 && sweep(true)) {
-    // Exact maximum over my keys, then the sums again against it (all terms <= 1).
-    bf16x8 kop[2][D / 32];
+  if (nu > 0 && sweep(acc0, true) && lane == 0) s_over = 1;
+  __syncthreads();
+  if (s_over) {
+    // Exact maximum of the row (over every wave's keys), then the sums again
+    // against it: all terms <= 1.
+    float mx[4];
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) m[qt] = kNegInf;
+    for (int qt = 0; qt < 4; ++qt) mx[qt] = kNegInf;
+    bf16x8 kop[2][D / 32];
     for (int u = 0; u < nu; ++u) {
       const int kb = chunk_kb(u);
       load_kchunk<D>(Kpbh, kb, lane, kop);
@@ -204,32 +254,26 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m[qt] = fmaxf(m[qt], acc[e >> 2][qt][e & 3]);
+        for (int e = 0; e < 8; ++e) mx[qt] = fmaxf(mx[qt], acc[e >> 2][qt][e & 3]);
     }
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      m[qt] = rows_max(m[qt]);
-      m[qt] *= c;
-    }
-    sweep(false);
+    for (int qt = 0; qt < 4; ++qt) mx[qt] = rows_max(mx[qt]);
+    publish_ref(mx);  // every wave read the first references before the barrier above
+    __syncthreads();
+    common_ref();
+    tot = 0.f;
+    if (nu > 0) sweep(acc0, false);
   }
 
-  // Merge the four key groups of each query: lse_q, then this wave's factor
-  // 2^(m - lse) for the query its lane stored (padding rows get 0).
-  s_ref[grp][kw][lane] = lg == 0 ? m[0] : lg == 1 ? m[1] : lg == 2 ? m[2] : m[3];  // lane = query lg*16 + lr
+  // Row totals: the four key groups' totals against the common reference add
+  // up directly; the factor for the query this lane stored is 1 / total (0
+  // for padding rows).
   s_tot[grp][kw][lane] = tot;
   __syncthreads();
   float f = 0.f;
   {
-    float mm = kNegInf;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) mm = fmaxf(mm, s_ref[grp][ww][lane]);
-    float l = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww)
-      if (s_ref[grp][ww][lane] != kNegInf) l += s_tot[grp][ww][lane] * fast_exp2(s_ref[grp][ww][lane] - mm);
-    const float mine = s_ref[grp][kw][lane];
-    if (row0 + lane < g.N && mine != kNegInf) f = fast_exp2(mine - mm) / l;
+    const float l = (s_tot[grp][0][lane] + s_tot[grp][1][lane]) + (s_tot[grp][2][lane] + s_tot[grp][3][lane]);
+    if (row0 + lane < g.N) f = 1.0f / l;
   }
   s_f[grp][kw][lane] = f;
   __syncthreads();  // every lane reads all 64 factors of its wave
@@ -257,7 +301,7 @@ __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void lse_simt_kernel(const Geom g, const T* __restrict__ Q,
-                                                      const T* __restrict__ K, float* __restrict__ lse2) {
+                                                      const T* __restrict__ K, float2* __restrict__ ml) {
   const int tiles = (g.N + 63) / 64;
   const int task = blockIdx.x;
   const int bh = task / tiles, t = task - bh * tiles;
@@ -290,13 +334,16 @@ __global__ __launch_bounds__(64) void lse_simt_kernel(const Geom g, const T* __r
     }
     __syncthreads();
   }
-  if (row < g.Na) lse2[(int64_t)bh * g.Na + row] = m + __log2f(s);
+  // the row maximum and the sum against it (log2 units); the block sums are
+  // taken against the maximum, so every key of probability >= 2^-126 yields a
+  // normal term, and divided by the sum afterwards
+  if (row < g.Na) ml[(int64_t)bh * g.Na + row] = float2{m, s};
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(128) void block_simt_kernel(const Geom g, const T* __restrict__ Q,
                                                          const T* __restrict__ K,
-                                                         const float* __restrict__ lse2,
+                                                         const float2* __restrict__ ml,
                                                          float* __restrict__ M) {
   const int task = blockIdx.x;
   const int bh = task / g.nq, i = task - bh * g.nq;
@@ -308,7 +355,8 @@ __global__ __launch_bounds__(128) void block_simt_kernel(const Geom g, const T* 
   float q[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) q[d] = valid ? to_f32(Qbh[(int64_t)row * g.qs[2] + d]) : 0.f;
-  const float l2 = valid ? lse2[(int64_t)bh * g.Na + row] : kPosInf;
+  const float2 rm = valid ? ml[(int64_t)bh * g.Na + row] : float2{0.f, 0.f};
+  const float mref = rm.x, inv_l = valid ? 1.0f / rm.y : 0.f;
   __shared__ float ks[32][D];
   __shared__ float red[128];
   const float c = g.scale_log2;
@@ -327,11 +375,11 @@ __global__ __launch_bounds__(128) void block_simt_kernel(const Geom g, const T* 
         float dot = 0.f;
 #pragma unroll
         for (int d = 0; d < D; ++d) dot = fmaf(q[d], ks[kk][d], dot);
-        tot += fast_exp2(dot * c - l2);
+        tot += fast_exp2(dot * c - mref);
       }
       __syncthreads();
     }
-    red[threadIdx.x] = tot;
+    red[threadIdx.x] = tot * inv_l;
     __syncthreads();
     if (threadIdx.x == 0) {
       float v = 0.f;
@@ -343,12 +391,12 @@ __global__ __launch_bounds__(128) void block_simt_kernel(const Geom g, const T* 
 }
 
 template <typename T, int D>
-hipError_t launch_simt(const Geom& g, const void* Q, const void* K, float* M, float* lse2, hipStream_t st) {
+hipError_t launch_simt(const Geom& g, const void* Q, const void* K, float* M, float2* ml, hipStream_t st) {
   const int tiles = (g.N + 63) / 64;
   hipLaunchKernelGGL((lse_simt_kernel<T, D>), dim3(g.B * g.H * tiles), dim3(64), 0, st, g,
-                     (const T*)Q, (const T*)K, lse2);
+                     (const T*)Q, (const T*)K, ml);
   hipLaunchKernelGGL((block_simt_kernel<T, D>), dim3(g.rows()), dim3(g.R), 0, st, g, (const T*)Q,
-                     (const T*)K, (const float*)lse2, M);
+                     (const T*)K, (const float2*)ml, M);
   return hipGetLastError();
 }
 
@@ -370,15 +418,15 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, fl
 }  // namespace
 
 // Workspace.  Matrix-core path: per-(query row, key block) sums S, fp32
-// [B*H*nq][R/64][nk][64], then the packed K.  SIMT path: the row log-sum-exp
-// in log2 units, fp32 [B*H][N_alloc].
+// [B*H*nq][R/64][nk][64], then the packed K.  SIMT path: per row the maximum
+// score (log2 units) and the sum of 2^(s - max), fp32 pairs [B*H][N_alloc].
 static size_t mass_s_bytes(const Geom& g) {
   return align_up((size_t)g.B * g.H * g.nq * (g.R / 64) * g.nk * 64 * sizeof(float), 256);
 }
 
 size_t mass_ws_bytes(const Geom& g) {
   if (mfma_path(g)) return mass_s_bytes(g) + (size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t);
-  return (size_t)g.B * g.H * g.Na * sizeof(float);
+  return (size_t)g.B * g.H * g.Na * sizeof(float2);
 }
 
 hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, void* ws,
@@ -388,12 +436,12 @@ hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float*
     __bf16* Kp = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(ws) + mass_s_bytes(g));
     return g.D == 128 ? launch_mfma<128>(g, Q, K, M, S, Kp, stream) : launch_mfma<64>(g, Q, K, M, S, Kp, stream);
   }
-  float* lse2 = reinterpret_cast<float*>(ws);
+  float2* ml = reinterpret_cast<float2*>(ws);
   if (g.bf16)
-    return g.D == 128 ? launch_simt<__bf16, 128>(g, Q, K, M, lse2, stream)
-                      : launch_simt<__bf16, 64>(g, Q, K, M, lse2, stream);
-  return g.D == 128 ? launch_simt<float, 128>(g, Q, K, M, lse2, stream)
-                    : launch_simt<float, 64>(g, Q, K, M, lse2, stream);
+    return g.D == 128 ? launch_simt<__bf16, 128>(g, Q, K, M, ml, stream)
+                      : launch_simt<__bf16, 64>(g, Q, K, M, ml, stream);
+  return g.D == 128 ? launch_simt<float, 128>(g, Q, K, M, ml, stream)
+                    : launch_simt<float, 64>(g, Q, K, M, ml, stream);
 }
 
 }  // namespace losa

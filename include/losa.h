@@ -108,20 +108,32 @@ const char* losa_status_string(losa_status status);
  * rows of query block i, so each row of blocks sums to 1.
  *
  * bf16 matrix-core path (head_dim 64/128, q_block 64/128): one pass over
- * K -- per query row and key block, the sum of exp(s - m) against a fixed
- * per-row reference m goes to the workspace, the row's log-sum-exp follows
- * from those sums, and M from the sums scaled by exp(m - LSE); rows whose
- * sums leave a safe range are redone against their exact maximum.  Other
- * shapes: two passes over K (the row log-sum-exp, then exp(s - LSE) summed
- * per key block).  Arithmetic: products and sums in fp32 (bf16 inputs are
- * exact in fp32), exponentials in fp32.
+ * K -- per query row and key block, the sum of exp(s - m) against one fixed
+ * per-row reference m (the largest score among the first keys each wave of
+ * the row's workgroup reads) goes to the workspace; the row total is the sum
+ * of those sums, and M the sums divided by it.  Rows whose sums leave a safe
+ * range (a later score far above m) are redone against their exact maximum.
+ * Other shapes: two passes over K (the row maximum and the sum against it,
+ * then exp(s - max) summed per key block).  Arithmetic: products and sums in
+ * fp32 (bf16 inputs are exact in fp32), exponentials in fp32.
+ *
+ * Dynamic range: m is a score of the row, hence at most its log-sum-exp, so
+ * every key whose attention probability is at least 2^-126 (fp32's smallest
+ * normal number) contributes a normal fp32 term; keys of smaller probability
+ * may be flushed to zero, which changes a mass by at most k_block * 2^-126.
+ * Masses at or above about 2^-110 * k_block / 64 are therefore exact to
+ * fp32 rounding (relative error far below 1e-3), and smaller ones to
+ * k_block * 2^-126 absolute.
  *
  * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
  * ws: at least *bytes from losa_block_mass_workspace.  bf16 matrix-core path:
  *    per-(query row, key block) partial sums, 4 * batch*heads*n_q*q_block*n_k
- *    bytes (805 MB for 12 heads x 32760 tokens, 64-token blocks), then K
- *    repacked in 32-token chunks; other paths: the row log-sum-exp,
- *    4 * batch*heads*tokens_alloc bytes.
+ *    bytes, then K repacked in 32-token chunks.  The partial sums grow with
+ *    the square of the token count: 0.81 GB for 12 heads x 32760 tokens
+ *    (64-token blocks), 14.3 GB for 40 heads x 75600 tokens (64-token
+ *    blocks), 10.6 GB for 24 heads x 118800 tokens (128-token blocks) and
+ *    42.4 GB for the same layer with 128-token query and 32-token key blocks.
+ *    Other paths: the row maximum and sum, 8 * batch*heads*tokens_alloc bytes.
  * ------------------------------------------------------------------------ */
 losa_status losa_block_mass_workspace(const losa_shape* shape, size_t* bytes);
 losa_status losa_block_mass(const losa_shape* shape, const void* Q, const void* K, float* M,

@@ -63,6 +63,19 @@ def mass_rel_err(M_gpu: np.ndarray, M_ref: np.ndarray) -> float:
     return float(np.max(np.abs(M_gpu.astype(np.float64) - M_ref) / M_ref))
 
 
+def check_masses_with_floor(M_gpu, M_ref, label):
+    """Relative error <= MASS_RTOL for masses in fp32's normal range; below
+    2^-126 (unrepresentable in the fp32 output) absolute error <= 2^-126."""
+    tiny = 2.0 ** -126
+    small = M_ref < tiny
+    if small.any():
+        assert np.abs(M_gpu[small] - M_ref[small]).max() <= tiny
+    rel = float((np.abs(M_gpu[~small] - M_ref[~small]) / M_ref[~small]).max())
+    say(f"{label}: mass rel err {rel:.2e} on {(~small).sum()} normal masses ({small.sum()} below 2^-126)")
+    assert rel <= MASS_RTOL
+    return small
+
+
 def row_csr(row_ptr: np.ndarray, col_idx: np.ndarray, r: int) -> np.ndarray:
     return np.asarray(col_idx[int(row_ptr[r]):int(row_ptr[r + 1])])
 

@@ -14,8 +14,8 @@ import torch
 
 import oracle as O
 import synthetic as S
-from tests.gpu_util import (ATTN_ATOL, MASS_RTOL, csr_to_device, layer_to_device, mass_rel_err, row_csr,
-                            say, to_device)
+from tests.gpu_util import (ATTN_ATOL, MASS_RTOL, check_masses_with_floor, csr_to_device, layer_to_device,
+                            mass_rel_err, row_csr, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -276,19 +276,6 @@ def score_gap_inputs(rng, H, Na, d):
     k[:, :, :256] = -a * u + rng.standard_normal((1, H, 256, d)) * 0.3
     v = rng.standard_normal((1, H, Na, d))
     return [S.bf16_bits_from_f32(x.astype(np.float32)) for x in (q, k, v)]
-
-
-def check_masses_with_floor(M_gpu, M_ref, label):
-    """Relative error <= MASS_RTOL for masses in fp32's normal range; below
-    2^-126 (unrepresentable in the fp32 output) absolute error <= 2^-126."""
-    tiny = 2.0 ** -126
-    small = M_ref < tiny
-    if small.any():
-        assert np.abs(M_gpu[small] - M_ref[small]).max() <= tiny
-    rel = float((np.abs(M_gpu[~small] - M_ref[~small]) / M_ref[~small]).max())
-    say(f"{label}: mass rel err {rel:.2e} on {(~small).sum()} normal masses ({small.sum()} below 2^-126)")
-    assert rel <= MASS_RTOL
-    return small
 
 
 @pytest.mark.parametrize("shift", [225.0, 2500.0])

@@ -86,3 +86,38 @@ def test_two_streams_match_one():
         for x, y in zip(got, ref):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
     say("two layers on two streams: every output identical to the one-stream run")
+
+
+def test_side_stream_with_library_allocated_buffers():
+    """Only stream= given: the binding allocates every workspace and output
+    itself, on that stream (so the caching allocator cannot hand a buffer
+    freed at return to other work while the side stream still uses it).
+    Meanwhile torch's current stream allocates and writes buffers of the same
+    sizes.  The results equal the same calls on the current stream."""
+    H, d, p, N, R, C = 4, 128, 0.95, 2000, 64, 64
+    q, k, v = _layer(13, H, N, 2048, d)
+    cur = torch.cuda.current_stream()
+    M0 = F.losa_block_mass(q, k, N, R, C)
+    rp0, ci0, or0 = F.losa_select(M0, p, N, R, C)
+    O0 = F.losa_sparse_attn(q, k, v, rp0, ci0, or0, N, R, C, out_dtype=torch.float32)
+    Od0, Md0 = F.losa_dense_attn_mass(q, k, v, N, R, C, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = [t.cpu() for t in (M0, rp0, or0, O0, Od0, Md0)]
+    nnz = int(rp0[-1].item())
+    ref.append(ci0[:nnz].cpu())
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    for rep in range(3):
+        M = F.losa_block_mass(q, k, N, R, C, stream=side)
+        rp, ci, order = F.losa_select(M, p, N, R, C, stream=side)
+        O = F.losa_sparse_attn(q, k, v, rp, ci, order, N, R, C, out_dtype=torch.float32, stream=side)
+        Od, Md = F.losa_dense_attn_mass(q, k, v, N, R, C, out_dtype=torch.float32, stream=side)
+        # the current stream meanwhile takes and scribbles over fresh memory
+        junk = [torch.full((n,), 249, dtype=torch.uint8, device=q.device) for n in (M0.numel() * 4, 1 << 24)]
+        del junk
+        side.synchronize()
+        got = [t.cpu() for t in (M, rp, order, O, Od, Md)] + [ci[:nnz].cpu()]
+        for x, y in zip(got, ref):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    torch.cuda.synchronize()
+    say("calls on a side stream with library-allocated buffers: identical to the current-stream run")
