@@ -39,6 +39,8 @@ __all__ = [
     "losa_block_mass",
     "losa_select_workspace",
     "losa_select",
+    "losa_select_noalloc",
+    "SELECT_SCRATCH_BYTES",
     "losa_sparse_attn_workspace",
     "losa_sparse_attn",
     "losa_retained_mass",
@@ -64,6 +66,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblosa.so"
 
 LOSA_F32 = 0
 LOSA_BF16 = 1
+SELECT_SCRATCH_BYTES = 32 << 20  # LOSA_SELECT_SCRATCH_BYTES
 STATUS = {
     0: "LOSA_OK",
     1: "LOSA_ERR_NULL",
@@ -124,6 +127,7 @@ def load_library() -> ctypes.CDLL:
         "losa_select_workspace": ([S, sz], i32),
         "losa_select": ([S, P, ctypes.POINTER(ctypes.c_double), i32, P, P, ctypes.c_int64, P, P,
                          ctypes.c_size_t, P], i32),
+        "losa_select_noalloc": ([S, P, ctypes.POINTER(ctypes.c_double), i32, P, P, ctypes.c_int64, P, P], i32),
         "losa_sparse_attn_workspace": ([S, sz], i32),
         "losa_sparse_attn": ([S, P, P, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
         "losa_retained_mass": ([S, P, P, P, P, P], i32),
@@ -320,6 +324,25 @@ def losa_select(M, p: Union[float, Sequence[float]], tokens: int, q_block: int, 
     _check(_L().losa_select(ctypes.byref(shp), _ptr(M), parr, len(pv), _ptr(row_ptr), _ptr(col_idx),
                             col_idx.numel(), _ptr(order), _ptr(ws), _nbytes(ws),
                             _stream(st)), "losa_select")
+    return row_ptr, col_idx, order
+
+
+def losa_select_noalloc(M, p: Union[float, Sequence[float]], tokens: int, q_block: int, k_block: int,
+                        row_ptr, col_idx, order=None, tokens_alloc: Optional[int] = None, head_dim: int = 128,
+                        dtype: int = LOSA_BF16, stream=None):
+    """losa_select without a workspace: the library's own device scratch array
+    holds the selector's scratch.  The caller passes every output (row_ptr,
+    col_idx, and order or None); nothing is allocated.  Returns them."""
+    st = _tstream(stream)
+    B, H, nq, nk = M.shape
+    Na = tokens_alloc if tokens_alloc is not None else max(nq * q_block, nk * k_block)
+    g = Geometry(B, H, int(tokens), Na, head_dim, int(q_block), int(k_block), dtype)
+    if g.n_q != nq or g.n_k != nk:
+        raise ValueError("M does not match tokens/q_block/k_block")
+    pv = [float(p)] if isinstance(p, (int, float)) else [float(x) for x in p]
+    parr = (ctypes.c_double * len(pv))(*pv)
+    _check(_L().losa_select_noalloc(ctypes.byref(g.shape()), _ptr(M), parr, len(pv), _ptr(row_ptr), _ptr(col_idx),
+                                    col_idx.numel(), _ptr(order), _stream(st)), "losa_select_noalloc")
     return row_ptr, col_idx, order
 
 

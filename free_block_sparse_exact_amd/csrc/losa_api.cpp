@@ -117,26 +117,60 @@ losa_status losa_select_workspace(const losa_shape* shape, size_t* bytes) {
   return LOSA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by losa_select and losa_select_noalloc (everything but the
+// workspace); fills g and pt.
+losa_status select_args(const losa_shape* shape, const float* M, const double* p, int32_t n_p,
+                        const int32_t* row_ptr, const int32_t* col_idx, int64_t col_capacity, Geom* g,
+                        losa::PTable* pt) {
+  losa_status st = make_geom(shape, g);
+  if (st != LOSA_OK) return st;
+  if (!M || !p || !row_ptr || !col_idx) return LOSA_ERR_NULL;
+  if (n_p != 1 && n_p != g->H) return LOSA_ERR_INVALID_ARG;
+  if (n_p > 1 && n_p > LOSA_MAX_HEADS_P) return LOSA_ERR_UNSUPPORTED;
+  memset(pt, 0, sizeof *pt);
+  pt->per_head = n_p > 1;
+  for (int t = 0; t < n_p; ++t) {
+    if (!(p[t] > 0.0 && p[t] <= 1.0)) return LOSA_ERR_INVALID_ARG;
+    pt->P[t] = (uint64_t)floor(p[t] * 4294967296.0 + 0.5);
+  }
+  if (col_capacity < (int64_t)g->rows() * g->nk) return LOSA_ERR_CAPACITY;
+  return LOSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 losa_status losa_select(const losa_shape* shape, const float* M, const double* p, int32_t n_p, int32_t* row_ptr,
                         int32_t* col_idx, int64_t col_capacity, int32_t* order, void* ws, size_t ws_bytes,
                         hipStream_t stream) {
   Geom g;
-  losa_status st = make_geom(shape, &g);
-  if (st != LOSA_OK) return st;
-  if (!M || !p || !row_ptr || !col_idx || !ws) return LOSA_ERR_NULL;
-  if (n_p != 1 && n_p != g.H) return LOSA_ERR_INVALID_ARG;
-  if (n_p > 1 && n_p > LOSA_MAX_HEADS_P) return LOSA_ERR_UNSUPPORTED;
   losa::PTable pt;
-  memset(&pt, 0, sizeof pt);
-  pt.per_head = n_p > 1;
-  for (int t = 0; t < n_p; ++t) {
-    if (!(p[t] > 0.0 && p[t] <= 1.0)) return LOSA_ERR_INVALID_ARG;
-    pt.P[t] = (uint64_t)floor(p[t] * 4294967296.0 + 0.5);
-  }
-  if (col_capacity < (int64_t)g.rows() * g.nk) return LOSA_ERR_CAPACITY;
+  const losa_status st = select_args(shape, M, p, n_p, row_ptr, col_idx, col_capacity, &g, &pt);
+  if (st != LOSA_OK) return st;
+  if (!ws) return LOSA_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return LOSA_ERR_WORKSPACE;
   losa::SelectWs layout;
   if (ws_bytes < losa::select_ws_bytes(g, &layout, reinterpret_cast<char*>(ws))) return LOSA_ERR_WORKSPACE;
+  return hip_status(losa::launch_select(g, M, pt, row_ptr, col_idx, order, layout, stream));
+}
+
+losa_status losa_select_noalloc(const losa_shape* shape, const float* M, const double* p, int32_t n_p,
+                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order,
+                                hipStream_t stream) {
+  Geom g;
+  losa::PTable pt;
+  const losa_status st = select_args(shape, M, p, n_p, row_ptr, col_idx, col_capacity, &g, &pt);
+  if (st != LOSA_OK) return st;
+  if (losa::select_ws_bytes(g, nullptr, nullptr) > LOSA_SELECT_SCRATCH_BYTES) return LOSA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (losa::select_scratch(&scratch) != hipSuccess) return LOSA_ERR_HIP;
+  losa::SelectWs layout;
+  losa::select_ws_bytes(g, &layout, reinterpret_cast<char*>(scratch));
   return hip_status(losa::launch_select(g, M, pt, row_ptr, col_idx, order, layout, stream));
 }
 

@@ -59,6 +59,9 @@ constexpr int kGroupRows = 32;    // rows per work group of the budget order (on
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base);
 hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr,
                          int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t stream);
+// Device address of the selector's file-scope scratch array on the current
+// device (looked up once per device).
+hipError_t select_scratch(void** ptr);
 // Online block thresholding: per-head theta (or one for all) by value.
 struct ThetaTable {
   double t[kMaxHeadsP];

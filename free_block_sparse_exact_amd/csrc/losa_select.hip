@@ -50,6 +50,8 @@
 #include "losa_device.hpp"
 #include "losa_internal.hpp"
 
+#include <mutex>
+
 namespace losa {
 namespace {
 
@@ -969,6 +971,35 @@ void launch_offsets_and_order(const Geom& g, const SelectWs& ws, int32_t* row_pt
                      (const int32_t*)ws.gkey, ws.gstart);
   hipLaunchKernelGGL(scatter_order_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, g.nq, ws.ngh,
                      (const int32_t*)ws.ranked, (const int32_t*)ws.gstart, order);
+}
+
+// Scratch of the allocation-free selector: one array per device, placed by
+// the code object loader.  In host code `scratch` names a host-side stand-in,
+// not device memory; the device address comes from hipGetSymbolAddress and is
+// what the kernels are given.
+static __device__ __align__(256) unsigned char scratch[LOSA_SELECT_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t select_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_retained_mass(const Geom& g, const float* M, const int32_t* row_ptr, const int32_t* col_idx,

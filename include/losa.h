@@ -33,9 +33,10 @@
  *   check returns its status and enqueues nothing.  LOSA_ERR_HIP reports a
  *   failed launch (hipGetLastError after the launches).  After any error the
  *   contents of the output buffers are unspecified.  No call throws.
- * Threads.  The library has no mutable global state; calls are thread-safe.
- *   Calls on one stream run in order; two calls writing the same buffers on
- *   different streams race.
+ * Threads.  Calls are thread-safe.  The only mutable global state is the
+ *   per-device address of losa_select_noalloc's scratch array, looked up
+ *   once per device under a lock.  Calls on one stream run in order; two
+ *   calls writing the same buffers on different streams race.
  *
  * Tensor layout.  Q, K, V (and O) are [batch, heads, tokens_alloc, head_dim]
  *   with the element strides given in losa_shape (batch, head, token), the
@@ -64,6 +65,8 @@ extern "C" {
  * carry its own p in losa_select. */
 #define LOSA_MAX_KEY_BLOCKS 4096
 #define LOSA_MAX_HEADS_P 128
+/* Size of the device scratch array behind losa_select_noalloc (32 MiB). */
+#define LOSA_SELECT_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum losa_status {
   LOSA_OK = 0,
@@ -178,6 +181,28 @@ losa_status losa_select_workspace(const losa_shape* shape, size_t* bytes);
 losa_status losa_select(const losa_shape* shape, const float* M, const double* p, int32_t n_p,
                         int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order,
                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Retained-mass block selection that allocates nothing.
+ * For callers that cannot allocate device memory or take a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, rules and results as losa_select (bit for
+ * bit), without ws/ws_bytes: the selector's scratch lives in a file-scope
+ * device array of LOSA_SELECT_SCRATCH_BYTES in the library, one per GPU the
+ * library runs on, held until the process ends.  Its address is looked up
+ * (hipGetSymbolAddress) on the first call on each device, with that device
+ * current; the stream must belong to the current device.  Nothing in the
+ * array needs to start at zero (the kernels clear what they count in).
+ *
+ * Shapes whose losa_select_workspace exceeds LOSA_SELECT_SCRATCH_BYTES are
+ * rejected with LOSA_ERR_WORKSPACE before any HIP call.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different threads without ordering) race and give
+ * unspecified lists; calls ordered on one stream are safe.
+ * ------------------------------------------------------------------------ */
+losa_status losa_select_noalloc(const losa_shape* shape, const float* M, const double* p, int32_t n_p,
+                                int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, int32_t* order,
+                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Frozen-pattern block-sparse attention.

@@ -136,6 +136,27 @@ def test_select_errors(lib):
 
 
 @no_gpu_only
+def test_select_noalloc_errors(lib):
+    """The allocation-free selection checks its arguments like losa_select and
+    refuses shapes whose scratch exceeds its device array, all before any HIP
+    call."""
+    s = shape()
+    rows, nk = 2 * 16, 16
+    p1 = (ctypes.c_double * 1)(0.99)
+
+    def sel(sh=s, p=p1, n_p=1, cap=rows * nk, rp=FAKE):
+        return lib.losa_select_noalloc(ctypes.byref(sh), FAKE, p, n_p, rp, FAKE, cap, None, None)
+
+    assert sel(cap=rows * nk - 1) == CAPACITY
+    assert sel(p=(ctypes.c_double * 1)(0.0)) == INVALID
+    assert sel(n_p=3) == INVALID
+    assert sel(rp=None) == NULL
+    big = geom(heads=127, tokens=4096 * 64 - 5, tokens_alloc=4096 * 64)
+    assert F.losa_select_workspace(big) > F.SELECT_SCRATCH_BYTES
+    assert sel(sh=big.shape(), cap=big.rows * big.n_k) == WORKSPACE
+
+
+@no_gpu_only
 def test_sparse_attn_errors(lib):
     s = shape()
 
