@@ -64,6 +64,19 @@ notes of the repository):
   theta times the largest mass seen so far, block j included -- in scores,
   within ln(1/theta) of the running maximum.  theta in (0, 1]; the
   comparison is made in fp64 on the fp32 masses.
+* On-the-fly block thresholding inside the attention pass (the Sol-Attn
+  page: blocks are chosen while the online softmax runs, by comparing each
+  block's proxy score with a threshold, without materialising the proxy map;
+  the page gives no formula): the proxy of key block j for query block i is
+  the pooled score sbar_ij = scale * qbar_i . kbar_j (block means over valid
+  tokens), weighted by the block's valid keys, a_j = sbar_ij + ln|B_j|; in
+  index order (the online pass's order) block j is kept when
+  a_j >= ln(theta) + max(a_0 .. a_j).  Since the pooled proxy mass is
+  P_j = exp(a_j) / Z, this is the online-thresholding rule above applied to P,
+  decided in the log domain so that Z (and the map P) is never needed.  The
+  decision is taken in fp64 with the interface's fp32 softmax scale widened
+  exactly; softmax over the kept blocks' valid tokens follows.  The page's
+  correction for the skipped blocks is not part of this reading.
 * Drift-triggered refresh (the HASTE page's temporal mask reuse: mask
   prediction is skipped while queries and keys have drifted little since it
   was last made; the page gives no measure): per (batch, head), the drift of
@@ -103,6 +116,8 @@ __all__ = [
     "ORDER_GROUP",
     "select_threshold_row",
     "select_threshold",
+    "pooled_scores",
+    "threshold_inpass_lists",
     "qk_drift",
     "refresh_heads",
     "merge_lists",
@@ -337,6 +352,55 @@ def select_threshold(M32: np.ndarray, theta) -> Tuple[np.ndarray, np.ndarray]:
                 row_ptr.append(row_ptr[-1] + kept.size)
     col_idx = np.concatenate(cols) if cols else np.zeros(0, np.int32)
     return np.asarray(row_ptr, np.int64), col_idx
+
+
+def pooled_scores(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int,
+                  scale: Optional[float] = None) -> np.ndarray:
+    """sbar[b, h, i, j] = scale * qbar_i . kbar_j (fp64): the mean over the valid
+    tokens of query block i against the mean over the valid tokens of key
+    block j.  scale defaults to 1/sqrt(d) rounded to fp32 (the interface
+    carries the softmax scale as an fp32 number)."""
+    B, H, _, d = q.shape
+    sc = float(np.float32(softmax_scale(d, scale)))
+    n_q = -(-n_valid // R)
+    n_k = -(-n_valid // C)
+    qbar = np.stack([q[:, :, i * R:min((i + 1) * R, n_valid)].mean(axis=2) for i in range(n_q)], axis=2)
+    kbar = np.stack([k[:, :, j * C:min((j + 1) * C, n_valid)].mean(axis=2) for j in range(n_k)], axis=2)
+    return np.einsum("bhid,bhjd->bhij", qbar, kbar) * sc
+
+
+def threshold_inpass_lists(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C: int, theta,
+                           scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray, float]:
+    """Kept blocks of on-the-fly block thresholding (module header): per row,
+    in index order, a_j = sbar_ij + ln|B_j| and block j is kept when
+    a_j >= ln(theta_h) + max(a_0 .. a_j).  ``theta`` is a scalar or one value
+    per head, each in (0, 1].  Returns (row_ptr, col_idx ascending, margin):
+    margin is the smallest |a_j - ln(theta_h) - max(a_0 .. a_j)| over all
+    decisions, i.e. how far the closest one lies from a tie."""
+    sbar = pooled_scores(q, k, n_valid, R, C, scale)
+    B, H, n_q, n_k = sbar.shape
+    t_h = np.broadcast_to(np.asarray(theta, dtype=np.float64), (H,))
+    ln_size = np.array([math.log(min(C, n_valid - j * C)) for j in range(n_k)], np.float64)
+    row_ptr = [0]
+    cols: List[np.ndarray] = []
+    margin = math.inf
+    for b in range(B):
+        for h in range(H):
+            ln_t = math.log(float(t_h[h]))
+            for i in range(n_q):
+                a = sbar[b, h, i] + ln_size
+                kept = []
+                run = -math.inf
+                for j in range(n_k):
+                    run = max(run, float(a[j]))
+                    gap = float(a[j]) - (ln_t + run)
+                    if gap >= 0.0:
+                        kept.append(j)
+                    margin = min(margin, abs(gap))
+                cols.append(np.asarray(kept, np.int32))
+                row_ptr.append(row_ptr[-1] + len(kept))
+    col_idx = np.concatenate(cols) if cols else np.zeros(0, np.int32)
+    return np.asarray(row_ptr, np.int64), col_idx, margin
 
 
 def select_float(M: np.ndarray, p) -> Tuple[np.ndarray, np.ndarray, List[Tuple[int, float]]]:

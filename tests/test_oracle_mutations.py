@@ -88,3 +88,47 @@ def test_planted_p_fixed_mistakes_fail(monkeypatch, wrong):
     monkeypatch.setattr(O, "p_fixed", wrong)
     monkeypatch.setattr(OL, "p_fixed", wrong)
     assert _some_pin_fails(P_PINS)
+
+
+# ---- on-the-fly thresholding against the pooled proxy
+
+def _inpass_without_block_sizes(q, k, n_valid, R, C, theta, scale=None):
+    sbar = O.pooled_scores(q, k, n_valid, R, C, scale)
+    B, H, n_q, n_k = sbar.shape
+    t_h = np.broadcast_to(np.asarray(theta, dtype=np.float64), (H,))
+    rp, cols, margin = [0], [], math.inf
+    for b in range(B):
+        for h in range(H):
+            for i in range(n_q):
+                run, kept = -math.inf, []
+                for j in range(n_k):
+                    run = max(run, float(sbar[b, h, i, j]))
+                    if sbar[b, h, i, j] >= math.log(t_h[h]) + run:
+                        kept.append(j)
+                cols.append(np.asarray(kept, np.int32))
+                rp.append(rp[-1] + len(kept))
+    return np.asarray(rp, np.int64), np.concatenate(cols), margin
+
+
+def _pooled_scores_padding_included(q, k, n_valid, R, C, scale=None):
+    B, H, Na, d = q.shape
+    sc = float(np.float32(O.softmax_scale(d, scale)))
+    n_q, n_k = -(-n_valid // R), -(-n_valid // C)
+    qbar = np.stack([q[:, :, i * R:(i + 1) * R].mean(axis=2) for i in range(n_q)], axis=2)
+    kbar = np.stack([k[:, :, j * C:(j + 1) * C].mean(axis=2) for j in range(n_k)], axis=2)
+    return np.einsum("bhid,bhjd->bhij", qbar, kbar) * sc
+
+
+INPASS_PINS = [pins.test_threshold_inpass_hand_worked, pins.test_threshold_inpass_is_the_online_rule_on_pooled_masses,
+               pins.test_pooled_scores_explicit_loops]
+
+
+def test_planted_inpass_mistakes_fail(monkeypatch):
+    assert not _some_pin_fails(INPASS_PINS)
+    with monkeypatch.context() as m:
+        m.setattr(O, "threshold_inpass_lists", _inpass_without_block_sizes)
+        assert _some_pin_fails(INPASS_PINS)
+    with monkeypatch.context() as m:
+        m.setattr(O, "pooled_scores", _pooled_scores_padding_included)
+        m.setattr(OL, "pooled_scores", _pooled_scores_padding_included)
+        assert _some_pin_fails(INPASS_PINS)

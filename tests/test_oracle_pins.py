@@ -736,3 +736,103 @@ def test_threshold_csr_and_per_head():
             for i in range(4):
                 r = O.row_id(b, h, i, 3, 4)
                 assert ci[rp[r]:rp[r + 1]].tolist() == O.select_threshold_row(M[b, h, i], [0.2, 0.6, 0.9][h]).tolist()
+
+
+# ---------------------------------------------------------------- on-the-fly thresholding (pooled proxy)
+
+def _blocky_qk(xs, C, R, n_valid, n_q):
+    """Queries all (1, 0); key block j all (x_j, 0): sbar_ij = scale * x_j."""
+    Na = max(n_q * R, len(xs) * C)
+    q = np.zeros((1, 1, Na, 2))
+    k = np.zeros((1, 1, Na, 2))
+    q[0, 0, :n_valid, 0] = 1.0
+    for j, x in enumerate(xs):
+        k[0, 0, j * C:min((j + 1) * C, n_valid), 0] = x
+    return q, k
+
+
+def test_threshold_inpass_hand_worked():
+    """Sol-Attn page, on-the-fly thresholding (reading in the oracle's header).
+    Scale 1, C = 4, block scores x = (0, 2, 0.5, 1.5), theta = e^-1:
+    a = x + ln|B_j|; full blocks: a = x + ln 4; running max after block 1 is
+    2 + ln 4; block 2: 0.5 + ln 4 < -1 + 2 + ln 4 -> dropped; block 3 (full):
+    1.5 + ln 4 >= 1 + ln 4 -> kept: {0, 1, 3}.  With N = 14 the last block has
+    2 valid keys: a_3 = 1.5 + ln 2 = 2.19 < 1 + ln 4 = 2.39 -> dropped: {0, 1}."""
+    theta = math.exp(-1.0)
+    q, k = _blocky_qk([0.0, 2.0, 0.5, 1.5], 4, 4, 16, 4)
+    rp, ci, margin = O.threshold_inpass_lists(q, k, 16, 4, 4, theta, scale=1.0)
+    assert rp.tolist() == [0, 3, 6, 9, 12] and ci.tolist() == [0, 1, 3] * 4
+    assert abs(margin - 0.5) < 1e-12   # blocks 2 and 3 lie 0.5 below and above the line
+    q, k = _blocky_qk([0.0, 2.0, 0.5, 1.5], 4, 4, 14, 4)
+    rp, ci, margin = O.threshold_inpass_lists(q, k, 14, 4, 4, theta, scale=1.0)
+    assert ci[:rp[1]].tolist() == [0, 1]
+    assert abs(margin - (math.log(2.0) - 0.5)) < 1e-12   # block 3: ln 2 - 0.5 below the line
+
+
+def test_threshold_inpass_is_the_online_rule_on_pooled_masses():
+    """Log-domain decision == the online-thresholding rule applied to the
+    pooled proxy masses P (Z cancels), wherever no decision is a near tie."""
+    rng = np.random.default_rng(31)
+    for n_valid, R, C, theta in ((300, 64, 32, 0.05), (777, 128, 64, 0.2), (1000, 64, 64, 0.01)):
+        Na = max(-(-n_valid // R) * R, -(-n_valid // C) * C)
+        q, k, _ = _rand_qkv(rng, 1, 2, Na, 16, n_valid, scale_q=4.0)
+        rp, ci, margin = O.threshold_inpass_lists(q, k, n_valid, R, C, theta)
+        assert margin > 1e-6
+        P = O.pooled_mass(q, k, n_valid, R, C, scale=float(np.float32(1.0 / 4.0)))
+        rp2, ci2 = O.select_threshold(P.astype(np.float32), theta)
+        assert np.array_equal(rp, rp2) and np.array_equal(ci, ci2)
+
+
+def test_threshold_inpass_limits():
+    """theta tiny keeps every block; theta = 1 keeps exactly the running-maximum
+    records (blocks whose weighted proxy is >= every earlier one)."""
+    rng = np.random.default_rng(32)
+    n_valid, R, C = 500, 64, 32
+    q, k, _ = _rand_qkv(rng, 1, 2, 512, 8, n_valid, scale_q=3.0)
+    n_q, n_k = 8, 16
+    rp, ci, _ = O.threshold_inpass_lists(q, k, n_valid, R, C, 1e-300)
+    assert int(rp[-1]) == 2 * n_q * n_k
+    rp, ci, _ = O.threshold_inpass_lists(q, k, n_valid, R, C, 1.0)
+    sbar = O.pooled_scores(q, k, n_valid, R, C)
+    sizes = [min(C, n_valid - j * C) for j in range(n_k)]
+    for r in range(2 * n_q):
+        h, i = divmod(r, n_q)
+        a = [sbar[0, h, i, j] + math.log(sizes[j]) for j in range(n_k)]
+        records = [j for j in range(n_k) if all(a[j] >= a[t] for t in range(j))]
+        assert ci[rp[r]:rp[r + 1]].tolist() == records
+
+
+def test_pooled_scores_explicit_loops():
+    """sbar by explicit loops over valid tokens (ragged query and key blocks)."""
+    rng = np.random.default_rng(33)
+    n_valid, R, C, d = 45, 16, 8, 3
+    q, k, _ = _rand_qkv(rng, 1, 1, 48, d, n_valid, 2.0)
+    q[0, 0, n_valid:] = 7.0   # padding must not enter the means
+    k[0, 0, n_valid:] = -5.0
+    sbar = O.pooled_scores(q, k, n_valid, R, C, scale=0.5)
+    for i in range(3):
+        rows = range(i * R, min((i + 1) * R, n_valid))
+        qb = [sum(q[0, 0, r, t] for r in rows) / len(rows) for t in range(d)]
+        for j in range(6):
+            keys = range(j * C, min((j + 1) * C, n_valid))
+            kb = [sum(k[0, 0, c, t] for c in keys) / len(keys) for t in range(d)]
+            assert abs(sbar[0, 0, i, j] - 0.5 * sum(qb[t] * kb[t] for t in range(d))) < 1e-13
+
+
+def test_threshold_inpass_blockwise_constant_is_exact_thresholding():
+    """Scores constant on every block pair: the pooled proxy equals the exact
+    masses, so the in-pass lists are the online rule on the exact masses."""
+    rng = np.random.default_rng(34)
+    n_valid, R, C = 200, 32, 64
+    n_q, n_k = 7, 4
+    q = np.zeros((1, 1, 256, 2))
+    k = np.zeros((1, 1, 256, 2))
+    for i in range(n_q):
+        q[0, 0, i * R:min((i + 1) * R, n_valid)] = rng.standard_normal(2) * 3
+    for j in range(n_k):
+        k[0, 0, j * C:min((j + 1) * C, n_valid)] = rng.standard_normal(2) * 3
+    rp, ci, margin = O.threshold_inpass_lists(q, k, n_valid, R, C, 0.1)
+    assert margin > 1e-6
+    M = O.block_mass(q, k, n_valid, R, C, scale=float(np.float32(1.0 / math.sqrt(2))))
+    rp2, ci2 = O.select_threshold(M.astype(np.float32), 0.1)
+    assert np.array_equal(rp, rp2) and np.array_equal(ci, ci2)
