@@ -352,9 +352,11 @@ def main():
     counts = np.diff(bufs.row_ptr.cpu().numpy().astype(np.int64))
     per_xcd = xcd_loads(bufs.order.cpu().numpy(), counts, R // 64)
     routing = None
+    inpass = None
     if all_legs:
         other_legs(F, torch, q, k, v, bufs, geom, wl, stream, dev, kernels, kept_flop)
         routing = pooled_routing(F, torch, q, k, bufs, geom, wl, stream, dev)
+        inpass = inpass_routing(F, torch, q, k, v, bufs, geom, wl, stream, dev)
     cpu = None
     if args.cpu_rows > 0:
         log("timing the CPU oracle baseline ...")
@@ -395,9 +397,68 @@ def main():
         "roofline_mass": roofline_mass,
         "roofline_select": roofline_select,
         "pooled_routing": routing,
+        "inpass_threshold": inpass,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
+
+
+INPASS_THETA = (0.1, 0.01, 0.001)
+
+
+def inpass_routing(F, torch, q, k, v, bufs, geom, wl, stream, dev):
+    """On-the-fly block thresholding inside the attention call
+    (losa_sparse_attn_threshold: pooled proxy, decisions in the kernel, no
+    proxy matrix) against the same rule as three calls (losa_pooled_mass ->
+    losa_select_threshold -> losa_sparse_attn): time, kept-block TFLOP/s,
+    coverage and recall under the exact masses (bufs.M holds them)."""
+    N, R, C, d = geom.tokens, geom.q_block, geom.k_block, geom.head_dim
+    rows, nk = geom.rows, geom.n_k
+    w = torch.tensor(np.tile(np.array([min(R, N - i * R) for i in range(geom.n_q)], np.float64), rows // geom.n_q),
+                     device=dev)
+    M = bufs.M.view(rows, nk).double()
+    total = (M.sum(dim=1) * w).sum()
+    ws_t = torch.empty(F.losa_sparse_attn_threshold_workspace(geom), dtype=torch.uint8, device=dev)
+    cnt = torch.empty(rows, dtype=torch.int32, device=dev)
+    mask = torch.empty((rows, (nk + 31) // 32), dtype=torch.int32, device=dev)
+    P = torch.empty_like(bufs.M)
+    ws_p = torch.empty(F.losa_pooled_mass_workspace(geom), dtype=torch.uint8, device=dev)
+    shifts = torch.arange(32, device=dev, dtype=torch.int32)
+    out = {"theta": list(INPASS_THETA), "inpass_ms": [], "inpass_tflops": [], "three_calls_ms": [],
+           "coverage": [], "recall": [], "same_blocks_as_three_calls": []}
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+    for theta in INPASS_THETA:
+        for e0, e1 in evs:
+            e0.record(stream)
+            F.losa_sparse_attn_threshold(q, k, v, theta, N, R, C, out=bufs.out, kept_count=cnt, kept_mask=mask,
+                                         ws=ws_t, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t_in = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[1:]]))
+        bits = ((mask.unsqueeze(-1) >> shifts) & 1).view(rows, -1)[:, :nk].bool()
+        nnz = int(cnt.sum().item())
+        kept = ((M * bits).sum(dim=1) * w).sum()
+        for e0, e1 in evs:
+            e0.record(stream)
+            F.losa_pooled_mass(q, k, N, R, C, out=P, ws=ws_p, stream=stream)
+            F.losa_select_threshold(P, theta, N, R, C, tokens_alloc=geom.tokens_alloc, row_ptr=bufs.row_ptr,
+                                    col_idx=bufs.col_idx, order=bufs.order, ws=bufs.ws_sel, stream=stream)
+            F.losa_sparse_attn(q, k, v, bufs.row_ptr, bufs.col_idx, bufs.order, N, R, C, out=bufs.out,
+                               ws=bufs.ws_attn, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t_3 = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs[1:]]))
+        out["inpass_ms"].append(t_in)
+        out["inpass_tflops"].append(4.0 * d * R * C * nnz / (t_in * 1e-3) / 1e12)
+        out["three_calls_ms"].append(t_3)
+        out["coverage"].append(nnz / float(rows * nk))
+        out["recall"].append(float(kept / total))
+        out["same_blocks_as_three_calls"].append(int(bufs.row_ptr[-1].item()) == nnz)
+        log(f"in-pass thresholding theta {theta}: {t_in:.3f} ms (three calls {t_3:.3f} ms), coverage "
+            f"{out['coverage'][-1]:.4f}, recall {out['recall'][-1]:.5f}")
+    out["note"] = ("recall under the exact masses of the layer; same_blocks_as_three_calls compares kept-block totals "
+                   "(the three-call path decides on fp32 proxy masses, the in-pass call on fp64 pooled scores)")
+    return out
 
 
 def other_legs(F, torch, q, k, v, bufs, geom, wl, stream, dev, kernels, kept_flop):

@@ -44,6 +44,8 @@ __all__ = [
     "losa_sparse_attn_workspace",
     "losa_sparse_attn",
     "losa_retained_mass",
+    "losa_sparse_attn_threshold_workspace",
+    "losa_sparse_attn_threshold",
     "losa_dense_attn_mass_workspace",
     "losa_dense_attn_mass",
     "losa_sparse_attn_mass_workspace",
@@ -131,6 +133,9 @@ def load_library() -> ctypes.CDLL:
         "losa_sparse_attn_workspace": ([S, sz], i32),
         "losa_sparse_attn": ([S, P, P, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
         "losa_retained_mass": ([S, P, P, P, P, P], i32),
+        "losa_sparse_attn_threshold_workspace": ([S, sz], i32),
+        "losa_sparse_attn_threshold": ([S, P, P, P, ctypes.POINTER(ctypes.c_double), i32, P, i32, P, P, P,
+                                        ctypes.c_size_t, P], i32),
         "losa_dense_attn_mass_workspace": ([S, sz], i32),
         "losa_dense_attn_mass": ([S, P, P, P, P, P, i32, P, ctypes.c_size_t, P], i32),
         "losa_sparse_attn_mass_workspace": ([S, sz], i32),
@@ -370,6 +375,42 @@ def losa_sparse_attn(q, k, v, row_ptr, col_idx, order, tokens: int, q_block: int
                                  _ptr(order), _ptr(out), odt, _ptr(ws), _nbytes(ws),
                                  _stream(st)), "losa_sparse_attn")
     return out
+
+
+def losa_sparse_attn_threshold_workspace(geom: Geometry) -> int:
+    n = ctypes.c_size_t()
+    _check(_L().losa_sparse_attn_threshold_workspace(ctypes.byref(geom.shape()), ctypes.byref(n)),
+           "losa_sparse_attn_threshold_workspace")
+    return n.value
+
+
+def losa_sparse_attn_threshold(q, k, v, theta: Union[float, Sequence[float]], tokens: int, q_block: int,
+                               k_block: int, softmax_scale: Optional[float] = None, out=None, out_dtype=None,
+                               kept_count=None, kept_mask=None, want_kept: bool = True, ws=None, stream=None):
+    """Sparse attention with on-the-fly block thresholding against the pooled
+    proxy (blocks chosen inside the attention kernel, no proxy matrix) ->
+    (O, kept_count int32 [rows] or None, kept_mask int32 [rows, ceil(n_k/32)] or None)."""
+    import torch
+    st = _tstream(stream)
+    g = Geometry.of(q, tokens, q_block, k_block, softmax_scale)
+    if out is None:
+        out = _empty(st, q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if want_kept and kept_count is None:
+        kept_count = _empty(st, g.rows, dtype=torch.int32, device=q.device)
+    if want_kept and kept_mask is None:
+        kept_mask = _empty(st, (g.rows, (g.n_k + 31) // 32), dtype=torch.int32, device=q.device)
+    odt = {torch.bfloat16: LOSA_BF16, torch.float32: LOSA_F32}[out.dtype]
+    shp = g.shape(q=q, k=k, v=v, o=out)
+    tv = [float(theta)] if isinstance(theta, (int, float)) else [float(x) for x in theta]
+    tarr = (ctypes.c_double * len(tv))(*tv)
+    nbytes = ctypes.c_size_t()
+    _check(_L().losa_sparse_attn_threshold_workspace(ctypes.byref(shp), ctypes.byref(nbytes)),
+           "losa_sparse_attn_threshold_workspace")
+    ws = _workspace(nbytes.value, q.device, ws, st)
+    _check(_L().losa_sparse_attn_threshold(ctypes.byref(shp), _ptr(q), _ptr(k), _ptr(v), tarr, len(tv), _ptr(out),
+                                           odt, _ptr(kept_count), _ptr(kept_mask), _ptr(ws), _nbytes(ws),
+                                           _stream(st)), "losa_sparse_attn_threshold")
+    return out, kept_count, kept_mask
 
 
 def losa_dense_attn_mass_workspace(geom: Geometry) -> int:

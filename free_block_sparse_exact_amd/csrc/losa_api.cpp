@@ -204,6 +204,49 @@ losa_status losa_sparse_attn(const losa_shape* shape, const void* Q, const void*
                                              stream));
 }
 
+losa_status losa_sparse_attn_threshold_workspace(const losa_shape* shape, size_t* bytes) {
+  Geom g;
+  if (!bytes) return LOSA_ERR_NULL;
+  const losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if (!losa::mfma_path(g)) return LOSA_ERR_UNSUPPORTED;
+  *bytes = losa::attn_threshold_ws_bytes(g);
+  return LOSA_OK;
+}
+
+losa_status losa_sparse_attn_threshold(const losa_shape* shape, const void* Q, const void* K, const void* V,
+                                       const double* theta, int32_t n_theta, void* O, losa_dtype o_dtype,
+                                       int32_t* kept_count, uint32_t* kept_mask, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  Geom g;
+  losa_status st = make_geom(shape, &g);
+  if (st != LOSA_OK) return st;
+  if (!losa::mfma_path(g)) return LOSA_ERR_UNSUPPORTED;
+  if ((st = check_input(g, Q, g.qs)) != LOSA_OK) return st;
+  if ((st = check_input(g, K, g.ks)) != LOSA_OK) return st;
+  if ((st = check_input(g, V, g.vs)) != LOSA_OK) return st;
+  if (!theta || !O || !ws) return LOSA_ERR_NULL;
+  if (n_theta != 1 && n_theta != g.H) return LOSA_ERR_INVALID_ARG;
+  if (n_theta > 1 && n_theta > LOSA_MAX_HEADS_P) return LOSA_ERR_UNSUPPORTED;
+  if (o_dtype != LOSA_F32 && o_dtype != LOSA_BF16) return LOSA_ERR_INVALID_ARG;
+  if (!aligned16(O) || !strides_ok(g.os, g.D, o_dtype == LOSA_BF16 ? 8 : 4)) return LOSA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(kept_count) & 3u) != 0 || (reinterpret_cast<uintptr_t>(kept_mask) & 3u) != 0)
+    return LOSA_ERR_INVALID_ARG;
+  losa::InPass ip;
+  memset(&ip, 0, sizeof ip);
+  ip.per_head = n_theta > 1;
+  for (int t = 0; t < n_theta; ++t) {
+    if (!(theta[t] > 0.0 && theta[t] <= 1.0)) return LOSA_ERR_INVALID_ARG;
+    ip.ln_theta[t] = log(theta[t]);
+  }
+  ip.ln_c = log((double)g.C);
+  ip.ln_last = log((double)(g.N - (g.nk - 1) * g.C));
+  if (ws_bytes < losa::attn_threshold_ws_bytes(g) || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return LOSA_ERR_WORKSPACE;
+  return hip_status(losa::launch_sparse_attn_threshold(g, Q, K, V, ip, O, o_dtype == LOSA_BF16, kept_count,
+                                                       kept_mask, ws, stream));
+}
+
 losa_status losa_dense_attn_mass_workspace(const losa_shape* shape, size_t* bytes) {
   Geom g;
   if (!bytes) return LOSA_ERR_NULL;

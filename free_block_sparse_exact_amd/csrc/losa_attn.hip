@@ -40,24 +40,144 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // exceeds this bound sends the wave to the exact two-pass path.
 constexpr float kPBound = 65536.0f;
 
+// On-the-fly block thresholding (Sol-Attn page: blocks are chosen while the
+// online softmax runs, by comparing each block's proxy score with a
+// threshold, without materialising a proxy map).  The proxy of key block j
+// for this query block is a_j = scale * qbar . kbar_j + ln|B_j| (pooled
+// score, weighted by the block's valid keys; fp64 throughout, the fp32 softmax
+// scale widened exactly); in index order, the order of the online pass, block
+// j is kept when a_j >= ln(theta) + max(a_0 .. a_j).  The kept blocks go to
+// list[] in ascending order, in LDS; the return value is their number.  The
+// whole workgroup (256 threads) takes part.  scratch: D + nk doubles and nk
+// bytes of LDS, free for the call.  mask_row (or null): the kept blocks as
+// bits, 32 per word.
+template <int D>
+__device__ int inpass_list(const Geom& g, const double* __restrict__ qbar_row, const double* __restrict__ kbar_bh,
+                           double ln_t, double ln_c, double ln_last, double* scratch, int32_t* list,
+                           uint32_t* __restrict__ mask_row) {
+  __shared__ double s_wmax[4];
+  __shared__ int s_wcnt[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nk = g.nk;
+  double* qv = scratch;       // [D]
+  double* av = scratch + D;   // [nk]
+  uint8_t* kf = reinterpret_cast<uint8_t*>(av + nk);  // [nk] keep flags
+  if (tid < D) qv[tid] = qbar_row[tid];
+  __syncthreads();
+  // Pooled scores, four blocks per wave and step: lane l takes block
+  // jb + l/16 and its D/16 dimensions from (l%16)*D/16 (contiguous 16-byte
+  // loads), then the 16 lanes of a block add their partial sums.  Eight steps
+  // are loaded before any is used, so their loads overlap.
+  {
+    constexpr int E = D / 16;  // doubles per lane
+    constexpr int kSteps = 8;
+    const int part = lane & 15, sub4 = lane >> 4;
+    double qr[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) qr[e] = qv[part * E + e];
+    const double sc = (double)g.scale;
+    for (int jb0 = 4 * w; jb0 < nk; jb0 += 16 * kSteps) {
+      double2 kk[kSteps][E / 2];
+#pragma unroll
+      for (int t = 0; t < kSteps; ++t) {
+        const int j = jb0 + 16 * t + sub4;
+        const double2* kj = reinterpret_cast<const double2*>(kbar_bh + (int64_t)min(j, nk - 1) * D + part * E);
+#pragma unroll
+        for (int e = 0; e < E / 2; ++e) kk[t][e] = kj[e];
+      }
+#pragma unroll
+      for (int t = 0; t < kSteps; ++t) {
+        const int j = jb0 + 16 * t + sub4;
+        double s = 0.0;
+#pragma unroll
+        for (int e = 0; e < E / 2; ++e) {
+          s = __builtin_fma(qr[2 * e], kk[t][e].x, s);
+          s = __builtin_fma(qr[2 * e + 1], kk[t][e].y, s);
+        }
+        s += __shfl_xor(s, 8, 16);
+        s += __shfl_xor(s, 4, 16);
+        s += __shfl_xor(s, 2, 16);
+        s += __shfl_xor(s, 1, 16);
+        if (part == 0 && j < nk) av[j] = s * sc + (j == nk - 1 ? ln_last : ln_c);
+      }
+    }
+  }
+  __syncthreads();
+  // Running maximum in index order: thread t owns blocks [t*per, t*per + per).
+  const int per = (nk + 255) / 256, j0 = tid * per, j1 = min(nk, j0 + per);
+  double m = -__builtin_huge_val();
+  for (int j = j0; j < j1; ++j) m = __builtin_fmax(m, av[j]);
+  double incl = m;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl = __builtin_fmax(incl, y);
+  }
+  double run = __shfl_up(incl, 1, 64);
+  if (lane == 0) run = -__builtin_huge_val();
+  if (lane == 63) s_wmax[w] = incl;
+  __syncthreads();
+  for (int ww = 0; ww < w; ++ww) run = __builtin_fmax(run, s_wmax[ww]);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) {
+    run = __builtin_fmax(run, av[j]);
+    const bool keep = av[j] >= ln_t + run;
+    kf[j] = keep ? 1 : 0;
+    cnt += keep ? 1 : 0;
+  }
+  // Exclusive scan of the counts in thread order: the list stays ascending.
+  int ci = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(ci, o, 64);
+    if (lane >= o) ci += y;
+  }
+  if (lane == 63) s_wcnt[w] = ci;
+  __syncthreads();
+  int off = ci - cnt, total = 0;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    const int c = s_wcnt[ww];
+    if (ww < w) off += c;
+    total += c;
+  }
+  for (int j = j0; j < j1; ++j)
+    if (kf[j]) list[off++] = j;
+  if (mask_row) {
+    for (int x = tid; x < (nk + 31) / 32; x += 256) {
+      uint32_t word = 0;
+      for (int b = 0; b < 32 && 32 * x + b < nk; ++b) word |= (uint32_t)kf[32 * x + b] << b;
+      mask_row[x] = word;
+    }
+  }
+  __syncthreads();  // the list is complete, and the scratch free again
+  return total;
+}
+
 // Workgroup: 4 waves (one per SIMD), one per key group.  Wave kw keeps the
 // running state of all 64 queries of the tile (4 query tiles of 16: every
 // K and V operand feeds four MFMAs) over the chunks kw, kw+4, kw+8, ... of
 // the row; the four key groups are merged through LDS at the end.  (With 32
 // queries per wave two waves fit a SIMD, but each K/V chunk is then read by
 // two waves and the texture path saturates: measured slower.)
-template <int D>
+//
+// kInPass: the row's blocks are not given but chosen inside this kernel by
+// on-the-fly thresholding (inpass_list) into an LDS list; rows run in index
+// order (their budgets are not known beforehand).
+template <int D, bool kInPass>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     const Geom g, const __bf16* __restrict__ Q, const __bf16* __restrict__ Kp, const __bf16* __restrict__ Vp,
     int nch, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    const int32_t* __restrict__ order, void* O, int o_bf16) {
+    const int32_t* __restrict__ order, void* O, int o_bf16, const double* __restrict__ qbar,
+    const double* __restrict__ kbar, const InPass ip, int32_t* __restrict__ kept_count,
+    uint32_t* __restrict__ kept_mask) {
   constexpr int DC = D / 32, DT = D / 16, kQT = 4;
   constexpr int LD = D + 4;   // merge slot row stride (floats)
-  extern __shared__ float lds[];  // merge slots [4][64][LD] f32, maxima [4][64], row sums [4][64]
+  extern __shared__ float lds[];  // merge slots [4][64][LD] f32, maxima [4][64], row sums [4][64]; in-pass list [nk]
   const int qhalves = g.R / 64;
   const int tix = xcd_block_task(blockIdx.x, gridDim.x);
   const int ridx = tix / qhalves, qsub = tix - ridx * qhalves;
-  const int row = order ? order[ridx] : ridx;
+  const int row = (!kInPass && order) ? order[ridx] : ridx;
   const int bh = row / g.nq, i = row - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
   const int lane = threadIdx.x & 63, kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,13 +213,31 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   }
 
   const float c = g.scale_log2;
-  const int beg = row_ptr[row], end = row_ptr[row + 1];
+  int beg, end;
+  int32_t* list = reinterpret_cast<int32_t*>(lds + 4 * 64 * LD + 512);  // in-pass kept blocks
+  if constexpr (kInPass) {
+    const double ln_t = ip.ln_theta[ip.per_head ? h : 0];
+    uint32_t* mask_row = (kept_mask && qsub == 0) ? kept_mask + (int64_t)row * ((g.nk + 31) / 32) : nullptr;
+    const int n = inpass_list<D>(g, qbar + (int64_t)row * D, kbar + (int64_t)bh * g.nk * D, ln_t, ip.ln_c,
+                                 ip.ln_last, reinterpret_cast<double*>(lds), list, mask_row);
+    if (kept_count && qsub == 0 && threadIdx.x == 0) kept_count[row] = n;
+    beg = 0;
+    end = n;
+  } else {
+    beg = row_ptr[row];
+    end = row_ptr[row + 1];
+  }
+  // Block at position p of the row's list.
+  auto list_at = [&](int p) -> int {
+    if constexpr (kInPass) return list[p];
+    else return col_idx[beg + p];
+  };
   const int sub = g.C / 32;
   const int nchunk = (end - beg) * sub;
 
   auto chunk_key = [&](int u) -> int {
     const int p = u / sub;
-    return col_idx[beg + p] * g.C + (u - p * sub) * 32;
+    return list_at(p) * g.C + (u - p * sub) * 32;
   };
   // Operand loads from the packed copies: 64 lanes x 16 contiguous bytes each.
   auto load_k = [&](int kb, bf16x8 (&kop)[2][DC]) {
@@ -213,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int x = base + j * kWave + lane;
-        hit[j] = __ballot(x < n && col_idx[beg + x] == g.nk - 1);
+        hit[j] = __ballot(x < n && list_at(x) == g.nk - 1);
       }
 #pragma unroll
       for (int j = 3; j >= 0; --j)
@@ -250,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     t = t < nmine ? t : nmine - 1;
     t = t == swap_a ? swap_b : (t == swap_b ? swap_a : t);
     const int u = kw + 4 * t, p = u >> sub_shift;
-    return col_idx[beg + p] * g.C + (u - (p << sub_shift)) * 32;
+    return list_at(p) * g.C + (u - (p << sub_shift)) * 32;
   };
   bool fallback = false;
   bf16x8 kop[2][DC], vop[DT];
@@ -490,9 +628,40 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* 
   hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)V, Kp, Vp, nch);
   const size_t lds = (size_t)(4 * 64 * (D + 4) + 512) * sizeof(float);  // 137 KB at d = 128
-  hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st,
+  InPass none;
+  none.per_head = 0;
+  hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st,
                      g, (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, row_ptr, col_idx, order, O,
-                     o_bf16);
+                     o_bf16, (const double*)nullptr, (const double*)nullptr, none, (int32_t*)nullptr,
+                     (uint32_t*)nullptr);
+  return hipGetLastError();
+}
+
+// In-pass thresholding workspace: fp64 block means of Q [B*H*nq][D] and of K
+// [B*H*nk][D], then the packed K and V.
+size_t means_bytes(const Geom& g) {
+  return align_up((size_t)g.B * g.H * g.nq * g.D * sizeof(double), 256) +
+         align_up((size_t)g.B * g.H * g.nk * g.D * sizeof(double), 256);
+}
+
+template <int D>
+hipError_t launch_inpass(const Geom& g, const void* Q, const void* K, const void* V, const InPass& ip, void* O,
+                         int o_bf16, int32_t* kept_count, uint32_t* kept_mask, void* ws, hipStream_t st) {
+  char* base = reinterpret_cast<char*>(ws);
+  double* qbar = reinterpret_cast<double*>(base);
+  double* kbar = reinterpret_cast<double*>(base + align_up((size_t)g.B * g.H * g.nq * g.D * sizeof(double), 256));
+  launch_block_means64(g, Q, K, qbar, kbar, st);
+  const int nch = vt_chunks(g);
+  __bf16* Kp = reinterpret_cast<__bf16*>(base + means_bytes(g));
+  __bf16* Vp = Kp + (size_t)g.B * g.H * nch * 32 * D;
+  hipLaunchKernelGGL((pack_kv_kernel<D, true>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
+                     (const __bf16*)K, (const __bf16*)V, Kp, Vp, nch);
+  // merge slots, maxima and row sums, then the kept-block list (153 KB at d = 128, n_k = 4096)
+  const size_t lds = (size_t)(4 * 64 * (D + 4) + 512) * sizeof(float) + (size_t)g.nk * sizeof(int32_t);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st, g,
+                     (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, (const int32_t*)nullptr,
+                     (const int32_t*)nullptr, (const int32_t*)nullptr, O, o_bf16, (const double*)qbar,
+                     (const double*)kbar, ip, kept_count, kept_mask);
   return hipGetLastError();
 }
 
@@ -509,6 +678,15 @@ hipError_t launch_simt(const Geom& g, const void* Q, const void* K, const void* 
 size_t attn_ws_bytes(const Geom& g) {
   if (!mfma_path(g)) return 0;
   return 2 * (size_t)g.B * g.H * g.D * (size_t)vt_chunks(g) * 32 * sizeof(uint16_t);  // packed K and V
+}
+
+size_t attn_threshold_ws_bytes(const Geom& g) { return means_bytes(g) + attn_ws_bytes(g); }
+
+hipError_t launch_sparse_attn_threshold(const Geom& g, const void* Q, const void* K, const void* V, const InPass& ip,
+                                        void* O, int o_bf16, int32_t* kept_count, uint32_t* kept_mask, void* ws,
+                                        hipStream_t stream) {
+  return g.D == 128 ? launch_inpass<128>(g, Q, K, V, ip, O, o_bf16, kept_count, kept_mask, ws, stream)
+                    : launch_inpass<64>(g, Q, K, V, ip, O, o_bf16, kept_count, kept_mask, ws, stream);
 }
 
 hipError_t launch_sparse_attn(const Geom& g, const void* Q, const void* K, const void* V,

@@ -104,6 +104,22 @@ hipError_t launch_sparse_attn_mass(const Geom& g, const void* Q, const void* K, 
 hipError_t launch_dense_attn_mass(const Geom& g, const void* Q, const void* K, const void* V, float* M, void* O,
                                   int o_bf16, void* ws, hipStream_t stream);
 
+// Sparse attention with on-the-fly block thresholding against the pooled
+// proxy: ln(theta) per head (or one for all) and the log of the valid keys of
+// a full and of the last key block, all computed on the host.
+struct InPass {
+  double ln_theta[kMaxHeadsP];
+  int per_head;
+  double ln_c, ln_last;
+};
+size_t attn_threshold_ws_bytes(const Geom& g);
+hipError_t launch_sparse_attn_threshold(const Geom& g, const void* Q, const void* K, const void* V, const InPass& ip,
+                                        void* O, int o_bf16, int32_t* kept_count, uint32_t* kept_mask, void* ws,
+                                        hipStream_t stream);
+// Block means of bf16 Q (query blocks) and K (key blocks) in fp64:
+// qbar [B*H*nq][D], kbar [B*H*nk][D].
+void launch_block_means64(const Geom& g, const void* Q, const void* K, double* qbar, double* kbar, hipStream_t st);
+
 // Pooled proxy masses (block-mean Q and K, block-weighted softmax).
 size_t pooled_ws_bytes(const Geom& g);
 hipError_t launch_pooled_mass(const Geom& g, const void* Q, const void* K, float* P, void* ws, hipStream_t stream);

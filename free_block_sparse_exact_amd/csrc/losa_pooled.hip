@@ -21,27 +21,30 @@
 namespace losa {
 namespace {
 
-// Mean over the valid tokens of block x (size blk) of X[b, h, :, :] -> out[bh][x][D] (fp32).
+// Mean over the valid tokens of block x (size blk) of X[b, h, :, :] -> out[bh][x][D],
+// accumulated and stored in Acc (fp32 for the pooled proxy masses; fp64 for the
+// on-the-fly thresholding inside the attention pass, whose block sums of bf16
+// inputs are then exact and whose means are correctly rounded).
 // Grid (n_blocks, B*H), 256 threads: thread = (token group, dimension).
-template <typename T, int D>
+template <typename T, int D, typename Acc>
 __global__ __launch_bounds__(256) void pool_kernel(const Geom g, const T* __restrict__ X, int64_t s0, int64_t s1,
-                                                   int64_t s2, int blk, int nblk, float* __restrict__ out) {
+                                                   int64_t s2, int blk, int nblk, Acc* __restrict__ out) {
   constexpr int G = 256 / D;  // token groups
-  __shared__ float part[G][D];
+  __shared__ Acc part[G][D];
   const int x = blockIdx.x, bh = blockIdx.y;
   const int b = bh / g.H, h = bh - b * g.H;
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
   const int t0 = x * blk, t1 = min(t0 + blk, g.N);
   const T* Xbh = X + b * s0 + h * s1;
-  float acc = 0.f;
-  for (int t = t0 + grp; t < t1; t += G) acc += (float)Xbh[(int64_t)t * s2 + d];
+  Acc acc = 0;
+  for (int t = t0 + grp; t < t1; t += G) acc += (Acc)(float)Xbh[(int64_t)t * s2 + d];
   part[grp][d] = acc;
   __syncthreads();
   if (grp == 0) {
-    float s = 0.f;
+    Acc s = 0;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) s += part[gg][d];
-    out[((int64_t)bh * nblk + x) * D + d] = s / (float)(t1 - t0);
+    out[((int64_t)bh * nblk + x) * D + d] = s / (Acc)(t1 - t0);
   }
 }
 
@@ -101,16 +104,31 @@ __global__ __launch_bounds__(256) void proxy_kernel(const Geom g, const float* _
 
 template <typename T, int D>
 hipError_t launch(const Geom& g, const void* Q, const void* K, float* P, float* qbar, float* kbar, hipStream_t st) {
-  hipLaunchKernelGGL((pool_kernel<T, D>), dim3(g.nq, g.B * g.H), dim3(256), 0, st, g, (const T*)Q, g.qs[0], g.qs[1],
-                     g.qs[2], g.R, g.nq, qbar);
-  hipLaunchKernelGGL((pool_kernel<T, D>), dim3(g.nk, g.B * g.H), dim3(256), 0, st, g, (const T*)K, g.ks[0], g.ks[1],
-                     g.ks[2], g.C, g.nk, kbar);
+  hipLaunchKernelGGL((pool_kernel<T, D, float>), dim3(g.nq, g.B * g.H), dim3(256), 0, st, g, (const T*)Q, g.qs[0],
+                     g.qs[1], g.qs[2], g.R, g.nq, qbar);
+  hipLaunchKernelGGL((pool_kernel<T, D, float>), dim3(g.nk, g.B * g.H), dim3(256), 0, st, g, (const T*)K, g.ks[0],
+                     g.ks[1], g.ks[2], g.C, g.nk, kbar);
   hipLaunchKernelGGL((proxy_kernel<D>), dim3(g.rows()), dim3(256), (size_t)g.nk * sizeof(float), st, g,
                      (const float*)qbar, (const float*)kbar, P);
   return hipGetLastError();
 }
 
+template <int D>
+void launch_means64(const Geom& g, const __bf16* Q, const __bf16* K, double* qbar, double* kbar, hipStream_t st) {
+  hipLaunchKernelGGL((pool_kernel<__bf16, D, double>), dim3(g.nq, g.B * g.H), dim3(256), 0, st, g, Q, g.qs[0],
+                     g.qs[1], g.qs[2], g.R, g.nq, qbar);
+  hipLaunchKernelGGL((pool_kernel<__bf16, D, double>), dim3(g.nk, g.B * g.H), dim3(256), 0, st, g, K, g.ks[0],
+                     g.ks[1], g.ks[2], g.C, g.nk, kbar);
+}
+
 }  // namespace
+
+void launch_block_means64(const Geom& g, const void* Q, const void* K, double* qbar, double* kbar, hipStream_t st) {
+  if (g.D == 128)
+    launch_means64<128>(g, (const __bf16*)Q, (const __bf16*)K, qbar, kbar, st);
+  else
+    launch_means64<64>(g, (const __bf16*)Q, (const __bf16*)K, qbar, kbar, st);
+}
 
 // Workspace: qbar fp32 [B*H*nq][D], then kbar fp32 [B*H*nk][D].
 size_t pooled_ws_bytes(const Geom& g) {

@@ -22,11 +22,12 @@
  * Conventions shared by every call
  * --------------------------------
  * Memory.  Every pointer named Q, K, V, O, M, P, row_ptr, col_idx, order,
- *   ws, kept, Q_ref, K_ref, drift, refresh, take_b (and the _a/_b list sets)
- *   is DEVICE memory owned by the caller; the library allocates nothing
- *   and keeps no pointer after a call returns.  The only host pointers are the
- *   losa_shape, the p array of losa_select, the theta array of
- *   losa_select_threshold and the size_t out-parameters.
+ *   ws, kept, kept_count, kept_mask, Q_ref, K_ref, drift, refresh, take_b
+ *   (and the _a/_b list sets) is DEVICE memory owned by the caller; the
+ *   library allocates nothing and keeps no pointer after a call returns.  The
+ *   only host pointers are the losa_shape, the p arrays of losa_select and
+ *   losa_select_noalloc, the theta arrays of losa_select_threshold and
+ *   losa_sparse_attn_threshold and the size_t out-parameters.
  * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
  *   returns without waiting.  Outputs are valid once the stream reaches them.
  * Errors.  Argument checks run on the host before any HIP call; a failed
@@ -234,6 +235,42 @@ losa_status losa_sparse_attn(const losa_shape* shape, const void* Q, const void*
                              const int32_t* row_ptr, const int32_t* col_idx, const int32_t* order,
                              void* O, losa_dtype o_dtype, void* ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention with on-the-fly block thresholding.
+ * Sol-Attn page (abstract): the key blocks a query block attends to are
+ * chosen while the online softmax runs, by comparing each block's proxy
+ * score with a threshold, without materialising a proxy map.  The page gives
+ * no rule; this library's reading: the proxy of key block j for query block
+ * i is a_j = scale * qbar_i . kbar_j + ln|B_j| -- the pooled score of the
+ * block means over valid tokens (see losa_pooled_mass), weighted by the
+ * block's valid keys -- and, visiting blocks in index order as the online
+ * pass does, block j is kept when a_j >= ln(theta) + max(a_0 .. a_j).  That
+ * is losa_select_threshold's rule applied to the pooled proxy masses with
+ * their normaliser cancelled, so no proxy matrix is formed or stored: each
+ * workgroup decides its row's blocks in LDS, then skips the dropped blocks'
+ * K/V loads and products.  O is the softmax attention over the kept blocks'
+ * valid tokens (as losa_sparse_attn computes it); the page's correction for
+ * the skipped blocks is not applied.  The decision is taken in fp64 (bf16
+ * block sums are exact there; the fp32 softmax scale is widened exactly);
+ * ln(theta) and the two block-size logarithms are computed on the host.
+ *
+ * bf16 matrix-core shapes only (head_dim 64/128, q_block 64/128); others
+ * return LOSA_ERR_UNSUPPORTED.
+ * theta: HOST array of n_theta doubles in (0, 1]; n_theta = 1 or heads.
+ * O: as for losa_sparse_attn (rows beyond tokens written as 0).
+ * kept_count: int32 [batch*heads*n_q] or NULL: the kept blocks per row.
+ * kept_mask: uint32 [batch*heads*n_q][ceil(n_k/32)] or NULL: bit j%32 of
+ *    word j/32 of row r is set when block j is kept.
+ * ws: at least *bytes from losa_sparse_attn_threshold_workspace: fp64 block
+ *    means of Q and K (8 * batch*heads*(n_q + n_k)*head_dim bytes), then K
+ *    and V repacked as for losa_sparse_attn.
+ * ------------------------------------------------------------------------ */
+losa_status losa_sparse_attn_threshold_workspace(const losa_shape* shape, size_t* bytes);
+losa_status losa_sparse_attn_threshold(const losa_shape* shape, const void* Q, const void* K, const void* V,
+                                       const double* theta, int32_t n_theta, void* O, losa_dtype o_dtype,
+                                       int32_t* kept_count, uint32_t* kept_mask, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Dense attention with exact block masses, in one pass (the construction

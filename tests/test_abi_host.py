@@ -305,3 +305,27 @@ def test_select_threshold_errors(lib):
     assert sel(t=(ctypes.c_double * 2)(0.1, 0.0), n_t=2) == INVALID
     assert sel(ws=0x100010) == WORKSPACE
     assert sel(ws_bytes=n.value - 1) == WORKSPACE
+
+
+@no_gpu_only
+def test_sparse_attn_threshold_errors(lib):
+    s = shape()
+    t1 = (ctypes.c_double * 1)(0.1)
+
+    def thr(sh=s, t=t1, n_t=1, ws=0x100000, ws_bytes=1 << 40, O=FAKE, o_dtype=F.LOSA_BF16, cnt=None, mask=None):
+        return lib.losa_sparse_attn_threshold(ctypes.byref(sh), FAKE, FAKE, FAKE, t, n_t, O, o_dtype, cnt, mask, ws,
+                                              ws_bytes, None)
+
+    assert thr(t=(ctypes.c_double * 1)(0.0)) == INVALID
+    assert thr(t=(ctypes.c_double * 1)(1.5)) == INVALID
+    assert thr(t=(ctypes.c_double * 2)(0.5, float("nan")), n_t=2) == INVALID
+    assert thr(n_t=3) == INVALID
+    assert thr(O=None) == NULL
+    assert thr(o_dtype=7) == INVALID
+    assert thr(cnt=FAKE + 2) == INVALID
+    assert thr(ws_bytes=64) == WORKSPACE
+    assert thr(ws=0x100010) == WORKSPACE
+    assert thr(sh=shape(dtype=F.LOSA_F32)) == UNSUPPORTED
+    assert thr(sh=shape(q_block=32)) == UNSUPPORTED
+    n = ctypes.c_size_t()
+    assert lib.losa_sparse_attn_threshold_workspace(ctypes.byref(s), ctypes.byref(n)) == OK and n.value > 0
