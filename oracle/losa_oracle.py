@@ -374,9 +374,11 @@ def threshold_inpass_lists(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C
     """Kept blocks of on-the-fly block thresholding (module header): per row,
     in index order, a_j = sbar_ij + ln|B_j| and block j is kept when
     a_j >= ln(theta_h) + max(a_0 .. a_j).  ``theta`` is a scalar or one value
-    per head, each in (0, 1].  Returns (row_ptr, col_idx ascending, margin):
-    margin is the smallest |a_j - ln(theta_h) - max(a_0 .. a_j)| over all
-    decisions, i.e. how far the closest one lies from a tie."""
+    per head, each in (0, 1].  Returns (row_ptr, col_idx ascending, margin).
+    With ln(theta) <= 0 a block j > 0 is kept exactly when
+    a_j >= ln(theta_h) + max(a_0 .. a_{j-1}); margin is the smallest
+    |a_j - ln(theta_h) - max(a_0 .. a_{j-1})| over all rows and blocks j > 0,
+    i.e. how far the closest decision lies from a tie (block 0 is always kept)."""
     sbar = pooled_scores(q, k, n_valid, R, C, scale)
     B, H, n_q, n_k = sbar.shape
     t_h = np.broadcast_to(np.asarray(theta, dtype=np.float64), (H,))
@@ -392,11 +394,11 @@ def threshold_inpass_lists(q: np.ndarray, k: np.ndarray, n_valid: int, R: int, C
                 kept = []
                 run = -math.inf
                 for j in range(n_k):
+                    if j > 0:
+                        margin = min(margin, abs(float(a[j]) - (ln_t + run)))
                     run = max(run, float(a[j]))
-                    gap = float(a[j]) - (ln_t + run)
-                    if gap >= 0.0:
+                    if float(a[j]) >= ln_t + run:
                         kept.append(j)
-                    margin = min(margin, abs(gap))
                 cols.append(np.asarray(kept, np.int32))
                 row_ptr.append(row_ptr[-1] + len(kept))
     col_idx = np.concatenate(cols) if cols else np.zeros(0, np.int32)
