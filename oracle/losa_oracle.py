@@ -453,8 +453,16 @@ def sparse_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_valid: 
         if keys.size == 0 or r1 <= r0:
             out.append(np.zeros((max(r1 - r0, 0), v.shape[-1]), np.float64))
             continue
-        a = attention_probs(q[b, h, r0:r1], k[b, h, keys], sc)
-        out.append(a @ v[b, h, keys])
+        # scores against every valid key, the discarded ones set to -inf (they
+        # leave the softmax: exp gives exactly 0), then the weights times V
+        s = (q[b, h, r0:r1] @ k[b, h, :n_valid].T) * sc
+        dropped = np.ones(n_valid, bool)
+        dropped[keys] = False
+        s[:, dropped] = -np.inf
+        s -= s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        a = e / e.sum(axis=1, keepdims=True)
+        out.append(a @ v[b, h, :n_valid])
     return out
 
 
