@@ -778,6 +778,10 @@ def run_reuse(args, wl):
     del ws_dense
     # every other step: sparse attention on the frozen lists with that step's Q/K
     sparse_ms, recalls = [], []
+    # rows whose recall the CPU baseline leg recomputes with the oracle (GPU side kept here)
+    sample_rows = [(h, i) for h in (0, H // 2, H - 1) for i in (0, nq // 2, nq - 1)]
+    sample_r = [h * nq + i for h, i in sample_rows]
+    sample_kept = []
     for s in range(wl.steps):
         load_step(s)
         if s != wl.construct_step:
@@ -792,6 +796,7 @@ def run_reuse(args, wl):
         F.losa_retained_mass(bufs.M, bufs.row_ptr, bufs.col_idx, N, R, C, out=bufs.kept, stream=stream)
         kept = bufs.kept.cpu().numpy().astype(np.float64)
         recalls.append(float((kept[:, 0] * w).sum() / (kept[:, 1] * w).sum()))
+        sample_kept.append(kept[sample_r])
         log(f"step {s}: recall {recalls[-1]:.6f}" + (f", sparse {sparse_ms[-1]:.3f} ms" if s != wl.construct_step else ""))
     # Reduced search at the last step (GSRS card: a later top-p search within the
     # earlier candidate set, on exact weights computed inside the attention
@@ -854,8 +859,73 @@ def run_reuse(args, wl):
                                   "(a static count, not measured busy time)",
         "reduced_search": reduced,
         "drift_refresh": refresh,
+        "cpu_baseline": None,
     }
+    if args.cpu_rows > 0:
+        log("timing the CPU oracle baseline (recall and sparse attention of sampled rows at every step) ...")
+        res["cpu_baseline"] = reuse_cpu_baseline(wl, steps_qk, v, bufs, sample_rows, sample_kept, args.cpu_budget)
     print(json.dumps(res))
+
+
+def reuse_cpu_baseline(wl, steps_qk, v, bufs, sample_rows, sample_kept, budget_s):
+    """The oracle on sampled rows of every step of the reuse trajectory: the
+    exact masses of each row under that step's Q/K (the recall of the frozen
+    lists, set beside the GPU's recall of the same rows) and the sparse
+    attention over the frozen list (timed, kept-block TFLOP/s).  Sample: three
+    rows (first, middle and last query block) of three heads per step; steps
+    past the time budget are skipped and reported as null."""
+    import oracle as O
+    import synthetic as S
+    N, R, C, d = wl.tokens, wl.block, wl.key_block, wl.head_dim
+    nq = wl.n_blocks
+    rp = bufs.row_ptr.cpu().numpy().astype(np.int64)
+    ci = bufs.col_idx[:int(rp[-1])].cpu().numpy()
+    vh = {h: S.to_f64(v[:, h:h + 1].cpu().view(torch_int16()).numpy(), wl.dtype) for h, _ in sample_rows}
+    t_start = time.time()
+    t_attn, flops = 0.0, 0.0
+    oracle_rec, gpu_rec = [], []
+    for s in range(wl.steps):
+        if time.time() - t_start > budget_s:
+            oracle_rec.append(None)
+            gpu_rec.append(None)
+            continue
+        num_o = den_o = num_g = den_g = 0.0
+        for t, (h, i) in enumerate(sample_rows):
+            qh = S.to_f64(steps_qk[s][0][:, h:h + 1].cpu().view(torch_int16()).numpy(), wl.dtype)
+            kh = S.to_f64(steps_qk[s][1][:, h:h + 1].cpu().view(torch_int16()).numpy(), wl.dtype)
+            m = O.block_mass_rows(qh, kh, N, R, C, [(0, 0, i)])[0]
+            r = h * nq + i
+            lst = ci[rp[r]:rp[r + 1]]
+            wi = min(R, N - i * R)
+            num_o += wi * m[lst].sum()
+            den_o += wi * m.sum()
+            num_g += wi * sample_kept[s][t, 0]
+            den_g += wi * sample_kept[s][t, 1]
+            rp1 = np.array([0] * (i + 1) + [len(lst)], np.int64)
+            t0 = time.time()
+            O.sparse_attention_rows(qh, kh, vh[h], N, R, C, rp1, lst.astype(np.int32), [(0, 0, i)])
+            t_attn += time.time() - t0
+            flops += 4.0 * d * R * C * len(lst)
+        oracle_rec.append(float(num_o / den_o))
+        gpu_rec.append(float(num_g / den_g))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    diffs = [abs(a - b) for a, b in zip(oracle_rec, gpu_rec) if a is not None]
+    return {"value": flops / t_attn / 1e12 if t_attn > 0 else None, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{len(sample_rows)} query blocks (first, middle, last of three heads) at each of "
+                      f"{sum(x is not None for x in oracle_rec)} steps: exact masses (recall of the frozen lists) and "
+                      f"sparse attention over the frozen list; value = the oracle's kept-block TFLOP/s on them",
+            "recall_sampled_oracle_per_step": oracle_rec, "recall_sampled_gpu_per_step": gpu_rec,
+            "recall_sampled_max_abs_diff": max(diffs) if diffs else None, "cpu": cpu_model()}
+
+
+def torch_int16():
+    import torch
+    return torch.int16
 
 
 def copy_calibration():

@@ -29,6 +29,7 @@ def _wl(wid, **kw):
 # (name, workload, heads, tokens, R, C, p)
 CASES = [
     ("wl0_f32_d64", S.get_workload("0"), None, None, 64, 64, 0.9),
+    ("wl0_f32_d64_p099", S.get_workload("0"), None, None, 64, 64, 0.99),  # the tiny workload as stated
     ("bf16_d128_r64_ragged", S.get_workload("1"), 2, 1000, 64, 64, 0.99),
     ("bf16_d128_r128_ragged", S.get_workload("3"), 2, 1000, 128, 128, 0.99),
     ("bf16_d128_r64_c32", S.get_workload("1"), 2, 777, 64, 32, 0.95),

@@ -119,3 +119,50 @@ def test_frozen_reuse_per_head_p():
             assert worst_o <= ATTN_ATOL
             assert abs(rec_o - rec_g) < 1e-5
             assert 0.5 < recall_gpu <= 1.0 + 1e-6
+
+
+def test_recall_every_step_sampled_rows():
+    """Recall of the frozen lists at every one of the 50 steps (BASELINE
+    reuse workload; LoSA page, Motivation Summary: recall of a pattern under
+    a later step's dense masses): on sampled rows of two heads, the GPU's
+    kept/total masses against the oracle's, step by step."""
+    from concurrent.futures import ThreadPoolExecutor
+    wl = S.get_workload("4")
+    R = C = wl.block
+    N, Na, nq = wl.tokens, wl.tokens_alloc, wl.n_blocks
+    heads = [1, 7]
+    layer = S.make_layer(wl, heads=heads, keep_f64=True)
+    p_heads = [float(layer.p_heads[h]) for h in heads]
+    rows = [(0, s, i) for s in range(2) for i in (0, 257, nq - 1)]   # slot s of the subset
+    with ThreadPoolExecutor(8) as pool:  # the generator's bulk draws release the GIL
+        steps = list(pool.map(lambda s: S.drift_qk(layer, s), range(wl.steps)))
+    q2d, k2d = to_device(steps[wl.construct_step][0], wl.dtype), to_device(steps[wl.construct_step][1], wl.dtype)
+    M2 = F.losa_block_mass(q2d, k2d, N, R, C)
+    rp, ci, _ = F.losa_select(M2, p_heads, N, R, C, tokens_alloc=Na, want_order=False)
+    torch.cuda.synchronize()
+    rp_h = rp.cpu().numpy().astype(np.int64)
+    ci_h = ci[:int(rp_h[-1])].cpu().numpy()
+    worst = 0.0
+    for s, (qs_, ks_) in enumerate(steps):
+        qd, kd = to_device(qs_, wl.dtype), to_device(ks_, wl.dtype)
+        Ms = F.losa_block_mass(qd, kd, N, R, C)
+        kept = F.losa_retained_mass(Ms, rp, ci, N, R, C).cpu().numpy().astype(np.float64)
+        num_o = den_o = num_g = den_g = 0.0
+        for slot in range(2):
+            qh, kh = S.to_f64(qs_[:, slot:slot + 1], wl.dtype), S.to_f64(ks_[:, slot:slot + 1], wl.dtype)
+            iis = [i for (_, sl, i) in rows if sl == slot]
+            Mref = O.block_mass_rows(qh, kh, N, R, C, [(0, 0, i) for i in iis])
+            for t, i in enumerate(iis):
+                r = slot * nq + i
+                wi = min(R, N - i * R)
+                lst = row_csr(rp_h, ci_h, r)
+                num_o += wi * Mref[t][lst].sum()
+                den_o += wi * Mref[t].sum()
+                num_g += wi * kept[r, 0]
+                den_g += wi * kept[r, 1]
+        rec_o, rec_g = num_o / den_o, num_g / den_g
+        worst = max(worst, abs(rec_o - rec_g))
+        if s % 7 == 0 or s == wl.steps - 1:
+            say(f"  step {s}: sampled-row recall oracle {rec_o:.6f}, GPU {rec_g:.6f}")
+        assert abs(rec_o - rec_g) < 1e-5, s
+    say(f"recall at all {wl.steps} steps: largest oracle/GPU difference {worst:.2e}")
