@@ -148,12 +148,14 @@ def test_select_bit_exact_full_shape(wid):
     assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref, M.shape[2]))
 
 
-@pytest.mark.parametrize("nk", [1, 2, 63, 64, 65, 127, 129, 200, 1000, 1217, 2047, 2048])
+@pytest.mark.parametrize("nk", [1, 2, 63, 64, 65, 127, 129, 200, 500, 600, 1000, 1217, 1400, 2047, 2048, 2500])
 def test_select_widths_and_ties(nk):
     """Row widths around every multiple of the 64-lane step up to the widest
-    one-wave row (2048 blocks), most rows adversarial (equal masses, exact
-    ties, zeros, one-hot, denormals, non-finite): lists and order bit-exact
-    for several p, ties cut in index order."""
+    one-wave row (2048 blocks), one width in each unrolled instance of the
+    one-wave cut (600, 1400 among them) and one (2500) on the
+    workgroup-per-row cut; most rows adversarial (equal masses, exact ties,
+    zeros, one-hot, denormals, non-finite): lists and order bit-exact for
+    several p, ties cut in index order."""
     rng = np.random.default_rng(300 + nk)
     C, R = 32, 128
     N = nk * C - 3 if nk > 1 else 20
