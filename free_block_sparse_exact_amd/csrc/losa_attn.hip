@@ -23,7 +23,11 @@
 //     the S accumulators to the next MFMA without any exchange;
 //   * no per-score maximum and no rescaling of O inside the loop (see the
 //     main loop); row sums use the bf16-rounded probabilities, matching the
-//     numerator;
+//     numerator, and come from the matrix cores: one more MFMA per query
+//     tile and chunk multiplies P^T by a block of ones, whose every row is
+//     then the column sums of P^T (replacing sixteen dot products and the
+//     adds per chunk: config 1 5.79 -> 5.49 ms, config 3 152.3 -> 150.4 ms
+//     on one box);
 //   * a two-stage software pipeline (scores of chunk t+1 beside the softmax
 //     and P.V of chunk t), chunk keys read from registers, and the MFMA form
 //     with vector-register results (built with -amdgpu-mfma-vgpr-form).
@@ -36,9 +40,11 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// A chunk whose per-lane probability sum against the wave's reference
-// exceeds this bound sends the wave to the exact two-pass path.
-constexpr float kPBound = 65536.0f;
+// A row sum against the wave's reference above this bound (or not finite)
+// sends the wave to the exact two-pass path once its chunks are done: with
+// every probability, and so the row sum, at most 2^100, neither P nor P.V
+// can have overflowed.
+constexpr float kLBound = 1.2676506e30f;  // 2^100
 
 // On-the-fly block thresholding (Sol-Attn page: blocks are chosen while the
 // online softmax runs, by comparing each block's proxy score with a
@@ -204,10 +210,12 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
 
   f32x4 o[DT][kQT];
   float m[kQT], l[kQT];
+  f32x4 lsum[kQT];  // row sums from the matrix cores (see pv)
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     m[qt] = kNegInf;
     l[qt] = 0.f;
+    lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -278,10 +286,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
       }
   };
   // Probabilities p = 2^(s*c - m) against the wave's fixed reference m, packed
-  // to bf16; the row sums take the packed values.  Returns whether some lane's
-  // sum left (0, kPBound] -- an overflow, or m not yet finite.
-  auto probs = [&](const f32x4 (&acc)[2][kQT], bf16x8 (&pop)[kQT]) -> bool {
-    bool over = false;
+  // to bf16 (the row sums are taken from these packed values by pv).
+  auto probs = [&](const f32x4 (&acc)[2][kQT], bf16x8 (&pop)[kQT]) {
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       const float nm = -m[qt];
@@ -289,11 +295,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
       pop[qt] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-      const float rs = sum_bf16x8(pop[qt]);
-      over |= !(rs <= kPBound);
-      l[qt] += rs;
     }
-    return over;
   };
   auto chunk_max = [&](const f32x4 (&acc)[2][kQT], float (&mx)[kQT]) {
 #pragma unroll
@@ -310,28 +312,39 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
       mx[qt] = rows_max(mx[qt]);
     }
   };
+  // O^T += V^T P^T, and the row sums: a block of ones as the A operand makes
+  // every row of lsum[qt] the column sums of P^T, so each lane holds the full
+  // sum of its query over the wave's chunks (element 0 is used).
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   auto pv = [&](const bf16x8 (&vop)[DT], const bf16x8 (&pop)[kQT]) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt) o[dt][qt] = mfma_bf16(vop[dt], pop[qt], o[dt][qt]);
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) lsum[qt] = mfma_bf16(ones, pop[qt], lsum[qt]);
   };
 
   // No maximum is tracked per score and O is never rescaled inside the loop:
   // the reference m is fixed at the wave's first chunk's maximum plus
-  // kHeadroom (log2 units), so later chunks may exceed it by up to
-  // kHeadroom + 16 before a sum leaves (0, kPBound]; terms more than ~60 below
-  // the maximum are negligible either way.  If that ever happens the wave,
-  // once through its chunks, drops its partial sums and recomputes them in
-  // two passes (exact maximum first), so all probabilities are <= 1.  The
-  // loop has a single exit: an early exit makes the register allocator shuffle
-  // the O accumulators on every trip.
+  // kHeadroom (log2 units).  Later chunks may exceed the first chunk's
+  // maximum by up to kHeadroom + 100 - log2(their count) before the row sum
+  // passes kLBound; terms more than ~60 below the maximum are negligible
+  // either way.  If the row sum passes kLBound or is not finite (an
+  // overflow, a reference that is not finite, or a NaN input) the wave, once
+  // through its chunks, drops its partial sums and recomputes them in two
+  // passes (exact maximum first), so all probabilities are <= 1.  The loop
+  // has a single exit: an early exit makes the register allocator shuffle the
+  // O accumulators on every trip.
   //
   // Software pipeline: iteration t issues the score MFMAs of chunk t+1 next to
-  // the softmax of chunk t, then P.V of chunk t; the scheduler is asked to
-  // alternate one MFMA with two vector instructions.  K of chunk t+2 is
-  // requested once the score MFMAs have read K, V of chunk t+1 once P.V has
-  // read V.
+  // the softmax of chunk t, then P.V of chunk t, in the compiler's own
+  // interleaving (asking it to alternate one MFMA with one or two vector
+  // instructions measured 3.5% and 6% slower on the HunyuanVideo 720p layer,
+  // and no faster elsewhere).  K of chunk t+2 is requested once the score
+  // MFMAs have read K, V of chunk t+1 once P.V has read V.
   //
   // Padding keys of the last block score exactly 0 against the zero rows of
   // the packed K, which can lie far above every real score of a row, so they
@@ -427,26 +440,22 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
       scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
       load_k(key_at(t + 2), kop);
       bf16x8 pop[kQT];
-      const bool over = probs(acc, pop);  // chunk t
+      probs(acc, pop);  // chunk t
       pv(vop, pop);
       load_v(key_at(t + 1), vop);
-#pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // then two vector ALU ops
-      }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = accn[kt][qt];
-      over_any |= over;
     }
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) over_any |= !(lsum[qt][0] <= kLBound);
     fallback = __any(over_any);
   }
   if (fallback) {
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
-      l[qt] = 0.f;
+      lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
       m[qt] = kNegInf;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -481,11 +490,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     }
   }
 
-  // Row sums: combine the four lane groups that share each query.
+  // Row sums: every lane already holds its query's sum over the wave's chunks.
 #pragma unroll
-  for (int qt = 0; qt < kQT; ++qt) {
-    l[qt] = rows_sum(l[qt]);
-  }
+  for (int qt = 0; qt < kQT; ++qt) l[qt] = lsum[qt][0];
 
   // Merge the four key groups in one step: every wave parks its partial O,
   // maxima and row sums in its own LDS slot, then wave kw combines dims
