@@ -41,7 +41,8 @@ hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float*
 // Selection.
 struct SelectWs {
   int32_t* counts;      // [rows]
-  uint64_t* kappa;      // [rows] boundary sort key of the last kept block
+  uint32_t* keep;       // [rows][keep_words] the kept blocks as bits (bit j%32 of word j/32)
+  int keep_words;       // ceil(nk / 32)
   int32_t* chunk_hist;  // [nchunk][nk + 1] rows per (chunk, nk - count), then that count's rows in the
                         // head's earlier chunks
   int32_t* chunk_sum;   // [nchunk] kept blocks per row chunk, then the chunk's first CSR slot

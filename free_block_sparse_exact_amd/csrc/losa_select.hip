@@ -6,9 +6,10 @@
 // Kernels, in launch order:
 //   cut         the cut in (mass desc, index asc) order over exact integer
 //               units, without sorting -> the kept count s and the sort key
-//               kappa of the last kept block: one wave per row
-//               (n_k <= 2048) by a radix select over the range of the
-//               row's keys, or one workgroup per row by radix select;
+//               kappa of the last kept block, and the row's kept blocks
+//               (sort key <= kappa) as bits: one wave per row (n_k <= 2048)
+//               by a radix select over the range of the row's keys, or one
+//               workgroup per row by radix select;
 //   chunk       one workgroup per chunk of up to 256 rows of one head:
 //               histogram of counts and kept total of the chunk (LDS, then
 //               plain stores: no global atomics, nothing to clear
@@ -24,8 +25,9 @@
 //   group_order one workgroup: the work groups (32 ranks of one head) by
 //               their first count, descending, stable -> each group's slot;
 //   scatter     one thread per rank: the row into its group's slots -> order;
-//   compact     one wave per row: block j is kept iff its sort key is
-//               <= kappa; write kept indices ascending at row_ptr[row].
+//   compact     one wave per row: from the kept bits, the kept indices
+//               ascending at row_ptr[row] (the masses are read once, by the
+//               cut).
 //
 // The same chunk / offsets / place kernels also serve two other list
 // builders here: online block thresholding (threshold kernel: counts, then
@@ -197,6 +199,16 @@ __global__ __launch_bounds__(kOrderChunk) void chunk_kernel(const int32_t* __res
 constexpr int kMaxPer = LOSA_MAX_KEY_BLOCKS / kSelThreads;
 static_assert(kMaxPer == 16, "the workgroup cut kernel serves rows of 2049 to 4096 blocks");
 
+// ORs the run of bits (bit t for block j0 + t, at most 32 of them) into an
+// LDS bit array of the row (bit j%32 of word j/32); the run may straddle two
+// words.
+__device__ __forceinline__ void or_bit_run(uint32_t* words, int j0, uint32_t bits) {
+  if (bits == 0) return;
+  const int w = j0 >> 5, sh = j0 & 31;
+  atomicOr(&words[w], bits << sh);
+  if (sh != 0 && (bits >> (32 - sh)) != 0) atomicOr(&words[w + 1], bits >> (32 - sh));
+}
+
 // One workgroup per row.  Finds the kept count s and the sort key kappa of
 // the s-th block in (mass desc, index asc) order without sorting: a radix
 // select, most significant digit first, over the inverted mass bits
@@ -206,11 +218,13 @@ static_assert(kMaxPer == 16, "the workgroup cut kernel serves rows of 2049 to 40
 // (everything before it included) reaches T; after the last pass the
 // candidates share one mass, and the cut within them falls by index.
 // Thread t owns the contiguous blocks [t*per, t*per + per), so thread order
-// is index order; kPer >= per bounds the per-thread register arrays.
+// is index order; kPer >= per bounds the per-thread register arrays.  The
+// row's kept count goes to counts, its kept blocks as bits to keep (the
+// blocks whose sort key is at most kappa's, kappa being the s-th block's).
 template <int kPer>
 __global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const float* __restrict__ M,
                                                           const PTable pt, int32_t* __restrict__ counts,
-                                                          uint64_t* __restrict__ kappa) {
+                                                          uint32_t* __restrict__ keep) {
   __shared__ uint64_t hsum[256];
   __shared__ uint32_t hnz[256];
   __shared__ uint64_t wsum64[kSelThreads / 64];
@@ -218,6 +232,7 @@ __global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const fl
   __shared__ uint32_t wred[kSelThreads / 64];
   __shared__ uint64_t s_below;
   __shared__ int s_jcut;
+  __shared__ uint32_t s_keep[LOSA_MAX_KEY_BLOCKS / 32];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = (row / g.nq) % g.H;
   const uint64_t P = pt.P[pt.per_head ? h : 0];
@@ -323,10 +338,17 @@ __global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const fl
     s = nbelow + (int)need;
     kap = sort_key(0xFFFFFFFFu - prefix, s_jcut);
   }
-  if (tid == 0) {
-    counts[row] = s;
-    kappa[row] = kap;
-  }
+  const int nw = (nk + 31) / 32;
+  if (tid < nw) s_keep[tid] = 0;
+  __syncthreads();
+  uint32_t bits = 0;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t)
+    if (t < mine && sort_key(0xFFFFFFFFu - ku[t], j0 + t) <= kap) bits |= 1u << t;
+  or_bit_run(s_keep, j0, bits);
+  __syncthreads();
+  for (int x = tid; x < nw; x += kSelThreads) keep[(int64_t)row * nw + x] = s_keep[x];
+  if (tid == 0) counts[row] = s;
 }
 
 // Wave reductions with a wave-uniform result: DPP within each 16-lane row
@@ -388,11 +410,12 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
 // by a radix select.  Among the blocks with ku = v (equal masses, equal units)
 // the cut falls on the need-th in index order.  Lane l owns the contiguous
 // blocks [l*per, l*per + per), per <= kPer, so lane order is index order.
+// The row's kept count goes to counts, its kept blocks as bits to keep.
 template <int kPer>
 __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float* __restrict__ M, const PTable pt,
                                                        int32_t* __restrict__ counts,
-                                                       uint64_t* __restrict__ kappa) {
-  __shared__ uint64_t cut_hist[4][256];  // per wave: units per digit of the radix select
+                                                       uint32_t* __restrict__ keep) {
+  __shared__ uint64_t cut_hist[4][256];  // per wave: units per digit of the radix select, then the kept bits
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= g.rows()) return;  // whole waves only
@@ -538,10 +561,21 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
     s = wave_sum_i32(nbelow) + (int)need;
     kap = sort_key(0xFFFFFFFFu - v, jcut < 0 ? 0 : jcut);
   }
-  if (lane == 0) {
-    counts[row] = s;
-    kappa[row] = kap;
-  }
+  // The kept blocks (sort key <= kappa) as bits, assembled in this wave's LDS
+  // (at most 64 words: n_k <= 2048 here), then stored coalesced.
+  uint32_t* words = reinterpret_cast<uint32_t*>(cut_hist[threadIdx.x >> 6]);
+  const int nw = (nk + 31) / 32;
+  wave_lds_sync();  // the histogram's last reads are done
+  words[lane] = 0;
+  wave_lds_sync();
+  uint32_t bits = 0;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t)
+    if (t < mine && sort_key(0xFFFFFFFFu - ku[t], j0 + t) <= kap) bits |= 1u << t;
+  or_bit_run(words, j0, bits);
+  wave_lds_sync();
+  if (lane < nw) keep[(int64_t)row * nw + lane] = words[lane];
+  if (lane == 0) counts[row] = s;
 }
 
 // Exclusive scan of data[0, n) into out by one workgroup (a multiple of 64
@@ -628,35 +662,28 @@ __global__ __launch_bounds__(256) void offsets_kernel(int nk, int nchunk, int cp
   block_exclusive_scan_i32(chunk_sum, nchunk, chunk_sum, row_ptr + rows, wsum);
 }
 
-// One wave per row (four rows per workgroup): lane l tests the blocks l,
-// l + 64, ... (coalesced loads, four in flight), and the kept ones -- sort
-// key <= kappa -- are written in index order at row_ptr[row] plus the
-// number kept before them (a ballot per 64 blocks).
-__global__ __launch_bounds__(256) void compact_kernel(const Geom g, const float* __restrict__ M,
-                                                      const uint64_t* __restrict__ kappa,
+// One wave per row (four rows per workgroup): the row's kept bits (from the
+// cut, 4 bytes per 32 blocks instead of the masses again) are loaded once,
+// one word per lane; for each 64 blocks lane l writes block 64 s + l, if
+// kept, at row_ptr[row] plus the number kept before it.
+__global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32_t* __restrict__ keep,
                                                       const int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ col_idx) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= g.rows()) return;  // whole waves only
-  const int nk = g.nk;
-  const float* Mrow = M + (int64_t)row * nk;
-  const uint64_t kap = kappa[row];
+  const int nk = g.nk, nw = (nk + 31) / 32;  // nw <= 128
+  const uint32_t* kr = keep + (int64_t)row * nw;
+  const uint32_t w0 = lane < nw ? kr[lane] : 0u, w1 = 64 + lane < nw ? kr[64 + lane] : 0u;
   const uint64_t lt = (1ull << lane) - 1ull;
   int pos = row_ptr[row];
-  for (int j0 = 0; j0 < nk; j0 += 4 * kWave) {
-    bool keep[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + u * kWave + lane;
-      keep[u] = j < nk && sort_key(sanitized_bits(Mrow[j]), j) <= kap;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint64_t m = __ballot(keep[u]);
-      if (keep[u]) col_idx[pos + __popcll(m & lt)] = j0 + u * kWave + lane;
-      pos += __popcll(m);
-    }
+  for (int s = 0; 64 * s < nk; ++s) {  // blocks [64 s, 64 s + 64): words 2s, 2s + 1
+    const int a = 2 * s, b = 2 * s + 1;
+    const uint32_t lo = __builtin_amdgcn_readlane(a < 64 ? w0 : w1, a & 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(b < 64 ? w0 : w1, b & 63);
+    const uint64_t m = ((uint64_t)hi << 32) | lo;
+    if ((m >> lane) & 1ull) col_idx[pos + __popcll(m & lt)] = 64 * s + lane;
+    pos += __popcll(m);
   }
 }
 
@@ -878,8 +905,9 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
   size_t off = 0;
   const size_t counts_off = off;
   off = align_up(off + (size_t)rows * sizeof(int32_t), 256);
-  const size_t kappa_off = off;
-  off = align_up(off + (size_t)rows * sizeof(uint64_t), 256);
+  const int keep_words = (g.nk + 31) / 32;
+  const size_t keep_off = off;
+  off = align_up(off + (size_t)rows * keep_words * sizeof(uint32_t), 256);
   const size_t hist_off = off;  // then chunk_sum and done
   off = align_up(off + ((size_t)(g.nk + 1) * nchunk + nchunk + 1) * sizeof(int32_t), 256);
   const size_t bucket_off = off;
@@ -891,7 +919,8 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
   off = align_up(off + (size_t)2 * heads * ngh * sizeof(int32_t), 256);
   if (layout) {
     layout->counts = reinterpret_cast<int32_t*>(base + counts_off);
-    layout->kappa = reinterpret_cast<uint64_t*>(base + kappa_off);
+    layout->keep = reinterpret_cast<uint32_t*>(base + keep_off);
+    layout->keep_words = keep_words;
     layout->chunk_hist = reinterpret_cast<int32_t*>(base + hist_off);
     layout->chunk_sum = layout->chunk_hist + (size_t)(g.nk + 1) * nchunk;
     layout->done = layout->chunk_sum + nchunk;
@@ -917,14 +946,14 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
     auto cut = per <= 2 ? cut_wave_kernel<2> : per <= 4 ? cut_wave_kernel<4> : per <= 8 ? cut_wave_kernel<8>
              : per <= 12 ? cut_wave_kernel<12> : per <= 16 ? cut_wave_kernel<16> : per <= 20 ? cut_wave_kernel<20>
              : per <= 24 ? cut_wave_kernel<24> : cut_wave_kernel<32>;
-    hipLaunchKernelGGL(cut, dim3((rows + 3) / 4), dim3(256), 0, st, g, M, pt, ws.counts, ws.kappa);
+    hipLaunchKernelGGL(cut, dim3((rows + 3) / 4), dim3(256), 0, st, g, M, pt, ws.counts, ws.keep);
   } else {
     const int per_t = (g.nk + kSelThreads - 1) / kSelThreads;
     auto cut = per_t <= 12 ? cut_kernel<12> : cut_kernel<kMaxPer>;
-    hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.kappa);
+    hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.keep);
   }
   launch_offsets_and_order(g, ws, row_ptr, order, st);
-  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, g, M, (const uint64_t*)ws.kappa,
+  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, g, (const uint32_t*)ws.keep,
                      (const int32_t*)row_ptr, col_idx);
   return hipGetLastError();
 }
