@@ -20,13 +20,15 @@
 // key of probability >= 2^-126 is never flushed by the exponential, and the
 // block sums keep fp32's relative precision down to there (at most C * 2^-126
 // is lost per mass, from keys of smaller probability).  p rounded to bf16
-// feeds the P.V product and its normaliser, p in fp32 feeds the block sums.
-// At the end of a block the wave stores the block sum of each query to the
-// workspace S (as the mass kernel does); with one reference the partial O,
-// row sums and row totals of the four waves simply add, and M follows from S
-// divided by the row total.  If a chunk's probabilities grow too large (a
-// score more than ~77 above the first chunks' maximum) or O is not finite,
-// the whole workgroup recomputes against the exact maximum of the row.
+// feeds the P.V product and its normaliser (the row sums, taken on the
+// matrix cores by one more MFMA per query tile against a block of ones), p
+// in fp32 feeds the block sums.  At the end of a block the wave stores the
+// block sum of each query to the workspace S (as the mass kernel does); with
+// one reference the partial O, row sums and row totals of the four waves
+// simply add, and M follows from S divided by the row total.  If a wave's
+// row sum ends above 2^100 or not finite (a score ~100 above the first
+// chunks' maximum, or a non-finite input) or O is not finite, the whole
+// workgroup recomputes against the exact maximum of the row.
 //
 // Padding keys of the last block score exactly 0 against the zero rows of
 // the packed K and must leave the softmax: the wave that owns the last block
@@ -48,7 +50,10 @@ namespace losa {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kPBound = 1.2089258e24f;  // 2^80: per-lane chunk sum of the bf16 P above it -> the exact path
+// A row sum above this bound (or not finite) after the wave's chunks sends the
+// workgroup to the exact path: with every probability at most 2^100, neither
+// P, nor P.V, nor a block sum can have overflowed.
+constexpr float kLBound = 1.2676506e30f;  // 2^100
 
 template <int D, bool kLists>
 __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
@@ -98,10 +103,12 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
 
   f32x4 o[DT][kQT];
   float m[kQT], l[kQT], blk[kQT], tot = 0.f;
+  f32x4 lsum[kQT];  // row sums of the bf16 P from the matrix cores (see pv)
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     m[qt] = kNegInf;
     l[qt] = 0.f;
+    lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     blk[qt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -201,9 +208,9 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
           if (dead) acc[kt][qt][r] = kNegInf;
       }
   };
-  // p = 2^(s*c - m): fp32 into the block sums, bf16 into P and the row sums.
-  auto probs = [&](const f32x4 (&acc)[2][kQT], bf16x8 (&pop)[kQT]) -> bool {
-    bool over = false;
+  // p = 2^(s*c - m): fp32 into the block sums, bf16 into P (and, by pv, into
+  // the row sums).
+  auto probs = [&](const f32x4 (&acc)[2][kQT], bf16x8 (&pop)[kQT]) {
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       const float nm = -m[qt];
@@ -212,11 +219,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
       blk[qt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       pop[qt] = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-      const float rs = sum_bf16x8(pop[qt]);
-      over |= !(rs <= kPBound);
-      l[qt] += rs;
     }
-    return over;
   };
   auto chunk_max = [&](const f32x4 (&acc)[2][kQT], float (&mx)[kQT]) {
 #pragma unroll
@@ -233,11 +236,19 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       mx[qt] = rows_max(mx[qt]);
     }
   };
+  // O^T += V^T P^T, and the row sums: a block of ones as the A operand makes
+  // every row of lsum[qt] the column sums of P^T (each lane ends with its
+  // query's full sum over the wave's chunks).
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   auto pv = [&](const bf16x8 (&vop)[DT], const bf16x8 (&pop)[kQT]) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt) o[dt][qt] = mfma_bf16(vop[dt], pop[qt], o[dt][qt]);
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) lsum[qt] = mfma_bf16(ones, pop[qt], lsum[qt]);
   };
   // Block end: lane (lg, lr) stores the block sum of query lg*16 + lr (sums
   // over the four lane groups formed by a transpose-reduce: two values swapped
@@ -303,14 +314,14 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
       load_k(key_at(t + 2) & ~1, kop);
       bf16x8 pop[kQT];
-      const bool over = probs(acc, pop);  // chunk t
+      probs(acc, pop);  // chunk t
       pv(vop, pop);
       load_v(key_at(t + 1) & ~1, vop);
       // Three vector instructions per MFMA: the block sums add 32 to the
       // sparse attention loop's ~110 per 64 MFMAs, and with two per MFMA the
       // rest bunched up in one stretch (config 3: 179 against 170 ms).
 #pragma unroll
-      for (int s = 0; s < 64; ++s) {
+      for (int s = 0; s < 64 + kQT; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then three vector ALU ops
       }
@@ -320,9 +331,10 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = accn[kt][qt];
-      over_any |= over;
     }
-    // O itself must be finite (its probabilities may reach 2^80)
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) over_any |= !(lsum[qt][0] <= kLBound);
+    // O itself must be finite (its probabilities may reach 2^100)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -339,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
     float mx[kQT];
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
-      l[qt] = 0.f;
+      lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
       mx[qt] = kNegInf;
       blk[qt] = 0.f;
 #pragma unroll
@@ -373,11 +385,9 @@ __global__ __launch_bounds__(256, 1) void dense_bf16_kernel(const Geom g, const 
     }
   }
 
-  // Row sums of P: combine the four lane groups that share each query.
+  // Row sums of P: every lane already holds its query's sum over the wave's chunks.
 #pragma unroll
-  for (int qt = 0; qt < kQT; ++qt) {
-    l[qt] = rows_sum(l[qt]);
-  }
+  for (int qt = 0; qt < kQT; ++qt) l[qt] = lsum[qt][0];
   // Block-sum total of the query this lane stored (lg*16 + lr).
   s_tot[kw][lane] = tot;
 
