@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     int nch, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ order, void* O, int o_bf16, const double* __restrict__ qbar,
     const double* __restrict__ kbar, const InPass ip, int32_t* __restrict__ kept_count,
-    uint32_t* __restrict__ kept_mask) {
+    uint32_t* __restrict__ kept_mask, int32_t* __restrict__ list_ws) {
   constexpr int DC = D / 32, DT = D / 16, kQT = 4;
   constexpr int LD = D + 4;   // merge slot row stride (floats)
   extern __shared__ float lds[];  // merge slots [4][64][LD] f32, maxima [4][64], row sums [4][64]; in-pass list [nk]
@@ -223,23 +223,31 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   const float c = g.scale_log2;
   int beg, end;
   int32_t* list = reinterpret_cast<int32_t*>(lds + 4 * 64 * LD + 512);  // in-pass kept blocks
+  const int32_t* lst;  // the row's list: block lst[p] at position p in [0, end - beg)
   if constexpr (kInPass) {
     const double ln_t = ip.ln_theta[ip.per_head ? h : 0];
     uint32_t* mask_row = (kept_mask && qsub == 0) ? kept_mask + (int64_t)row * ((g.nk + 31) / 32) : nullptr;
     const int n = inpass_list<D>(g, qbar + (int64_t)row * D, kbar + (int64_t)bh * g.nk * D, ln_t, ip.ln_c,
                                  ip.ln_last, reinterpret_cast<double*>(lds), list, mask_row);
     if (kept_count && qsub == 0 && threadIdx.x == 0) kept_count[row] = n;
+    // The loop reads the list from this task's slot in global memory, as it
+    // reads a CSR row: read from LDS, the compiler scheduled the loop's
+    // operand loads so that every trip waited for all of them (the in-pass
+    // call took 15-23% longer than the sparse attention on the same blocks;
+    // 3-14% of it is recovered this way).
+    int32_t* gl = list_ws + (int64_t)tix * g.nk;
+    for (int x = threadIdx.x; x < n; x += 256) gl[x] = list[x];
+    __syncthreads();  // the whole list is written before any wave reads it
     beg = 0;
     end = n;
+    lst = gl;
   } else {
     beg = row_ptr[row];
     end = row_ptr[row + 1];
+    lst = col_idx + beg;
   }
   // Block at position p of the row's list.
-  auto list_at = [&](int p) -> int {
-    if constexpr (kInPass) return list[p];
-    else return col_idx[beg + p];
-  };
+  auto list_at = [&](int p) -> int { return lst[p]; };
   const int sub = g.C / 32;
   const int nchunk = (end - beg) * sub;
 
@@ -640,12 +648,11 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, const void* 
   hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st,
                      g, (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, row_ptr, col_idx, order, O,
                      o_bf16, (const double*)nullptr, (const double*)nullptr, none, (int32_t*)nullptr,
-                     (uint32_t*)nullptr);
+                     (uint32_t*)nullptr, (int32_t*)nullptr);
   return hipGetLastError();
 }
 
-// In-pass thresholding workspace: fp64 block means of Q [B*H*nq][D] and of K
-// [B*H*nk][D], then the packed K and V.
+// Bytes of the fp64 block means of Q [B*H*nq][D] and of K [B*H*nk][D].
 size_t means_bytes(const Geom& g) {
   return align_up((size_t)g.B * g.H * g.nq * g.D * sizeof(double), 256) +
          align_up((size_t)g.B * g.H * g.nk * g.D * sizeof(double), 256);
@@ -658,6 +665,7 @@ hipError_t launch_inpass(const Geom& g, const void* Q, const void* K, const void
   double* qbar = reinterpret_cast<double*>(base);
   double* kbar = reinterpret_cast<double*>(base + align_up((size_t)g.B * g.H * g.nq * g.D * sizeof(double), 256));
   launch_block_means64(g, Q, K, qbar, kbar, st);
+  int32_t* list_ws = reinterpret_cast<int32_t*>(base + means_bytes(g) + attn_ws_bytes(g));
   const int nch = vt_chunks(g);
   __bf16* Kp = reinterpret_cast<__bf16*>(base + means_bytes(g));
   __bf16* Vp = Kp + (size_t)g.B * g.H * nch * 32 * D;
@@ -668,7 +676,7 @@ hipError_t launch_inpass(const Geom& g, const void* Q, const void* K, const void
   hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(g.rows() * (g.R / 64)), dim3(256), lds, st, g,
                      (const __bf16*)Q, (const __bf16*)Kp, (const __bf16*)Vp, nch, (const int32_t*)nullptr,
                      (const int32_t*)nullptr, (const int32_t*)nullptr, O, o_bf16, (const double*)qbar,
-                     (const double*)kbar, ip, kept_count, kept_mask);
+                     (const double*)kbar, ip, kept_count, kept_mask, list_ws);
   return hipGetLastError();
 }
 
@@ -687,7 +695,11 @@ size_t attn_ws_bytes(const Geom& g) {
   return 2 * (size_t)g.B * g.H * g.D * (size_t)vt_chunks(g) * 32 * sizeof(uint16_t);  // packed K and V
 }
 
-size_t attn_threshold_ws_bytes(const Geom& g) { return means_bytes(g) + attn_ws_bytes(g); }
+// In-pass thresholding workspace: the block means, the packed K and V, then
+// one list slot of n_k int32 per task (workgroup).
+size_t attn_threshold_ws_bytes(const Geom& g) {
+  return means_bytes(g) + attn_ws_bytes(g) + (size_t)g.rows() * (g.R / 64) * g.nk * sizeof(int32_t);
+}
 
 hipError_t launch_sparse_attn_threshold(const Geom& g, const void* Q, const void* K, const void* V, const InPass& ip,
                                         void* O, int o_bf16, int32_t* kept_count, uint32_t* kept_mask, void* ws,

@@ -263,8 +263,11 @@ losa_status losa_sparse_attn(const losa_shape* shape, const void* Q, const void*
  * kept_mask: uint32 [batch*heads*n_q][ceil(n_k/32)] or NULL: bit j%32 of
  *    word j/32 of row r is set when block j is kept.
  * ws: at least *bytes from losa_sparse_attn_threshold_workspace: fp64 block
- *    means of Q and K (8 * batch*heads*(n_q + n_k)*head_dim bytes), then K
- *    and V repacked as for losa_sparse_attn.
+ *    means of Q and K (8 * batch*heads*(n_q + n_k)*head_dim bytes), K and V
+ *    repacked as for losa_sparse_attn, then one slot per 64-query tile for
+ *    its list of kept blocks (4 * batch*heads*n_q*(q_block/64)*n_k bytes;
+ *    only the kept blocks' indices are written).  Nothing of the proxy
+ *    scores is stored.
  * ------------------------------------------------------------------------ */
 losa_status losa_sparse_attn_threshold_workspace(const losa_shape* shape, size_t* bytes);
 losa_status losa_sparse_attn_threshold(const losa_shape* shape, const void* Q, const void* K, const void* V,
