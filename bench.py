@@ -78,11 +78,7 @@ PMC_KERNELS = [("attn_bf16_kernel", "attn", "losa_sparse_attn"),
                ("pack_kv_kernelILi128ELb0", "pack_k", "losa_block_mass"),
                ("cut_wave_kernel", "cut", "losa_select"),
                ("cut_kernel", "cut_wg", "losa_select"),
-               ("chunk_kernel", "chunk", "losa_select"),
-               ("offsets_kernel", "offsets", "losa_select"),
-               ("place_kernel", "place", "losa_select"),
-               ("group_order_kernel", "group_order", "losa_select"),
-               ("scatter_order_kernel", "scatter_order", "losa_select"),
+               ("order_kernel", "order", "losa_select"),
                ("compact_kernel", "compact", "losa_select")]
 
 
@@ -641,7 +637,7 @@ def refresh_calls(F, torch, q, k, bufs, geom, wl, stream, dev):
                      "bytes": drift_bytes, "launches": "drift_partial + drift_final",
                      "note": "Q, K and their references read once; not in ms_per_step"},
         "merge_lists": {"ms": merge_ms, "gbs": merge_bytes / (merge_ms * 1e-3) / 1e9, "bytes": merge_bytes,
-                        "launches": "pick_counts + chunk + offsets + place + copy_lists",
+                        "launches": "pick_counts + order + copy_lists",
                         "note": "launch-latency bound at this size; not in ms_per_step"},
     }
 
@@ -1013,12 +1009,8 @@ TRACE_KERNELS = [
     ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
     ("cut_wave_kernel", "cut_wave_kernel", "losa_select"),
     ("cut_kernel", "cut_kernel", "losa_select"),
-    ("chunk_kernel", "chunk_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
-    ("offsets_kernel", "offsets_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
+    ("order_kernel", "order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("compact_kernel", "compact_kernel", "losa_select"),
-    ("group_order_kernel", "group_order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
-    ("scatter_order_kernel", "scatter_order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
-    ("place_kernel", "place_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
     ("drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),
     ("drift_final_kernel", "drift_final_kernel", "losa_qk_drift"),

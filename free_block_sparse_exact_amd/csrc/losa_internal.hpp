@@ -40,22 +40,18 @@ hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float*
 
 // Selection.
 struct SelectWs {
-  int32_t* counts;      // [rows]
+  int32_t* counts;      // [rows] kept blocks per row
   uint32_t* keep;       // [rows][keep_words] the kept blocks as bits (bit j%32 of word j/32)
   int keep_words;       // ceil(nk / 32)
-  int32_t* chunk_hist;  // [nchunk][nk + 1] rows per (chunk, nk - count), then that count's rows in the
-                        // head's earlier chunks
-  int32_t* chunk_sum;   // [nchunk] kept blocks per row chunk, then the chunk's first CSR slot
-  int32_t* done;        // [1] finished workgroups of the offsets kernel
-  int32_t* bucket;      // [B*H][nk + 1] the head's rows per nk - count
-  int nchunk;           // B*H*cph row chunks, each inside one head
-  int cph;              // chunks per head: ceil(nq / kOrderChunk)
+  int32_t* local_off;   // [rows] kept blocks of the head's earlier rows
+  int32_t* head_total;  // [B*H] kept blocks per head
+  int32_t* head_base;   // [B*H] first col_idx slot of each head
+  int32_t* done;        // [1] finished workgroups of the order kernel (cleared by the count kernel before it)
   int32_t* ranked;      // [rows] row of rank r in head h at h * nq + r
   int32_t* gkey;        // [B*H*ngh] count of each work group's first row
   int32_t* gstart;      // [B*H*ngh] first order slot of each work group
   int ngh;              // work groups per head: ceil(nq / kGroupRows)
 };
-constexpr int kOrderChunk = 256;  // rows per placement chunk for the budget order
 constexpr int kGroupRows = 32;    // rows per work group of the budget order (one XCD's CUs)
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base);
 hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_t* row_ptr,
@@ -70,10 +66,11 @@ struct ThetaTable {
 };
 hipError_t launch_select_threshold(const Geom& g, const float* M, const ThetaTable& tt, int32_t* row_ptr,
                                    int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t stream);
-// Row offsets and work order from the kept counts in ws.counts (shared by
-// the selector and the list merge).
-void launch_offsets_and_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, int32_t* order,
-                              hipStream_t stream);
+// Row offsets of each head and (want_order) the work order's ranks and
+// group slots from the kept counts in ws.counts, one launch; the writing
+// kernel after it stores row_ptr and order (shared by the selector, online
+// thresholding and the list merge).
+void launch_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, bool want_order, hipStream_t stream);
 // Per-head choice between two list sets (selector workspace).
 hipError_t launch_merge_lists(const Geom& g, const int32_t* take_b, const int32_t* rpa, const int32_t* cia,
                               const int32_t* rpb, const int32_t* cib, int32_t* row_ptr, int32_t* col_idx,

@@ -9,30 +9,23 @@
 //               kappa of the last kept block, and the row's kept blocks
 //               (sort key <= kappa) as bits: one wave per row (n_k <= 2048)
 //               by a radix select over the range of the row's keys, or one
-//               workgroup per row by radix select;
-//   chunk       one workgroup per chunk of up to 256 rows of one head:
-//               histogram of counts and kept total of the chunk (LDS, then
-//               plain stores: no global atomics, nothing to clear
-//               beforehand, so the sequence can sit inside a captured graph);
-//   offsets     one thread per count: exclusive scan, head by head, over
-//               the head's row chunks of that count's histogram column
-//               (-> the head's rows of that count); the last workgroup to
-//               finish scans the per-chunk kept totals (-> first CSR slot
-//               per chunk, and row_ptr[rows]);
-//   place       one workgroup per chunk: row_ptr of its rows (chunk base +
-//               scan of counts), and each row's stable rank by count,
-//               descending, inside its head (-> ranked rows, group keys);
-//   group_order one workgroup: the work groups (32 ranks of one head) by
-//               their first count, descending, stable -> each group's slot;
-//   scatter     one thread per rank: the row into its group's slots -> order;
-//   compact     one wave per row: from the kept bits, the kept indices
-//               ascending at row_ptr[row] (the masses are read once, by the
-//               cut).
+//               workgroup per row by radix select; the row arrives through
+//               LDS from coalesced loads;
+//   order       one workgroup per (batch, head): the exclusive scan of the
+//               head's counts (its rows' offsets inside the head) and, when
+//               the work order is wanted, the head's rows ranked by count
+//               (a stable counting sort in LDS); the last workgroup to
+//               finish scans the heads' totals (-> each head's first CSR
+//               slot, row_ptr[rows]) and places the work groups by their
+//               first count (another stable counting sort) -> each group's
+//               first order slot;
+//   compact     one wave per row: row_ptr[row], the row's entry in the work
+//               order, and from the kept bits the kept indices ascending
+//               from row_ptr[row] (the masses are read once, by the cut).
 //
-// The same chunk / offsets / place kernels also serve two other list
-// builders here: online block thresholding (threshold kernel: counts, then
-// the kept indices) and the per-head merge of two list sets (pick_counts,
-// then copy_lists).
+// The same order kernel also serves two other list builders here: online
+// block thresholding (threshold kernel: counts, then the kept indices) and
+// the per-head merge of two list sets (pick_counts, then copy_lists).
 //
 // Work order: each (batch, head)'s n_q rows ranked by kept count,
 // descending, ties by row index; the ranks cut into groups of 32 (what one
@@ -152,49 +145,6 @@ __device__ __forceinline__ uint64_t match_lanes(int key, bool active, int nbits)
   return eq;
 }
 
-// Chunk c covers rows h * nq + k * kOrderChunk + [0, kOrderChunk) of head
-// h = c / cph, k = c % cph (cph chunks per head), cut at the head's end.
-struct ChunkRows {
-  int row, valid, head;
-  __device__ ChunkRows(int chunk, int nq, int cph) {
-    head = chunk / cph;
-    const int local = (chunk - head * cph) * kOrderChunk + (int)threadIdx.x;
-    valid = local < nq;
-    row = head * nq + local;
-  }
-};
-
-// One workgroup per chunk: the chunk's histogram of nk - count (built in
-// LDS, stored whole, zeros included) and its kept total.  Workgroup 0 also
-// clears the offsets kernel's done counter.  Plain stores only, so nothing
-// needs clearing beforehand.
-__global__ __launch_bounds__(kOrderChunk) void chunk_kernel(const int32_t* __restrict__ counts, int nq, int cph,
-                                                            int nk, int32_t* __restrict__ hist,
-                                                            int32_t* __restrict__ chunk_sum, int32_t* done) {
-  extern __shared__ int hl[];  // [nk + 1]
-  __shared__ int wsum[kOrderChunk / 64];
-  const int chunk = blockIdx.x;
-  for (int x = threadIdx.x; x <= nk; x += blockDim.x) hl[x] = 0;
-  __syncthreads();
-  const ChunkRows cr(chunk, nq, cph);
-  const int cnt = cr.valid ? counts[cr.row] : 0;
-  if (cr.valid) atomicAdd(&hl[nk - cnt], 1);
-  int v = cnt;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int32_t* hrow = hist + (int64_t)chunk * (nk + 1);
-  for (int x = threadIdx.x; x <= nk; x += blockDim.x) hrow[x] = hl[x];
-  if (threadIdx.x == 0) {
-    int t = 0;
-#pragma unroll
-    for (int ww = 0; ww < kOrderChunk / 64; ++ww) t += wsum[ww];
-    chunk_sum[chunk] = t;
-    if (chunk == 0) *done = 0;
-  }
-}
-
 // Most key blocks one thread of the cut kernel owns.
 constexpr int kMaxPer = LOSA_MAX_KEY_BLOCKS / kSelThreads;
 static_assert(kMaxPer == 16, "the workgroup cut kernel serves rows of 2049 to 4096 blocks");
@@ -224,7 +174,7 @@ __device__ __forceinline__ void or_bit_run(uint32_t* words, int j0, uint32_t bit
 template <int kPer>
 __global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const float* __restrict__ M,
                                                           const PTable pt, int32_t* __restrict__ counts,
-                                                          uint32_t* __restrict__ keep) {
+                                                          uint32_t* __restrict__ keep, int32_t* __restrict__ done) {
   __shared__ uint64_t hsum[256];
   __shared__ uint32_t hnz[256];
   __shared__ uint64_t wsum64[kSelThreads / 64];
@@ -233,7 +183,11 @@ __global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const fl
   __shared__ uint64_t s_below;
   __shared__ int s_jcut;
   __shared__ uint32_t s_keep[LOSA_MAX_KEY_BLOCKS / 32];
+  // the row's mass bits, block j at word j + j/32 (a pad word per 32 keeps
+  // the threads' runs of per words on distinct banks)
+  __shared__ uint32_t s_stage[kSelThreads * kPer + kSelThreads * kPer / 32];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (row == 0 && tid == 0) *done = 0;  // the order kernel's counter
   const int h = (row / g.nq) % g.H;
   const uint64_t P = pt.P[pt.per_head ? h : 0];
   const int nk = g.nk;
@@ -243,11 +197,30 @@ __global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const fl
   const int mine = max(0, min(per, nk - j0));  // valid blocks of this thread
   if (tid == 0) s_jcut = 0;
 
+  // Coalesced loads (block 256 c + tid), all issued before the first is
+  // used (addresses clamped into the row), staged in LDS; then each thread
+  // reads back its own contiguous run.
+  {
+    float x[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int j = kSelThreads * c + tid;
+      x[c] = Mrow[j < nk ? j : nk - 1];
+    }
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int j = kSelThreads * c + tid;
+      s_stage[j + (j >> 5)] = sanitized_bits(x[c]);
+    }
+  }
+  __syncthreads();
   uint32_t ku[kPer];
   uint32_t umax = 0;
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    const uint32_t u = t < mine ? sanitized_bits(Mrow[j0 + t]) : 0u;
+    const int j = j0 + t;  // < kSelThreads kPer for every t < kPer: inside the staged words
+    const uint32_t sj = s_stage[j + (j >> 5)];
+    const uint32_t u = t < mine ? sj : 0u;
     ku[t] = 0xFFFFFFFFu - u;
     umax = umax > u ? umax : u;
   }
@@ -403,82 +376,118 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
   return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
 }
 
+// The units of block mass bits u with the row's frexp exponent e:
+// ceil(m * 2^(51 - e)), exact.
+__device__ __forceinline__ uint64_t row_units(uint32_t u, int e) {
+  const int ef = (int)(u >> 23);
+  if (ef >= 99 + e && ef > 0) return (uint64_t)((u & 0x7FFFFFu) | 0x800000u) << (ef - 99 - e);
+  return fixed_units(u, e);
+}
+
 // One wave per row (four rows per workgroup), no workgroup barriers.  The
 // cut is the least inverted-bits value v with F(v) = sum of the units q of
-// the blocks with ku <= v reaching T, found over the range of the blocks'
-// ku (F only steps at those values, so v is one of them, and F(v - 1) < T)
-// by a radix select.  Among the blocks with ku = v (equal masses, equal units)
-// the cut falls on the need-th in index order.  Lane l owns the contiguous
-// blocks [l*per, l*per + per), per <= kPer, so lane order is index order.
-// The row's kept count goes to counts, its kept blocks as bits to keep.
+// the blocks with ku <= v reaching T (F only steps at the blocks' keys, so v
+// is one of them, and F(v - 1) < T); in mass bits u = 2^32 - 1 - ku that is
+// the largest uv with the units of the blocks of u >= uv reaching T.  Among
+// the blocks with u = uv (equal masses, equal units) the cut falls on the
+// need-th in index order.  Lane l owns the contiguous blocks [l kPer,
+// l kPer + kPer) (kPer odd, 64 kPer >= nk; blocks past nk read as 0), so lane
+// order is index order.
+//
+// The search runs over rel = umax - u in [0, umax - umin] (umin: the least
+// positive mass).  A radix pass over the top 8 bits of the range (units
+// summed per digit in an LDS histogram) finds the digit whose band of masses
+// holds the cut; when at most 64 blocks fall in that band (the usual case)
+// they are listed in index order and each listed block's cumulative units are
+// counted directly against the others; otherwise further radix passes of 8
+// bits narrow the band.  Units are mant << (exponent shift) for masses within
+// 2^27 of the row maximum (exact, no rounding) and the general ceil rule for
+// smaller or denormal ones.  The row's kept count goes to counts, its kept
+// blocks as bits to keep.
 template <int kPer>
 __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float* __restrict__ M, const PTable pt,
                                                        int32_t* __restrict__ counts,
-                                                       uint32_t* __restrict__ keep) {
-  __shared__ uint64_t cut_hist[4][256];  // per wave: units per digit of the radix select, then the kept bits
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= g.rows()) return;  // whole waves only
+                                                       uint32_t* __restrict__ keep, int32_t* __restrict__ done) {
+  static_assert(kPer % 2 == 1 && kPer <= 31, "odd runs: lanes reading runs of kPer words hit distinct banks");
+  // per wave: the staged row (kept for the listing); the radix histogram, then the listed blocks, then the
+  // kept bits
+  __shared__ uint32_t stage_all[4][64 * kPer];
+  __shared__ uint64_t hist_all[4][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wv;
+  if (row == 0 && lane == 0) *done = 0;  // the order kernel's counter
+  if (row >= g.rows()) return;           // whole waves only
   const int h = (row / g.nq) % g.H;
   const uint64_t P = pt.P[pt.per_head ? h : 0];
   const int nk = g.nk;
-  const float* Mrow = M + (int64_t)row * nk;
-  const int per = (nk + kWave - 1) / kWave;
-  const int j0 = lane * per;
-  const int mine = max(0, min(per, nk - j0));
+  const int j0 = lane * kPer;
+  uint32_t* stage = stage_all[wv];
+  uint64_t* hist = hist_all[wv];
 
-  uint32_t ku[kPer];
-  uint32_t umax = 0;
+  // The row through LDS: coalesced loads of block 64 c + lane (buffer loads:
+  // blocks past the row's end read as 0 without a memory access), then each
+  // lane reads back its own run.
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(M + (int64_t)row * nk), (short)0, nk * 4, 0x00020000);
+    uint32_t x[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) x[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (64 * c + lane) * 4, 0, 0);
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) stage[64 * c + lane] = sanitized_bits(__uint_as_float(x[c]));
+  }
+  wave_lds_sync();
+  uint32_t u[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) u[t] = stage[j0 + t];
+  uint32_t umax = 0, umin = 0xFFFFFFFFu;  // largest mass; least positive mass
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    const uint32_t u = t < mine ? sanitized_bits(Mrow[j0 + t]) : 0u;
-    ku[t] = 0xFFFFFFFFu - u;
-    umax = umax > u ? umax : u;
+    umax = max(umax, u[t]);
+    umin = min(umin, u[t] ? u[t] : 0xFFFFFFFFu);
   }
   umax = wave_max_u32_uniform(umax);
 
   int s;
-  uint64_t kap;
+  uint32_t gt = 0, eq = 0;  // this lane's blocks with u > uv, and with u == uv (bit t: block j0 + t)
+  int jcut = nk;            // kept: u > uv, or u == uv and index <= jcut
   if (P == (1ull << 32)) {  // keep everything
     s = nk;
-    kap = ~0ull;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) gt |= (j0 + t < nk ? 1u : 0u) << t;
   } else {
     const int e = umax ? frexp_exp(umax) : 0;
+    const int c = 99 + e;
+    const uint32_t fast_lo = (uint32_t)max(c, 1) << 23;  // masses with bits >= this take the shift rule
     uint64_t q[kPer];
-    uint64_t run = 0;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0, kmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int t = 0; t < kPer; ++t) {
-      q[t] = t < mine ? fixed_units(0xFFFFFFFFu - ku[t], e) : 0;
-      run += q[t];
-      if (t < mine) kmin = kmin < ku[t] ? kmin : ku[t];
-      if (q[t] > 0) {
-        lo = lo < ku[t] ? lo : ku[t];
-        hi = hi > ku[t] ? hi : ku[t];
-      }
+      const uint32_t mant = u[t] ? ((u[t] & 0x7FFFFFu) | 0x800000u) : 0u;
+      q[t] = (uint64_t)mant << (((int)(u[t] >> 23) - c) & 63);
     }
+    if (__ballot(umin < fast_lo)) {  // masses below 2^-27 of the row maximum, or denormal: the rounded rule
+#pragma unroll
+      for (int t = 0; t < kPer; ++t)
+        if (u[t] != 0 && u[t] < fast_lo) q[t] = fixed_units(u[t], e);
+    }
+    uint64_t run = 0;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) run += q[t];
     const uint64_t T = threshold(P, wave_sum_u64(run));
-    uint32_t v;
-    if (T == 0) {
-      v = wave_min_u32(kmin);  // the first block in sorted order
-    } else {  // T > 0: some block has units, and F(max ku of those) = total >= T
-      // F steps only at keys of blocks with units, all in [lo, hi]: a radix
-      // select over rel = ku - lo, most significant 8-bit digit of the
-      // range first.  Each pass sums the units of the blocks still in the
-      // prefix's range per digit (this wave's histogram in LDS, exact u64
-      // sums) and keeps the least digit at which acc + the running sum
-      // reaches T.  At most four passes, against up to 32 bisection steps
-      // that each re-sum the whole row.
-      lo = wave_min_u32(lo);
-      hi = wave_max_u32_uniform(hi);
-      const uint32_t width = hi - lo;
-      uint64_t* hist = cut_hist[threadIdx.x >> 6];
+    uint64_t below = 0;  // units of the blocks with u > uv
+    uint32_t uv = umax;  // T == 0, or one positive mass value: the cut is at the largest mass
+    if (T != 0) {
+      umin = wave_min_u32(umin);
+      const uint32_t width = umax - umin;
+      // rel = umax - u for masses, all ones for zeros (outside every band)
       uint32_t rel[kPer];
 #pragma unroll
-      for (int t = 0; t < kPer; ++t) rel[t] = ku[t] - lo;
+      for (int t = 0; t < kPer; ++t) rel[t] = u[t] ? umax - u[t] : 0xFFFFFFFFu;
       uint32_t pre = 0;  // digits found so far
       uint64_t acc = 0;  // units of the blocks below the prefix's range
-      for (int top = width ? 32 - __builtin_clz(width) : 0; top > 0;) {
+      int top = width ? 32 - __builtin_clz(width) : 0;
+      bool listed = false;
+      for (int pass = 0; top > 0 && !listed; ++pass) {
         const int shift = top > 8 ? top - 8 : 0;
         const uint32_t dmask = (1u << (top - shift)) - 1u;
         const uint32_t above = top >= 32 ? 0u : (0xFFFFFFFFu << top);
@@ -487,91 +496,131 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
         hist[4 * lane + 2] = 0;
         hist[4 * lane + 3] = 0;
         wave_lds_sync();
+        if (pass == 0) {  // every block: zeros add 0 to some bin
 #pragma unroll
-        for (int t = 0; t < kPer; ++t)
-          if (q[t] > 0 && ((rel[t] ^ pre) & above) == 0)
+          for (int t = 0; t < kPer; ++t)
             atomicAdd(reinterpret_cast<unsigned long long*>(hist + ((rel[t] >> shift) & dmask)),
                       (unsigned long long)q[t]);
-        wave_lds_sync();
-        uint64_t c[4];  // inclusive sums of this lane's digits 4 lane .. 4 lane + 3
-        c[0] = hist[4 * lane];
+        } else {  // the blocks in the prefix's range (zeros never are: pre + 2^top - 1 <= width < all ones)
 #pragma unroll
-        for (int k = 1; k < 4; ++k) c[k] = c[k - 1] + hist[4 * lane + k];
-        uint64_t inc = c[3];  // inclusive scan over lanes
+          for (int t = 0; t < kPer; ++t)
+            if (((rel[t] ^ pre) & above) == 0)
+              atomicAdd(reinterpret_cast<unsigned long long*>(hist + ((rel[t] >> shift) & dmask)),
+                        (unsigned long long)q[t]);
+        }
+        wave_lds_sync();
+        uint64_t cs[4];  // inclusive sums of this lane's digits 4 lane .. 4 lane + 3
+        cs[0] = hist[4 * lane];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) cs[k] = cs[k - 1] + hist[4 * lane + k];
+        uint64_t inc = cs[3];  // inclusive scan over lanes
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
           const uint32_t xl = __shfl_up((uint32_t)inc, o, kWave), xh = __shfl_up((uint32_t)(inc >> 32), o, kWave);
           if (lane >= o) inc += ((uint64_t)xh << 32) | xl;
         }
-        const uint64_t base = acc + (inc - c[3]);
+        const uint64_t base = acc + (inc - cs[3]);
         // this lane's least digit reaching T (4: none), and the units below it
         int k = 4;
         uint64_t bel = 0;
 #pragma unroll
         for (int kk = 3; kk >= 0; --kk)
-          if (base + c[kk] >= T) {
+          if (base + cs[kk] >= T) {
             k = kk;
-            bel = kk ? c[kk - 1] : 0;
+            bel = kk ? cs[kk - 1] : 0;
           }
         // some lane hits: acc plus all units in the prefix's range is F(end of the range) >= T
         const uint64_t hit = __ballot(k < 4);
         const int lf = __builtin_ctzll(hit);
         const uint32_t digit = 4u * lf + (uint32_t)__builtin_amdgcn_readlane(k, lf);
-        const uint64_t add = (inc - c[3]) + bel;
+        const uint64_t add = (inc - cs[3]) + bel;
         acc += ((uint64_t)lane_u32((uint32_t)(add >> 32), lf) << 32) | lane_u32((uint32_t)add, lf);
         pre |= digit << shift;
         top = shift;
-        wave_lds_sync();  // every lane has read the histogram before the next pass clears it
-      }
-      v = lo + pre;
-    }
-    uint64_t below = 0;
-    int nbelow = 0, nties = 0;
+        wave_lds_sync();  // every lane has read the histogram before it is cleared or reused
+        if (top == 0) break;
+        // the blocks of the chosen digit: rel in [pre, pre + 2^top); listed when at most 64
+        const uint32_t span = (1u << top) - 1u;
+        uint32_t smask = 0;
 #pragma unroll
-    for (int t = 0; t < kPer; ++t) {
-      if (t < mine) {
-        below += ku[t] < v ? q[t] : 0;
-        nbelow += ku[t] < v ? 1 : 0;
-        nties += ku[t] == v ? 1 : 0;
+        for (int t = 0; t < kPer; ++t) smask |= (rel[t] - pre <= span ? 1u : 0u) << t;
+        const int cnt = __popc(smask);
+        int incl = cnt;  // listed blocks of lanes <= this one
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int x = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += x;
+        }
+        const int nlist = __builtin_amdgcn_readlane(incl, 63);
+        if (nlist > 64) continue;
+        // (mass bits, index) and units of each listed block, in index order
+        int at = incl - cnt;
+        while (smask) {
+          const int t = __builtin_ctz(smask);
+          smask &= smask - 1u;
+          const uint32_t uj = stage[j0 + t];
+          hist[2 * at] = (uint64_t)uj | ((uint64_t)(j0 + t) << 32);
+          hist[2 * at + 1] = row_units(uj, e);
+          ++at;
+        }
+        wave_lds_sync();
+        const uint32_t ui = lane < nlist ? (uint32_t)hist[2 * lane] : 0u;
+        uint64_t fle = acc, flt = acc;  // units of the blocks with u >= ui, and with u > ui
+        for (int x = 0; x < nlist; ++x) {
+          const uint32_t ux = (uint32_t)hist[2 * x];
+          const uint64_t qx = hist[2 * x + 1];
+          fle += ux >= ui ? qx : 0;
+          flt += ux > ui ? qx : 0;
+        }
+        // the cut: the largest listed mass whose cumulative units reach T
+        uv = wave_max_u32_uniform(lane < nlist && fle >= T ? ui : 0u);
+        const uint64_t at_v = __ballot(lane < nlist && ui == uv);
+        const int lv = __builtin_ctzll(at_v);
+        below = ((uint64_t)lane_u32((uint32_t)(flt >> 32), lv) << 32) | lane_u32((uint32_t)flt, lv);
+        listed = true;
+        wave_lds_sync();  // the list is read before its space is reused
+      }
+      if (!listed) {
+        uv = umax - pre;
+        below = acc;
       }
     }
-    below = wave_sum_u64(below);
-    const uint64_t qu = fixed_units(0xFFFFFFFFu - v, e);
+    const uint64_t qu = row_units(uv, e);
     uint64_t need = 1;
     if (below < T && qu > 0) need = (T - below + qu - 1) / qu;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      gt |= (u[t] > uv ? 1u : 0u) << t;
+      eq |= (u[t] == uv && j0 + t < nk ? 1u : 0u) << t;
+    }
+    const int nties = __popc(eq);
     int incl = nties;  // ties owned by lanes <= this one
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const int x = __shfl_up(incl, o, kWave);
       if (lane >= o) incl += x;
     }
-    int jcut = -1;
-    int rank = incl - nties;
-    if ((int64_t)need > rank && (int64_t)need <= incl) {
-#pragma unroll
-      for (int t = 0; t < kPer; ++t) {
-        if (t < mine && ku[t] == v) {
-          ++rank;
-          if (rank == (int)need) jcut = j0 + t;
-        }
-      }
+    // the need-th tie in index order: in the lane whose ties cover it
+    const int before = incl - nties;
+    int jc = -1;
+    if ((int64_t)need > before && (int64_t)need <= incl) {
+      uint32_t w = eq;
+      for (int r = before + 1; r < (int)need; ++r) w &= w - 1u;
+      jc = j0 + __builtin_ctz(w);
     }
-    const uint64_t owner = __ballot(jcut >= 0);
-    jcut = __builtin_amdgcn_readlane(jcut, owner ? __builtin_ctzll(owner) : 0);
-    s = wave_sum_i32(nbelow) + (int)need;
-    kap = sort_key(0xFFFFFFFFu - v, jcut < 0 ? 0 : jcut);
+    const uint64_t owner = __ballot(jc >= 0);
+    jcut = __builtin_amdgcn_readlane(jc, owner ? __builtin_ctzll(owner) : 0);
+    s = wave_sum_i32(__popc(gt)) + (int)need;
   }
-  // The kept blocks (sort key <= kappa) as bits, assembled in this wave's LDS
-  // (at most 64 words: n_k <= 2048 here), then stored coalesced.
-  uint32_t* words = reinterpret_cast<uint32_t*>(cut_hist[threadIdx.x >> 6]);
+  // The kept blocks (u > uv, or u == uv up to jcut) as bits, assembled in this
+  // wave's LDS (at most 64 words: n_k <= 2048 here), then stored coalesced.
+  const int upto = jcut - j0 + 1;  // ties at t < upto are kept
+  const uint32_t tmask = upto >= 32 ? 0xFFFFFFFFu : (upto <= 0 ? 0u : (1u << upto) - 1u);
+  const uint32_t bits = gt | (eq & tmask);
+  uint32_t* words = reinterpret_cast<uint32_t*>(hist);
   const int nw = (nk + 31) / 32;
-  wave_lds_sync();  // the histogram's last reads are done
   words[lane] = 0;
   wave_lds_sync();
-  uint32_t bits = 0;
-#pragma unroll
-  for (int t = 0; t < kPer; ++t)
-    if (t < mine && sort_key(0xFFFFFFFFu - ku[t], j0 + t) <= kap) bits |= 1u << t;
   or_bit_run(words, j0, bits);
   wave_lds_sync();
   if (lane < nw) keep[(int64_t)row * nw + lane] = words[lane];
@@ -619,56 +668,32 @@ __device__ void block_exclusive_scan_i32(const int32_t* data, int n, int32_t* ou
   __syncthreads();
 }
 
-// One thread per count bucket b = nk - count: within each head, the column
-// hist[.][b] over the head's cph chunks becomes its exclusive scan, and
-// bucket[head][b] the head's total.  The last workgroup to finish (counted
-// in *done) turns chunk_sum into the first CSR slot of each chunk and writes
-// row_ptr[rows].
-__global__ __launch_bounds__(256) void offsets_kernel(int nk, int nchunk, int cph, int rows,
-                                                      int32_t* __restrict__ hist, int32_t* chunk_sum,
-                                                      int32_t* __restrict__ bucket, int32_t* done,
-                                                      int32_t* __restrict__ row_ptr) {
-  __shared__ int wsum[256 / 64];
-  __shared__ int last;
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b <= nk) {
-    int run = 0, k = 0, h = 0;  // running total, chunk within the head, head
-    auto step = [&](int c, int v) {
-      if (k == 0) run = 0;
-      hist[(int64_t)c * (nk + 1) + b] = run;
-      run += v;
-      if (++k == cph) {
-        bucket[(int64_t)h * (nk + 1) + b] = run;
-        k = 0;
-        ++h;
-      }
-    };
-    int c = 0;
-    for (; c + 8 <= nchunk; c += 8) {  // eight loads in flight per thread
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)(c + u) * (nk + 1) + b];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) step(c + u, v[u]);
-    }
-    for (; c < nchunk; ++c) step(c, hist[(int64_t)c * (nk + 1) + b]);
+// The first col_idx slot of row's list: its head's first slot plus the kept
+// blocks of the head's earlier rows (both written by order_kernel).  Lane 0
+// of the row's wave stores it as row_ptr[row]; lane 1 places the row at rank
+// position `row` (rank r of head h) into the work order when one is wanted
+// (a slot outside [0, rows) cannot arise from the order kernel and is not
+// written).
+__device__ __forceinline__ int finish_row(const SelectWs& ws, int nq, int rows, int row, int lane, int32_t* row_ptr,
+                                          int32_t* order) {
+  const int h = row / nq;
+  const int start = ws.head_base[h] + ws.local_off[row];
+  if (lane == 0) row_ptr[row] = start;
+  if (order && lane == 1) {
+    const int r = row - h * nq;
+    const int slot = ws.gstart[h * ws.ngh + r / kGroupRows] + r % kGroupRows;
+    if ((unsigned)slot < (unsigned)rows) order[slot] = ws.ranked[row];
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = atomicAdd(done, 1) == (int)gridDim.x - 1;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  block_exclusive_scan_i32(chunk_sum, nchunk, chunk_sum, row_ptr + rows, wsum);
+  return start;
 }
 
 // One wave per row (four rows per workgroup): the row's kept bits (from the
 // cut, 4 bytes per 32 blocks instead of the masses again) are loaded once,
 // one word per lane; for each 64 blocks lane l writes block 64 s + l, if
-// kept, at row_ptr[row] plus the number kept before it.
+// kept, at the row's first slot plus the number kept before it.
 __global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32_t* __restrict__ keep,
-                                                      const int32_t* __restrict__ row_ptr,
-                                                      int32_t* __restrict__ col_idx) {
+                                                      const SelectWs ws, int32_t* __restrict__ row_ptr,
+                                                      int32_t* __restrict__ order, int32_t* __restrict__ col_idx) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= g.rows()) return;  // whole waves only
@@ -676,118 +701,188 @@ __global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32
   const uint32_t* kr = keep + (int64_t)row * nw;
   const uint32_t w0 = lane < nw ? kr[lane] : 0u, w1 = 64 + lane < nw ? kr[64 + lane] : 0u;
   const uint64_t lt = (1ull << lane) - 1ull;
-  int pos = row_ptr[row];
+  int pos = finish_row(ws, g.nq, g.rows(), row, lane, row_ptr, order);
+  const unsigned cap = (unsigned)g.rows() * (unsigned)nk;  // the capacity checked on the host (< 2^31)
   for (int s = 0; 64 * s < nk; ++s) {  // blocks [64 s, 64 s + 64): words 2s, 2s + 1
     const int a = 2 * s, b = 2 * s + 1;
     const uint32_t lo = __builtin_amdgcn_readlane(a < 64 ? w0 : w1, a & 63);
     const uint32_t hi = __builtin_amdgcn_readlane(b < 64 ? w0 : w1, b & 63);
     const uint64_t m = ((uint64_t)hi << 32) | lo;
-    if ((m >> lane) & 1ull) col_idx[pos + __popcll(m & lt)] = 64 * s + lane;
+    const int at = pos + __popcll(m & lt);
+    if (((m >> lane) & 1ull) && (unsigned)at < cap) col_idx[at] = 64 * s + lane;
     pos += __popcll(m);
   }
 }
 
-// One workgroup (kOrderChunk threads) per chunk of rows.  row_ptr of the
-// chunk's rows: the chunk's first CSR slot plus the scan of their counts.
-// Then (if the work order is wanted) each row's rank r in its head by count
-// descending, stable: h * nq + r is h * nq + (rows of the head with a larger
-// count: the exclusive scan of bucket[h]) + hist[chunk][nk - c] (rows of
-// count c in earlier chunks of the head) plus the rows of that count already
-// placed by earlier waves of this chunk; waves take turns so that rows keep
-// their index order within a count.  ranked[h * nq + r] = row, and the rows
-// of rank r = 0 mod kGroupRows record their count as their group's key.
-__global__ __launch_bounds__(kOrderChunk) void place_kernel(const int32_t* __restrict__ counts, int nq, int cph,
-                                                            int nk, const int32_t* __restrict__ hist,
-                                                            const int32_t* __restrict__ bucket,
-                                                            const int32_t* __restrict__ chunk_base,
-                                                            int32_t* __restrict__ row_ptr,
-                                                            int32_t* __restrict__ ranked, int ngh,
-                                                            int32_t* __restrict__ gkey) {
-  extern __shared__ int run[];  // [nk + 1] next free slot of each count, relative to the head's first
-  __shared__ int wsum[kOrderChunk / 64];
-  __shared__ int wscan[kOrderChunk / 64];
-  const int chunk = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const ChunkRows cr(chunk, nq, cph);
-  const int row = cr.row;
-  const int cnt = cr.valid ? counts[row] : 0;
-  int v = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  int before = chunk_base[chunk];
-#pragma unroll
-  for (int ww = 0; ww < kOrderChunk / 64; ++ww)
-    if (ww < w) before += wsum[ww];
-  if (cr.valid) row_ptr[row] = before + v - cnt;
-  if (!ranked) return;
-  block_exclusive_scan_i32(bucket + (int64_t)cr.head * (nk + 1), nk + 1, run, nullptr, wscan);
-  const int32_t* hrow = hist + (int64_t)chunk * (nk + 1);
-  const int head0 = cr.head * nq;
-  const int bkt = nk - cnt;
-  const int nbits = 32 - __builtin_clz(nk);  // bkt <= nk
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int turn = 0; turn < kOrderChunk / 64; ++turn) {  // waves in row order: the ranks are stable
-    __syncthreads();
-    if (w == turn) {
-      const uint64_t eq = match_lanes(bkt, cr.valid, nbits);
-      if (cr.valid) {
-        const int r = hrow[bkt] + run[bkt] + __popcll(eq & lt);  // rank within the head
-        ranked[head0 + r] = row;
-        if (r % kGroupRows == 0) gkey[cr.head * ngh + r / kGroupRows] = cnt;  // the group's first count
+constexpr int kOrderThreads = 1024;
+constexpr int kSortMax = 16384;  // keys one workgroup sorts in LDS (64 KB)
+
+// Ascending bitonic sort of the n keys in s[] (LDS, n a power of two, at
+// least 64) by the whole workgroup (a multiple of 64 threads).  Compare-
+// exchange distances of 64 or more go through LDS with a barrier each;
+// shorter ones stay inside a wave (key i on lane i mod 64, partners by lane
+// exchange), with all stages of sizes 2 to 64 in one register pass.
+__device__ void bitonic_sort_lds(uint32_t* s, int n) {
+  const int nt = blockDim.x;
+  auto in_wave = [&](int k, int j_top) {  // stages of size k, distances j_top .. 1
+    for (int i = threadIdx.x; i < n; i += nt) {  // whole waves: n and nt are multiples of 64
+      uint32_t x = s[i];
+      for (int j = j_top; j > 0; j >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)x, j, kWave);
+        x = (((i & j) == 0) == ((i & k) == 0)) ? min(x, y) : max(x, y);
       }
-      wave_lds_sync();  // every lane has read run[] before the first lane of each key moves it on
-      if (cr.valid && (eq & lt) == 0) run[bkt] += __popcll(eq);
+      s[i] = x;
     }
+    __syncthreads();
+  };
+  // sizes 2 .. 64: one register pass
+  for (int i = threadIdx.x; i < n; i += nt) {
+    uint32_t x = s[i];
+    for (int k = 2; k <= 64; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)x, j, kWave);
+        x = (((i & j) == 0) == ((i & k) == 0)) ? min(x, y) : max(x, y);
+      }
+    s[i] = x;
+  }
+  __syncthreads();
+  for (int k = 128; k <= n; k <<= 1) {
+    for (int j = k >> 1; j >= 64; j >>= 1) {
+      for (int i = threadIdx.x; i < n / 2; i += nt) {
+        const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1)), b = a + j;  // the i-th pair of this stage
+        const uint32_t x = s[a], y = s[b];
+        if ((x > y) == ((a & k) == 0)) {
+          s[a] = y;
+          s[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+    in_wave(k, 32);
   }
 }
 
-// The work order's groups: group (h, k) holds ranks [k * kGroupRows,
-// (k + 1) * kGroupRows) of head h (the last group of a head holds
-// nq - (ngh - 1) * kGroupRows rows when nq is not a multiple of kGroupRows);
-// groups run by key descending, ties by group index (head, then k).  One
-// workgroup: a counting sort over the keys in LDS (all groups, and the short
-// head-last groups) and a stable placement in group-index order.  A group's
-// first slot is kGroupRows * R - (kGroupRows - last) * S, with R the groups
-// and S the short groups placed before it.
-__global__ __launch_bounds__(256) void group_order_kernel(int ngroups, int ngh, int last, int nk,
-                                                          const int32_t* __restrict__ gkey,
-                                                          int32_t* __restrict__ gstart) {
-  extern __shared__ int gl[];  // [2][nk + 1]: groups, then short groups, per key bucket nk - key
-  __shared__ int wsum[256 / 64];
-  int* all = gl;
-  int* shrt = gl + nk + 1;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int x = threadIdx.x; x < 2 * (nk + 1); x += 256) gl[x] = 0;
+__host__ __device__ inline int pow2_at_least(int n) {
+  int p = 64;  // the sort's least size
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Row offsets and the work order from the kept counts, one workgroup per
+// (batch, head), then a hand-off to the last workgroup to finish.
+//   per head h: local_off[row] = the kept blocks of the head's earlier rows,
+//     head_total[h]; when the order is wanted, the head's rows ranked by
+//     count descending, ties by row: a sort of the unique keys
+//     (nk - count) << 14 | local row (nq <= 16384) -> ranked[h nq + r] = row
+//     of rank r, gkey[h ngh + k] = the count of rank 32 k, the first
+//     (largest) of work group k;
+//   last workgroup: head_base = exclusive scan of head_total, row_ptr[rows];
+//     the work groups by key descending, ties by group index (head, then k):
+//     a sort of the unique keys (nk - key) << 14 | group (up to 16384
+//     groups; beyond, a stable counting sort over the key buckets whose
+//     waves take turns); a group's first order slot is the rows of the
+//     groups before it (32 each, the head's last group nq - 32 (ngh - 1)).
+// *done must be 0 on entry (the count kernel before this one clears it).
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const Geom g, const int32_t* __restrict__ counts,
+                                                              const SelectWs ws, int32_t* __restrict__ row_ptr,
+                                                              int want_order) {
+  extern __shared__ uint32_t ol[];  // sort keys; in the turn-based group placement [2][nk + 1] bucket slots
+  __shared__ int wsum[kOrderThreads / 64];
+  __shared__ int last;
+  const int h = blockIdx.x, nq = g.nq, nk = g.nk, tid = threadIdx.x;
+  const int32_t* hc = counts + (int64_t)h * nq;
+  block_exclusive_scan_i32(hc, nq, ws.local_off + (int64_t)h * nq, ws.head_total + h, wsum);
+  if (want_order) {
+    const int n = pow2_at_least(nq);
+    for (int i = tid; i < n; i += blockDim.x)
+      ol[i] = i < nq ? ((uint32_t)(nk - hc[i]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort_lds(ol, n);
+    int32_t* ranked = ws.ranked + (int64_t)h * nq;
+    int32_t* gkey = ws.gkey + (int64_t)h * ws.ngh;
+    for (int r = tid; r < nq; r += blockDim.x) {
+      const uint32_t k = ol[r];
+      ranked[r] = h * nq + (int)(k & 0x3FFFu);
+      if (r % kGroupRows == 0) gkey[r / kGroupRows] = nk - (int)(k >> 14);
+    }
+  }
+  __syncthreads();  // the workgroup's stores are done (to L2) ...
+  if (tid == 0) {
+    __threadfence();  // ... and made visible to every XCD before the count moves
+    last = atomicAdd(ws.done, 1) == (int)gridDim.x - 1;
+  }
   __syncthreads();
-  const bool has_short = last < kGroupRows;
-  const int nbits = 32 - __builtin_clz(nk);  // nk - key <= nk
-  for (int gi = threadIdx.x; gi < ngroups; gi += 256) {
-    const int b = nk - gkey[gi];
+  if (!last) return;
+  __threadfence();
+  const int heads = gridDim.x;
+  block_exclusive_scan_i32(ws.head_total, heads, ws.head_base, row_ptr + (int64_t)heads * nq, wsum);
+  if (!want_order) return;
+  const int ngh = ws.ngh;
+  const int lastn = nq - (ngh - 1) * kGroupRows;  // rows of each head's last group
+  const int ngroups = heads * ngh;
+  if (ngroups <= kSortMax) {
+    const int n = pow2_at_least(ngroups);
+    for (int i = tid; i < n; i += blockDim.x)
+      ol[i] = i < ngroups ? ((uint32_t)(nk - ws.gkey[i]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort_lds(ol, n);
+    // first slots: exclusive scan of the group sizes in sorted order, each
+    // thread over a contiguous run of positions
+    const int per = (ngroups + blockDim.x - 1) / blockDim.x, p0 = tid * per;
+    int run = 0;
+    for (int p = p0; p < min(p0 + per, ngroups); ++p)
+      run += (int)(ol[p] & 0x3FFFu) % ngh == ngh - 1 ? lastn : kGroupRows;
+    const int lane = tid & 63, w = tid >> 6;
+    int v = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o, kWave);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    int slot = v - run;
+    for (int ww = 0; ww < w; ++ww) slot += wsum[ww];
+    for (int p = p0; p < min(p0 + per, ngroups); ++p) {
+      const int gi = (int)(ol[p] & 0x3FFFu);
+      ws.gstart[gi] = slot;
+      slot += gi % ngh == ngh - 1 ? lastn : kGroupRows;
+    }
+    return;
+  }
+  // More groups than one sort holds: a stable counting sort over the buckets
+  // nk - key; groups before a group come from a placement over all groups,
+  // short groups before it (the heads' last groups when lastn < 32) from the
+  // same placement restricted to them, counted with one more ballot.
+  const bool has_short = lastn < kGroupRows;
+  const int nbits = 32 - __builtin_clz(nk);  // buckets nk - key <= nk
+  int* all = reinterpret_cast<int*>(ol);
+  int* shrt = all + nk + 1;
+  for (int x = tid; x < 2 * (nk + 1); x += blockDim.x) all[x] = 0;
+  __syncthreads();
+  for (int gi = tid; gi < ngroups; gi += blockDim.x) {
+    const int b = nk - ws.gkey[gi];
     atomicAdd(&all[b], 1);
     if (has_short && gi % ngh == ngh - 1) atomicAdd(&shrt[b], 1);
   }
   __syncthreads();
-  block_exclusive_scan_i32(all, nk + 1, all, nullptr, wsum);  // now the next slot per bucket
+  block_exclusive_scan_i32(all, nk + 1, all, nullptr, wsum);  // the first slot per bucket
   block_exclusive_scan_i32(shrt, nk + 1, shrt, nullptr, wsum);
-  for (int t0 = 0; t0 < ngroups; t0 += 256) {
-    const int gi = t0 + (int)threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int t0 = 0; t0 < ngroups; t0 += blockDim.x) {
+    const int gi = t0 + tid;
     const bool valid = gi < ngroups;
-    const int b = valid ? nk - gkey[gi] : 0;
+    const int b = valid ? nk - ws.gkey[gi] : 0;
     const bool is_short = valid && has_short && gi % ngh == ngh - 1;
-    for (int turn = 0; turn < 4; ++turn) {  // waves in group order: the slots are stable
+    for (int turn = 0; turn < nw && t0 + 64 * turn < ngroups; ++turn) {  // waves in group order: stable slots
       __syncthreads();
       if (w == turn) {
         const uint64_t eq = match_lanes(b, valid, nbits);
         const uint64_t es = eq & __ballot(is_short);
-        const uint64_t lt = (1ull << lane) - 1ull;
         if (valid) {
           const int R = all[b] + __popcll(eq & lt), S = shrt[b] + __popcll(es & lt);
-          gstart[gi] = kGroupRows * R - (kGroupRows - last) * S;
+          ws.gstart[gi] = kGroupRows * R - (kGroupRows - lastn) * S;
         }
         wave_lds_sync();  // every lane has read the slots before the first lane of each key moves them on
         if (valid && (eq & lt) == 0) {
@@ -799,36 +894,27 @@ __global__ __launch_bounds__(256) void group_order_kernel(int ngroups, int ngh, 
   }
 }
 
-// order[first slot of the row's group + rank within the group] = row.
-__global__ __launch_bounds__(256) void scatter_order_kernel(int rows, int nq, int ngh,
-                                                            const int32_t* __restrict__ ranked,
-                                                            const int32_t* __restrict__ gstart,
-                                                            int32_t* __restrict__ order) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= rows) return;
-  const int h = p / nq, r = p - h * nq;
-  order[gstart[h * ngh + r / kGroupRows] + r % kGroupRows] = ranked[p];
-}
-
 // Online block thresholding (the Sol-Attn page's block thresholding during
 // the online-softmax pass): visiting the row's key blocks in index order,
 // block j is kept when m_j >= theta * max(m_0 .. m_j), on the sanitised fp32
 // masses, compared in fp64.  One wave per row, 64 blocks per step: coalesced
 // loads, an inclusive max scan across the wave, and the running maximum
 // carried from the previous step.  kWrite = false: the kept count into
-// counts[row]; true: the kept indices, ascending, from row_ptr[row].
+// ws.counts[row] (and the order kernel's done counter cleared); true: the
+// kept indices, ascending, from the row's first slot, with row_ptr and the
+// work order stored.
 template <bool kWrite>
 __global__ __launch_bounds__(256) void threshold_kernel(const Geom g, const float* __restrict__ M, const ThetaTable tt,
-                                                        int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ row_ptr,
-                                                        int32_t* __restrict__ col_idx) {
+                                                        const SelectWs ws, int32_t* __restrict__ row_ptr,
+                                                        int32_t* __restrict__ order, int32_t* __restrict__ col_idx) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (!kWrite && blockIdx.x == 0 && threadIdx.x == 0) *ws.done = 0;
   if (row >= g.rows()) return;  // the whole wave
   const int nk = g.nk;
   const double theta = tt.t[tt.per_head ? (row / g.nq) % g.H : 0];
   const float* Mrow = M + (int64_t)row * nk;
-  int32_t* dst = kWrite ? col_idx + row_ptr[row] : nullptr;
+  int32_t* dst = kWrite ? col_idx + finish_row(ws, g.nq, g.rows(), row, lane, row_ptr, order) : nullptr;
   float carry = 0.f;  // largest mass before this step's blocks
   int kept = 0;
   for (int j0 = 0; j0 < nk; j0 += kWave) {
@@ -847,38 +933,40 @@ __global__ __launch_bounds__(256) void threshold_kernel(const Geom g, const floa
     kept += __popcll(bal);
     carry = __shfl(run, kWave - 1, kWave);
   }
-  if (!kWrite && lane == 0) counts[row] = kept;
+  if (!kWrite && lane == 0) ws.counts[row] = kept;
 }
 
 // List merge: row r takes its count from set b when its head is flagged,
 // from set a otherwise (clamped to [0, nk], so a malformed count cannot
-// place a row outside the output).
+// place a row outside the output).  Also clears the order kernel's done
+// counter.
 __global__ __launch_bounds__(256) void pick_counts_kernel(int rows, int nq, int nk, const int32_t* __restrict__ take_b,
                                                           const int32_t* __restrict__ rpa,
-                                                          const int32_t* __restrict__ rpb,
-                                                          int32_t* __restrict__ counts) {
+                                                          const int32_t* __restrict__ rpb, const SelectWs ws) {
   const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r == 0) *ws.done = 0;
   if (r >= rows) return;
   const int32_t* rp = take_b[r / nq] ? rpb : rpa;
-  counts[r] = min(max(rp[r + 1] - rp[r], 0), nk);
+  ws.counts[r] = min(max(rp[r + 1] - rp[r], 0), nk);
 }
 
-// One wave per row: copy the chosen set's indices to row_ptr[r].
+// One wave per row: copy the chosen set's indices to the row's first slot
+// (row_ptr and the work order stored on the way).
 __global__ __launch_bounds__(256) void copy_lists_kernel(int rows, int nq, const int32_t* __restrict__ take_b,
                                                          const int32_t* __restrict__ rpa,
                                                          const int32_t* __restrict__ cia,
                                                          const int32_t* __restrict__ rpb,
-                                                         const int32_t* __restrict__ cib,
-                                                         const int32_t* __restrict__ counts,
-                                                         const int32_t* __restrict__ row_ptr,
+                                                         const int32_t* __restrict__ cib, const SelectWs ws,
+                                                         int32_t* __restrict__ row_ptr, int32_t* __restrict__ order,
                                                          int32_t* __restrict__ col_idx) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
   const bool b = take_b[r / nq] != 0;
   const int32_t* src = (b ? cib : cia) + (b ? rpb : rpa)[r];
-  int32_t* dst = col_idx + row_ptr[r];
-  const int n = counts[r];
-  for (int t = threadIdx.x & 63; t < n; t += 64) dst[t] = src[t];
+  int32_t* dst = col_idx + finish_row(ws, nq, rows, r, lane, row_ptr, order);
+  const int n = ws.counts[r];
+  for (int t = lane; t < n; t += 64) dst[t] = src[t];
 }
 
 __global__ __launch_bounds__(64) void retained_kernel(const Geom g, const float* __restrict__ M,
@@ -898,38 +986,33 @@ __global__ __launch_bounds__(64) void retained_kernel(const Geom g, const float*
 }  // namespace
 
 size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
-  const int rows = g.rows();
-  const int heads = g.B * g.H;
-  const int cph = (g.nq + kOrderChunk - 1) / kOrderChunk;
-  const int nchunk = heads * cph;
-  size_t off = 0;
-  const size_t counts_off = off;
-  off = align_up(off + (size_t)rows * sizeof(int32_t), 256);
+  const size_t rows = (size_t)g.rows();
+  const size_t heads = (size_t)g.B * g.H;
   const int keep_words = (g.nk + 31) / 32;
-  const size_t keep_off = off;
-  off = align_up(off + (size_t)rows * keep_words * sizeof(uint32_t), 256);
-  const size_t hist_off = off;  // then chunk_sum and done
-  off = align_up(off + ((size_t)(g.nk + 1) * nchunk + nchunk + 1) * sizeof(int32_t), 256);
-  const size_t bucket_off = off;
-  off = align_up(off + (size_t)heads * (g.nk + 1) * sizeof(int32_t), 256);
   const int ngh = (g.nq + kGroupRows - 1) / kGroupRows;
-  const size_t ranked_off = off;
-  off = align_up(off + (size_t)rows * sizeof(int32_t), 256);
-  const size_t gkey_off = off;  // then gstart
-  off = align_up(off + (size_t)2 * heads * ngh * sizeof(int32_t), 256);
+  size_t off = 0;
+  auto take = [&](size_t ints) {
+    const size_t at = off;
+    off = align_up(off + ints * sizeof(int32_t), 256);
+    return reinterpret_cast<int32_t*>(base + at);
+  };
+  int32_t* counts = take(rows);
+  int32_t* keep = take(rows * keep_words);
+  int32_t* local_off = take(rows);
+  int32_t* head_total = take(2 * heads + 1);  // then head_base and done
+  int32_t* ranked = take(rows);
+  int32_t* gkey = take(2 * heads * ngh);  // then gstart
   if (layout) {
-    layout->counts = reinterpret_cast<int32_t*>(base + counts_off);
-    layout->keep = reinterpret_cast<uint32_t*>(base + keep_off);
+    layout->counts = counts;
+    layout->keep = reinterpret_cast<uint32_t*>(keep);
     layout->keep_words = keep_words;
-    layout->chunk_hist = reinterpret_cast<int32_t*>(base + hist_off);
-    layout->chunk_sum = layout->chunk_hist + (size_t)(g.nk + 1) * nchunk;
-    layout->done = layout->chunk_sum + nchunk;
-    layout->bucket = reinterpret_cast<int32_t*>(base + bucket_off);
-    layout->nchunk = nchunk;
-    layout->cph = cph;
-    layout->ranked = reinterpret_cast<int32_t*>(base + ranked_off);
-    layout->gkey = reinterpret_cast<int32_t*>(base + gkey_off);
-    layout->gstart = layout->gkey + (size_t)heads * ngh;
+    layout->local_off = local_off;
+    layout->head_total = head_total;
+    layout->head_base = head_total + heads;
+    layout->done = head_total + 2 * heads;
+    layout->ranked = ranked;
+    layout->gkey = gkey;
+    layout->gstart = gkey + heads * ngh;
     layout->ngh = ngh;
   }
   return off;
@@ -941,20 +1024,22 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
   // Up to 2048 key blocks a wave per row; beyond, a workgroup
   // per row (radix select), which spreads a long row over 256 threads.  The
   // per-thread arrays are unrolled, so the instance fits the row closely.
-  const int per = (g.nk + kWave - 1) / kWave;
-  if (per <= 32) {
-    auto cut = per <= 2 ? cut_wave_kernel<2> : per <= 4 ? cut_wave_kernel<4> : per <= 8 ? cut_wave_kernel<8>
-             : per <= 12 ? cut_wave_kernel<12> : per <= 16 ? cut_wave_kernel<16> : per <= 20 ? cut_wave_kernel<20>
-             : per <= 24 ? cut_wave_kernel<24> : cut_wave_kernel<32>;
-    hipLaunchKernelGGL(cut, dim3((rows + 3) / 4), dim3(256), 0, st, g, M, pt, ws.counts, ws.keep);
+  const int per = ((g.nk + kWave - 1) / kWave) | 1;  // odd runs per lane
+  if (per <= 31) {
+    using CutFn = void (*)(const Geom, const float*, const PTable, int32_t*, uint32_t*, int32_t*);
+    static const CutFn cuts[16] = {cut_wave_kernel<1>,  cut_wave_kernel<3>,  cut_wave_kernel<5>,  cut_wave_kernel<7>,
+                                   cut_wave_kernel<9>,  cut_wave_kernel<11>, cut_wave_kernel<13>, cut_wave_kernel<15>,
+                                   cut_wave_kernel<17>, cut_wave_kernel<19>, cut_wave_kernel<21>, cut_wave_kernel<23>,
+                                   cut_wave_kernel<25>, cut_wave_kernel<27>, cut_wave_kernel<29>, cut_wave_kernel<31>};
+    hipLaunchKernelGGL(cuts[per / 2], dim3((rows + 3) / 4), dim3(256), 0, st, g, M, pt, ws.counts, ws.keep, ws.done);
   } else {
     const int per_t = (g.nk + kSelThreads - 1) / kSelThreads;
     auto cut = per_t <= 12 ? cut_kernel<12> : cut_kernel<kMaxPer>;
-    hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.keep);
+    hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.keep, ws.done);
   }
-  launch_offsets_and_order(g, ws, row_ptr, order, st);
-  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, g, (const uint32_t*)ws.keep,
-                     (const int32_t*)row_ptr, col_idx);
+  launch_order(g, ws, row_ptr, order != nullptr, st);
+  hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, g, (const uint32_t*)ws.keep, ws,
+                     row_ptr, order, col_idx);
   return hipGetLastError();
 }
 
@@ -962,11 +1047,10 @@ hipError_t launch_select_threshold(const Geom& g, const float* M, const ThetaTab
                                    int32_t* col_idx, int32_t* order, const SelectWs& ws, hipStream_t st) {
   const int rows = g.rows();
   const dim3 grid((rows + 3) / 4);
-  hipLaunchKernelGGL(threshold_kernel<false>, grid, dim3(256), 0, st, g, M, tt, ws.counts, (const int32_t*)nullptr,
-                     (int32_t*)nullptr);
-  launch_offsets_and_order(g, ws, row_ptr, order, st);
-  hipLaunchKernelGGL(threshold_kernel<true>, grid, dim3(256), 0, st, g, M, tt, (int32_t*)nullptr,
-                     (const int32_t*)row_ptr, col_idx);
+  hipLaunchKernelGGL(threshold_kernel<false>, grid, dim3(256), 0, st, g, M, tt, ws, (int32_t*)nullptr,
+                     (int32_t*)nullptr, (int32_t*)nullptr);
+  launch_order(g, ws, row_ptr, order != nullptr, st);
+  hipLaunchKernelGGL(threshold_kernel<true>, grid, dim3(256), 0, st, g, M, tt, ws, row_ptr, order, col_idx);
   return hipGetLastError();
 }
 
@@ -975,31 +1059,19 @@ hipError_t launch_merge_lists(const Geom& g, const int32_t* take_b, const int32_
                               int32_t* order, const SelectWs& ws, hipStream_t st) {
   const int rows = g.rows();
   hipLaunchKernelGGL(pick_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, g.nq, g.nk, take_b, rpa,
-                     rpb, ws.counts);
-  launch_offsets_and_order(g, ws, row_ptr, order, st);
+                     rpb, ws);
+  launch_order(g, ws, row_ptr, order != nullptr, st);
   hipLaunchKernelGGL(copy_lists_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, rows, g.nq, take_b, rpa, cia, rpb,
-                     cib, (const int32_t*)ws.counts, (const int32_t*)row_ptr, col_idx);
+                     cib, ws, row_ptr, order, col_idx);
   return hipGetLastError();
 }
 
-// From the kept counts in ws.counts: row_ptr, and (order != NULL) the work order.
-void launch_offsets_and_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, int32_t* order, hipStream_t st) {
-  const int rows = g.rows();
-  const size_t hist_lds = (size_t)(g.nk + 1) * sizeof(int);
-  hipLaunchKernelGGL(chunk_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
-                     g.nq, ws.cph, g.nk, ws.chunk_hist, ws.chunk_sum, ws.done);
-  hipLaunchKernelGGL(offsets_kernel, dim3((g.nk + 1 + 255) / 256), dim3(256), 0, st, g.nk, ws.nchunk, ws.cph,
-                     rows, ws.chunk_hist, ws.chunk_sum, ws.bucket, ws.done, row_ptr);
-  hipLaunchKernelGGL(place_kernel, dim3(ws.nchunk), dim3(kOrderChunk), hist_lds, st, (const int32_t*)ws.counts,
-                     g.nq, ws.cph, g.nk, (const int32_t*)ws.chunk_hist, (const int32_t*)ws.bucket,
-                     (const int32_t*)ws.chunk_sum, row_ptr, order ? ws.ranked : nullptr, ws.ngh, ws.gkey);
-  if (!order) return;
+void launch_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, bool want_order, hipStream_t st) {
   const int ngroups = g.B * g.H * ws.ngh;
-  const int last = g.nq - (ws.ngh - 1) * kGroupRows;
-  hipLaunchKernelGGL(group_order_kernel, dim3(1), dim3(256), 2 * hist_lds, st, ngroups, ws.ngh, last, g.nk,
-                     (const int32_t*)ws.gkey, ws.gstart);
-  hipLaunchKernelGGL(scatter_order_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, g.nq, ws.ngh,
-                     (const int32_t*)ws.ranked, (const int32_t*)ws.gstart, order);
+  const int group_words = ngroups <= kSortMax ? pow2_at_least(ngroups) : 2 * (g.nk + 1);
+  const size_t lds = want_order ? (size_t)max(pow2_at_least(g.nq), group_words) * sizeof(uint32_t) : 0;
+  hipLaunchKernelGGL(order_kernel, dim3(g.B * g.H), dim3(kOrderThreads), lds, st, g, (const int32_t*)ws.counts, ws,
+                     row_ptr, want_order ? 1 : 0);
 }
 
 // Scratch of the allocation-free selector: one array per device, placed by

@@ -99,6 +99,57 @@ def cut_range_radix(m32, p):
     return _finish(ku, q, T, lo + pre, e)
 
 
+def cut_range_listed(m32, p):
+    """One wave per row, as the GPU runs it: the same range radix select over
+    rel = umax - u (u the mass bits, umax the largest, the range up to the least
+    positive mass), but after each pass, when at most 64 blocks fall in the chosen
+    digit's band, those blocks are listed in index order and the cut is taken
+    among them directly: for each listed block its cumulative units (every block
+    before the band plus the listed blocks of equal or larger mass); the cut is
+    the largest listed mass whose cumulative units reach T, and the units
+    before it are those of the larger masses only."""
+    ku, q, T, P, e = _row_setup(m32, p)
+    if P == 1 << 32:
+        return np.arange(len(ku))
+    u = [0xFFFFFFFF - k for k in ku]
+    umax = max(u)
+    if T == 0:
+        return _finish(ku, q, T, 0xFFFFFFFF - umax, e)
+    umin = min(x for x in u if x > 0)
+    top = (umax - umin).bit_length()
+    pre, acc, first = 0, 0, True
+    while top > 0:
+        shift = max(top - 8, 0)
+        hs = [0] * (1 << (top - shift))
+        for x, qq in zip(u, q):
+            r = umax - x
+            if first:
+                hs[(r >> shift) & (len(hs) - 1)] += qq  # blocks without units add 0
+            elif x > 0 and r >> top == pre >> top:
+                hs[(r >> shift) & (len(hs) - 1)] += qq
+        first = False
+        cum = 0
+        for d, hh in enumerate(hs):
+            if acc + cum + hh >= T:
+                break
+            cum += hh
+        acc += cum
+        pre |= d << shift
+        top = shift
+        if top == 0:
+            break
+        band = [j for j, x in enumerate(u) if x > 0 and 0 <= (umax - x) - pre < (1 << top)]
+        if len(band) > 64:
+            continue
+        fle = [acc + sum(q[k] for k in band if u[k] >= u[j]) for j in band]
+        hits = [u[j] for j, f in zip(band, fle) if f >= T]
+        uv = max(hits)
+        below = acc + sum(q[k] for k in band if u[k] > uv)
+        assert below == sum(qq for x, qq in zip(u, q) if x > uv)
+        return _finish(ku, q, T, 0xFFFFFFFF - uv, e)
+    return _finish(ku, q, T, 0xFFFFFFFF - (umax - pre), e)
+
+
 def cut_radix(m32, p):
     ku, q, T, P, e = _row_setup(m32, p)
     if P == 1 << 32:
@@ -135,14 +186,21 @@ def _rows(rng, nk):
     bad = rng.random(nk).astype(np.float32)
     bad[rng.integers(nk, size=3)] = [np.nan, np.inf, -1.0]
     out.append(bad)
+    # most blocks within a few ulps of one mass and a few far from it: the first
+    # digit's band then holds more than 64 blocks (further radix passes)
+    clu = (1.0 + rng.integers(0, 512, nk) * 2.0 ** -23).astype(np.float32)
+    clu[rng.integers(nk, size=max(1, nk // 50))] = 8.0
+    clu[rng.integers(nk, size=max(1, nk // 50))] = 1e-3
+    out.append(clu / np.float32(clu.sum()))
     return out
 
 
-@pytest.mark.parametrize("nk", [1, 2, 5, 64, 300])
+@pytest.mark.parametrize("nk", [1, 2, 5, 64, 300, 1000])
 @pytest.mark.parametrize("p", [1e-9, 0.5, 0.75, 0.9, 0.99, 0.995, 1.0])
 def test_sort_free_cuts_equal_sorted_prefix_rule(nk, p):
     rng = np.random.default_rng(nk * 1000 + int(p * 1000))
     for m in _rows(rng, nk):
         ref = O.select_contract_row(m, p)[0]
         assert np.array_equal(cut_range_radix(m, p), ref)
+        assert np.array_equal(cut_range_listed(m, p), ref)
         assert np.array_equal(cut_radix(m, p), ref)
