@@ -413,7 +413,8 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
   // kept bits
   __shared__ uint32_t stage_all[4][64 * kPer];
   __shared__ uint64_t hist_all[4][256];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // wave-uniform values live in scalar registers (the buffer descriptor too)
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * 4 + wv;
   if (row == 0 && lane == 0) *done = 0;  // the order kernel's counter
   if (row >= g.rows()) return;           // whole waves only
@@ -586,12 +587,16 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
       }
     }
     const uint64_t qu = row_units(uv, e);
-    uint64_t need = 1;
-    if (below < T && qu > 0) need = (T - below + qu - 1) / qu;
+    uint64_t need = 1;  // one tie is enough unless T lies beyond the first
+    if (below < T && qu > 0 && T - below > qu) need = (T - below + qu - 1) / qu;
 #pragma unroll
     for (int t = 0; t < kPer; ++t) {
       gt |= (u[t] > uv ? 1u : 0u) << t;
-      eq |= (u[t] == uv && j0 + t < nk ? 1u : 0u) << t;
+      eq |= (u[t] == uv ? 1u : 0u) << t;
+    }
+    if (uv == 0) {  // an all-zero row: blocks past nk (read as 0) are no ties
+      const int nv = min(max(nk - j0, 0), kPer);
+      eq &= nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
     }
     const int nties = __popc(eq);
     int incl = nties;  // ties owned by lanes <= this one
@@ -689,18 +694,19 @@ __device__ __forceinline__ int finish_row(const SelectWs& ws, int nq, int rows, 
 
 // One wave per row (four rows per workgroup): the row's kept bits (from the
 // cut, 4 bytes per 32 blocks instead of the masses again) are loaded once,
-// one word per lane; for each 64 blocks lane l writes block 64 s + l, if
-// kept, at the row's first slot plus the number kept before it.
+// one word per lane; for each 64 blocks (a wave-uniform 64-bit mask m) lane
+// l writes block 64 s + l, if kept, at the row's first slot plus the kept
+// blocks before it (all 64 when m is full: the common case, one coalesced
+// store of consecutive indices).
 __global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32_t* __restrict__ keep,
                                                       const SelectWs ws, int32_t* __restrict__ row_ptr,
                                                       int32_t* __restrict__ order, int32_t* __restrict__ col_idx) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= g.rows()) return;  // whole waves only
   const int nk = g.nk, nw = (nk + 31) / 32;  // nw <= 128
   const uint32_t* kr = keep + (int64_t)row * nw;
   const uint32_t w0 = lane < nw ? kr[lane] : 0u, w1 = 64 + lane < nw ? kr[64 + lane] : 0u;
-  const uint64_t lt = (1ull << lane) - 1ull;
   int pos = finish_row(ws, g.nq, g.rows(), row, lane, row_ptr, order);
   const unsigned cap = (unsigned)g.rows() * (unsigned)nk;  // the capacity checked on the host (< 2^31)
   for (int s = 0; 64 * s < nk; ++s) {  // blocks [64 s, 64 s + 64): words 2s, 2s + 1
@@ -708,7 +714,7 @@ __global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32
     const uint32_t lo = __builtin_amdgcn_readlane(a < 64 ? w0 : w1, a & 63);
     const uint32_t hi = __builtin_amdgcn_readlane(b < 64 ? w0 : w1, b & 63);
     const uint64_t m = ((uint64_t)hi << 32) | lo;
-    const int at = pos + __popcll(m & lt);
+    const int at = pos + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
     if (((m >> lane) & 1ull) && (unsigned)at < cap) col_idx[at] = 64 * s + lane;
     pos += __popcll(m);
   }
@@ -908,7 +914,7 @@ __global__ __launch_bounds__(256) void threshold_kernel(const Geom g, const floa
                                                         const SelectWs ws, int32_t* __restrict__ row_ptr,
                                                         int32_t* __restrict__ order, int32_t* __restrict__ col_idx) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (!kWrite && blockIdx.x == 0 && threadIdx.x == 0) *ws.done = 0;
   if (row >= g.rows()) return;  // the whole wave
   const int nk = g.nk;
@@ -959,7 +965,7 @@ __global__ __launch_bounds__(256) void copy_lists_kernel(int rows, int nq, const
                                                          const int32_t* __restrict__ cib, const SelectWs ws,
                                                          int32_t* __restrict__ row_ptr, int32_t* __restrict__ order,
                                                          int32_t* __restrict__ col_idx) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (r >= rows) return;
   const int lane = threadIdx.x & 63;
   const bool b = take_b[r / nq] != 0;
