@@ -335,6 +335,27 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
     for (int qt = 0; qt < kQT; ++qt) lsum[qt] = mfma_bf16(ones, pop[qt], lsum[qt]);
   };
 
+  auto scores_qt = [&](const bf16x8 (&kop)[2][DC], int qt, f32x4 (&acc)[2][kQT]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      acc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) acc[kt][qt] = mfma_bf16(kop[kt][dc], qop[qt][dc], acc[kt][qt]);
+    }
+  };
+  auto probs_qt = [&](const f32x4 (&acc)[2][kQT], int qt, bf16x8& pq) {
+    const float nm = -m[qt];
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
+    pq = pack8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+  };
+  auto pv_qt = [&](const bf16x8 (&vop)[DT], int qt, const bf16x8& pq) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt][qt] = mfma_bf16(vop[dt], pq, o[dt][qt]);
+    lsum[qt] = mfma_bf16(ones, pq, lsum[qt]);
+  };
+
   // No maximum is tracked per score and O is never rescaled inside the loop:
   // the reference m is fixed at the wave's first chunk's maximum plus
   // kHeadroom (log2 units).  Later chunks may exceed the first chunk's
@@ -347,12 +368,14 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
   // has a single exit: an early exit makes the register allocator shuffle the
   // O accumulators on every trip.
   //
-  // Software pipeline: iteration t issues the score MFMAs of chunk t+1 next to
-  // the softmax of chunk t, then P.V of chunk t, in the compiler's own
-  // interleaving (asking it to alternate one MFMA with one or two vector
-  // instructions measured 3.5% and 6% slower on the HunyuanVideo 720p layer,
-  // and no faster elsewhere).  K of chunk t+2 is requested once the score
-  // MFMAs have read K, V of chunk t+1 once P.V has read V.
+  // Software pipeline: iteration t takes the query tiles in turn -- the
+  // softmax of chunk t, the score MFMAs of chunk t+1 into the same
+  // accumulators, P.V of chunk t -- in the compiler's own interleaving
+  // (asking it to alternate one MFMA with one or two vector instructions
+  // measured 3.5% and 6% slower on the HunyuanVideo 720p layer, and no
+  // faster elsewhere; all scores of chunk t+1 into a second buffer, copied
+  // back each trip, 0.8% slower there).  K of chunk t+2 and V of chunk t+1
+  // are requested once the iteration's MFMAs have read K and V.
   //
   // Padding keys of the last block score exactly 0 against the zero rows of
   // the packed K, which can lie far above every real score of a row, so they
@@ -444,17 +467,18 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(
         const int k0 = __builtin_amdgcn_readlane(win0, r & 63), k1 = __builtin_amdgcn_readlane(win1, r & 63);
         return r < 64 ? k0 : k1;
       };
-      f32x4 accn[2][kQT];
-      scores(kop, accn);  // chunk t+1 (the last iteration recomputes the last chunk)
-      load_k(key_at(t + 2), kop);
+      // per query tile: the softmax of chunk t, the scores of chunk t+1 into
+      // the registers just read (the last iteration recomputes the last
+      // chunk), P.V of chunk t -- no second score buffer and no copies
       bf16x8 pop[kQT];
-      probs(acc, pop);  // chunk t
-      pv(vop, pop);
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt) {
+        probs_qt(acc, qt, pop[qt]);
+        scores_qt(kop, qt, acc);
+        pv_qt(vop, qt, pop[qt]);
+      }
+      load_k(key_at(t + 2), kop);
       load_v(key_at(t + 1), vop);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < kQT; ++qt) acc[kt][qt] = accn[kt][qt];
     }
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) over_any |= !(lsum[qt][0] <= kLBound);

@@ -376,6 +376,38 @@ __device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
   return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
 }
 
+// Inclusive scans over the wave by DPP moves (no LDS): within each 16-lane
+// row by shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row add
+// 0), then lane 15 of rows 0 and 2 into rows 1 and 3, and lane 31 into rows
+// 2 and 3.  All 64 lanes must be active.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp0_u32(uint32_t v) {  // lanes without a source get 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp0_u32<0x111>(v);
+  v += dpp0_u32<0x112>(v);
+  v += dpp0_u32<0x114>(v);
+  v += dpp0_u32<0x118>(v);
+  v += dpp0_u32<0x142, 0xA>(v);
+  v += dpp0_u32<0x143, 0xC>(v);
+  return v;
+}
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint64_t dpp0_add_u64(uint64_t v) {
+  return v + (((uint64_t)dpp0_u32<kCtrl, kRowMask>((uint32_t)(v >> 32)) << 32) |
+              dpp0_u32<kCtrl, kRowMask>((uint32_t)v));
+}
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  v = dpp0_add_u64<0x111>(v);
+  v = dpp0_add_u64<0x112>(v);
+  v = dpp0_add_u64<0x114>(v);
+  v = dpp0_add_u64<0x118>(v);
+  v = dpp0_add_u64<0x142, 0xA>(v);
+  v = dpp0_add_u64<0x143, 0xC>(v);
+  return v;
+}
+
 // The units of block mass bits u with the row's frexp exponent e:
 // ceil(m * 2^(51 - e)), exact.
 __device__ __forceinline__ uint64_t row_units(uint32_t u, int e) {
@@ -413,6 +445,7 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
   // kept bits
   __shared__ uint32_t stage_all[4][64 * kPer];
   __shared__ uint64_t hist_all[4][256];
+  __shared__ uint32_t eq_all[4][64];  // per wave: each lane's tie bits, from the listed band
   // wave-uniform values live in scalar registers (the buffer descriptor too)
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * 4 + wv;
@@ -475,19 +508,20 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
 #pragma unroll
     for (int t = 0; t < kPer; ++t) run += q[t];
     const uint64_t T = threshold(P, wave_sum_u64(run));
-    uint64_t below = 0;  // units of the blocks with u > uv
-    uint32_t uv = umax;  // T == 0, or one positive mass value: the cut is at the largest mass
+    uint64_t below = 0;   // units of the blocks with u > uv
+    uint32_t uv = umax;   // T == 0, or one positive mass value: the cut is at the largest mass
+    bool listed = false;  // the cut found among the listed blocks of a band (their ties in eq)
     if (T != 0) {
       umin = wave_min_u32(umin);
       const uint32_t width = umax - umin;
-      // rel = umax - u for masses, all ones for zeros (outside every band)
+      // rel = umax - u: in [0, width] for masses, umax > width for zeros (which
+      // add no units to any bin and lie outside every band cut at width)
       uint32_t rel[kPer];
 #pragma unroll
-      for (int t = 0; t < kPer; ++t) rel[t] = u[t] ? umax - u[t] : 0xFFFFFFFFu;
+      for (int t = 0; t < kPer; ++t) rel[t] = umax - u[t];
       uint32_t pre = 0;  // digits found so far
       uint64_t acc = 0;  // units of the blocks below the prefix's range
       int top = width ? 32 - __builtin_clz(width) : 0;
-      bool listed = false;
       for (int pass = 0; top > 0 && !listed; ++pass) {
         const int shift = top > 8 ? top - 8 : 0;
         const uint32_t dmask = (1u << (top - shift)) - 1u;
@@ -502,7 +536,7 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
           for (int t = 0; t < kPer; ++t)
             atomicAdd(reinterpret_cast<unsigned long long*>(hist + ((rel[t] >> shift) & dmask)),
                       (unsigned long long)q[t]);
-        } else {  // the blocks in the prefix's range (zeros never are: pre + 2^top - 1 <= width < all ones)
+        } else {  // the blocks in the prefix's range (a zero, if there, adds 0)
 #pragma unroll
           for (int t = 0; t < kPer; ++t)
             if (((rel[t] ^ pre) & above) == 0)
@@ -514,12 +548,7 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
         cs[0] = hist[4 * lane];
 #pragma unroll
         for (int k = 1; k < 4; ++k) cs[k] = cs[k - 1] + hist[4 * lane + k];
-        uint64_t inc = cs[3];  // inclusive scan over lanes
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const uint32_t xl = __shfl_up((uint32_t)inc, o, kWave), xh = __shfl_up((uint32_t)(inc >> 32), o, kWave);
-          if (lane >= o) inc += ((uint64_t)xh << 32) | xl;
-        }
+        const uint64_t inc = wave_incl_scan_u64(cs[3]);  // inclusive scan over lanes
         const uint64_t base = acc + (inc - cs[3]);
         // this lane's least digit reaching T (4: none), and the units below it
         int k = 4;
@@ -541,17 +570,12 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
         wave_lds_sync();  // every lane has read the histogram before it is cleared or reused
         if (top == 0) break;
         // the blocks of the chosen digit: rel in [pre, pre + 2^top); listed when at most 64
-        const uint32_t span = (1u << top) - 1u;
+        const uint32_t span = min((1u << top) - 1u, width - pre);  // the band ends at width: zeros stay out
         uint32_t smask = 0;
 #pragma unroll
         for (int t = 0; t < kPer; ++t) smask |= (rel[t] - pre <= span ? 1u : 0u) << t;
         const int cnt = __popc(smask);
-        int incl = cnt;  // listed blocks of lanes <= this one
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int x = __shfl_up(incl, o, kWave);
-          if (lane >= o) incl += x;
-        }
+        const int incl = (int)wave_incl_scan_u32((uint32_t)cnt);  // listed blocks of lanes <= this one
         const int nlist = __builtin_amdgcn_readlane(incl, 63);
         if (nlist > 64) continue;
         // (mass bits, index) and units of each listed block, in index order
@@ -575,9 +599,21 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
         }
         // the cut: the largest listed mass whose cumulative units reach T
         uv = wave_max_u32_uniform(lane < nlist && fle >= T ? ui : 0u);
-        const uint64_t at_v = __ballot(lane < nlist && ui == uv);
+        const bool tie = lane < nlist && ui == uv;
+        const uint64_t at_v = __ballot(tie);
         const int lv = __builtin_ctzll(at_v);
         below = ((uint64_t)lane_u32((uint32_t)(flt >> 32), lv) << 32) | lane_u32((uint32_t)flt, lv);
+        // every block of mass uv lies in the band, so the listed ties are all of
+        // them: their bits go to the owning lanes' tie words
+        uint32_t* eqw = eq_all[wv];
+        eqw[lane] = 0;
+        wave_lds_sync();
+        if (tie) {
+          const int j = (int)(hist[2 * lane] >> 32);
+          atomicOr(&eqw[j / kPer], 1u << (j % kPer));
+        }
+        wave_lds_sync();
+        eq = eqw[lane];
         listed = true;
         wave_lds_sync();  // the list is read before its space is reused
       }
@@ -590,21 +626,17 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
     uint64_t need = 1;  // one tie is enough unless T lies beyond the first
     if (below < T && qu > 0 && T - below > qu) need = (T - below + qu - 1) / qu;
 #pragma unroll
-    for (int t = 0; t < kPer; ++t) {
-      gt |= (u[t] > uv ? 1u : 0u) << t;
-      eq |= (u[t] == uv ? 1u : 0u) << t;
-    }
-    if (uv == 0) {  // an all-zero row: blocks past nk (read as 0) are no ties
-      const int nv = min(max(nk - j0, 0), kPer);
-      eq &= nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+    for (int t = 0; t < kPer; ++t) gt |= (u[t] > uv ? 1u : 0u) << t;
+    if (!listed) {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) eq |= (u[t] == uv ? 1u : 0u) << t;
+      if (uv == 0) {  // an all-zero row: blocks past nk (read as 0) are no ties
+        const int nv = min(max(nk - j0, 0), kPer);
+        eq &= nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+      }
     }
     const int nties = __popc(eq);
-    int incl = nties;  // ties owned by lanes <= this one
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int x = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += x;
-    }
+    const int incl = (int)wave_incl_scan_u32((uint32_t)nties);  // ties owned by lanes <= this one
     // the need-th tie in index order: in the lane whose ties cover it
     const int before = incl - nties;
     int jc = -1;
@@ -708,47 +740,79 @@ __global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32
   const uint32_t* kr = keep + (int64_t)row * nw;
   const uint32_t w0 = lane < nw ? kr[lane] : 0u, w1 = 64 + lane < nw ? kr[64 + lane] : 0u;
   int pos = finish_row(ws, g.nq, g.rows(), row, lane, row_ptr, order);
-  const unsigned cap = (unsigned)g.rows() * (unsigned)nk;  // the capacity checked on the host (< 2^31)
+  // the row's slots lie inside the capacity checked on the host (rows * nk <
+  // 2^31) unless the offsets are not the order kernel's; then nothing is written
+  if (pos < 0 || (int64_t)pos + ws.counts[row] > (int64_t)g.rows() * nk) return;
+  int32_t* dst = col_idx + pos;
   for (int s = 0; 64 * s < nk; ++s) {  // blocks [64 s, 64 s + 64): words 2s, 2s + 1
     const int a = 2 * s, b = 2 * s + 1;
     const uint32_t lo = __builtin_amdgcn_readlane(a < 64 ? w0 : w1, a & 63);
     const uint32_t hi = __builtin_amdgcn_readlane(b < 64 ? w0 : w1, b & 63);
-    const uint64_t m = ((uint64_t)hi << 32) | lo;
-    const int at = pos + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-    if (((m >> lane) & 1ull) && (unsigned)at < cap) col_idx[at] = 64 * s + lane;
-    pos += __popcll(m);
+    if ((lo & hi) == 0xFFFFFFFFu) {  // all 64 kept
+      dst[lane] = 64 * s + lane;
+      dst += 64;
+    } else {
+      const uint64_t m = ((uint64_t)hi << 32) | lo;
+      if ((m >> lane) & 1ull) dst[__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))] = 64 * s + lane;
+      dst += __popcll(m);
+    }
   }
 }
 
 constexpr int kOrderThreads = 1024;
 constexpr int kSortMax = 16384;  // keys one workgroup sorts in LDS (64 KB)
 
+// x from lane (lane ^ J), by DPP moves and gfx950 lane swaps (no LDS); every
+// lane must be active.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  if constexpr (J == 1) {
+    return dpp_u32<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (J == 2) {
+    return dpp_u32<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (J == 4) {
+    return dpp_u32<0x141>(dpp_u32<0x1B>(x));  // quad_perm [3, 2, 1, 0] (xor 3), then row_half_mirror (xor 7)
+  } else if constexpr (J == 8) {
+    return dpp_u32<0x128>(x);  // row_ror 8 (xor 8 within a 16-lane row)
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);  // rows (0,0,2,2), (1,1,3,3)
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane distances 1 .. 32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);  // halves (lo,lo), (hi,hi)
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+
+// One in-wave compare-exchange of a bitonic stage: element i keeps the
+// smaller key when it is the lower of its pair in an ascending block (or the
+// upper in a descending one), else the larger.
+template <int J>
+__device__ __forceinline__ uint32_t bitonic_cx(uint32_t x, int i, int k) {
+  const uint32_t y = xor_lane<J>(x);
+  return (((i & J) == 0) == ((i & k) == 0)) ? min(x, y) : max(x, y);
+}
+
+// In-wave stages of a block of size k, distances min(k/2, 32) down to 1.
+__device__ __forceinline__ uint32_t bitonic_wave(uint32_t x, int i, int k) {
+  if (k >= 64) x = bitonic_cx<32>(x, i, k);
+  if (k >= 32) x = bitonic_cx<16>(x, i, k);
+  if (k >= 16) x = bitonic_cx<8>(x, i, k);
+  if (k >= 8) x = bitonic_cx<4>(x, i, k);
+  if (k >= 4) x = bitonic_cx<2>(x, i, k);
+  return bitonic_cx<1>(x, i, k);
+}
+
 // Ascending bitonic sort of the n keys in s[] (LDS, n a power of two, at
 // least 64) by the whole workgroup (a multiple of 64 threads).  Compare-
 // exchange distances of 64 or more go through LDS with a barrier each;
 // shorter ones stay inside a wave (key i on lane i mod 64, partners by lane
-// exchange), with all stages of sizes 2 to 64 in one register pass.
+// exchange), with all stages of block sizes 2 to 64 in one register pass.
 __device__ void bitonic_sort_lds(uint32_t* s, int n) {
   const int nt = blockDim.x;
-  auto in_wave = [&](int k, int j_top) {  // stages of size k, distances j_top .. 1
-    for (int i = threadIdx.x; i < n; i += nt) {  // whole waves: n and nt are multiples of 64
-      uint32_t x = s[i];
-      for (int j = j_top; j > 0; j >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)x, j, kWave);
-        x = (((i & j) == 0) == ((i & k) == 0)) ? min(x, y) : max(x, y);
-      }
-      s[i] = x;
-    }
-    __syncthreads();
-  };
-  // sizes 2 .. 64: one register pass
-  for (int i = threadIdx.x; i < n; i += nt) {
+  for (int i = threadIdx.x; i < n; i += nt) {  // whole waves: n and nt are multiples of 64
     uint32_t x = s[i];
-    for (int k = 2; k <= 64; k <<= 1)
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)x, j, kWave);
-        x = (((i & j) == 0) == ((i & k) == 0)) ? min(x, y) : max(x, y);
-      }
+    for (int k = 2; k <= 64; k <<= 1) x = bitonic_wave(x, i, k);
     s[i] = x;
   }
   __syncthreads();
@@ -764,7 +828,8 @@ __device__ void bitonic_sort_lds(uint32_t* s, int n) {
       }
       __syncthreads();
     }
-    in_wave(k, 32);
+    for (int i = threadIdx.x; i < n; i += nt) s[i] = bitonic_wave(s[i], i, k);
+    __syncthreads();
   }
 }
 
@@ -772,6 +837,29 @@ __host__ __device__ inline int pow2_at_least(int n) {
   int p = 64;  // the sort's least size
   while (p < n) p <<= 1;
   return p;
+}
+
+// Exclusive scan of the per-thread values v over the workgroup (wsum: one
+// int per wave); the total goes to *total when given.
+__device__ __forceinline__ int block_exclusive_scan_reg(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int ww = 0; ww < nw; ++ww) {
+    const int s = wsum[ww];
+    if (ww < w) before += s;
+    all += s;
+  }
+  __syncthreads();
+  if (total) *total = all;
+  return before + inc - v;
 }
 
 // Row offsets and the work order from the kept counts, one workgroup per
@@ -788,6 +876,7 @@ __host__ __device__ inline int pow2_at_least(int n) {
 //     groups; beyond, a stable counting sort over the key buckets whose
 //     waves take turns); a group's first order slot is the rows of the
 //     groups before it (32 each, the head's last group nq - 32 (ngh - 1)).
+// The counts are read once, each thread a contiguous run of at most 16.
 // *done must be 0 on entry (the count kernel before this one clears it).
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const Geom g, const int32_t* __restrict__ counts,
                                                               const SelectWs ws, int32_t* __restrict__ row_ptr,
@@ -796,20 +885,42 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const Geom g, cons
   __shared__ int wsum[kOrderThreads / 64];
   __shared__ int last;
   const int h = blockIdx.x, nq = g.nq, nk = g.nk, tid = threadIdx.x;
-  const int32_t* hc = counts + (int64_t)h * nq;
-  block_exclusive_scan_i32(hc, nq, ws.local_off + (int64_t)h * nq, ws.head_total + h, wsum);
-  if (want_order) {
-    const int n = pow2_at_least(nq);
-    for (int i = tid; i < n; i += blockDim.x)
-      ol[i] = i < nq ? ((uint32_t)(nk - hc[i]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_sort_lds(ol, n);
-    int32_t* ranked = ws.ranked + (int64_t)h * nq;
-    int32_t* gkey = ws.gkey + (int64_t)h * ws.ngh;
-    for (int r = tid; r < nq; r += blockDim.x) {
-      const uint32_t k = ol[r];
-      ranked[r] = h * nq + (int)(k & 0x3FFFu);
-      if (r % kGroupRows == 0) gkey[r / kGroupRows] = nk - (int)(k >> 14);
+  {
+    const int32_t* hc = counts + (int64_t)h * nq;
+    const int per = (nq + (int)blockDim.x - 1) / (int)blockDim.x, i0 = tid * per;  // per <= 16
+    int cnt[16];
+    int run = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      cnt[k] = (k < per && i0 + k < nq) ? hc[i0 + k] : 0;
+      run += cnt[k];
+    }
+    int off = block_exclusive_scan_reg(run, wsum, ws.head_total + h);
+    int32_t* lo = ws.local_off + (int64_t)h * nq;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k < per && i0 + k < nq) {
+        lo[i0 + k] = off;
+        off += cnt[k];
+      }
+    if (want_order) {
+      const int n = pow2_at_least(nq);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < per && i0 + k < n) {
+          const int i = i0 + k;
+          ol[i] = i < nq ? ((uint32_t)(nk - cnt[k]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
+        }
+      for (int i = per * (int)blockDim.x + tid; i < n; i += blockDim.x) ol[i] = 0xFFFFFFFFu;  // beyond the runs
+      __syncthreads();
+      bitonic_sort_lds(ol, n);
+      int32_t* ranked = ws.ranked + (int64_t)h * nq;
+      int32_t* gkey = ws.gkey + (int64_t)h * ws.ngh;
+      for (int r = tid; r < nq; r += blockDim.x) {
+        const uint32_t k = ol[r];
+        ranked[r] = h * nq + (int)(k & 0x3FFFu);
+        if (r % kGroupRows == 0) gkey[r / kGroupRows] = nk - (int)(k >> 14);
+      }
     }
   }
   __syncthreads();  // the workgroup's stores are done (to L2) ...

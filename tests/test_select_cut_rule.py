@@ -125,8 +125,8 @@ def cut_range_listed(m32, p):
             r = umax - x
             if first:
                 hs[(r >> shift) & (len(hs) - 1)] += qq  # blocks without units add 0
-            elif x > 0 and r >> top == pre >> top:
-                hs[(r >> shift) & (len(hs) - 1)] += qq
+            elif r >> top == pre >> top:
+                hs[(r >> shift) & (len(hs) - 1)] += qq  # a zero in range adds 0
         first = False
         cum = 0
         for d, hh in enumerate(hs):
@@ -138,7 +138,10 @@ def cut_range_listed(m32, p):
         top = shift
         if top == 0:
             break
-        band = [j for j, x in enumerate(u) if x > 0 and 0 <= (umax - x) - pre < (1 << top)]
+        # the band ends at the width of the range, so zeros (rel = umax) stay out
+        hi_rel = min(pre + (1 << top) - 1, umax - umin)
+        band = [j for j, x in enumerate(u) if pre <= umax - x <= hi_rel]
+        assert all(u[j] > 0 for j in band)
         if len(band) > 64:
             continue
         fle = [acc + sum(q[k] for k in band if u[k] >= u[j]) for j in band]
