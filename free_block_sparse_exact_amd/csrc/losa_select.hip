@@ -5,20 +5,20 @@
 //
 // Kernels, in launch order:
 //   cut         the cut in (mass desc, index asc) order over exact integer
-//               units, without sorting -> the kept count s and the sort key
-//               kappa of the last kept block, and the row's kept blocks
-//               (sort key <= kappa) as bits: one wave per row (n_k <= 2048)
-//               by a radix select over the range of the row's keys, or one
-//               workgroup per row by radix select; the row arrives through
-//               LDS from coalesced loads;
+//               units, without sorting -> the kept count s and the row's
+//               kept blocks as bits: one wave per row (n_k <= 64 * 31) or
+//               one workgroup per row (up to 4096); the row arrives through
+//               LDS from coalesced buffer loads, one radix pass over the
+//               range of its masses finds the band of masses that holds the
+//               cut, and the cut is taken among the (usually few) blocks of
+//               that band, with further radix passes when the band is wide;
 //   order       one workgroup per (batch, head): the exclusive scan of the
 //               head's counts (its rows' offsets inside the head) and, when
-//               the work order is wanted, the head's rows ranked by count
-//               (a stable counting sort in LDS); the last workgroup to
+//               the work order is wanted, the head's rows ranked by count (a
+//               bitonic sort of unique keys in LDS); the last workgroup to
 //               finish scans the heads' totals (-> each head's first CSR
-//               slot, row_ptr[rows]) and places the work groups by their
-//               first count (another stable counting sort) -> each group's
-//               first order slot;
+//               slot, row_ptr[rows]) and sorts the work groups by their
+//               first count -> each group's first order slot;
 //   compact     one wave per row: row_ptr[row], the row's entry in the work
 //               order, and from the kept bits the kept indices ascending
 //               from row_ptr[row] (the masses are read once, by the cut).
@@ -89,41 +89,6 @@ __device__ __forceinline__ uint64_t threshold(uint64_t P, uint64_t total) {
   return ((hi << 32) | (lo >> 32)) + ((lo & 0xFFFFFFFFull) != 0 ? 1 : 0);
 }
 
-// Inclusive scan of a uint64 over the workgroup (blockDim = kSelThreads).
-__device__ __forceinline__ uint64_t block_inclusive_scan_u64(uint64_t v, uint64_t* wsum, uint64_t* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  if (lane == 63) wsum[w] = v;
-  __syncthreads();
-  uint64_t before = 0, all = 0;
-#pragma unroll
-  for (int ww = 0; ww < kSelThreads / 64; ++ww) {
-    const uint64_t s = wsum[ww];
-    if (ww < w) before += s;
-    all += s;
-  }
-  __syncthreads();
-  *total = all;
-  return v + before;
-}
-
-__device__ __forceinline__ int block_sum_i32(int v, int* wsum) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  if (lane == 0) wsum[w] = v;
-  __syncthreads();
-  int all = 0;
-#pragma unroll
-  for (int ww = 0; ww < kSelThreads / 64; ++ww) all += wsum[ww];
-  __syncthreads();
-  return all;
-}
-
 // Orders this wave's LDS accesses across its lanes (the waves of a
 // workgroup work on different rows and do not meet).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -145,9 +110,6 @@ __device__ __forceinline__ uint64_t match_lanes(int key, bool active, int nbits)
   return eq;
 }
 
-// Most key blocks one thread of the cut kernel owns.
-constexpr int kMaxPer = LOSA_MAX_KEY_BLOCKS / kSelThreads;
-static_assert(kMaxPer == 16, "the workgroup cut kernel serves rows of 2049 to 4096 blocks");
 
 // ORs the run of bits (bit t for block j0 + t, at most 32 of them) into an
 // LDS bit array of the row (bit j%32 of word j/32); the run may straddle two
@@ -157,171 +119,6 @@ __device__ __forceinline__ void or_bit_run(uint32_t* words, int j0, uint32_t bit
   const int w = j0 >> 5, sh = j0 & 31;
   atomicOr(&words[w], bits << sh);
   if (sh != 0 && (bits >> (32 - sh)) != 0) atomicOr(&words[w + 1], bits >> (32 - sh));
-}
-
-// One workgroup per row.  Finds the kept count s and the sort key kappa of
-// the s-th block in (mass desc, index asc) order without sorting: a radix
-// select, most significant digit first, over the inverted mass bits
-// ku = 2^32-1-u (ascending ku = descending mass), four passes of 8 bits.
-// Each pass sums the fixed-point units q of the remaining candidates per
-// digit and keeps the first non-empty digit at which the running sum
-// (everything before it included) reaches T; after the last pass the
-// candidates share one mass, and the cut within them falls by index.
-// Thread t owns the contiguous blocks [t*per, t*per + per), so thread order
-// is index order; kPer >= per bounds the per-thread register arrays.  The
-// row's kept count goes to counts, its kept blocks as bits to keep (the
-// blocks whose sort key is at most kappa's, kappa being the s-th block's).
-template <int kPer>
-__global__ __launch_bounds__(kSelThreads) void cut_kernel(const Geom g, const float* __restrict__ M,
-                                                          const PTable pt, int32_t* __restrict__ counts,
-                                                          uint32_t* __restrict__ keep, int32_t* __restrict__ done) {
-  __shared__ uint64_t hsum[256];
-  __shared__ uint32_t hnz[256];
-  __shared__ uint64_t wsum64[kSelThreads / 64];
-  __shared__ int wsum32[kSelThreads / 64];
-  __shared__ uint32_t wred[kSelThreads / 64];
-  __shared__ uint64_t s_below;
-  __shared__ int s_jcut;
-  __shared__ uint32_t s_keep[LOSA_MAX_KEY_BLOCKS / 32];
-  // the row's mass bits, block j at word j + j/32 (a pad word per 32 keeps
-  // the threads' runs of per words on distinct banks)
-  __shared__ uint32_t s_stage[kSelThreads * kPer + kSelThreads * kPer / 32];
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (row == 0 && tid == 0) *done = 0;  // the order kernel's counter
-  const int h = (row / g.nq) % g.H;
-  const uint64_t P = pt.P[pt.per_head ? h : 0];
-  const int nk = g.nk;
-  const float* Mrow = M + (int64_t)row * nk;
-  const int per = (nk + kSelThreads - 1) / kSelThreads;
-  const int j0 = tid * per;
-  const int mine = max(0, min(per, nk - j0));  // valid blocks of this thread
-  if (tid == 0) s_jcut = 0;
-
-  // Coalesced loads (block 256 c + tid), all issued before the first is
-  // used (addresses clamped into the row), staged in LDS; then each thread
-  // reads back its own contiguous run.
-  {
-    float x[kPer];
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const int j = kSelThreads * c + tid;
-      x[c] = Mrow[j < nk ? j : nk - 1];
-    }
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const int j = kSelThreads * c + tid;
-      s_stage[j + (j >> 5)] = sanitized_bits(x[c]);
-    }
-  }
-  __syncthreads();
-  uint32_t ku[kPer];
-  uint32_t umax = 0;
-#pragma unroll
-  for (int t = 0; t < kPer; ++t) {
-    const int j = j0 + t;  // < kSelThreads kPer for every t < kPer: inside the staged words
-    const uint32_t sj = s_stage[j + (j >> 5)];
-    const uint32_t u = t < mine ? sj : 0u;
-    ku[t] = 0xFFFFFFFFu - u;
-    umax = umax > u ? umax : u;
-  }
-  umax = wave_max_u32(umax);
-  if (lane == 0) wred[w] = umax;
-  __syncthreads();
-#pragma unroll
-  for (int ww = 0; ww < kSelThreads / 64; ++ww) umax = umax > wred[ww] ? umax : wred[ww];
-  __syncthreads();
-
-  int s;
-  uint64_t kap;
-  if (P == (1ull << 32)) {  // keep everything
-    s = nk;
-    kap = ~0ull;
-  } else {
-    const int e = umax ? frexp_exp(umax) : 0;
-    uint64_t q[kPer];
-    uint64_t run = 0;
-#pragma unroll
-    for (int t = 0; t < kPer; ++t) {
-      q[t] = t < mine ? fixed_units(0xFFFFFFFFu - ku[t], e) : 0;
-      run += q[t];
-    }
-    uint64_t total;
-    block_inclusive_scan_u64(run, wsum64, &total);
-    const uint64_t T = threshold(P, total);
-
-    uint32_t prefix = 0;  // digits fixed so far
-    uint64_t below = 0;   // units of all blocks ordered before the candidates
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hsum[tid] = 0;
-      hnz[tid] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int t = 0; t < kPer; ++t) {
-        if (t < mine && ((uint64_t)ku[t] >> (shift + 8)) == prefix) {
-          const int d = (ku[t] >> shift) & 255;
-          atomicAdd(reinterpret_cast<unsigned long long*>(&hsum[d]), (unsigned long long)q[t]);
-          hnz[d] = 1;
-        }
-      }
-      __syncthreads();
-      const uint64_t hs = hsum[tid];
-      uint64_t all;
-      const uint64_t cum = block_inclusive_scan_u64(hs, wsum64, &all);  // bins in ascending digit order
-      const bool hit = hnz[tid] != 0 && below + cum >= T;
-      const uint64_t bal = __ballot(hit);
-      if (lane == 0) wred[w] = bal ? (uint32_t)(w * 64 + __builtin_ctzll(bal)) : 0xFFFFFFFFu;
-      __syncthreads();
-      uint32_t bin = wred[0];
-#pragma unroll
-      for (int ww = 1; ww < kSelThreads / 64; ++ww) bin = bin < wred[ww] ? bin : wred[ww];
-      bin = bin < 255u ? bin : 255u;  // a hit always exists: the candidates' units reach T
-      if ((uint32_t)tid == bin) s_below = below + cum - hs;
-      __syncthreads();
-      below = s_below;
-      prefix = (prefix << 8) | bin;
-    }
-    // The cut lies among the blocks whose inverted bits equal prefix (all
-    // with units qu): the need-th of them in index order.
-    const uint64_t qu = fixed_units(0xFFFFFFFFu - prefix, e);
-    uint64_t need = 1;
-    if (below < T && qu > 0) need = (T - below + qu - 1) / qu;
-    int nbelow = 0, nties = 0;
-#pragma unroll
-    for (int t = 0; t < kPer; ++t) {
-      if (t < mine) {
-        nbelow += ku[t] < prefix ? 1 : 0;
-        nties += ku[t] == prefix ? 1 : 0;
-      }
-    }
-    nbelow = block_sum_i32(nbelow, wsum32);
-    uint64_t tie_all;
-    const uint64_t tie_incl = block_inclusive_scan_u64((uint64_t)nties, wsum64, &tie_all);
-    uint64_t rank = tie_incl - (uint64_t)nties;  // ties owned by earlier threads
-    if (need > rank && need <= tie_incl) {
-#pragma unroll
-      for (int t = 0; t < kPer; ++t) {
-        if (t < mine && ku[t] == prefix) {
-          ++rank;
-          if (rank == need) s_jcut = j0 + t;
-        }
-      }
-    }
-    __syncthreads();
-    s = nbelow + (int)need;
-    kap = sort_key(0xFFFFFFFFu - prefix, s_jcut);
-  }
-  const int nw = (nk + 31) / 32;
-  if (tid < nw) s_keep[tid] = 0;
-  __syncthreads();
-  uint32_t bits = 0;
-#pragma unroll
-  for (int t = 0; t < kPer; ++t)
-    if (t < mine && sort_key(0xFFFFFFFFu - ku[t], j0 + t) <= kap) bits |= 1u << t;
-  or_bit_run(s_keep, j0, bits);
-  __syncthreads();
-  for (int x = tid; x < nw; x += kSelThreads) keep[(int64_t)row * nw + x] = s_keep[x];
-  if (tid == 0) counts[row] = s;
 }
 
 // Wave reductions with a wave-uniform result: DPP within each 16-lane row
@@ -662,6 +459,257 @@ __global__ __launch_bounds__(256) void cut_wave_kernel(const Geom g, const float
   wave_lds_sync();
   if (lane < nw) keep[(int64_t)row * nw + lane] = words[lane];
   if (lane == 0) counts[row] = s;
+}
+
+// One workgroup (four waves) per row, for rows of more than 64 * 31 blocks:
+// the wave kernel's search with block-wide reductions.  Thread t owns the
+// contiguous blocks [t kPer, t kPer + kPer) (kPer odd, 256 kPer >= nk;
+// blocks past nk read as 0), so thread order is index order.
+template <int kPer>
+__global__ __launch_bounds__(kSelThreads) void cut_group_kernel(const Geom g, const float* __restrict__ M,
+                                                                const PTable pt, int32_t* __restrict__ counts,
+                                                                uint32_t* __restrict__ keep,
+                                                                int32_t* __restrict__ done) {
+  static_assert(kPer % 2 == 1 && kPer <= 31, "odd runs: threads reading runs of kPer words hit distinct banks");
+  __shared__ uint32_t stage[kSelThreads * kPer];  // the staged row
+  __shared__ uint64_t hist[256];                  // the radix histogram, then the listed blocks
+  __shared__ uint32_t words[kSelThreads];         // each thread's tie bits, then the row's kept bits
+  __shared__ uint64_t r64[4];
+  __shared__ uint32_t r32[4];
+  __shared__ uint64_t s_u64[2];
+  __shared__ int s_i32[2];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (row == 0 && tid == 0) *done = 0;  // the order kernel's counter
+  const int h = (row / g.nq) % g.H;
+  const uint64_t P = pt.P[pt.per_head ? h : 0];
+  const int nk = g.nk;
+  const int j0 = tid * kPer;
+
+  // block-wide reductions: each wave's value (uniform), then the four in LDS
+  auto block_max_u32 = [&](uint32_t v) {
+    v = wave_max_u32_uniform(v);
+    if (lane == 0) r32[w] = v;
+    __syncthreads();
+    const uint32_t r = max(max(r32[0], r32[1]), max(r32[2], r32[3]));
+    __syncthreads();
+    return r;
+  };
+  auto block_min_u32 = [&](uint32_t v) {
+    v = wave_min_u32(v);
+    if (lane == 0) r32[w] = v;
+    __syncthreads();
+    const uint32_t r = min(min(r32[0], r32[1]), min(r32[2], r32[3]));
+    __syncthreads();
+    return r;
+  };
+  auto block_sum_u64 = [&](uint64_t v) {
+    v = wave_sum_u64(v);
+    if (lane == 0) r64[w] = v;
+    __syncthreads();
+    const uint64_t r = (r64[0] + r64[1]) + (r64[2] + r64[3]);
+    __syncthreads();
+    return r;
+  };
+  // inclusive scan over the block's threads (thread order)
+  auto block_incl_scan_u32 = [&](uint32_t v) {
+    v = wave_incl_scan_u32(v);
+    if (lane == 63) r32[w] = v;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int ww = 0; ww < w; ++ww) before += r32[ww];
+    __syncthreads();
+    return v + before;
+  };
+
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(M + (int64_t)row * nk), (short)0, nk * 4, 0x00020000);
+    uint32_t x[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) x[c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (kSelThreads * c + tid) * 4, 0, 0);
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) stage[kSelThreads * c + tid] = sanitized_bits(__uint_as_float(x[c]));
+  }
+  __syncthreads();
+  uint32_t u[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) u[t] = stage[j0 + t];
+  uint32_t umax = 0, umin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    umax = max(umax, u[t]);
+    umin = min(umin, u[t] ? u[t] : 0xFFFFFFFFu);
+  }
+  umax = block_max_u32(umax);
+
+  int s;
+  uint32_t gt = 0, eq = 0;
+  int jcut = nk;
+  if (P == (1ull << 32)) {
+    s = nk;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) gt |= (j0 + t < nk ? 1u : 0u) << t;
+  } else {
+    const int e = umax ? frexp_exp(umax) : 0;
+    const int c = 99 + e;
+    const uint32_t fast_lo = (uint32_t)max(c, 1) << 23;
+    uint64_t q[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const uint32_t mant = u[t] ? ((u[t] & 0x7FFFFFu) | 0x800000u) : 0u;
+      q[t] = (uint64_t)mant << (((int)(u[t] >> 23) - c) & 63);
+    }
+    if (__ballot(umin < fast_lo)) {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t)
+        if (u[t] != 0 && u[t] < fast_lo) q[t] = fixed_units(u[t], e);
+    }
+    uint64_t run = 0;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) run += q[t];
+    const uint64_t T = threshold(P, block_sum_u64(run));
+    uint64_t below = 0;
+    uint32_t uv = umax;
+    bool listed = false;
+    if (T != 0) {
+      umin = block_min_u32(umin);
+      const uint32_t width = umax - umin;
+      uint32_t rel[kPer];
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) rel[t] = umax - u[t];
+      uint32_t pre = 0;
+      uint64_t acc = 0;
+      int top = width ? 32 - __builtin_clz(width) : 0;
+      for (int pass = 0; top > 0 && !listed; ++pass) {
+        const int shift = top > 8 ? top - 8 : 0;
+        const uint32_t dmask = (1u << (top - shift)) - 1u;
+        const uint32_t above = top >= 32 ? 0u : (0xFFFFFFFFu << top);
+        hist[tid] = 0;
+        __syncthreads();
+        if (pass == 0) {
+#pragma unroll
+          for (int t = 0; t < kPer; ++t)
+            atomicAdd(reinterpret_cast<unsigned long long*>(hist + ((rel[t] >> shift) & dmask)),
+                      (unsigned long long)q[t]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < kPer; ++t)
+            if (((rel[t] ^ pre) & above) == 0)
+              atomicAdd(reinterpret_cast<unsigned long long*>(hist + ((rel[t] >> shift) & dmask)),
+                        (unsigned long long)q[t]);
+        }
+        __syncthreads();
+        // thread t holds digit t: inclusive scan of the units over the digits
+        const uint64_t hv = hist[tid];
+        uint64_t inc = wave_incl_scan_u64(hv);
+        if (lane == 63) r64[w] = inc;
+        __syncthreads();
+        for (int ww = 0; ww < w; ++ww) inc += r64[ww];
+        const uint64_t hitm = __ballot(acc + inc >= T);  // the least digit reaching T, by wave
+        if (lane == 0) r32[w] = hitm ? (uint32_t)(64 * w + __builtin_ctzll(hitm)) : 0xFFFFFFFFu;
+        __syncthreads();
+        const uint32_t digit = min(min(r32[0], r32[1]), min(r32[2], r32[3]));  // exists: acc + all >= T
+        if ((uint32_t)tid == digit) s_u64[0] = acc + inc - hv;
+        __syncthreads();
+        acc = s_u64[0];
+        pre |= digit << shift;
+        top = shift;
+        if (top == 0) break;
+        const uint32_t span = min((1u << top) - 1u, width - pre);
+        uint32_t smask = 0;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) smask |= (rel[t] - pre <= span ? 1u : 0u) << t;
+        const int cnt = __popc(smask);
+        const int incl = (int)block_incl_scan_u32((uint32_t)cnt);
+        if (tid == kSelThreads - 1) s_i32[0] = incl;
+        __syncthreads();
+        const int nlist = s_i32[0];
+        if (nlist > 64) continue;
+        int at = incl - cnt;
+        while (smask) {
+          const int t = __builtin_ctz(smask);
+          smask &= smask - 1u;
+          const uint32_t uj = stage[j0 + t];
+          hist[2 * at] = (uint64_t)uj | ((uint64_t)(j0 + t) << 32);
+          hist[2 * at + 1] = row_units(uj, e);
+          ++at;
+        }
+        __syncthreads();
+        // wave 0 resolves the cut among the listed blocks
+        if (w == 0) {
+          const uint32_t ui = lane < nlist ? (uint32_t)hist[2 * lane] : 0u;
+          uint64_t fle = acc, flt = acc;
+          for (int x = 0; x < nlist; ++x) {
+            const uint32_t ux = (uint32_t)hist[2 * x];
+            const uint64_t qx = hist[2 * x + 1];
+            fle += ux >= ui ? qx : 0;
+            flt += ux > ui ? qx : 0;
+          }
+          const uint32_t cut = wave_max_u32_uniform(lane < nlist && fle >= T ? ui : 0u);
+          const uint64_t at_v = __ballot(lane < nlist && ui == cut);
+          const int lv = __builtin_ctzll(at_v);
+          if (lane == 0) {
+            s_u64[1] = ((uint64_t)lane_u32((uint32_t)(flt >> 32), lv) << 32) | lane_u32((uint32_t)flt, lv);
+            s_i32[1] = (int)cut;
+          }
+        }
+        words[tid] = 0;
+        __syncthreads();
+        uv = (uint32_t)s_i32[1];
+        below = s_u64[1];
+        // the ties: every block of mass uv lies in the band and is listed
+        if (tid < nlist && (uint32_t)hist[2 * tid] == uv) {
+          const int j = (int)(hist[2 * tid] >> 32);
+          atomicOr(&words[j / kPer], 1u << (j % kPer));
+        }
+        __syncthreads();
+        eq = words[tid];
+        listed = true;
+        __syncthreads();
+      }
+      if (!listed) {
+        uv = umax - pre;
+        below = acc;
+      }
+    }
+    const uint64_t qu = row_units(uv, e);
+    uint64_t need = 1;
+    if (below < T && qu > 0 && T - below > qu) need = (T - below + qu - 1) / qu;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) gt |= (u[t] > uv ? 1u : 0u) << t;
+    if (!listed) {
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) eq |= (u[t] == uv ? 1u : 0u) << t;
+      if (uv == 0) {
+        const int nv = min(max(nk - j0, 0), kPer);
+        eq &= nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+      }
+    }
+    const int nties = __popc(eq);
+    const int incl = (int)block_incl_scan_u32((uint32_t)nties);
+    const int before = incl - nties;
+    if ((int64_t)need > before && (int64_t)need <= incl) {
+      uint32_t wd = eq;
+      for (int r = before + 1; r < (int)need; ++r) wd &= wd - 1u;
+      s_i32[0] = j0 + __builtin_ctz(wd);  // one thread owns the need-th tie
+    }
+    const int nbelow = (int)block_incl_scan_u32((uint32_t)__popc(gt));  // thread 255: all
+    if (tid == kSelThreads - 1) s_i32[1] = nbelow;
+    __syncthreads();
+    jcut = s_i32[0];
+    s = s_i32[1] + (int)need;
+  }
+  const int upto = jcut - j0 + 1;
+  const uint32_t tmask = upto >= 32 ? 0xFFFFFFFFu : (upto <= 0 ? 0u : (1u << upto) - 1u);
+  const uint32_t bits = gt | (eq & tmask);
+  const int nw = (nk + 31) / 32;
+  words[tid] = 0;
+  __syncthreads();
+  or_bit_run(words, j0, bits);
+  __syncthreads();
+  for (int x = tid; x < nw; x += kSelThreads) keep[(int64_t)row * nw + x] = words[x];
+  if (tid == 0) counts[row] = s;
 }
 
 // Exclusive scan of data[0, n) into out by one workgroup (a multiple of 64
@@ -1149,10 +1197,13 @@ hipError_t launch_select(const Geom& g, const float* M, const PTable& pt, int32_
                                    cut_wave_kernel<17>, cut_wave_kernel<19>, cut_wave_kernel<21>, cut_wave_kernel<23>,
                                    cut_wave_kernel<25>, cut_wave_kernel<27>, cut_wave_kernel<29>, cut_wave_kernel<31>};
     hipLaunchKernelGGL(cuts[per / 2], dim3((rows + 3) / 4), dim3(256), 0, st, g, M, pt, ws.counts, ws.keep, ws.done);
-  } else {
-    const int per_t = (g.nk + kSelThreads - 1) / kSelThreads;
-    auto cut = per_t <= 12 ? cut_kernel<12> : cut_kernel<kMaxPer>;
-    hipLaunchKernelGGL(cut, dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.keep, ws.done);
+  } else {  // 1985 .. 4096 blocks: a workgroup per row, odd runs of 9 .. 17 per thread
+    using CutFn = void (*)(const Geom, const float*, const PTable, int32_t*, uint32_t*, int32_t*);
+    static const CutFn cuts[5] = {cut_group_kernel<9>, cut_group_kernel<11>, cut_group_kernel<13>,
+                                  cut_group_kernel<15>, cut_group_kernel<17>};
+    const int per_t = ((g.nk + kSelThreads - 1) / kSelThreads) | 1;
+    hipLaunchKernelGGL(cuts[(per_t - 9) / 2], dim3(rows), dim3(kSelThreads), 0, st, g, M, pt, ws.counts, ws.keep,
+                       ws.done);
   }
   launch_order(g, ws, row_ptr, order != nullptr, st);
   hipLaunchKernelGGL(compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, g, (const uint32_t*)ws.keep, ws,
