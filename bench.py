@@ -77,7 +77,7 @@ PMC_KERNELS = [("attn_bf16_kernel", "attn", "losa_sparse_attn"),
                ("mass_bf16_kernel", "mass", "losa_block_mass"),
                ("pack_kv_kernelILi128ELb0", "pack_k", "losa_block_mass"),
                ("cut_wave_kernel", "cut", "losa_select"),
-               ("cut_kernel", "cut_wg", "losa_select"),
+               ("cut_group_kernel", "cut_group", "losa_select"),
                ("order_kernel", "order", "losa_select"),
                ("compact_kernel", "compact", "losa_select")]
 
@@ -1008,7 +1008,7 @@ TRACE_KERNELS = [
     ("pool_kernel", "pool_kernel", "losa_pooled_mass"),
     ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
     ("cut_wave_kernel", "cut_wave_kernel", "losa_select"),
-    ("cut_kernel", "cut_kernel", "losa_select"),
+    ("cut_group_kernel", "cut_group_kernel", "losa_select"),
     ("order_kernel", "order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
     ("compact_kernel", "compact_kernel", "losa_select"),
     ("retained_kernel", "retained_kernel", "losa_retained_mass"),
