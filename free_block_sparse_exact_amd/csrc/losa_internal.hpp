@@ -49,7 +49,7 @@ struct SelectWs {
   int32_t* done;        // [1] finished workgroups of the order kernel (cleared by the count kernel before it)
   int32_t* ranked;      // [rows] row of rank r in head h at h * nq + r
   int32_t* gkey;        // [B*H*ngh] count of each work group's first row
-  int32_t* gstart;      // [B*H*ngh] first order slot of each work group
+  int32_t* bucket_start;  // [B*H][nk + 2] first rank in the head of count nk - b (b = nk + 1: n_q)
   int ngh;              // work groups per head: ceil(nq / kGroupRows)
 };
 constexpr int kGroupRows = 32;    // rows per work group of the budget order (one XCD's CUs)

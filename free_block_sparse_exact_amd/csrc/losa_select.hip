@@ -97,20 +97,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The active lanes of this wave whose key equals this lane's (0 <= key <
-// 2^nbits): one ballot per key bit, so a wave of many distinct keys costs
-// no more than a wave of one.
-__device__ __forceinline__ uint64_t match_lanes(int key, bool active, int nbits) {
-  uint64_t eq = __ballot(active);
-  for (int i = 0; i < nbits; ++i) {
-    const bool bit = (key >> i) & 1;
-    const uint64_t bm = __ballot(bit);
-    eq &= bit ? bm : ~bm;
-  }
-  return eq;
-}
-
-
 // ORs the run of bits (bit t for block j0 + t, at most 32 of them) into an
 // LDS bit array of the row (bit j%32 of word j/32); the run may straddle two
 // words.
@@ -754,20 +740,43 @@ __device__ void block_exclusive_scan_i32(const int32_t* data, int n, int32_t* ou
 }
 
 // The first col_idx slot of row's list: its head's first slot plus the kept
-// blocks of the head's earlier rows (both written by order_kernel).  Lane 0
-// of the row's wave stores it as row_ptr[row]; lane 1 places the row at rank
-// position `row` (rank r of head h) into the work order when one is wanted
-// (a slot outside [0, rows) cannot arise from the order kernel and is not
+// blocks of the head's earlier rows (both written by order_kernel); lane 0 of
+// the row's wave stores it as row_ptr[row].  With a work order, the wave also
+// fills order position... the row index taken as a rank position p (rank r
+// of head h): its work group (h, r / 32) has the key x = gkey (its first
+// count); the groups before it are k = r / 32 of its own head, and of every
+// other head h' those with a key > x, or >= x when h' < h (ties by head):
+// ceil(rows of h' with count > x (or >= x) / 32), from h''s bucket starts;
+// among them the short ones (each head's last group, nq - 32 (ngh - 1) rows)
+// come from the heads' last keys the same way.  order[32 R - (32 - last) S +
+// r mod 32] = ranked[p] (a slot outside [0, rows) cannot arise and is not
 // written).
-__device__ __forceinline__ int finish_row(const SelectWs& ws, int nq, int rows, int row, int lane, int32_t* row_ptr,
+__device__ __forceinline__ int finish_row(const Geom& g, const SelectWs& ws, int row, int lane, int32_t* row_ptr,
                                           int32_t* order) {
-  const int h = row / nq;
+  const int nq = g.nq, nk = g.nk, h = row / nq;
   const int start = ws.head_base[h] + ws.local_off[row];
   if (lane == 0) row_ptr[row] = start;
-  if (order && lane == 1) {
-    const int r = row - h * nq;
-    const int slot = ws.gstart[h * ws.ngh + r / kGroupRows] + r % kGroupRows;
-    if ((unsigned)slot < (unsigned)rows) order[slot] = ws.ranked[row];
+  if (order) {
+    const int heads = g.B * g.H, ngh = ws.ngh, r = row - h * nq, k = r / kGroupRows;
+    const int lastn = nq - (ngh - 1) * kGroupRows;
+    const int x = ws.gkey[h * ngh + k], b = nk - x;
+    int R = k, S = 0;
+    for (int h0 = 0; h0 < heads; h0 += kWave) {  // the other heads, 64 at a time
+      const int hh = h0 + lane;
+      int t = 0, sh = 0;
+      if (hh < heads && hh != h) {
+        const int32_t* bs = ws.bucket_start + (int64_t)hh * (nk + 2);
+        t = ((hh < h ? bs[b + 1] : bs[b]) + kGroupRows - 1) / kGroupRows;
+        if (lastn < kGroupRows) {
+          const int y = ws.gkey[hh * ngh + ngh - 1];
+          sh = (hh < h ? y >= x : y > x) ? 1 : 0;
+        }
+      }
+      R += wave_sum_i32(t);
+      S += wave_sum_i32(sh);
+    }
+    const int slot = kGroupRows * R - (kGroupRows - lastn) * S + r % kGroupRows;
+    if (lane == 0 && (unsigned)slot < (unsigned)g.rows()) order[slot] = ws.ranked[row];
   }
   return start;
 }
@@ -787,7 +796,7 @@ __global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32
   const int nk = g.nk, nw = (nk + 31) / 32;  // nw <= 128
   const uint32_t* kr = keep + (int64_t)row * nw;
   const uint32_t w0 = lane < nw ? kr[lane] : 0u, w1 = 64 + lane < nw ? kr[64 + lane] : 0u;
-  int pos = finish_row(ws, g.nq, g.rows(), row, lane, row_ptr, order);
+  int pos = finish_row(g, ws, row, lane, row_ptr, order);
   // the row's slots lie inside the capacity checked on the host (rows * nk <
   // 2^31) unless the offsets are not the order kernel's; then nothing is written
   if (pos < 0 || (int64_t)pos + ws.counts[row] > (int64_t)g.rows() * nk) return;
@@ -808,7 +817,6 @@ __global__ __launch_bounds__(256) void compact_kernel(const Geom g, const uint32
 }
 
 constexpr int kOrderThreads = 1024;
-constexpr int kSortMax = 16384;  // keys one workgroup sorts in LDS (64 KB)
 
 // x from lane (lane ^ J), by DPP moves and gfx950 lane swaps (no LDS); every
 // lane must be active.
@@ -910,26 +918,23 @@ __device__ __forceinline__ int block_exclusive_scan_reg(int v, int* wsum, int* t
   return before + inc - v;
 }
 
-// Row offsets and the work order from the kept counts, one workgroup per
-// (batch, head), then a hand-off to the last workgroup to finish.
+// Row offsets and the work order's ranks from the kept counts, one
+// workgroup per (batch, head), then a hand-off to the last workgroup to
+// finish (*done must be 0 on entry: the count kernel before clears it).
 //   per head h: local_off[row] = the kept blocks of the head's earlier rows,
 //     head_total[h]; when the order is wanted, the head's rows ranked by
 //     count descending, ties by row: a sort of the unique keys
 //     (nk - count) << 14 | local row (nq <= 16384) -> ranked[h nq + r] = row
-//     of rank r, gkey[h ngh + k] = the count of rank 32 k, the first
-//     (largest) of work group k;
-//   last workgroup: head_base = exclusive scan of head_total, row_ptr[rows];
-//     the work groups by key descending, ties by group index (head, then k):
-//     a sort of the unique keys (nk - key) << 14 | group (up to 16384
-//     groups; beyond, a stable counting sort over the key buckets whose
-//     waves take turns); a group's first order slot is the rows of the
-//     groups before it (32 each, the head's last group nq - 32 (ngh - 1)).
+//     of rank r, gkey[h ngh + k] = the count of rank 32 k (the first, largest,
+//     of work group k), and bucket_start[h][b] = the first rank of bucket
+//     b = nk - count (b = nk + 1: nq);
+//   last workgroup: head_base = exclusive scan of head_total, row_ptr[rows].
+// The work groups' order slots follow per row from these (finish_row).
 // The counts are read once, each thread a contiguous run of at most 16.
-// *done must be 0 on entry (the count kernel before this one clears it).
 __global__ __launch_bounds__(kOrderThreads) void order_kernel(const Geom g, const int32_t* __restrict__ counts,
                                                               const SelectWs ws, int32_t* __restrict__ row_ptr,
                                                               int want_order) {
-  extern __shared__ uint32_t ol[];  // sort keys; in the turn-based group placement [2][nk + 1] bucket slots
+  extern __shared__ uint32_t ol[];  // sort keys
   __shared__ int wsum[kOrderThreads / 64];
   __shared__ int last;
   const int h = blockIdx.x, nq = g.nq, nk = g.nk, tid = threadIdx.x;
@@ -957,17 +962,29 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const Geom g, cons
       for (int k = 0; k < 16; ++k)
         if (k < per && i0 + k < n) {
           const int i = i0 + k;
-          ol[i] = i < nq ? ((uint32_t)(nk - cnt[k]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
+          ol[i] = i < nq ? ((uint32_t)(nk - min(max(cnt[k], 0), nk)) << 14) | (uint32_t)i : 0xFFFFFFFFu;
         }
       for (int i = per * (int)blockDim.x + tid; i < n; i += blockDim.x) ol[i] = 0xFFFFFFFFu;  // beyond the runs
       __syncthreads();
       bitonic_sort_lds(ol, n);
       int32_t* ranked = ws.ranked + (int64_t)h * nq;
       int32_t* gkey = ws.gkey + (int64_t)h * ws.ngh;
+      int32_t* bst = ws.bucket_start + (int64_t)h * (nk + 2);
       for (int r = tid; r < nq; r += blockDim.x) {
         const uint32_t k = ol[r];
         ranked[r] = h * nq + (int)(k & 0x3FFFu);
         if (r % kGroupRows == 0) gkey[r / kGroupRows] = nk - (int)(k >> 14);
+      }
+      // bucket b starts at the first rank whose key is at least b << 14: a
+      // binary search over the sorted keys (padding keys are all ones)
+      const int lg = 31 - __builtin_clz(n);
+      for (int b = tid; b <= nk + 1; b += blockDim.x) {
+        const uint32_t kb = (uint32_t)b << 14;
+        int lo = 0;  // keys before lo are < kb
+        for (int step = n >> 1, it = 0; it <= lg; ++it, step >>= 1)
+          if (step > 0 && ol[lo + step - 1] < kb) lo += step;
+        if (lo < n && ol[lo] < kb) ++lo;
+        bst[b] = min(lo, nq);
       }
     }
   }
@@ -979,84 +996,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(const Geom g, cons
   __syncthreads();
   if (!last) return;
   __threadfence();
-  const int heads = gridDim.x;
-  block_exclusive_scan_i32(ws.head_total, heads, ws.head_base, row_ptr + (int64_t)heads * nq, wsum);
-  if (!want_order) return;
-  const int ngh = ws.ngh;
-  const int lastn = nq - (ngh - 1) * kGroupRows;  // rows of each head's last group
-  const int ngroups = heads * ngh;
-  if (ngroups <= kSortMax) {
-    const int n = pow2_at_least(ngroups);
-    for (int i = tid; i < n; i += blockDim.x)
-      ol[i] = i < ngroups ? ((uint32_t)(nk - ws.gkey[i]) << 14) | (uint32_t)i : 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_sort_lds(ol, n);
-    // first slots: exclusive scan of the group sizes in sorted order, each
-    // thread over a contiguous run of positions
-    const int per = (ngroups + blockDim.x - 1) / blockDim.x, p0 = tid * per;
-    int run = 0;
-    for (int p = p0; p < min(p0 + per, ngroups); ++p)
-      run += (int)(ol[p] & 0x3FFFu) % ngh == ngh - 1 ? lastn : kGroupRows;
-    const int lane = tid & 63, w = tid >> 6;
-    int v = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(v, o, kWave);
-      if (lane >= o) v += t;
-    }
-    if (lane == 63) wsum[w] = v;
-    __syncthreads();
-    int slot = v - run;
-    for (int ww = 0; ww < w; ++ww) slot += wsum[ww];
-    for (int p = p0; p < min(p0 + per, ngroups); ++p) {
-      const int gi = (int)(ol[p] & 0x3FFFu);
-      ws.gstart[gi] = slot;
-      slot += gi % ngh == ngh - 1 ? lastn : kGroupRows;
-    }
-    return;
-  }
-  // More groups than one sort holds: a stable counting sort over the buckets
-  // nk - key; groups before a group come from a placement over all groups,
-  // short groups before it (the heads' last groups when lastn < 32) from the
-  // same placement restricted to them, counted with one more ballot.
-  const bool has_short = lastn < kGroupRows;
-  const int nbits = 32 - __builtin_clz(nk);  // buckets nk - key <= nk
-  int* all = reinterpret_cast<int*>(ol);
-  int* shrt = all + nk + 1;
-  for (int x = tid; x < 2 * (nk + 1); x += blockDim.x) all[x] = 0;
-  __syncthreads();
-  for (int gi = tid; gi < ngroups; gi += blockDim.x) {
-    const int b = nk - ws.gkey[gi];
-    atomicAdd(&all[b], 1);
-    if (has_short && gi % ngh == ngh - 1) atomicAdd(&shrt[b], 1);
-  }
-  __syncthreads();
-  block_exclusive_scan_i32(all, nk + 1, all, nullptr, wsum);  // the first slot per bucket
-  block_exclusive_scan_i32(shrt, nk + 1, shrt, nullptr, wsum);
-  const int lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int t0 = 0; t0 < ngroups; t0 += blockDim.x) {
-    const int gi = t0 + tid;
-    const bool valid = gi < ngroups;
-    const int b = valid ? nk - ws.gkey[gi] : 0;
-    const bool is_short = valid && has_short && gi % ngh == ngh - 1;
-    for (int turn = 0; turn < nw && t0 + 64 * turn < ngroups; ++turn) {  // waves in group order: stable slots
-      __syncthreads();
-      if (w == turn) {
-        const uint64_t eq = match_lanes(b, valid, nbits);
-        const uint64_t es = eq & __ballot(is_short);
-        if (valid) {
-          const int R = all[b] + __popcll(eq & lt), S = shrt[b] + __popcll(es & lt);
-          ws.gstart[gi] = kGroupRows * R - (kGroupRows - lastn) * S;
-        }
-        wave_lds_sync();  // every lane has read the slots before the first lane of each key moves them on
-        if (valid && (eq & lt) == 0) {
-          all[b] += __popcll(eq);
-          shrt[b] += __popcll(es);
-        }
-      }
-    }
-  }
+  block_exclusive_scan_i32(ws.head_total, gridDim.x, ws.head_base, row_ptr + (int64_t)gridDim.x * nq, wsum);
 }
 
 // Online block thresholding (the Sol-Attn page's block thresholding during
@@ -1079,7 +1019,7 @@ __global__ __launch_bounds__(256) void threshold_kernel(const Geom g, const floa
   const int nk = g.nk;
   const double theta = tt.t[tt.per_head ? (row / g.nq) % g.H : 0];
   const float* Mrow = M + (int64_t)row * nk;
-  int32_t* dst = kWrite ? col_idx + finish_row(ws, g.nq, g.rows(), row, lane, row_ptr, order) : nullptr;
+  int32_t* dst = kWrite ? col_idx + finish_row(g, ws, row, lane, row_ptr, order) : nullptr;
   float carry = 0.f;  // largest mass before this step's blocks
   int kept = 0;
   for (int j0 = 0; j0 < nk; j0 += kWave) {
@@ -1117,19 +1057,19 @@ __global__ __launch_bounds__(256) void pick_counts_kernel(int rows, int nq, int 
 
 // One wave per row: copy the chosen set's indices to the row's first slot
 // (row_ptr and the work order stored on the way).
-__global__ __launch_bounds__(256) void copy_lists_kernel(int rows, int nq, const int32_t* __restrict__ take_b,
+__global__ __launch_bounds__(256) void copy_lists_kernel(const Geom g, const int32_t* __restrict__ take_b,
                                                          const int32_t* __restrict__ rpa,
                                                          const int32_t* __restrict__ cia,
                                                          const int32_t* __restrict__ rpb,
                                                          const int32_t* __restrict__ cib, const SelectWs ws,
                                                          int32_t* __restrict__ row_ptr, int32_t* __restrict__ order,
                                                          int32_t* __restrict__ col_idx) {
-  const int r = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), rows = g.rows(), nq = g.nq;
   if (r >= rows) return;
   const int lane = threadIdx.x & 63;
   const bool b = take_b[r / nq] != 0;
   const int32_t* src = (b ? cib : cia) + (b ? rpb : rpa)[r];
-  int32_t* dst = col_idx + finish_row(ws, nq, rows, r, lane, row_ptr, order);
+  int32_t* dst = col_idx + finish_row(g, ws, r, lane, row_ptr, order);
   const int n = ws.counts[r];
   for (int t = lane; t < n; t += 64) dst[t] = src[t];
 }
@@ -1166,7 +1106,8 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
   int32_t* local_off = take(rows);
   int32_t* head_total = take(2 * heads + 1);  // then head_base and done
   int32_t* ranked = take(rows);
-  int32_t* gkey = take(2 * heads * ngh);  // then gstart
+  int32_t* gkey = take(heads * (size_t)ngh);
+  int32_t* bucket_start = take(heads * (size_t)(g.nk + 2));
   if (layout) {
     layout->counts = counts;
     layout->keep = reinterpret_cast<uint32_t*>(keep);
@@ -1177,7 +1118,7 @@ size_t select_ws_bytes(const Geom& g, SelectWs* layout, char* base) {
     layout->done = head_total + 2 * heads;
     layout->ranked = ranked;
     layout->gkey = gkey;
-    layout->gstart = gkey + heads * ngh;
+    layout->bucket_start = bucket_start;
     layout->ngh = ngh;
   }
   return off;
@@ -1229,15 +1170,13 @@ hipError_t launch_merge_lists(const Geom& g, const int32_t* take_b, const int32_
   hipLaunchKernelGGL(pick_counts_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, g.nq, g.nk, take_b, rpa,
                      rpb, ws);
   launch_order(g, ws, row_ptr, order != nullptr, st);
-  hipLaunchKernelGGL(copy_lists_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, rows, g.nq, take_b, rpa, cia, rpb,
-                     cib, ws, row_ptr, order, col_idx);
+  hipLaunchKernelGGL(copy_lists_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, g, take_b, rpa, cia, rpb, cib, ws,
+                     row_ptr, order, col_idx);
   return hipGetLastError();
 }
 
 void launch_order(const Geom& g, const SelectWs& ws, int32_t* row_ptr, bool want_order, hipStream_t st) {
-  const int ngroups = g.B * g.H * ws.ngh;
-  const int group_words = ngroups <= kSortMax ? pow2_at_least(ngroups) : 2 * (g.nk + 1);
-  const size_t lds = want_order ? (size_t)max(pow2_at_least(g.nq), group_words) * sizeof(uint32_t) : 0;
+  const size_t lds = want_order ? (size_t)pow2_at_least(g.nq) * sizeof(uint32_t) : 0;
   hipLaunchKernelGGL(order_kernel, dim3(g.B * g.H), dim3(kOrderThreads), lds, st, g, (const int32_t*)ws.counts, ws,
                      row_ptr, want_order ? 1 : 0);
 }
