@@ -148,14 +148,16 @@ def test_select_bit_exact_full_shape(wid):
     assert np.array_equal(order.cpu().numpy(), O.budget_order(rp_ref, M.shape[2]))
 
 
-@pytest.mark.parametrize("nk", [1, 2, 63, 64, 65, 127, 129, 200, 500, 600, 1000, 1217, 1400, 2047, 2048, 2500])
+@pytest.mark.parametrize("nk", [1, 2, 63, 64, 65, 127, 129, 200, 400, 500, 600, 800, 900, 1000, 1200, 1217, 1400, 1550,
+                                1700, 1800, 1984, 2047, 2048, 2500, 3200, 3500])
 def test_select_widths_and_ties(nk):
-    """Row widths around every multiple of the 64-lane step up to the widest
-    one-wave row (2048 blocks), one width in each unrolled instance of the
-    one-wave cut (600, 1400 among them) and one (2500) on the
-    workgroup-per-row cut; most rows adversarial (equal masses, exact ties,
-    zeros, one-hot, denormals, non-finite): lists and order bit-exact for
-    several p, ties cut in index order."""
+    """Row widths around multiples of the 64-lane step, at least one width in
+    every instance of the one-wave cut (odd runs of 1 .. 31 blocks per lane:
+    up to 1984 blocks) and of the workgroup-per-row cut (runs of 9 .. 17 per
+    thread: 1985 .. 4096 blocks; 4096 itself in test_maximum_key_block_count,
+    3713 in the full-shape tests); most rows adversarial (equal masses, exact
+    ties, zeros, one-hot, denormals, non-finite): lists and order bit-exact
+    for several p, ties cut in index order."""
     rng = np.random.default_rng(300 + nk)
     C, R = 32, 128
     N = nk * C - 3 if nk > 1 else 20
