@@ -86,11 +86,42 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _strip_c_comments(text: str) -> str:
+    """C/C++/HIP source without its comments, each run of whitespace one
+    space: what the compiler sees (string and character literals are kept
+    as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_hash(paths) -> str:
+    """Hash of the sources a call's kernels are built from; comments and
+    layout of the C++/HIP files do not count (they change no kernel)."""
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+            data = f.read()
+        if p.endswith((".hip", ".hpp", ".h", ".cpp")):
+            data = _strip_c_comments(data.decode("utf-8")).encode("utf-8")
+        h.update(data)
     return h.hexdigest()[:16]
 
 
@@ -1035,7 +1066,7 @@ def summarize_trace(trace_dir, name, command):
              "    " + command, "",
              "| kernel | call | launches | average us | min us | max us | share of GPU time |",
              "|---|---|---|---|---|---|---|"]
-    per_call = {}
+    per_call, ran = {}, set()
     for r in rows:
         label = next(((short, call) for frag, short, call in TRACE_KERNELS if frag in r["Name"]), None)
         if label is None:
@@ -1044,10 +1075,15 @@ def summarize_trace(trace_dir, name, command):
         avg = float(r["AverageNs"]) / 1e3
         lines.append(f"| {short} | {call} | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
-        for c in call.split(", "):
+        calls = call.split(", ")
+        for c in calls:
             per_call[c] = per_call.get(c, 0.0) + avg
+        if len(calls) == 1:
+            ran.add(calls[0])
+    # A kernel shared by several calls (the packing, the work order) does not
+    # show which of them ran: a call is listed when a kernel of its own did.
     lines += ["", "Average per library call (sum of its kernels' average durations):", ""]
-    lines += [f"* {call}: {us / 1e3:.3f} ms" for call, us in per_call.items()]
+    lines += [f"* {call}: {us / 1e3:.3f} ms" for call, us in per_call.items() if call in ran]
     lines.append("")
     out = os.path.join(ROOT, "profiles", name + ".md")
     with open(out, "w") as f:

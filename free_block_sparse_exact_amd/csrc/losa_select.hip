@@ -15,13 +15,16 @@
 //   order       one workgroup per (batch, head): the exclusive scan of the
 //               head's counts (its rows' offsets inside the head) and, when
 //               the work order is wanted, the head's rows ranked by count (a
-//               bitonic sort of unique keys in LDS); the last workgroup to
-//               finish scans the heads' totals (-> each head's first CSR
-//               slot, row_ptr[rows]) and sorts the work groups by their
-//               first count -> each group's first order slot;
-//   compact     one wave per row: row_ptr[row], the row's entry in the work
-//               order, and from the kept bits the kept indices ascending
-//               from row_ptr[row] (the masses are read once, by the cut).
+//               bitonic sort of unique keys in LDS) with, for every count,
+//               the first rank in the head that holds it (binary searches
+//               over the sorted keys); the last workgroup to finish scans
+//               the heads' totals (-> each head's first CSR slot,
+//               row_ptr[rows]);
+//   compact     one wave per row: row_ptr[row]; the first order slot of the
+//               row's work group, counted from every head's count bucket
+//               starts (the groups that come before it in the order); and
+//               from the kept bits the kept indices ascending from
+//               row_ptr[row] (the masses are read once, by the cut).
 //
 // The same order kernel also serves two other list builders here: online
 // block thresholding (threshold kernel: counts, then the kept indices) and
@@ -742,8 +745,8 @@ __device__ void block_exclusive_scan_i32(const int32_t* data, int n, int32_t* ou
 // The first col_idx slot of row's list: its head's first slot plus the kept
 // blocks of the head's earlier rows (both written by order_kernel); lane 0 of
 // the row's wave stores it as row_ptr[row].  With a work order, the wave also
-// fills order position... the row index taken as a rank position p (rank r
-// of head h): its work group (h, r / 32) has the key x = gkey (its first
+// fills one order slot, reading its row index as a rank position p (rank r
+// of head h): the work group (h, r / 32) has the key x = gkey (its first
 // count); the groups before it are k = r / 32 of its own head, and of every
 // other head h' those with a key > x, or >= x when h' < h (ties by head):
 // ceil(rows of h' with count > x (or >= x) / 32), from h''s bucket starts;
