@@ -48,6 +48,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -72,14 +73,29 @@ CALL_SOURCES = {
 CALL_SOURCES["losa_select"] = [_CSRC + "losa_select.hip", _CSRC + "losa_device.hpp", _CSRC + "losa_internal.hpp",
                                "free_block_sparse_exact_amd/_build.py"]
 # kernel name fragment -> (part, call) for the traffic summary
-PMC_KERNELS = [("attn_bf16_kernel", "attn", "losa_sparse_attn"),
-               ("pack_kv_kernelILi128ELb1", "pack_kv", "losa_sparse_attn"),
-               ("mass_bf16_kernel", "mass", "losa_block_mass"),
-               ("pack_kv_kernelILi128ELb0", "pack_k", "losa_block_mass"),
-               ("cut_wave_kernel", "cut", "losa_select"),
-               ("cut_group_kernel", "cut_group", "losa_select"),
-               ("order_kernel", "order", "losa_select"),
-               ("compact_kernel", "compact", "losa_select")]
+# Kernel names as rocprofv3 reports them (mangled or demangled): regular
+# expressions, first match wins, so a template instance that belongs to
+# another call comes before its plain name.
+_ATTN_INPASS = r"attn_bf16_kernel(<\d+, true>|ILi\d+ELb1)"
+_ATTN = r"attn_bf16_kernel(<\d+, false>|ILi\d+ELb0)"
+_DENSE_LISTS = r"dense_bf16_kernel(<\d+, true>|ILi\d+ELb1)"
+_DENSE = r"dense_bf16_kernel(<\d+, false>|ILi\d+ELb0)"
+_PACK_KV = r"pack_kv_kernel(<\d+, true>|ILi\d+ELb1)"
+_PACK_K = r"pack_kv_kernel(<\d+, false>|ILi\d+ELb0)"
+# kernel name pattern -> (part, call) for the traffic summary
+PMC_KERNELS = [(_ATTN, "attn", "losa_sparse_attn"),
+               (_PACK_KV, "pack_kv", "losa_sparse_attn"),
+               (r"mass_bf16_kernel", "mass", "losa_block_mass"),
+               (_PACK_K, "pack_k", "losa_block_mass"),
+               (r"cut_wave_kernel", "cut", "losa_select"),
+               (r"cut_group_kernel", "cut_group", "losa_select"),
+               (r"order_kernel", "order", "losa_select"),
+               (r"compact_kernel", "compact", "losa_select")]
+
+
+def kernel_label(name, table):
+    """The first entry of table whose pattern occurs in the kernel name."""
+    return next((e[1:] for e in table if re.search(e[0], name)), None)
 
 
 def log(*a):
@@ -997,7 +1013,7 @@ def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
     ff, wf = copy_factor(copy_fetch_dir, "FETCH_SIZE"), copy_factor(copy_write_dir, "WRITE_SIZE")
 
     def per_launch(tab, key):
-        vals = [v for k, vs in tab.items() if key in k for v in vs]
+        vals = [v for k, vs in tab.items() if re.search(key, k) for v in vs]
         return float(np.mean(vals)) if vals else 0.0
 
     calls = {}
@@ -1026,31 +1042,31 @@ def summarize_pmc(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir
     print(json.dumps(out))
 
 
-# kernel name fragment -> (short name, call it belongs to)
+# kernel name pattern -> (short name, call it belongs to)
 TRACE_KERNELS = [
-    ("attn_bf16_kernel", "attn_bf16_kernel", "losa_sparse_attn"),
-    ("pack_kv_kernelILi128ELb1", "pack_kv_kernel (K and V)",
-     "losa_sparse_attn, losa_dense_attn_mass, losa_sparse_attn_mass"),
-    ("pack_kv_kernelILi128ELb0", "pack_kv_kernel (K only)", "losa_block_mass"),
-    ("mass_bf16_kernel", "mass_bf16_kernel", "losa_block_mass"),
-    ("dense_bf16_kernel<128, true>", "dense_bf16_kernel (lists)", "losa_sparse_attn_mass"),
-    ("dense_bf16_kernelILi128ELb1", "dense_bf16_kernel (lists)", "losa_sparse_attn_mass"),
-    ("dense_bf16_kernel", "dense_bf16_kernel", "losa_dense_attn_mass"),
-    ("pool_kernel", "pool_kernel", "losa_pooled_mass"),
-    ("proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
-    ("cut_wave_kernel", "cut_wave_kernel", "losa_select"),
-    ("cut_group_kernel", "cut_group_kernel", "losa_select"),
-    ("order_kernel", "order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
-    ("compact_kernel", "compact_kernel", "losa_select"),
-    ("retained_kernel", "retained_kernel", "losa_retained_mass"),
-    ("drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),
-    ("drift_final_kernel", "drift_final_kernel", "losa_qk_drift"),
-    ("threshold_kernel<false>", "threshold_kernel (counts)", "losa_select_threshold"),
-    ("threshold_kernelILb0", "threshold_kernel (counts)", "losa_select_threshold"),
-    ("threshold_kernel<true>", "threshold_kernel (indices)", "losa_select_threshold"),
-    ("threshold_kernelILb1", "threshold_kernel (indices)", "losa_select_threshold"),
-    ("pick_counts_kernel", "pick_counts_kernel", "losa_merge_lists"),
-    ("copy_lists_kernel", "copy_lists_kernel", "losa_merge_lists"),
+    (_ATTN_INPASS, "attn_bf16_kernel (in-pass thresholding)", "losa_sparse_attn_threshold"),
+    (_ATTN, "attn_bf16_kernel", "losa_sparse_attn"),
+    (_PACK_KV, "pack_kv_kernel (K and V)",
+     "losa_sparse_attn, losa_dense_attn_mass, losa_sparse_attn_mass, losa_sparse_attn_threshold"),
+    (_PACK_K, "pack_kv_kernel (K only)", "losa_block_mass"),
+    (r"mass_bf16_kernel", "mass_bf16_kernel", "losa_block_mass"),
+    (_DENSE_LISTS, "dense_bf16_kernel (lists)", "losa_sparse_attn_mass"),
+    (_DENSE, "dense_bf16_kernel", "losa_dense_attn_mass"),
+    (r"pool_kernel(<__bf16, \d+, double>|IDF16bLi\d+EdE)", "pool_kernel (fp64 block means)",
+     "losa_sparse_attn_threshold"),
+    (r"pool_kernel", "pool_kernel", "losa_pooled_mass"),
+    (r"proxy_kernel", "proxy_kernel", "losa_pooled_mass"),
+    (r"cut_wave_kernel", "cut_wave_kernel", "losa_select"),
+    (r"cut_group_kernel", "cut_group_kernel", "losa_select"),
+    (r"order_kernel", "order_kernel", "losa_select, losa_select_threshold, losa_merge_lists"),
+    (r"compact_kernel", "compact_kernel", "losa_select"),
+    (r"retained_kernel", "retained_kernel", "losa_retained_mass"),
+    (r"drift_partial_kernel", "drift_partial_kernel", "losa_qk_drift"),
+    (r"drift_final_kernel", "drift_final_kernel", "losa_qk_drift"),
+    (r"threshold_kernel(<false>|ILb0)", "threshold_kernel (counts)", "losa_select_threshold"),
+    (r"threshold_kernel(<true>|ILb1)", "threshold_kernel (indices)", "losa_select_threshold"),
+    (r"pick_counts_kernel", "pick_counts_kernel", "losa_merge_lists"),
+    (r"copy_lists_kernel", "copy_lists_kernel", "losa_merge_lists"),
 ]
 
 
@@ -1066,9 +1082,9 @@ def summarize_trace(trace_dir, name, command):
              "    " + command, "",
              "| kernel | call | launches | average us | min us | max us | share of GPU time |",
              "|---|---|---|---|---|---|---|"]
-    per_call, ran = {}, set()
+    per_call, own, shared = {}, {}, {}
     for r in rows:
-        label = next(((short, call) for frag, short, call in TRACE_KERNELS if frag in r["Name"]), None)
+        label = kernel_label(r["Name"], TRACE_KERNELS)
         if label is None:
             continue
         short, call = label
@@ -1076,14 +1092,20 @@ def summarize_trace(trace_dir, name, command):
         lines.append(f"| {short} | {call} | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
         calls = call.split(", ")
-        for c in calls:
-            per_call[c] = per_call.get(c, 0.0) + avg
         if len(calls) == 1:
-            ran.add(calls[0])
-    # A kernel shared by several calls (the packing, the work order) does not
-    # show which of them ran: a call is listed when a kernel of its own did.
-    lines += ["", "Average per library call (sum of its kernels' average durations):", ""]
-    lines += [f"* {call}: {us / 1e3:.3f} ms" for call, us in per_call.items() if call in ran]
+            own.setdefault(calls[0], []).append((avg, int(r["Calls"])))
+        else:
+            for c in calls:
+                shared[c] = shared.get(c, 0.0) + avg
+    # A kernel shared by several calls (the packing, the work order) runs once
+    # per call and does not show which of them ran: a call is listed when a
+    # kernel of its own did.  A call's own kernels launch n or a multiple of n
+    # times (n = its fewest), e.g. the block means once for Q and once for K.
+    for c, ks in own.items():
+        n = min(k for _, k in ks)
+        per_call[c] = shared.get(c, 0.0) + sum(a * round(k / n) for a, k in ks)
+    lines += ["", "Average per library call (its kernels' average durations times their launches per call):", ""]
+    lines += [f"* {call}: {us / 1e3:.3f} ms" for call, us in per_call.items()]
     lines.append("")
     out = os.path.join(ROOT, "profiles", name + ".md")
     with open(out, "w") as f:
@@ -1091,10 +1113,9 @@ def summarize_trace(trace_dir, name, command):
     print("\n".join(lines))
 
 
-CLOCK_KERNELS = [("attn_bf16_kernel", "attn_bf16_kernel", "sparse_attn"),
-                 ("mass_bf16_kernel", "mass_bf16_kernel", "block_mass"),
-                 ("dense_bf16_kernel<128, false>", "dense_bf16_kernel", "dense_attn_mass"),
-                 ("dense_bf16_kernelILi128ELb0", "dense_bf16_kernel", "dense_attn_mass")]
+CLOCK_KERNELS = [(_ATTN, "attn_bf16_kernel", "sparse_attn"),
+                 (r"mass_bf16_kernel", "mass_bf16_kernel", "block_mass"),
+                 (_DENSE, "dense_bf16_kernel", "dense_attn_mass")]
 N_XCD, N_SE = 8, 32          # MI355X: 8 XCDs, 4 shader engines each
 PEAK_CLOCK_GHZ = 2.4         # the clock the published 2.5 PFLOP/s bf16 peak assumes
 
@@ -1107,14 +1128,14 @@ def summarize_clock(pmc_dir, trace_dir, name, commands):
     import csv
     pmc = {}
     for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
-        lab = next((k for frag, k, _ in CLOCK_KERNELS if frag in r["Kernel_Name"]), None)
+        lab = (kernel_label(r["Kernel_Name"], CLOCK_KERNELS) or (None,))[0]
         if lab is None:
             continue
         d = pmc.setdefault(lab, {}).setdefault(r["Dispatch_Id"], {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     durs = {}
     for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
-        lab = next((k for frag, k, _ in CLOCK_KERNELS if frag in r["Kernel_Name"]), None)
+        lab = (kernel_label(r["Kernel_Name"], CLOCK_KERNELS) or (None,))[0]
         if lab is not None:
             durs.setdefault(lab, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     trace = {lab: float(np.median(v)) for lab, v in durs.items()}
@@ -1123,7 +1144,7 @@ def summarize_clock(pmc_dir, trace_dir, name, commands):
     lines += ["    " + c for c in commands.split(" ;; ")]
     lines += ["", "GRBM_GUI_ACTIVE is summed over the 8 XCDs and SQ_BUSY_CYCLES over the 32 shader "
               "engines; both give the busy cycles of one XCD.  Clock = those cycles / the kernel's "
-              f"average duration in the kernel trace (no counters attached).  The published bf16 peak "
+              f"median duration in the kernel trace (no counters attached).  The published bf16 peak "
               f"(2.5 PFLOP/s) assumes {PEAK_CLOCK_GHZ} GHz.", "",
               "| kernel | dispatches | GRBM cycles per XCD (M) | SQ busy cycles per SE (M) | trace median us | "
               "sustained clock GHz | share of the 2.4 GHz rate |",
@@ -1152,7 +1173,7 @@ def summarize_mfma(pmc_dir, name, command):
     import csv
     per = {}
     for r in csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))):
-        lab = next((k for frag, k, _ in CLOCK_KERNELS if frag in r["Kernel_Name"]), None)
+        lab = (kernel_label(r["Kernel_Name"], CLOCK_KERNELS) or (None,))[0]
         if lab is None:
             continue
         d = per.setdefault(lab, {}).setdefault(r["Dispatch_Id"], {})
