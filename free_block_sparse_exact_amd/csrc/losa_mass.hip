@@ -94,8 +94,13 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
     }
 }
 
-// Grid: B*H*nq workgroups of 256*QG threads (QG = R/64 query groups), two
-// waves per SIMD.
+// Grid: one workgroup of 256 threads (four waves) per 64-row query group,
+// B*H*nq*(R/64) in all, three per CU (151 registers: three waves per SIMD).
+// For R = 128 the group writes its partial masses (sums over its 64 rows,
+// not yet divided by the block's rows) to P[half][row][j], and a second
+// kernel adds the two halves: M = (P[0] + P[1]) / rows.  One 512-thread
+// workgroup per 128-row block would leave room for only one workgroup per
+// CU, two waves per SIMD.
 //
 // Reference.  The four waves of a query group share one reference per query:
 // the largest score of their first chunks, exchanged through LDS before the
@@ -113,25 +118,26 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
 // maximum; if a block sum or a row total leaves [0, 2^100] (a score ~83 above
 // it; or a non-finite input), the whole workgroup recomputes against the
 // exact maximum of the row (every term <= 1), overwriting its S entries.
-template <int D, int QG>
-__global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
-                                                                     const __bf16* __restrict__ Kp, int nch,
-                                                                     float* __restrict__ S, float* __restrict__ M) {
+template <int D>
+__global__ __launch_bounds__(256, 2) void mass_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
+                                                           const __bf16* __restrict__ Kp, int nch,
+                                                           float* __restrict__ S, float* __restrict__ M,
+                                                           float* __restrict__ P) {
   constexpr float kSumBound = 1.2676506e30f;  // 2^100
-  __shared__ float s_ref[QG][4][64], s_tot[QG][4][64], s_f[QG][4][64];
+  __shared__ float s_ref[4][64], s_tot[4][64], s_f[4][64];
   __shared__ int s_over;
-  extern __shared__ float part[];  // [QG][nk] per-group partial masses (QG > 1)
+  const int hv = g.R / 64;  // query groups per block
   const int rows = g.B * g.H * g.nq;
-  const int task = xcd_task(blockIdx.x, rows);
-  const int bh = task / g.nq, i = task - bh * g.nq;
+  const int task = xcd_task(blockIdx.x, rows * hv);  // = row * hv + group
+  const int row = task / hv, grp = task - row * hv;
+  const int bh = row / g.nq, i = row - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = w >> 2, kw = w & 3;
+  const int lane = threadIdx.x & 63, kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
   const __bf16* Kpbh = Kp + (int64_t)bh * nch * (32 * D);
   const int row0 = i * g.R + grp * 64;
-  float* Sg = S + ((int64_t)task * QG + grp) * g.nk * 64;  // [nk][64] of this query group
+  float* Sg = S + (int64_t)task * g.nk * 64;  // [nk][64] of this query group
 
   QTile<D> q;
   q.load(Qbh, g.qs[2], row0, g.N, lr, lg);
@@ -154,14 +160,14 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
   auto common_ref = [&]() {
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
-      float mm = s_ref[grp][0][qt * 16 + lr];
+      float mm = s_ref[0][qt * 16 + lr];
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) mm = fmaxf(mm, s_ref[grp][ww][qt * 16 + lr]);
+      for (int ww = 1; ww < 4; ++ww) mm = fmaxf(mm, s_ref[ww][qt * 16 + lr]);
       m[qt] = mm;
     }
   };
   auto publish_ref = [&](const float (&mx)[4]) {  // lane (lg, lr) holds query lg*16 + lr's entry
-    s_ref[grp][kw][lane] = (lg == 0 ? mx[0] : lg == 1 ? mx[1] : lg == 2 ? mx[2] : mx[3]) * c;
+    s_ref[kw][lane] = (lg == 0 ? mx[0] : lg == 1 ? mx[1] : lg == 2 ? mx[2] : mx[3]) * c;
   };
 
   // One sweep over my chunks against m (acc0: the scores of chunk 0 when
@@ -268,28 +274,32 @@ __global__ __launch_bounds__(256 * QG, 2 / QG) void mass_bf16_kernel(const Geom 
   // Row totals: the four key groups' totals against the common reference add
   // up directly; the factor for the query this lane stored is 1 / total (0
   // for padding rows).
-  s_tot[grp][kw][lane] = tot;
+  s_tot[kw][lane] = tot;
   __syncthreads();
   float f = 0.f;
   {
-    const float l = (s_tot[grp][0][lane] + s_tot[grp][1][lane]) + (s_tot[grp][2][lane] + s_tot[grp][3][lane]);
+    const float l = (s_tot[0][lane] + s_tot[1][lane]) + (s_tot[2][lane] + s_tot[3][lane]);
     if (row0 + lane < g.N) f = 1.0f / l;
   }
-  s_f[grp][kw][lane] = f;
+  s_f[kw][lane] = f;
   __syncthreads();  // every lane reads all 64 factors of its wave
-  const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
-  float* Mrow = M + (int64_t)task * g.nk;
-  if (QG == 1) blocks_from_sums(Sg, s_f[grp][kw], kw, nb, inv_rows, Mrow, lane);
-  else blocks_from_sums(Sg, s_f[grp][kw], kw, nb, 1.0f, part + grp * g.nk, lane);
-  if (QG > 1) {
-    __syncthreads();
-    for (int j = threadIdx.x; j < g.nk; j += blockDim.x) {
-      float v = part[j];
-#pragma unroll
-      for (int gg = 1; gg < QG; ++gg) v += part[gg * g.nk + j];
-      Mrow[j] = v * inv_rows;
-    }
+  if (hv == 1) {
+    const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
+    blocks_from_sums(Sg, s_f[kw], kw, nb, inv_rows, M + (int64_t)row * g.nk, lane);
+  } else {
+    blocks_from_sums(Sg, s_f[kw], kw, nb, 1.0f, P + ((int64_t)grp * rows + row) * g.nk, lane);
   }
+}
+
+// R = 128: M[row][j] = (P[0][row][j] + P[1][row][j]) / (valid rows of the block).
+__global__ __launch_bounds__(256) void add_groups_kernel(const Geom g, const float* __restrict__ P,
+                                                         float* __restrict__ M) {
+  const int64_t n = (int64_t)g.rows() * g.nk;
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= n) return;
+  const int i = (int)((k / g.nk) % g.nq);
+  const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
+  M[k] = (P[k] + P[n + k]) * inv_rows;
 }
 
 // ------------------------------------------------------------------ SIMT path
@@ -401,40 +411,50 @@ hipError_t launch_simt(const Geom& g, const void* Q, const void* K, float* M, fl
 }
 
 template <int D>
-hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* S, __bf16* Kp,
+hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* S, __bf16* Kp, float* P,
                        hipStream_t st) {
   const int nch = packed_chunks(g);
   hipLaunchKernelGGL((pack_kv_kernel<D, false>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)nullptr, Kp, (__bf16*)nullptr, nch);
-  if (g.R == 64)
-    hipLaunchKernelGGL((mass_bf16_kernel<D, 1>), dim3(g.rows()), dim3(256), 0, st, g, (const __bf16*)Q,
-                       (const __bf16*)Kp, nch, S, M);
-  else
-    hipLaunchKernelGGL((mass_bf16_kernel<D, 2>), dim3(g.rows()), dim3(512), (size_t)2 * g.nk * sizeof(float), st,
-                       g, (const __bf16*)Q, (const __bf16*)Kp, nch, S, M);
+  const int hv = g.R / 64;
+  hipLaunchKernelGGL((mass_bf16_kernel<D>), dim3(g.rows() * hv), dim3(256), 0, st, g, (const __bf16*)Q,
+                     (const __bf16*)Kp, nch, S, M, P);
+  if (hv > 1) {
+    const int64_t n = (int64_t)g.rows() * g.nk;
+    hipLaunchKernelGGL(add_groups_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g, (const float*)P,
+                       M);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Workspace.  Matrix-core path: per-(query row, key block) sums S, fp32
-// [B*H*nq][R/64][nk][64], then the packed K.  SIMT path: per row the maximum
-// score (log2 units) and the sum of 2^(s - max), fp32 pairs [B*H][N_alloc].
+// [B*H*nq][R/64][nk][64], then the packed K, then (R = 128) the two query
+// groups' partial masses P, fp32 [2][B*H*nq][nk].  SIMT path: per row the
+// maximum score (log2 units) and the sum of 2^(s - max), fp32 pairs
+// [B*H][N_alloc].
 static size_t mass_s_bytes(const Geom& g) {
   return align_up((size_t)g.B * g.H * g.nq * (g.R / 64) * g.nk * 64 * sizeof(float), 256);
 }
+static size_t mass_kp_bytes(const Geom& g) {
+  return align_up((size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t), 256);
+}
 
 size_t mass_ws_bytes(const Geom& g) {
-  if (mfma_path(g)) return mass_s_bytes(g) + (size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t);
+  if (mfma_path(g))
+    return mass_s_bytes(g) + mass_kp_bytes(g) + (g.R == 64 ? 0 : (size_t)2 * g.rows() * g.nk * sizeof(float));
   return (size_t)g.B * g.H * g.Na * sizeof(float2);
 }
 
 hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, void* ws,
                              hipStream_t stream) {
   if (mfma_path(g)) {
-    float* S = reinterpret_cast<float*>(ws);
-    __bf16* Kp = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(ws) + mass_s_bytes(g));
-    return g.D == 128 ? launch_mfma<128>(g, Q, K, M, S, Kp, stream) : launch_mfma<64>(g, Q, K, M, S, Kp, stream);
+    char* base = reinterpret_cast<char*>(ws);
+    float* S = reinterpret_cast<float*>(base);
+    __bf16* Kp = reinterpret_cast<__bf16*>(base + mass_s_bytes(g));
+    float* P = g.R == 64 ? nullptr : reinterpret_cast<float*>(base + mass_s_bytes(g) + mass_kp_bytes(g));
+    return g.D == 128 ? launch_mfma<128>(g, Q, K, M, S, Kp, P, stream) : launch_mfma<64>(g, Q, K, M, S, Kp, P, stream);
   }
   float2* ml = reinterpret_cast<float2*>(ws);
   if (g.bf16)

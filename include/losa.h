@@ -114,7 +114,7 @@ const char* losa_status_string(losa_status status);
  * bf16 matrix-core path (head_dim 64/128, q_block 64/128): one pass over
  * K -- per query row and key block, the sum of exp(s - m) against one fixed
  * per-row reference m (the largest score among the first keys each wave of
- * the row's workgroup reads) goes to the workspace; the row total is the sum
+ * the row's 64-row group reads) goes to the workspace; the row total is the sum
  * of those sums, and M the sums divided by it.  Rows whose sums leave a safe
  * range (a later score far above m) are redone against their exact maximum.
  * Other shapes: two passes over K (the row maximum and the sum against it,
@@ -132,7 +132,9 @@ const char* losa_status_string(losa_status status);
  * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
  * ws: at least *bytes from losa_block_mass_workspace.  bf16 matrix-core path:
  *    per-(query row, key block) partial sums, 4 * batch*heads*n_q*q_block*n_k
- *    bytes, then K repacked in 32-token chunks.  The partial sums grow with
+ *    bytes, then K repacked in 32-token chunks, then (q_block 128) the two
+ *    64-row groups' partial masses, 8 * batch*heads*n_q*n_k bytes (166 MB
+ *    for 24 heads x 118800 tokens with 128-token blocks).  The partial sums grow with
  *    the square of the token count: 0.81 GB for 12 heads x 32760 tokens
  *    (64-token blocks), 14.3 GB for 40 heads x 75600 tokens (64-token
  *    blocks), 10.6 GB for 24 heads x 118800 tokens (128-token blocks) and
