@@ -94,13 +94,15 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
     }
 }
 
-// Grid: one workgroup of 256 threads (four waves) per 64-row query group,
-// B*H*nq*(R/64) in all, three per CU (151 registers: three waves per SIMD).
-// For R = 128 the group writes its partial masses (sums over its 64 rows,
-// not yet divided by the block's rows) to P[half][row][j], and a second
-// kernel adds the two halves: M = (P[0] + P[1]) / rows.  One 512-thread
-// workgroup per 128-row block would leave room for only one workgroup per
-// CU, two waves per SIMD.
+// Grid: one workgroup of 256 threads (four waves) per query block, B*H*nq
+// in all, three per CU (151 registers: three waves per SIMD).  QG = R/64
+// query groups of 64 rows; each has WPG = 4/QG waves, which split the key
+// blocks between them (wave kw of a group takes blocks kw, kw + WPG, ...).
+// With R = 128 the two groups' waves read the same K chunks side by side on
+// one CU, and their partial masses are added in LDS.  (Eight waves for
+// R = 128, four per group, leave room for one workgroup per CU: two waves
+// per SIMD; one workgroup per group instead streams every K chunk to two
+// CUs, twice the traffic beyond L2.)
 //
 // Reference.  The four waves of a query group share one reference per query:
 // the largest score of their first chunks, exchanged through LDS before the
@@ -118,35 +120,35 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
 // maximum; if a block sum or a row total leaves [0, 2^100] (a score ~83 above
 // it; or a non-finite input), the whole workgroup recomputes against the
 // exact maximum of the row (every term <= 1), overwriting its S entries.
-template <int D>
+template <int D, int QG>
 __global__ __launch_bounds__(256, 2) void mass_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
                                                            const __bf16* __restrict__ Kp, int nch,
-                                                           float* __restrict__ S, float* __restrict__ M,
-                                                           float* __restrict__ P) {
+                                                           float* __restrict__ S, float* __restrict__ M) {
+  constexpr int WPG = 4 / QG;                 // waves per query group
   constexpr float kSumBound = 1.2676506e30f;  // 2^100
-  __shared__ float s_ref[4][64], s_tot[4][64], s_f[4][64];
+  __shared__ float s_ref[QG][WPG][64], s_tot[QG][WPG][64], s_f[QG][WPG][64];
   __shared__ int s_over;
-  const int hv = g.R / 64;  // query groups per block
+  extern __shared__ float part[];  // [QG][nk] the groups' partial masses (QG > 1)
   const int rows = g.B * g.H * g.nq;
-  const int task = xcd_task(blockIdx.x, rows * hv);  // = row * hv + group
-  const int row = task / hv, grp = task - row * hv;
+  const int row = xcd_task(blockIdx.x, rows);
   const int bh = row / g.nq, i = row - bh * g.nq;
   const int b = bh / g.H, h = bh - b * g.H;
-  const int lane = threadIdx.x & 63, kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w / WPG, kw = w - grp * WPG;
   const int lr = lane & 15, lg = lane >> 4;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
   const __bf16* Kpbh = Kp + (int64_t)bh * nch * (32 * D);
   const int row0 = i * g.R + grp * 64;
-  float* Sg = S + (int64_t)task * g.nk * 64;  // [nk][64] of this query group
+  float* Sg = S + ((int64_t)row * QG + grp) * g.nk * 64;  // [nk][64] of this query group
 
   QTile<D> q;
   q.load(Qbh, g.qs[2], row0, g.N, lr, lg);
 
   const float c = g.scale_log2;
   const int sub = g.C / 32, sub_shift = __builtin_ctz(sub);
-  const int nb = g.nk > kw ? (g.nk - kw + 3) / 4 : 0;  // my key blocks kw, kw+4, ...
-  const int nu = nb * sub;                              // their 32-key chunks
-  auto chunk_kb = [&](int u) { return (kw + 4 * (u >> sub_shift)) * g.C + 32 * (u & (sub - 1)); };
+  const int nb = g.nk > kw ? (g.nk - kw + WPG - 1) / WPG : 0;  // my key blocks kw, kw+WPG, ...
+  const int nu = nb * sub;                                      // their 32-key chunks
+  auto chunk_kb = [&](int u) { return (kw + WPG * (u >> sub_shift)) * g.C + 32 * (u & (sub - 1)); };
 
   // Block sums: lane (lg, lr) holds partial sums over its keys for queries
   // qt*16 + lr, qt = 0..3; the totals over the four lane groups are formed so
@@ -155,19 +157,19 @@ __global__ __launch_bounds__(256, 2) void mass_bf16_kernel(const Geom g, const _
   // 16 away.
   auto reduce_mine = [&](const float (&v)[4]) -> float { return rows_sum_own(v); };
   // The query group's common reference for the queries of this lane's four
-  // tiles, from the four waves' entries in s_ref (scaled, log2 units).
+  // tiles, from its waves' entries in s_ref (scaled, log2 units).
   float m[4];
   auto common_ref = [&]() {
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
-      float mm = s_ref[0][qt * 16 + lr];
+      float mm = s_ref[grp][0][qt * 16 + lr];
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) mm = fmaxf(mm, s_ref[ww][qt * 16 + lr]);
+      for (int ww = 1; ww < WPG; ++ww) mm = fmaxf(mm, s_ref[grp][ww][qt * 16 + lr]);
       m[qt] = mm;
     }
   };
   auto publish_ref = [&](const float (&mx)[4]) {  // lane (lg, lr) holds query lg*16 + lr's entry
-    s_ref[kw][lane] = (lg == 0 ? mx[0] : lg == 1 ? mx[1] : lg == 2 ? mx[2] : mx[3]) * c;
+    s_ref[grp][kw][lane] = (lg == 0 ? mx[0] : lg == 1 ? mx[1] : lg == 2 ? mx[2] : mx[3]) * c;
   };
 
   // One sweep over my chunks against m (acc0: the scores of chunk 0 when
@@ -180,13 +182,16 @@ __global__ __launch_bounds__(256, 2) void mass_bf16_kernel(const Geom g, const _
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
       const float nm = -m[qt];
-      float sum = 0.f;
+      // Seeded with the first term rather than 0 (0 + x is not folded, since
+      // it would differ for x = -0): four fewer additions per chunk, the same
+      // sums (no term is -0).
+      float sum = fast_exp2(__builtin_fmaf(acc[0][qt][0], c, nm));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
+      for (int e = 1; e < 8; ++e) sum += fast_exp2(__builtin_fmaf(acc[e >> 2][qt][e & 3], c, nm));
       blk[qt] += sum;
     }
     if ((u & (sub - 1)) == sub - 1) {  // block complete: store this lane's query's sum, add it to the total
-      const int j = kw + 4 * (u >> sub_shift);
+      const int j = kw + WPG * (u >> sub_shift);
       const float v = reduce_mine(blk);
       tot += v;
       over |= !(v <= kSumBound);
@@ -274,32 +279,35 @@ __global__ __launch_bounds__(256, 2) void mass_bf16_kernel(const Geom g, const _
   // Row totals: the four key groups' totals against the common reference add
   // up directly; the factor for the query this lane stored is 1 / total (0
   // for padding rows).
-  s_tot[kw][lane] = tot;
+  s_tot[grp][kw][lane] = tot;
   __syncthreads();
   float f = 0.f;
   {
-    const float l = (s_tot[0][lane] + s_tot[1][lane]) + (s_tot[2][lane] + s_tot[3][lane]);
+    const float(&t)[WPG][64] = s_tot[grp];
+    float l;
+    if constexpr (WPG == 4)
+      l = (t[0][lane] + t[1][lane]) + (t[2][lane] + t[3][lane]);
+    else
+      l = t[0][lane] + t[1][lane];
     if (row0 + lane < g.N) f = 1.0f / l;
   }
-  s_f[kw][lane] = f;
+  s_f[grp][kw][lane] = f;
   __syncthreads();  // every lane reads all 64 factors of its wave
-  if (hv == 1) {
-    const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
-    blocks_from_sums(Sg, s_f[kw], kw, nb, inv_rows, M + (int64_t)row * g.nk, lane);
-  } else {
-    blocks_from_sums(Sg, s_f[kw], kw, nb, 1.0f, P + ((int64_t)grp * rows + row) * g.nk, lane);
-  }
-}
-
-// R = 128: M[row][j] = (P[0][row][j] + P[1][row][j]) / (valid rows of the block).
-__global__ __launch_bounds__(256) void add_groups_kernel(const Geom g, const float* __restrict__ P,
-                                                         float* __restrict__ M) {
-  const int64_t n = (int64_t)g.rows() * g.nk;
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (k >= n) return;
-  const int i = (int)((k / g.nk) % g.nq);
   const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
-  M[k] = (P[k] + P[n + k]) * inv_rows;
+  float* Mrow = M + (int64_t)row * g.nk;
+  auto block_of = [kw](int bb) { return kw + WPG * bb; };
+  if (QG == 1) {
+    blocks_from_sums(Sg, s_f[grp][kw], nb, inv_rows, Mrow, lane, block_of);
+  } else {
+    blocks_from_sums(Sg, s_f[grp][kw], nb, 1.0f, part + grp * g.nk, lane, block_of);
+    __syncthreads();
+    for (int j = threadIdx.x; j < g.nk; j += blockDim.x) {
+      float v = part[j];
+#pragma unroll
+      for (int gg = 1; gg < QG; ++gg) v += part[gg * g.nk + j];
+      Mrow[j] = v * inv_rows;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ SIMT path
@@ -411,50 +419,40 @@ hipError_t launch_simt(const Geom& g, const void* Q, const void* K, float* M, fl
 }
 
 template <int D>
-hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* S, __bf16* Kp, float* P,
+hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, float* S, __bf16* Kp,
                        hipStream_t st) {
   const int nch = packed_chunks(g);
   hipLaunchKernelGGL((pack_kv_kernel<D, false>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)nullptr, Kp, (__bf16*)nullptr, nch);
-  const int hv = g.R / 64;
-  hipLaunchKernelGGL((mass_bf16_kernel<D>), dim3(g.rows() * hv), dim3(256), 0, st, g, (const __bf16*)Q,
-                     (const __bf16*)Kp, nch, S, M, P);
-  if (hv > 1) {
-    const int64_t n = (int64_t)g.rows() * g.nk;
-    hipLaunchKernelGGL(add_groups_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g, (const float*)P,
-                       M);
-  }
+  if (g.R == 64)
+    hipLaunchKernelGGL((mass_bf16_kernel<D, 1>), dim3(g.rows()), dim3(256), 0, st, g, (const __bf16*)Q,
+                       (const __bf16*)Kp, nch, S, M);
+  else
+    hipLaunchKernelGGL((mass_bf16_kernel<D, 2>), dim3(g.rows()), dim3(256), (size_t)2 * g.nk * sizeof(float), st,
+                       g, (const __bf16*)Q, (const __bf16*)Kp, nch, S, M);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Workspace.  Matrix-core path: per-(query row, key block) sums S, fp32
-// [B*H*nq][R/64][nk][64], then the packed K, then (R = 128) the two query
-// groups' partial masses P, fp32 [2][B*H*nq][nk].  SIMT path: per row the
-// maximum score (log2 units) and the sum of 2^(s - max), fp32 pairs
-// [B*H][N_alloc].
+// [B*H*nq][R/64][nk][64], then the packed K.  SIMT path: per row the maximum
+// score (log2 units) and the sum of 2^(s - max), fp32 pairs [B*H][N_alloc].
 static size_t mass_s_bytes(const Geom& g) {
   return align_up((size_t)g.B * g.H * g.nq * (g.R / 64) * g.nk * 64 * sizeof(float), 256);
 }
-static size_t mass_kp_bytes(const Geom& g) {
-  return align_up((size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t), 256);
-}
 
 size_t mass_ws_bytes(const Geom& g) {
-  if (mfma_path(g))
-    return mass_s_bytes(g) + mass_kp_bytes(g) + (g.R == 64 ? 0 : (size_t)2 * g.rows() * g.nk * sizeof(float));
+  if (mfma_path(g)) return mass_s_bytes(g) + (size_t)g.B * g.H * packed_chunks(g) * 32 * g.D * sizeof(uint16_t);
   return (size_t)g.B * g.H * g.Na * sizeof(float2);
 }
 
 hipError_t launch_block_mass(const Geom& g, const void* Q, const void* K, float* M, void* ws,
                              hipStream_t stream) {
   if (mfma_path(g)) {
-    char* base = reinterpret_cast<char*>(ws);
-    float* S = reinterpret_cast<float*>(base);
-    __bf16* Kp = reinterpret_cast<__bf16*>(base + mass_s_bytes(g));
-    float* P = g.R == 64 ? nullptr : reinterpret_cast<float*>(base + mass_s_bytes(g) + mass_kp_bytes(g));
-    return g.D == 128 ? launch_mfma<128>(g, Q, K, M, S, Kp, P, stream) : launch_mfma<64>(g, Q, K, M, S, Kp, P, stream);
+    float* S = reinterpret_cast<float*>(ws);
+    __bf16* Kp = reinterpret_cast<__bf16*>(reinterpret_cast<char*>(ws) + mass_s_bytes(g));
+    return g.D == 128 ? launch_mfma<128>(g, Q, K, M, S, Kp, stream) : launch_mfma<64>(g, Q, K, M, S, Kp, stream);
   }
   float2* ml = reinterpret_cast<float2*>(ws);
   if (g.bf16)

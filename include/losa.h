@@ -132,9 +132,7 @@ const char* losa_status_string(losa_status status);
  * M: fp32 [batch, heads, n_q, n_k], contiguous (written completely).
  * ws: at least *bytes from losa_block_mass_workspace.  bf16 matrix-core path:
  *    per-(query row, key block) partial sums, 4 * batch*heads*n_q*q_block*n_k
- *    bytes, then K repacked in 32-token chunks, then (q_block 128) the two
- *    64-row groups' partial masses, 8 * batch*heads*n_q*n_k bytes (166 MB
- *    for 24 heads x 118800 tokens with 128-token blocks).  The partial sums grow with
+ *    bytes, then K repacked in 32-token chunks.  The partial sums grow with
  *    the square of the token count: 0.81 GB for 12 heads x 32760 tokens
  *    (64-token blocks), 14.3 GB for 40 heads x 75600 tokens (64-token
  *    blocks), 10.6 GB for 24 heads x 118800 tokens (128-token blocks) and
