@@ -94,15 +94,17 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
     }
 }
 
-// Grid: one workgroup of 256 threads (four waves) per query block, B*H*nq
-// in all, three per CU (151 registers: three waves per SIMD).  QG = R/64
-// query groups of 64 rows; each has WPG = 4/QG waves, which split the key
-// blocks between them (wave kw of a group takes blocks kw, kw + WPG, ...).
-// With R = 128 the two groups' waves read the same K chunks side by side on
-// one CU, and their partial masses are added in LDS.  (Eight waves for
-// R = 128, four per group, leave room for one workgroup per CU: two waves
-// per SIMD; one workgroup per group instead streams every K chunk to two
-// CUs, twice the traffic beyond L2.)
+// Grid: workgroups of 256 threads (four waves), three per CU (151
+// registers: three waves per SIMD).  A workgroup holds two query groups of
+// 64 rows, two waves each; the two waves of a group split the key blocks
+// (wave kw takes blocks kw, kw + 2, ...), so both groups read every K chunk
+// side by side on one CU.  R = 128: the groups are the halves of one query
+// block (B*H*nq workgroups) and their partial masses are added in LDS.
+// R = 64 (kPair): the groups are two neighbouring query blocks of one head
+// (B*H*ceil(nq/2) workgroups), each writing its own row of M.  (Eight waves
+// for R = 128, four per group, leave room for one workgroup per CU: two
+// waves per SIMD; one workgroup per group streams every K chunk to two CUs,
+// twice the traffic beyond L2.)
 //
 // Reference.  The four waves of a query group share one reference per query:
 // the largest score of their first chunks, exchanged through LDS before the
@@ -120,33 +122,50 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
 // maximum; if a block sum or a row total leaves [0, 2^100] (a score ~83 above
 // it; or a non-finite input), the whole workgroup recomputes against the
 // exact maximum of the row (every term <= 1), overwriting its S entries.
-template <int D, int QG>
+template <int D, bool kPair>
 __global__ __launch_bounds__(256, 2) void mass_bf16_kernel(const Geom g, const __bf16* __restrict__ Q,
                                                            const __bf16* __restrict__ Kp, int nch,
                                                            float* __restrict__ S, float* __restrict__ M) {
-  constexpr int WPG = 4 / QG;                 // waves per query group
+  constexpr int QG = 2, WPG = 2;              // query groups, waves per group
   constexpr float kSumBound = 1.2676506e30f;  // 2^100
   __shared__ float s_ref[QG][WPG][64], s_tot[QG][WPG][64], s_f[QG][WPG][64];
   __shared__ int s_over;
-  extern __shared__ float part[];  // [QG][nk] the groups' partial masses (QG > 1)
-  const int rows = g.B * g.H * g.nq;
-  const int row = xcd_task(blockIdx.x, rows);
-  const int bh = row / g.nq, i = row - bh * g.nq;
-  const int b = bh / g.H, h = bh - b * g.H;
+  extern __shared__ float part[];  // [QG][nk] the halves' partial masses (R = 128)
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = w / WPG, kw = w - grp * WPG;
   const int lr = lane & 15, lg = lane >> 4;
+  // row: the query block whose row of M (and, with kPair, S) this group
+  // serves; i: its index in the head; valid: false for the missing second
+  // block of a head with odd n_q (its waves do no work).
+  int row, bh, i;
+  bool valid = true;
+  if constexpr (kPair) {
+    const int nq2 = (g.nq + 1) >> 1;
+    const int task = xcd_task(blockIdx.x, g.B * g.H * nq2);
+    bh = task / nq2;
+    i = 2 * (task - bh * nq2) + grp;
+    valid = i < g.nq;
+    row = bh * g.nq + i;
+  } else {
+    row = xcd_task(blockIdx.x, g.B * g.H * g.nq);
+    bh = row / g.nq;
+    i = row - bh * g.nq;
+  }
+  const int b = bh / g.H, h = bh - b * g.H;
   const __bf16* Qbh = Q + b * g.qs[0] + h * g.qs[1];
   const __bf16* Kpbh = Kp + (int64_t)bh * nch * (32 * D);
-  const int row0 = i * g.R + grp * 64;
-  float* Sg = S + ((int64_t)row * QG + grp) * g.nk * 64;  // [nk][64] of this query group
+  const int row0 = kPair ? i * g.R : i * g.R + grp * 64;
+  // [nk][64] of this query group
+  float* Sg = S + (kPair ? (int64_t)row : (int64_t)row * QG + grp) * g.nk * 64;
 
   QTile<D> q;
-  q.load(Qbh, g.qs[2], row0, g.N, lr, lg);
+  // A missing block reads rows 0..63 (allocated for every head) as padding:
+  // all of them zero, no access beyond n_q * R.
+  q.load(Qbh, g.qs[2], valid ? row0 : 0, valid ? g.N : 0, lr, lg);
 
   const float c = g.scale_log2;
   const int sub = g.C / 32, sub_shift = __builtin_ctz(sub);
-  const int nb = g.nk > kw ? (g.nk - kw + WPG - 1) / WPG : 0;  // my key blocks kw, kw+WPG, ...
+  const int nb = valid && g.nk > kw ? (g.nk - kw + WPG - 1) / WPG : 0;  // my key blocks kw, kw+WPG, ...
   const int nu = nb * sub;                                      // their 32-key chunks
   auto chunk_kb = [&](int u) { return (kw + WPG * (u >> sub_shift)) * g.C + 32 * (u & (sub - 1)); };
 
@@ -283,21 +302,16 @@ __global__ __launch_bounds__(256, 2) void mass_bf16_kernel(const Geom g, const _
   __syncthreads();
   float f = 0.f;
   {
-    const float(&t)[WPG][64] = s_tot[grp];
-    float l;
-    if constexpr (WPG == 4)
-      l = (t[0][lane] + t[1][lane]) + (t[2][lane] + t[3][lane]);
-    else
-      l = t[0][lane] + t[1][lane];
+    const float l = s_tot[grp][0][lane] + s_tot[grp][1][lane];
     if (row0 + lane < g.N) f = 1.0f / l;
   }
   s_f[grp][kw][lane] = f;
   __syncthreads();  // every lane reads all 64 factors of its wave
-  const float inv_rows = 1.0f / (float)min(g.R, g.N - i * g.R);
+  const float inv_rows = valid ? 1.0f / (float)min(g.R, g.N - i * g.R) : 0.f;
   float* Mrow = M + (int64_t)row * g.nk;
   auto block_of = [kw](int bb) { return kw + WPG * bb; };
-  if (QG == 1) {
-    blocks_from_sums(Sg, s_f[grp][kw], nb, inv_rows, Mrow, lane, block_of);
+  if constexpr (kPair) {
+    blocks_from_sums(Sg, s_f[grp][kw], nb, inv_rows, Mrow, lane, block_of);  // nothing when !valid (nb = 0)
   } else {
     blocks_from_sums(Sg, s_f[grp][kw], nb, 1.0f, part + grp * g.nk, lane, block_of);
     __syncthreads();
@@ -425,11 +439,11 @@ hipError_t launch_mfma(const Geom& g, const void* Q, const void* K, float* M, fl
   hipLaunchKernelGGL((pack_kv_kernel<D, false>), dim3((unsigned)(nch / 2), g.B * g.H), dim3(256), 0, st, g,
                      (const __bf16*)K, (const __bf16*)nullptr, Kp, (__bf16*)nullptr, nch);
   if (g.R == 64)
-    hipLaunchKernelGGL((mass_bf16_kernel<D, 1>), dim3(g.rows()), dim3(256), 0, st, g, (const __bf16*)Q,
-                       (const __bf16*)Kp, nch, S, M);
+    hipLaunchKernelGGL((mass_bf16_kernel<D, true>), dim3(g.B * g.H * ((g.nq + 1) / 2)), dim3(256), 0, st, g,
+                       (const __bf16*)Q, (const __bf16*)Kp, nch, S, M);
   else
-    hipLaunchKernelGGL((mass_bf16_kernel<D, 2>), dim3(g.rows()), dim3(256), (size_t)2 * g.nk * sizeof(float), st,
-                       g, (const __bf16*)Q, (const __bf16*)Kp, nch, S, M);
+    hipLaunchKernelGGL((mass_bf16_kernel<D, false>), dim3(g.rows()), dim3(256), (size_t)2 * g.nk * sizeof(float),
+                       st, g, (const __bf16*)Q, (const __bf16*)Kp, nch, S, M);
   return hipGetLastError();
 }
 
