@@ -41,3 +41,32 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+@pytest.mark.parametrize("name, short, call", [
+    ("void losa::(anonymous namespace)::attn_bf16_kernel<128, false>(losa::Geom, ...)",
+     "attn_bf16_kernel", "losa_sparse_attn"),
+    ("void losa::(anonymous namespace)::attn_bf16_kernel<128, true>(losa::Geom, ...)",
+     "attn_bf16_kernel (in-pass thresholding)", "losa_sparse_attn_threshold"),
+    ("_ZN4losa12_GLOBAL__N_116attn_bf16_kernelILi64ELb1EEEvNS_4GeomE",
+     "attn_bf16_kernel (in-pass thresholding)", "losa_sparse_attn_threshold"),
+    ("_ZN4losa14pack_kv_kernelILi128ELb0EEEvNS_4GeomEPKDF16bS3_PDF16bS4_i",
+     "pack_kv_kernel (K only)", "losa_block_mass"),
+    ("void losa::(anonymous namespace)::dense_bf16_kernel<128, true>(losa::Geom, ...)",
+     "dense_bf16_kernel (lists)", "losa_sparse_attn_mass"),
+    ("void losa::(anonymous namespace)::dense_bf16_kernel<128, false>(losa::Geom, ...)",
+     "dense_bf16_kernel", "losa_dense_attn_mass"),
+    ("_ZN4losa12_GLOBAL__N_111pool_kernelIDF16bLi128EdEEvNS_4GeomEPKT_llliiPT1_",
+     "pool_kernel (fp64 block means)", "losa_sparse_attn_threshold"),
+    ("_ZN4losa12_GLOBAL__N_111pool_kernelIDF16bLi128EfEEvNS_4GeomEPKT_llliiPT1_",
+     "pool_kernel", "losa_pooled_mass"),
+    ("void losa::(anonymous namespace)::threshold_kernel<true>(losa::Geom, ...)",
+     "threshold_kernel (indices)", "losa_select_threshold"),
+])
+def test_trace_kernel_names_map_to_their_calls(name, short, call):
+    assert bench.kernel_label(name, bench.TRACE_KERNELS) == (short, call)
+
+
+def test_clock_kernels_skip_the_in_pass_instance():
+    assert bench.kernel_label("attn_bf16_kernel<128, true>(...)", bench.CLOCK_KERNELS) is None
+    assert bench.kernel_label("attn_bf16_kernel<128, false>(...)", bench.CLOCK_KERNELS)[0] == "attn_bf16_kernel"
