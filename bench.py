@@ -270,7 +270,7 @@ def main():
                     help="run only the first HEADS heads of the workload (one GPU's share under head sharding)")
     ap.add_argument("--cpu-rows", type=int, default=16, help="query blocks in the oracle CPU baseline (0: skip)")
     ap.add_argument("--legs", choices=("all", "step"), default="all",
-                    help="step: time the step only (no construction, reduced-search, refresh, graph and routing "
+                    help="step: time the step only (no construction, reduced-search, refresh, selector-cache, graph and routing "
                          "legs), e.g. under a profiler")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--refresh-tau", type=float, default=0.75,
@@ -547,6 +547,44 @@ def other_legs(F, torch, q, k, v, bufs, geom, wl, stream, dev, kernels, kept_flo
                                    "note": "sparse attention plus the exact masses within the lists (reduced "
                                            "search); kept-block flops; not in ms_per_step"}
     kernels.update(refresh_calls(F, torch, q, k, bufs, geom, wl, stream, dev))
+    kernels["select_cache"] = select_cache_leg(F, torch, bufs, geom, wl, stream, dev)
+
+
+def select_cache_leg(F, torch, bufs, geom, wl, stream, dev, reps=10):
+    """The selector alone, cold and warm.  Cold: a 512 MB buffer (twice the
+    256 MB Infinity Cache) is overwritten before each call, so the masses come
+    from HBM.  Warm: the call repeated back to back (in the step, the masses
+    were written by the mass kernel just before)."""
+    N, R, C, Na = wl.tokens, wl.block, wl.key_block, wl.tokens_alloc
+    nnz = int(bufs.row_ptr[-1].item())
+    sel_bytes = 4.0 * geom.rows * geom.n_k + 4.0 * nnz + 8.0 * geom.rows
+
+    def sel():
+        F.losa_select(bufs.M, wl.p, N, R, C, tokens_alloc=Na, row_ptr=bufs.row_ptr, col_idx=bufs.col_idx,
+                      order=bufs.order, ws=bufs.ws_sel, stream=stream)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = {}
+    for kind in ("cold", "warm"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        sel()
+        for e0, e1 in evs:
+            if kind == "cold":
+                flush.fill_(1)  # a fill kernel on the same stream
+            e0.record(stream)
+            sel()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+        gbs = sel_bytes / (ms * 1e-3) / 1e9
+        out[f"{kind}_ms"] = ms
+        out[f"{kind}_GBps"] = gbs
+        out[f"{kind}_frac_hbm_peak"] = gbs / PEAK_HBM_GBS
+    del flush
+    out["algorithmic_bytes"] = sel_bytes
+    out["note"] = ("median of %d calls; cold: a 512 MB buffer overwritten before each call; not in ms_per_step"
+                   % reps)
+    return out
 
 
 ROUTING_P = (0.9, 0.95, 0.99, 0.995, 0.999)
