@@ -7,14 +7,16 @@
 // with s = q.k * scale and lse_q the log-sum-exp of row q over all valid keys.
 //
 // bf16 matrix-core path (d in {64, 128}, R in {64, 128}): ONE pass over K.
-// A workgroup owns one query block (R/64 groups of 64 rows, four waves per
-// group); the waves of a group split the KEY BLOCKS (wave w takes blocks
-// j = w, w+4, ...).  For every query the group fixes one reference m, the
-// largest score of the waves' first chunks (log2 units; scores are
-// pre-multiplied by scale*log2(e)); each wave sums 2^(s*c - m) per key block,
-// writes that per-(query, block) sum to a workspace S and keeps the row
-// total.  Once the four waves' totals are added, the workgroup reads S back:
-//   M[i,j] = (1/rows) * sum_q S[q,j] / total_q.
+// A workgroup holds two query groups of 64 rows (the halves of one 128-row
+// block, or two neighbouring 64-row blocks of one head), two waves each; the
+// two waves of a group split the KEY BLOCKS (wave w takes blocks j = w,
+// w+2, ...).  For every query the group fixes one reference m, the largest
+// score of its waves' first chunks (log2 units; scores are pre-multiplied by
+// scale*log2(e)); each wave sums 2^(s*c - m) per key block, writes that
+// per-(query, block) sum to a workspace S and keeps the row total.  Once
+// the two waves' totals are added, the group reads S back:
+//   M[i,j] = (1/rows) * sum_q S[q,j] / total_q
+// (for a 128-row block, the two halves' sums over their rows added first).
 // The scores and exponentials are computed once (a two-pass form computes
 // both twice); S costs 4 bytes per (query row, key block) of HBM traffic each
 // way.  S^T = K Q^T is formed with 16x16x32 bf16 MFMA: lane l owns query
@@ -106,7 +108,7 @@ __device__ __forceinline__ void mask_tail(int kb, int n_valid, int lg, f32x4 (&a
 // waves per SIMD; one workgroup per group streams every K chunk to two CUs,
 // twice the traffic beyond L2.)
 //
-// Reference.  The four waves of a query group share one reference per query:
+// Reference.  The two waves of a query group share one reference per query:
 // the largest score of their first chunks, exchanged through LDS before the
 // sweep (no headroom).  It is an actual score of the row, so it is at most
 // the row's log-sum-exp: every term 2^(s*c - m) is at least the probability
